@@ -1,0 +1,200 @@
+"""CPU oracle for the routed MoE layer with NVFP4 experts.
+
+TEST INFRASTRUCTURE ONLY: the plain fp64 reference that the GPU library is
+checked against.  Only the tests, the smoke check and the benchmark's CPU
+baseline may import this package; the GPU library never does.  The C source
+(oracle.c / oracle.h) cites, per function, the passage of the pages it
+follows.  This module only marshals numpy arrays to it.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from .build import LIB, build
+
+_lib = None
+_c_i64 = ctypes.c_int64
+_p = ctypes.c_void_p
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        path = os.environ.get("ORACLE_LIB")  # a mutated build, for checking the pins
+        if not path:
+            src = os.path.join(os.path.dirname(LIB), "oracle.c")
+            if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(src):
+                build()
+            path = LIB
+        L = ctypes.CDLL(path)
+        L.oracle_e2m1_value.restype = ctypes.c_double
+        L.oracle_e2m1_value.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3_value.restype = ctypes.c_double
+        L.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+        L.oracle_e2m1_round.restype = ctypes.c_uint8
+        L.oracle_e2m1_round.argtypes = [ctypes.c_double]
+        L.oracle_e4m3_round.restype = ctypes.c_uint8
+        L.oracle_e4m3_round.argtypes = [ctypes.c_double]
+        L.oracle_nvfp4_matrix_bytes.restype = ctypes.c_size_t
+        L.oracle_nvfp4_matrix_bytes.argtypes = [_c_i64, _c_i64]
+        L.oracle_nvfp4_quantize.restype = None
+        L.oracle_nvfp4_quantize.argtypes = [_p, _c_i64, _c_i64, _p, _p, _p]
+        L.oracle_nvfp4_dequantize.restype = None
+        L.oracle_nvfp4_dequantize.argtypes = [_p, _p, ctypes.c_float, _c_i64, _c_i64, _p]
+        L.oracle_router_logits.restype = None
+        L.oracle_router_logits.argtypes = [_p, _c_i64, _c_i64, _p, _c_i64, _p, _p]
+        L.oracle_topk_softmax.restype = None
+        L.oracle_topk_softmax.argtypes = [_p, _c_i64, _c_i64, ctypes.c_int, _p, _p]
+        L.oracle_permute.restype = None
+        L.oracle_permute.argtypes = [_p, _c_i64, _c_i64, ctypes.c_int, _p, _p, _p]
+        L.oracle_swiglu_token.restype = None
+        L.oracle_swiglu_token.argtypes = [_p, _p, _p, _p, _c_i64, _c_i64, _p]
+        L.oracle_moe_layer.restype = ctypes.c_int
+        L.oracle_moe_layer.argtypes = [_p, _c_i64, _c_i64, _c_i64, _p, _p, _p, _c_i64, ctypes.c_int, _p,
+                                       ctypes.c_int, _p, _p, _p, _p, _p, _p, _p, _p]
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def e2m1_value(code):
+    return lib().oracle_e2m1_value(code)
+
+
+def e4m3_value(code):
+    return lib().oracle_e4m3_value(code)
+
+
+def e2m1_round(r):
+    return lib().oracle_e2m1_round(float(r))
+
+
+def e4m3_round(t):
+    return lib().oracle_e4m3_round(float(t))
+
+
+def nvfp4_matrix_bytes(N, K):
+    return lib().oracle_nvfp4_matrix_bytes(N, K)
+
+
+class NVFP4:
+    """One quantised matrix: q [N][K/2] u8, sf [N][K/16] u8, gs fp32."""
+
+    def __init__(self, q, sf, gs):
+        self.q, self.sf, self.gs = q, sf, np.float32(gs)
+
+    @property
+    def shape(self):
+        return (self.q.shape[0], self.q.shape[1] * 2)
+
+
+def nvfp4_quantize(w):
+    w = _c(w, np.float32)
+    N, K = w.shape
+    assert K % 16 == 0
+    q = np.empty((N, K // 2), np.uint8)
+    sf = np.empty((N, K // 16), np.uint8)
+    gs = np.zeros(1, np.float32)
+    lib().oracle_nvfp4_quantize(_ptr(w), N, K, _ptr(q), _ptr(sf), _ptr(gs))
+    return NVFP4(q, sf, gs[0])
+
+
+def nvfp4_dequantize(m):
+    N, K = m.shape
+    out = np.empty((N, K), np.float64)
+    lib().oracle_nvfp4_dequantize(_ptr(_c(m.q, np.uint8)), _ptr(_c(m.sf, np.uint8)), float(m.gs), N, K, _ptr(out))
+    return out
+
+
+def router_logits(x_bf16, wr_bf16, bias=None):
+    x = _c(x_bf16, np.uint16)
+    wr = _c(wr_bf16, np.uint16)
+    T, H = x.shape
+    E = wr.shape[1]
+    b = None if bias is None else _c(bias, np.float32)
+    out = np.empty((T, E), np.float32)
+    lib().oracle_router_logits(_ptr(x), T, H, _ptr(wr), E, _ptr(b), _ptr(out))
+    return out
+
+
+def topk_softmax(logits, k):
+    l = _c(logits, np.float32)
+    T, E = l.shape
+    ids = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float64)
+    lib().oracle_topk_softmax(_ptr(l), T, E, k, _ptr(ids), _ptr(w))
+    return ids, w
+
+
+def permute(ids, E):
+    ids = _c(ids, np.int32)
+    T, k = ids.shape
+    offsets = np.empty(E + 1, np.int32)
+    sp = np.empty(T * k, np.int32)
+    pp = np.empty(T * k, np.int32)
+    lib().oracle_permute(_ptr(ids), T, E, k, _ptr(offsets), _ptr(sp), _ptr(pp))
+    return offsets, sp, pp
+
+
+def swiglu_token(gate, up, down, x_row_bf16):
+    I, H = gate.shape
+    out = np.empty(H, np.float64)
+    lib().oracle_swiglu_token(_ptr(_c(gate, np.float64)), _ptr(_c(up, np.float64)), _ptr(_c(down, np.float64)),
+                              _ptr(_c(x_row_bf16, np.uint16)), H, I, _ptr(out))
+    return out
+
+
+class _Expert(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p * 3), ("sf", ctypes.c_void_p * 3), ("gs", ctypes.c_float * 3)]
+
+
+def moe_layer(x_bf16, experts, E, k, wr_bf16=None, bias=None, logits_in=None, nthreads=1, want_rows=False):
+    """experts: mapping expert id -> (gate, up, down) NVFP4 triples; experts
+    that no token selects may be absent.  Returns a dict of numpy arrays."""
+    x = _c(x_bf16, np.uint16)
+    T, H = x.shape
+    any_ex = next(iter(experts.values()))
+    I = any_ex[0].shape[0]
+    keep = []
+    structs = (ctypes.POINTER(_Expert) * E)()
+    for e, mats in experts.items():
+        s = _Expert()
+        for m in range(3):
+            q = _c(mats[m].q, np.uint8)
+            sf = _c(mats[m].sf, np.uint8)
+            keep += [q, sf]
+            s.q[m] = q.ctypes.data
+            s.sf[m] = sf.ctypes.data
+            s.gs[m] = float(mats[m].gs)
+        keep.append(s)
+        structs[e] = ctypes.pointer(s)
+    wr = None if wr_bf16 is None else _c(wr_bf16, np.uint16)
+    b = None if bias is None else _c(bias, np.float32)
+    li = None if logits_in is None else _c(logits_in, np.float32)
+    if li is None and wr is None:
+        raise ValueError("need router weights or logits")
+    logits = np.empty((T, E), np.float32)
+    ids = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float64)
+    offsets = np.empty(E + 1, np.int32)
+    sp = np.empty(T * k, np.int32)
+    pp = np.empty(T * k, np.int32)
+    rows = np.empty((T * k, H), np.float64) if want_rows else None
+    y = np.empty((T, H), np.float64)
+    rc = lib().oracle_moe_layer(_ptr(x), T, H, I, _ptr(wr), _ptr(b), _ptr(li), E, k,
+                                ctypes.cast(structs, ctypes.c_void_p), nthreads, _ptr(logits), _ptr(ids), _ptr(w),
+                                _ptr(offsets), _ptr(sp), _ptr(pp), _ptr(rows), _ptr(y))
+    if rc != 0:
+        raise RuntimeError("oracle_moe_layer: a selected expert was not provided")
+    out = dict(logits=logits, ids=ids, w=w, offsets=offsets, sorted_pairs=sp, pair_pos=pp, y=y)
+    if want_rows:
+        out["rows"] = rows
+    return out
