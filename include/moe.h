@@ -1,0 +1,181 @@
+/* moe.h - C ABI of libmoe.so: the routed mixture-of-experts layer with NVFP4
+ * experts on one AMD Instinct MI355X (gfx950).
+ *
+ * What the layer computes (the pages this follows):
+ *   - a router scores every token against E experts and picks k of them
+ *     (16 of 896 in Kimi-K3: al-engr.com Kimi-K3 NVFP4 plan, table "What we
+ *     verified today"; "Computation and Data Movement for Inference",
+ *     section 3.4 "Decode experts");
+ *   - the route records are sorted by expert so that one load of an
+ *     expert's weights serves its whole bucket (same essay, section 4 "The
+ *     flow of an MoE prefill layer" and section 15 "Prefill and midfill
+ *     turn sparse routing into dense expert batches");
+ *   - each selected expert runs its three matrices (gate, up, down:
+ *     "Serving Kimi-K3 ... with 8xB300 GPUs", section "The model, as the
+ *     serving system sees it") as a SwiGLU FFN on NVFP4 weights (e2m1
+ *     values, an e4m3 scale per 16 values, a per-expert fp32 global scale:
+ *     al-engr.com plan, section "What has to be built - and the discovery
+ *     that changed it"; "Serving Kimi-K3", section "Number formats on
+ *     Blackwell");
+ *   - the expert outputs go back to token order, weighted and summed
+ *     (essay, sections 4 and 5).
+ * The entry points mirror that statement of the problem: prepare
+ * (moe_route), compute (moe_expert_ffn), and the whole layer (moe_layer).
+ * The al-engr.com plan splits its expert call the same way, into a prepare
+ * step, the expert compute and a finalize step (section "What has to be
+ * built - and the discovery that changed it"), and its expert workers are
+ * handed a token's global expert ids and send back one row per expert
+ * (section "Track A - the Spark tier, starting now").
+ *
+ * Conventions for every entry point:
+ *   - Pointers named d_* or documented as device pointers point to device
+ *     memory that the caller owns and keeps alive until the enqueued work
+ *     has finished; the library never allocates, frees or synchronises.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
+ *     the null stream).  Calls are asynchronous and may be captured in a
+ *     HIP graph.
+ *   - Arguments are validated on the host before anything is enqueued; on a
+ *     non-OK return nothing was launched and moe_last_error() says why.  A
+ *     launch failure returns MOE_ERR_HIP; outputs are then undefined.
+ *   - No C++ exception crosses this boundary.
+ *   - Same inputs on the same GPU give bit-identical outputs: there are no
+ *     floating-point atomics.
+ *   - Shape limits: 1 <= k <= 64, k <= E <= 1024 with E a multiple of 8,
+ *     H and I multiples of 256, 0 <= T and T*k < 2^31.  T = 0 is a no-op
+ *     returning MOE_OK once the dimensions are valid (pointers are then not
+ *     examined).
+ *   - Pointers must be 16-byte aligned.
+ *   - Activations (x) must be finite with |x| < 65504, and so must the
+ *     intermediate h = SiLU(x.W_gate)*(x.W_up): the expert GEMMs run on
+ *     fp16 matrix cores (the NVFP4 products are exact in fp16; see the
+ *     design notes).  Outside that range results are inf/NaN, not silently
+ *     wrong. */
+#ifndef MOE_H
+#define MOE_H
+#include <stddef.h>
+#include <stdint.h>
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_ARG = 1,       /* NULL pointer where one is required, bad enum */
+  MOE_ERR_SHAPE = 2,     /* dimensions outside the limits above          */
+  MOE_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned             */
+  MOE_ERR_WORKSPACE = 4, /* ws_bytes smaller than the size required      */
+  MOE_ERR_HIP = 5        /* a HIP launch failed                          */
+} moe_status;
+
+/* T tokens, H hidden size, I expert intermediate size, E experts, k experts
+ * per token. */
+typedef struct {
+  int32_t T, H, I, E, k;
+} moe_dims;
+
+/* One NVFP4 matrix per expert, stacked over the E experts.  For a logical
+ * weight W[N][K] (N outputs, K the reduction axis):
+ *   q  [E][N][K/2]  e2m1 codes, two per byte, element k even in the low
+ *                   nibble; code = sign(bit 3) | exponent(bits 2:1, bias 1)
+ *                   | mantissa(bit 0): magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6
+ *   sf [E][N][K/16] OCP e4m3 (E4M3FN) scale of 16 consecutive k of a row
+ *   gs [E]          fp32 per-tensor global scale
+ * Dequantised weight: W[n][k] = e2m1(q) * e4m3(sf) * gs. */
+typedef struct {
+  const uint8_t* q;
+  const uint8_t* sf;
+  const float* gs;
+} moe_nvfp4;
+
+/* gate and up: N = I, K = H.  down: N = H, K = I.  All device pointers. */
+typedef struct {
+  moe_nvfp4 gate, up, down;
+} moe_experts;
+
+/* Bytes of device workspace that moe_route, moe_expert_ffn and moe_layer
+ * need for dims d (the same figure serves all three; 0 if d is invalid). */
+size_t moe_workspace_bytes(moe_dims d);
+
+/* Quantise one fp32 matrix w[N][K] (device) to NVFP4 (device outputs q
+ * [N][K/2], sf [N][K/16], gs [1]), the weight store the FFN reads.
+ * Rule (fp32, divisions correctly rounded): amax = max|w|; gs = amax/2688
+ * (= 6 * 448; 1 if amax = 0); per 16-element block along K:
+ * sf = e4m3_rne((blockmax / 6) / gs), saturating at 448; d = e4m3(sf) * gs;
+ * code = nearest e2m1 to |w|/d, ties to the even code, saturating at 6;
+ * sign bit only for w < 0 with a non-zero code; sf = 0 gives zero codes.
+ * The pages give the format but not the rounding rule; this is the reading
+ * taken.  Needs K % 16 == 0, N >= 1 and a workspace of at least
+ * moe_quantize_workspace_bytes() bytes. */
+size_t moe_quantize_workspace_bytes(void);
+moe_status moe_quantize_nvfp4(const float* w, int64_t N, int64_t K, uint8_t* q, uint8_t* sf, float* gs, void* ws,
+                              size_t ws_bytes, void* stream);
+
+/* Route T tokens (device pointers):
+ *   x              [T][H] bf16 activations, or NULL: then `logits` is an
+ *                  input (fp32 [T][E]) and the router GEMM is skipped;
+ *   w_router       [H][E] bf16 router weight (ignored when x is NULL);
+ *   bias           [E] fp32 added to the logits, or NULL;
+ *   logits         [T][E] fp32: logits = x.W_r + bias (fp32 accumulation);
+ *   topk_ids       [T][k] int32: the k largest logits in the order (logit
+ *                  descending, expert index ascending), so ties go to the
+ *                  lower index;
+ *   topk_w         [T][k] fp32: softmax over the k selected logits, which
+ *                  equals softmax over all E then renormalising the k;
+ *   expert_offsets [E+1] int32: exclusive prefix sum of per-expert counts;
+ *   sorted_pairs   [T*k] int32: route records f = t*k + j in (expert,
+ *                  token) order;
+ *   pair_pos       [T*k] int32: inverse of sorted_pairs.
+ * ids, offsets and the permutation are exact functions of the fp32
+ * logits. */
+moe_status moe_route(moe_dims d, const void* x, const void* w_router, const float* bias, float* logits,
+                     int32_t* topk_ids, float* topk_w, int32_t* expert_offsets, int32_t* sorted_pairs,
+                     int32_t* pair_pos, void* ws, size_t ws_bytes, void* stream);
+
+/* Run every selected expert on its bucket (device pointers):
+ *   x              [T][H] bf16 activations;
+ *   expert_offsets [E+1], sorted_pairs [T*k]: as produced by moe_route;
+ *   w              NVFP4 experts (the struct itself is host memory, read
+ *                  during the call only);
+ *   rows           [T*k][H] fp32 output: rows[p] = SwiGLU FFN of expert e
+ *                  on token sorted_pairs[p]/k, for p in e's bucket, i.e.
+ *                  (SiLU(x.Wg) * (x.Wu)).Wd, unweighted, in sorted order. */
+moe_status moe_expert_ffn(moe_dims d, const void* x, const int32_t* expert_offsets, const int32_t* sorted_pairs,
+                          const moe_experts* w, float* rows, void* ws, size_t ws_bytes, void* stream);
+
+/* The whole layer: y[t] = sum_j topk_w[t][j] * FFN_{topk_ids[t][j]}(x[t]),
+ * summed in fp32 over ascending j and rounded to bf16 (device pointers):
+ *   x [T][H] bf16, w_router [H][E] bf16, bias [E] fp32 or NULL,
+ *   y [T][H] bf16 output,
+ *   topk_ids_out [T][k] int32 / topk_w_out [T][k] fp32: optional copies of
+ *   the routing (NULL to skip). */
+moe_status moe_layer(moe_dims d, const void* x, const void* w_router, const float* bias, const moe_experts* w,
+                     void* y, int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes, void* stream);
+
+const char* moe_status_string(moe_status s);
+/* Detail of the last non-OK return on the calling thread. */
+const char* moe_last_error(void);
+
+/* ---- kernel timing for measurement ----------------------------------------
+ * Kernels of the path, in launch order within moe_layer. */
+typedef enum {
+  MOE_KERNEL_ROUTER = 0,  /* router logits (slab partials + reduction)   */
+  MOE_KERNEL_TOPK = 1,    /* softmax + top-k                             */
+  MOE_KERNEL_PERMUTE = 2, /* histogram, scan and scatter (three kernels) */
+  MOE_KERNEL_CAST = 3,    /* activations bf16 -> fp16                    */
+  MOE_KERNEL_GATEUP = 4,  /* grouped gate/up GEMM + SiLU*mul             */
+  MOE_KERNEL_DOWN = 5,    /* grouped down GEMM                           */
+  MOE_KERNEL_COMBINE = 6, /* weighted un-permute and sum                 */
+  MOE_KERNEL_COUNT = 7
+} moe_kernel;
+
+/* While armed, each launch of `kernel` on the calling thread records
+ * events[2i] before and events[2i+1] after the i-th launch (i < n_pairs) on
+ * the launch stream; events are hipEvent_t handles the caller created and
+ * later reads with hipEventElapsedTime.  Pass events = NULL to disarm.
+ * Returns the number of pairs recorded since the last arming. */
+int moe_profile_arm(moe_kernel kernel, void** events, int n_pairs);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

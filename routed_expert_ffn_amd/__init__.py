@@ -1,0 +1,190 @@
+"""Python binding of libmoe.so, the MI355X (gfx950) routed-MoE layer with
+NVFP4 experts.
+
+Argument marshalling only: every step of the layer runs in the HIP kernels
+behind the C ABI in include/moe.h, whose entry points this module mirrors by
+name.  torch is used for device memory and streams.  If libmoe.so is not
+built, loading fails loudly; there is no CPU fallback.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe.so")
+
+MOE_OK = 0
+STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_ARG", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_ALIGN", 4: "MOE_ERR_WORKSPACE",
+                5: "MOE_ERR_HIP"}
+KERNELS = {"router": 0, "topk": 1, "permute": 2, "cast": 3, "gateup": 4, "down": 5, "combine": 6}
+# Symbols include/moe.h declares.
+EXPORTS = ("moe_workspace_bytes", "moe_quantize_workspace_bytes", "moe_quantize_nvfp4", "moe_route",
+           "moe_expert_ffn", "moe_layer", "moe_status_string", "moe_last_error", "moe_profile_arm")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status, detail):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {detail}")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("k", ctypes.c_int32)]
+
+
+class NVFP4(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("sf", ctypes.c_void_p), ("gs", ctypes.c_void_p)]
+
+
+class Experts(ctypes.Structure):
+    _fields_ = [("gate", NVFP4), ("up", NVFP4), ("down", NVFP4)]
+
+
+_lib = None
+_p = ctypes.c_void_p
+
+
+def lib():
+    """Load libmoe.so (built in tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        L.moe_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_workspace_bytes.argtypes = [Dims]
+        L.moe_quantize_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_quantize_workspace_bytes.argtypes = []
+        L.moe_quantize_nvfp4.restype = ctypes.c_int
+        L.moe_quantize_nvfp4.argtypes = [_p, ctypes.c_int64, ctypes.c_int64, _p, _p, _p, _p, ctypes.c_size_t, _p]
+        L.moe_route.restype = ctypes.c_int
+        L.moe_route.argtypes = [Dims, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]
+        L.moe_expert_ffn.restype = ctypes.c_int
+        L.moe_expert_ffn.argtypes = [Dims, _p, _p, _p, ctypes.POINTER(Experts), _p, _p, ctypes.c_size_t, _p]
+        L.moe_layer.restype = ctypes.c_int
+        L.moe_layer.argtypes = [Dims, _p, _p, _p, ctypes.POINTER(Experts), _p, _p, _p, _p, ctypes.c_size_t, _p]
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_status_string.argtypes = [ctypes.c_int]
+        L.moe_last_error.restype = ctypes.c_char_p
+        L.moe_last_error.argtypes = []
+        L.moe_profile_arm.restype = ctypes.c_int
+        L.moe_profile_arm.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != MOE_OK:
+        raise MoeError(status, lib().moe_last_error().decode())
+
+
+def _ptr(t):
+    """Device address of a torch tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def dims(T, H, I, E, k):
+    return Dims(T, H, I, E, k)
+
+
+# ---- the C ABI, by name ------------------------------------------------------
+
+def moe_workspace_bytes(d):
+    return lib().moe_workspace_bytes(d)
+
+
+def moe_quantize_workspace_bytes():
+    return lib().moe_quantize_workspace_bytes()
+
+
+def moe_quantize_nvfp4(w, q, sf, gs, ws, stream=None):
+    N, K = w.shape
+    _check(lib().moe_quantize_nvfp4(_ptr(w), N, K, _ptr(q), _ptr(sf), _ptr(gs), _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_route(d, x, w_router, bias, logits, topk_ids, topk_w, expert_offsets, sorted_pairs, pair_pos, ws,
+              stream=None):
+    _check(lib().moe_route(d, _ptr(x), _ptr(w_router), _ptr(bias), _ptr(logits), _ptr(topk_ids), _ptr(topk_w),
+                           _ptr(expert_offsets), _ptr(sorted_pairs), _ptr(pair_pos), _ptr(ws),
+                           ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_expert_ffn(d, x, expert_offsets, sorted_pairs, experts, rows, ws, stream=None):
+    _check(lib().moe_expert_ffn(d, _ptr(x), _ptr(expert_offsets), _ptr(sorted_pairs), ctypes.byref(experts.c()),
+                                _ptr(rows), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_layer(d, x, w_router, bias, experts, y, topk_ids_out, topk_w_out, ws, stream=None):
+    _check(lib().moe_layer(d, _ptr(x), _ptr(w_router), _ptr(bias), ctypes.byref(experts.c()), _ptr(y),
+                           _ptr(topk_ids_out), _ptr(topk_w_out), _ptr(ws), ws.numel() * ws.element_size(),
+                           _stream(stream)))
+
+
+def moe_profile_arm(kernel, events=None):
+    """Arm timing of one kernel (name or id) with a list of torch.cuda.Event
+    pairs (enable_timing=True); returns the pairs recorded since the last
+    arming.  events=None disarms."""
+    kid = KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
+    if not events:
+        return lib().moe_profile_arm(kid, None, 0)
+    for ev in events:  # torch creates the underlying hipEvent_t lazily, at the first record
+        ev.record()
+    handles = (ctypes.c_void_p * len(events))(*[ev.cuda_event for ev in events])
+    moe_profile_arm._keep = handles
+    return lib().moe_profile_arm(kid, handles, len(events) // 2)
+
+
+# ---- device memory holders (plumbing) ------------------------------------------
+
+class ExpertStore:
+    """NVFP4 weights of E experts, stacked per matrix, resident in HBM:
+    q [E][N][K/2] u8, sf [E][N][K/16] u8, gs [E] fp32 for gate/up (N = I,
+    K = H) and down (N = H, K = I)."""
+
+    MATS = ("gate", "up", "down")
+
+    def __init__(self, E, H, I, device="cuda"):
+        import torch
+        self.E, self.H, self.I = E, H, I
+        self.t = {}
+        for m in self.MATS:
+            N, K = self.shape(m)
+            self.t[m] = (torch.empty((E, N, K // 2), dtype=torch.uint8, device=device),
+                         torch.empty((E, N, K // 16), dtype=torch.uint8, device=device),
+                         torch.empty((E,), dtype=torch.float32, device=device))
+        self._qws = torch.empty(max(256, moe_quantize_workspace_bytes()), dtype=torch.uint8, device=device)
+
+    def shape(self, m):
+        return (self.I, self.H) if m in ("gate", "up") else (self.H, self.I)
+
+    def quantize_into(self, e, m, w_f32, stream=None):
+        """Quantise fp32 w [N][K] (device) with moe_quantize_nvfp4 into expert e."""
+        q, sf, gs = self.t[m]
+        moe_quantize_nvfp4(w_f32, q[e], sf[e], gs[e:e + 1], self._qws, stream)
+
+    def c(self):
+        mats = []
+        for m in self.MATS:
+            q, sf, gs = self.t[m]
+            mats.append(NVFP4(q.data_ptr(), sf.data_ptr(), gs.data_ptr()))
+        self._c = Experts(*mats)
+        return self._c
+
+    def nbytes_per_expert(self):
+        return sum(q[0].numel() + sf[0].numel() + 4 for q, sf, _ in self.t.values())

@@ -1,0 +1,306 @@
+// C ABI of libmoe.so (declared and documented in include/moe.h): argument
+// validation, workspace carve-up and the launch sequence on the caller's
+// stream.  Nothing here allocates, frees, synchronises or reads device
+// memory, so every entry point can be captured in a HIP graph.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+moe_status hip_fail(hipError_t e, const char* what) {
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Prof {
+  int kernel = -1;
+  void** events = nullptr;
+  int n_pairs = 0;
+  int used = 0;
+};
+thread_local Prof g_prof;
+
+moe_status check_dims(const moe_dims& d) {
+  if (d.T < 0) return fail(MOE_ERR_SHAPE, "T = %d is negative", d.T);
+  if (d.H <= 0 || d.H % 256) return fail(MOE_ERR_SHAPE, "H = %d must be a positive multiple of 256", d.H);
+  if (d.I <= 0 || d.I % 256) return fail(MOE_ERR_SHAPE, "I = %d must be a positive multiple of 256", d.I);
+  if (d.k < 1 || d.k > 64) return fail(MOE_ERR_SHAPE, "k = %d must be in [1, 64]", d.k);
+  if (d.E < d.k || d.E > 1024 || d.E % 8)
+    return fail(MOE_ERR_SHAPE, "E = %d must be a multiple of 8 in [k, 1024]", d.E);
+  if ((long long)d.T * d.k >= (1LL << 31)) return fail(MOE_ERR_SHAPE, "T*k = %lld is too large", (long long)d.T * d.k);
+  return MOE_OK;
+}
+
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Workspace regions (byte offsets, 256-byte aligned).  moe_layer uses all of
+// them; moe_route and moe_expert_ffn use subsets of the same layout.
+struct Layout {
+  size_t part, logits, ids, w, masks, counts, base, offsets, sorted, pos, active, nact, x16, h, rows, total;
+};
+
+Layout layout(const moe_dims& d) {
+  Layout L;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t r = o;
+    o += align256(bytes);
+    return r;
+  };
+  const size_t T = (size_t)d.T, H = (size_t)d.H, I = (size_t)d.I, E = (size_t)d.E, P = T * (size_t)d.k;
+  const size_t S = (size_t)moe::router_slabs(d.T, d.H, d.E), nb = (size_t)moe::perm_blocks(d.T);
+  L.part = take(S * T * E * 4);
+  L.logits = take(T * E * 4);
+  L.ids = take(P * 4);
+  L.w = take(P * 4);
+  L.masks = take(nb * E * 8);
+  L.counts = take(nb * E * 4);
+  L.base = take(nb * E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.sorted = take(P * 4);
+  L.pos = take(P * 4);
+  L.active = take(E * 4);
+  L.nact = take(4);
+  L.x16 = take(T * H * 2);
+  L.h = take(P * I * 2);
+  L.rows = take(P * H * 4);
+  L.total = o;
+  return L;
+}
+
+template <class T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+moe_status check_ws(const moe_dims& d, void* ws, size_t ws_bytes) {
+  const size_t need = layout(d).total;
+  if (!ws) return fail(MOE_ERR_ARG, "workspace is NULL");
+  if (!aligned16(ws)) return fail(MOE_ERR_ALIGN, "workspace is not 16-byte aligned");
+  if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  return MOE_OK;
+}
+
+moe_status check_ptr(const void* p, const char* name, bool required = true) {
+  if (!p) return required ? fail(MOE_ERR_ARG, "%s is NULL", name) : MOE_OK;
+  if (!aligned16(p)) return fail(MOE_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  return MOE_OK;
+}
+
+moe_status check_experts(const moe_experts* w) {
+  if (!w) return fail(MOE_ERR_ARG, "experts struct is NULL");
+  const moe_nvfp4* m[3] = {&w->gate, &w->up, &w->down};
+  const char* names[3] = {"gate", "up", "down"};
+  for (int i = 0; i < 3; i++) {
+    if (!m[i]->q || !m[i]->sf || !m[i]->gs) return fail(MOE_ERR_ARG, "%s weights have a NULL pointer", names[i]);
+    if (!aligned16(m[i]->q) || !aligned16(m[i]->sf) || !aligned16(m[i]->gs))
+      return fail(MOE_ERR_ALIGN, "%s weights are not 16-byte aligned", names[i]);
+  }
+  return MOE_OK;
+}
+
+#define TRY(expr)                       \
+  do {                                  \
+    moe_status _s = (expr);             \
+    if (_s != MOE_OK) return _s;        \
+  } while (0)
+
+#define LAUNCH(kernel_id, stream, call, what)    \
+  do {                                           \
+    moe::prof_before(kernel_id, stream);         \
+    hipError_t _e = (call);                      \
+    if (_e != hipSuccess) return hip_fail(_e, what); \
+    moe::prof_after(kernel_id, stream);          \
+  } while (0)
+
+// Enqueue routing; logits may be an input (x == NULL).
+moe_status enqueue_route(const moe_dims& d, const void* x, const void* wr, const float* bias, float* logits,
+                         int32_t* ids, float* w, int32_t* offsets, int32_t* sorted, int32_t* pos, void* ws,
+                         hipStream_t s) {
+  const Layout L = layout(d);
+  if (x) {
+    const int slabs = moe::router_slabs(d.T, d.H, d.E);
+    moe::prof_before(MOE_KERNEL_ROUTER, s);
+    hipError_t e = moe::launch_router(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wr),
+                                      at<float>(ws, L.part), d.T, d.H, d.E, slabs, s);
+    if (e != hipSuccess) return hip_fail(e, "router");
+    e = moe::launch_logits_reduce(at<float>(ws, L.part), bias, logits, d.T, d.E, slabs, s);
+    if (e != hipSuccess) return hip_fail(e, "router reduce");
+    moe::prof_after(MOE_KERNEL_ROUTER, s);
+  }
+  LAUNCH(MOE_KERNEL_TOPK, s, moe::launch_topk(logits, d.T, d.E, d.k, ids, w, s), "top-k");
+  LAUNCH(MOE_KERNEL_PERMUTE, s,
+         moe::launch_permute(ids, d.T, d.E, d.k, at<uint64_t>(ws, L.masks), at<int32_t>(ws, L.counts),
+                             at<int32_t>(ws, L.base), offsets, sorted, pos, at<int32_t>(ws, L.active),
+                             at<int32_t>(ws, L.nact), s),
+         "permute");
+  return MOE_OK;
+}
+
+moe_status enqueue_ffn(const moe_dims& d, const void* x, const int32_t* offsets, const int32_t* sorted,
+                       const moe_experts* w, float* rows, void* ws, hipStream_t s) {
+  const Layout L = layout(d);
+  moe::FfnArgs a;
+  a.T = d.T;
+  a.H = d.H;
+  a.I = d.I;
+  a.E = d.E;
+  a.k = d.k;
+  a.max_active = moe::max_active(d);
+  a.x16 = at<f16>(ws, L.x16);
+  a.offsets = offsets;
+  a.sorted_pairs = sorted;
+  a.active = at<int32_t>(ws, L.active);
+  a.n_active = at<int32_t>(ws, L.nact);
+  a.w = w;
+  a.h = at<f16>(ws, L.h);
+  a.rows = rows;
+  LAUNCH(MOE_KERNEL_CAST, s,
+         moe::launch_cast(static_cast<const uint16_t*>(x), at<f16>(ws, L.x16), (long long)d.T * d.H, s), "cast");
+  LAUNCH(MOE_KERNEL_GATEUP, s, moe::launch_gateup(a, s), "gate/up");
+  LAUNCH(MOE_KERNEL_DOWN, s, moe::launch_down(a, s), "down");
+  return MOE_OK;
+}
+
+}  // namespace
+
+void moe::prof_before(moe_kernel k, hipStream_t s) {
+  if (g_prof.events && g_prof.kernel == (int)k && g_prof.used < g_prof.n_pairs)
+    (void)hipEventRecord(static_cast<hipEvent_t>(g_prof.events[2 * g_prof.used]), s);
+}
+
+void moe::prof_after(moe_kernel k, hipStream_t s) {
+  if (g_prof.events && g_prof.kernel == (int)k && g_prof.used < g_prof.n_pairs) {
+    (void)hipEventRecord(static_cast<hipEvent_t>(g_prof.events[2 * g_prof.used + 1]), s);
+    g_prof.used++;
+  }
+}
+
+extern "C" {
+
+size_t moe_workspace_bytes(moe_dims d) {
+  if (check_dims(d) != MOE_OK) return 0;
+  return layout(d).total;
+}
+
+size_t moe_quantize_workspace_bytes(void) { return 256; }
+
+moe_status moe_quantize_nvfp4(const float* w, int64_t N, int64_t K, uint8_t* q, uint8_t* sf, float* gs, void* ws,
+                              size_t ws_bytes, void* stream) {
+  if (N < 1 || K < 16 || K % 16) return fail(MOE_ERR_SHAPE, "N = %lld, K = %lld: need N >= 1 and K a multiple of 16",
+                                             (long long)N, (long long)K);
+  TRY(check_ptr(w, "w"));
+  TRY(check_ptr(q, "q"));
+  if (!sf || !gs) return fail(MOE_ERR_ARG, "sf or gs is NULL");
+  if ((uintptr_t)gs & 3u) return fail(MOE_ERR_ALIGN, "gs is not 4-byte aligned");
+  if (!ws) return fail(MOE_ERR_ARG, "workspace is NULL");
+  if ((uintptr_t)ws & 3u) return fail(MOE_ERR_ALIGN, "workspace is not 4-byte aligned");
+  if (ws_bytes < moe_quantize_workspace_bytes())
+    return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, moe_quantize_workspace_bytes());
+  hipError_t e = moe::launch_quantize(w, N, K, q, sf, gs, static_cast<uint32_t*>(ws), (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "quantize");
+  return MOE_OK;
+}
+
+moe_status moe_route(moe_dims d, const void* x, const void* w_router, const float* bias, float* logits,
+                     int32_t* topk_ids, float* topk_w, int32_t* expert_offsets, int32_t* sorted_pairs,
+                     int32_t* pair_pos, void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_dims(d));
+  if (d.T == 0) return MOE_OK;
+  TRY(check_ptr(x, "x", false));
+  if (x) TRY(check_ptr(w_router, "w_router"));
+  TRY(check_ptr(bias, "bias", false));
+  TRY(check_ptr(logits, "logits"));
+  TRY(check_ptr(topk_ids, "topk_ids"));
+  TRY(check_ptr(topk_w, "topk_w"));
+  TRY(check_ptr(expert_offsets, "expert_offsets"));
+  TRY(check_ptr(sorted_pairs, "sorted_pairs"));
+  TRY(check_ptr(pair_pos, "pair_pos"));
+  TRY(check_ws(d, ws, ws_bytes));
+  return enqueue_route(d, x, w_router, bias, logits, topk_ids, topk_w, expert_offsets, sorted_pairs, pair_pos, ws,
+                       (hipStream_t)stream);
+}
+
+moe_status moe_expert_ffn(moe_dims d, const void* x, const int32_t* expert_offsets, const int32_t* sorted_pairs,
+                          const moe_experts* w, float* rows, void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_dims(d));
+  if (d.T == 0) return MOE_OK;
+  TRY(check_ptr(x, "x"));
+  TRY(check_ptr(expert_offsets, "expert_offsets"));
+  TRY(check_ptr(sorted_pairs, "sorted_pairs"));
+  TRY(check_experts(w));
+  TRY(check_ptr(rows, "rows"));
+  TRY(check_ws(d, ws, ws_bytes));
+  const Layout L = layout(d);
+  hipStream_t s = (hipStream_t)stream;
+  {
+    hipError_t e = moe::launch_active_list(expert_offsets, d.E, at<int32_t>(ws, L.active), at<int32_t>(ws, L.nact), s);
+    if (e != hipSuccess) return hip_fail(e, "active list");
+  }
+  return enqueue_ffn(d, x, expert_offsets, sorted_pairs, w, rows, ws, s);
+}
+
+moe_status moe_layer(moe_dims d, const void* x, const void* w_router, const float* bias, const moe_experts* w,
+                     void* y, int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_dims(d));
+  if (d.T == 0) return MOE_OK;
+  TRY(check_ptr(x, "x"));
+  TRY(check_ptr(w_router, "w_router"));
+  TRY(check_ptr(bias, "bias", false));
+  TRY(check_experts(w));
+  TRY(check_ptr(y, "y"));
+  TRY(check_ptr(topk_ids_out, "topk_ids_out", false));
+  TRY(check_ptr(topk_w_out, "topk_w_out", false));
+  TRY(check_ws(d, ws, ws_bytes));
+  const Layout L = layout(d);
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, L.ids);
+  float* wts = topk_w_out ? topk_w_out : at<float>(ws, L.w);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* sorted = at<int32_t>(ws, L.sorted);
+  int32_t* pos = at<int32_t>(ws, L.pos);
+  float* rows = at<float>(ws, L.rows);
+  TRY(enqueue_route(d, x, w_router, bias, at<float>(ws, L.logits), ids, wts, offsets, sorted, pos, ws, s));
+  TRY(enqueue_ffn(d, x, offsets, sorted, w, rows, ws, s));
+  LAUNCH(MOE_KERNEL_COMBINE, s,
+         moe::launch_combine(rows, pos, wts, d.T, d.H, d.k, static_cast<uint16_t*>(y), s), "combine");
+  return MOE_OK;
+}
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_ARG: return "invalid argument";
+    case MOE_ERR_SHAPE: return "unsupported shape";
+    case MOE_ERR_ALIGN: return "misaligned pointer";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+int moe_profile_arm(moe_kernel kernel, void** events, int n_pairs) {
+  const int used = g_prof.used;
+  g_prof.kernel = (int)kernel;
+  g_prof.events = (events && n_pairs > 0) ? events : nullptr;
+  g_prof.n_pairs = events ? n_pairs : 0;
+  g_prof.used = 0;
+  return used;
+}
+
+}  // extern "C"

@@ -1,0 +1,58 @@
+// Host-side interface between the C ABI (api.hip) and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.h"
+#include "moe.h"
+
+namespace moe {
+
+// The router's partial sums over H are split in this many slabs for T tokens.
+int router_slabs(int T, int H, int E);
+// The permutation works on blocks of 64 tokens (one wavefront each).
+inline int perm_blocks(int T) { return (T + 63) / 64; }
+// Largest number of distinct experts that T tokens can select.
+inline int max_active(const moe_dims& d) {
+  long long p = (long long)d.T * d.k;
+  return (int)(p < d.E ? p : d.E);
+}
+
+// Kernel-timing hook (see moe_profile_arm).
+void prof_before(moe_kernel k, hipStream_t s);
+void prof_after(moe_kernel k, hipStream_t s);
+
+// Launchers.  Each enqueues on `s` and returns hipGetLastError().
+hipError_t launch_router(const uint16_t* x, const uint16_t* wr, float* part, int T, int H, int E, int slabs,
+                         hipStream_t s);
+hipError_t launch_logits_reduce(const float* part, const float* bias, float* logits, int T, int E, int slabs,
+                                hipStream_t s);
+hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s);
+hipError_t launch_permute(const int32_t* ids, int T, int E, int k, uint64_t* masks, int32_t* counts, int32_t* base,
+                          int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_pos, int32_t* active,
+                          int32_t* n_active, hipStream_t s);
+hipError_t launch_active_list(const int32_t* offsets, int E, int32_t* active, int32_t* n_active, hipStream_t s);
+hipError_t launch_cast(const uint16_t* x, f16* x16, long long n, hipStream_t s);
+
+struct FfnArgs {
+  int T, H, I, E, k;
+  int max_active;                 // grid bound on the number of active experts
+  const f16* x16;                 // [T][H]
+  const int32_t* offsets;         // [E+1]
+  const int32_t* sorted_pairs;    // [P]
+  const int32_t* active;          // [max_active] expert ids with work
+  const int32_t* n_active;        // [1]
+  const moe_experts* w;
+  f16* h;                         // [P][I]
+  float* rows;                    // [P][H]
+};
+hipError_t launch_gateup(const FfnArgs& a, hipStream_t s);
+hipError_t launch_down(const FfnArgs& a, hipStream_t s);
+hipError_t launch_combine(const float* rows, const int32_t* pair_pos, const float* w, int T, int H, int k,
+                          uint16_t* y, hipStream_t s);
+
+hipError_t launch_quantize(const float* w, int64_t N, int64_t K, uint8_t* q, uint8_t* sf, float* gs, uint32_t* ws,
+                           hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,97 @@
+"""The C ABI boundary on the host: libmoe.so loads and exports every entry
+point include/moe.h declares, and argument validation rejects bad calls
+before anything reaches the GPU (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import routed_expert_ffn_amd as moe
+from synth.workloads import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\**\s*(moe_[a-z_0-9]+)\s*\(", text, flags=re.M))
+
+
+def test_exports_match_header():
+    decl = declared_functions()
+    assert decl == set(moe.EXPORTS), decl ^ set(moe.EXPORTS)
+    L = ctypes.CDLL(moe.LIB_PATH)
+    for name in decl:
+        assert hasattr(L, name), name
+
+
+def test_workspace_sizes():
+    for wl in WORKLOADS.values():
+        d = moe.dims(wl.T, wl.H, wl.I, wl.E, wl.k)
+        n = moe.moe_workspace_bytes(d)
+        # at least the per-pair rows, h and the fp16 copy of x
+        assert n >= wl.P * wl.H * 4 + wl.P * wl.I * 2 + wl.T * wl.H * 2
+        assert n % 256 == 0
+    assert moe.moe_workspace_bytes(moe.dims(1, 7168, 2048, 896, 0)) == 0
+    assert moe.moe_quantize_workspace_bytes() >= 4
+
+
+FAKE = 1 << 20  # aligned, never dereferenced: validation fails first
+
+
+def _route(d, **kw):
+    a = dict(x=FAKE, wr=FAKE, bias=None, logits=FAKE, ids=FAKE, w=FAKE, off=FAKE, sp=FAKE, pp=FAKE, ws=FAKE,
+             ws_bytes=moe.moe_workspace_bytes(d) if moe.moe_workspace_bytes(d) else 1 << 30)
+    a.update(kw)
+    return moe.lib().moe_route(d, a["x"], a["wr"], a["bias"], a["logits"], a["ids"], a["w"], a["off"], a["sp"],
+                               a["pp"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("T,H,I,E,k", [(-1, 512, 256, 896, 16), (8, 500, 256, 896, 16), (8, 512, 200, 896, 16),
+                                       (8, 512, 256, 896, 0), (8, 512, 256, 896, 65), (8, 512, 256, 12, 16),
+                                       (8, 512, 256, 2048, 16), (8, 512, 256, 900, 16), (1 << 27, 512, 256, 896, 16)])
+def test_bad_shapes_rejected(T, H, I, E, k):
+    d = moe.dims(T, H, I, E, k)
+    assert _route(d) == 2  # MOE_ERR_SHAPE
+    assert moe.lib().moe_last_error()
+
+
+def test_bad_pointers_and_workspace_rejected():
+    d = moe.dims(8, 512, 256, 896, 16)
+    assert _route(d, logits=None) == 1          # MOE_ERR_ARG
+    assert _route(d, ids=FAKE + 4) == 3         # MOE_ERR_ALIGN
+    assert _route(d, ws_bytes=1024) == 4        # MOE_ERR_WORKSPACE
+    assert b"workspace" in moe.lib().moe_last_error()
+    assert _route(d, ws=None) == 1
+    # x == NULL is the logits-in mode, router weights may then be NULL too
+    assert _route(moe.dims(8, 512, 256, 896, 16), x=None, wr=None, logits=None) == 1
+
+
+def test_layer_and_ffn_validation():
+    d = moe.dims(8, 512, 256, 896, 16)
+    ex = moe.Experts(moe.NVFP4(FAKE, FAKE, FAKE), moe.NVFP4(FAKE, FAKE, FAKE), moe.NVFP4(FAKE, None, FAKE))
+    big = moe.moe_workspace_bytes(d)
+    L = moe.lib()
+    assert L.moe_layer(d, FAKE, FAKE, None, ctypes.byref(ex), FAKE, None, None, FAKE, big, None) == 1
+    ex.down.sf = FAKE + 8
+    assert L.moe_layer(d, FAKE, FAKE, None, ctypes.byref(ex), FAKE, None, None, FAKE, big, None) == 3
+    assert L.moe_layer(d, FAKE, FAKE, None, None, FAKE, None, None, FAKE, big, None) == 1
+    assert L.moe_expert_ffn(d, FAKE, FAKE, FAKE, None, FAKE, FAKE, big, None) == 1
+    assert L.moe_quantize_nvfp4(FAKE, 4, 24, FAKE, FAKE, FAKE, FAKE, 256, None) == 2
+    assert L.moe_quantize_nvfp4(FAKE, 4, 32, FAKE, FAKE, FAKE, FAKE, 2, None) == 4
+
+
+def test_t_zero_is_ok_without_touching_anything():
+    d = moe.dims(0, 512, 256, 896, 16)
+    assert moe.lib().moe_layer(d, None, None, None, None, None, None, None, None, 0, None) == 0
+    assert _route(d, x=None, logits=None) == 0
+
+
+def test_status_strings_and_errors():
+    L = moe.lib()
+    for s in range(6):
+        assert L.moe_status_string(s)
+    with pytest.raises(moe.MoeError):
+        moe._check(2)
