@@ -1,0 +1,245 @@
+"""Benchmark of the routed-MoE layer (NVFP4 experts) on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_1]
+
+A step is one moe_layer call (router, top-k, permutation, grouped gate/up +
+SiLU*mul, grouped down, combine) on one batch of T synthetic tokens, with all
+896 experts' NVFP4 weights (22.2 GB) resident in HBM.  Every step uses fresh
+tokens (the generator's next T tokens), so each step routes to different
+experts and reads their weights cold, as a decode step of a real model does.
+Prints one JSON line: whole-layer tokens/s, the dominant kernel's achieved
+bandwidth against the HBM roofline (timed with HIP events on the launch
+stream inside the timed region), and the CPU oracle timed on a bounded
+sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + achieved HBM TB/s (decode) / MFMA TFLOPS (prefill), 1 GPU"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix, published
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_1")
+    ap.add_argument("--cpu-tokens", type=int, default=None, help="tokens in the oracle's timed sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-breakdown", action="store_true")
+    return ap.parse_args()
+
+
+def nvfp4_bytes(N, K):
+    return N * (K // 2) + N * (K // 16) + 4
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for f in ("kernels_ffn.hip", "common.h"):
+        h.update(open(os.path.join(ROOT, "routed_expert_ffn_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload, sha):
+    """HBM traffic of the gate/up kernel per launch, from the committed
+    rocprofv3 counter summary, if it was taken on this kernel source."""
+    path = os.path.join(PROFILES, f"gateup_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_sha") != sha:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import routed_expert_ffn_amd as moe
+    import synth
+    from synth.workloads import WORKLOADS, bias_for
+
+    wl = WORKLOADS[args.workload]
+    T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.k
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    steps, warmup = args.steps, args.warmup
+    n_batches = steps + warmup
+
+    # ---- resident inputs -------------------------------------------------------
+    t_setup = time.perf_counter()
+    store = moe.ExpertStore(E, H, I, device=dev)
+    buf = {m: torch.empty(store.shape(m), dtype=torch.float32, device=dev) for m in store.MATS}
+    for e in range(E):
+        for mi, m in enumerate(store.MATS):
+            synth.gpu_expert_f32(wl.seed, e, mi, buf[m])
+            store.quantize_into(e, m, buf[m])
+    del buf
+    wr = torch.empty((H, E), dtype=torch.bfloat16, device=dev)
+    synth.gpu_router_bf16(wl.seed, wr)
+    b = bias_for(wl)
+    bias = None if b is None else torch.tensor(b, device=dev)
+    # one batch of T fresh tokens per step
+    xs = torch.empty((n_batches * T, H), dtype=torch.bfloat16, device=dev)
+    synth.gpu_x_bf16(wl.seed, xs)
+    d = moe.dims(T, H, I, E, k)
+    ws = torch.empty(moe.moe_workspace_bytes(d), dtype=torch.uint8, device=dev)
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ids = torch.empty((n_batches, T, k), dtype=torch.int32, device=dev)
+    wts = torch.empty((n_batches, T, k), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+
+    def step(i):
+        moe.moe_layer(d, xs[i * T:(i + 1) * T], wr, bias, store, y, ids[i], wts[i], ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region ------------------------------------------------------------
+    kev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
+    moe.moe_profile_arm("gateup", kev)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(warmup, n_batches):
+        step(i)
+    end.record()
+    torch.cuda.synchronize()
+    n_rec = moe.moe_profile_arm("gateup", None)
+    elapsed_ms = start.elapsed_time(end)
+    assert n_rec == steps
+    gateup_ms = [kev[2 * i].elapsed_time(kev[2 * i + 1]) for i in range(steps)]
+
+    ids_np = ids.cpu().numpy()
+    distinct = np.array([len(np.unique(ids_np[i])) for i in range(warmup, n_batches)])
+
+    # ---- algorithmic work ------------------------------------------------------------
+    ms_per_step = elapsed_ms / steps
+    expert_bytes = 2 * nvfp4_bytes(I, H) + nvfp4_bytes(H, I)
+    layer_bytes = distinct.mean() * expert_bytes + H * E * 2 + 2 * T * H * 2
+    layer_flops = 2 * T * H * E + 6 * T * k * H * I
+    gateup_unit = 2 * nvfp4_bytes(I, H)              # one active expert's gate+up weights
+    gateup_bytes = distinct * gateup_unit + T * H * 2 + T * k * I * 2
+    gateup_avg_ms = float(np.mean(gateup_ms))
+    achieved = float(np.mean(gateup_bytes)) / (gateup_avg_ms * 1e-3) / 1e9
+    sha = kernel_source_sha()
+    prefill = T >= 4096
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(wl.name, sha),
+                "kernel": "gateup_kernel (grouped gate/up + SiLU*mul)",
+                "algorithmic_bytes_per_launch": int(np.mean(gateup_bytes)), "avg_launch_ms": round(gateup_avg_ms, 5)}
+    if prefill:
+        gu_flops = 4 * T * k * H * I
+        tf = gu_flops / (gateup_avg_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(tf, 1), "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tf / FP16_MFMA_PEAK_TFLOPS, 4), "traffic": load_traffic(wl.name, sha),
+                    "kernel": "gateup_kernel (grouped gate/up + SiLU*mul)",
+                    "algorithmic_flops_per_launch": gu_flops, "avg_launch_ms": round(gateup_avg_ms, 5)}
+
+    out = {
+        "metric": METRIC,
+        "value": round(T * steps / (elapsed_ms * 1e-3), 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: MoE layer T={T} H={H} I={I} E={E} top-{k}, NVFP4 experts, bf16 "
+                               f"activations, fresh tokens every step",
+                   "T": T, "H": H, "I": I, "E": E, "k": k, "zipf_beta": wl.beta, "seed": wl.seed},
+        "roofline": roofline,
+        "layer": {"algorithmic_bytes": int(layer_bytes), "hbm_GBps": round(layer_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+                  "hbm_frac": round(layer_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                  "TFLOPs": round(layer_flops / (ms_per_step * 1e-3) / 1e12, 3),
+                  "distinct_experts_mean": float(distinct.mean())},
+        "setup_s": round(setup_s, 2),
+        "kernel_source_sha": sha,
+    }
+
+    # ---- per-kernel breakdown (after the timed region; not part of the value) ----
+    if not args.no_breakdown:
+        reps = min(steps, 20)
+        br = {}
+        for name in moe.KERNELS:
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+            moe.moe_profile_arm(name, evs)
+            for i in range(reps):
+                step(warmup + i)
+            torch.cuda.synchronize()
+            n = moe.moe_profile_arm(name, None)
+            br[name] = round(float(np.mean([evs[2 * j].elapsed_time(evs[2 * j + 1]) for j in range(n)])), 5) if n else None
+        out["kernel_ms"] = br
+
+    if not args.no_cpu_baseline:
+        n_tok = args.cpu_tokens or (8 if T <= 16 else 4)
+        out["cpu_baseline"] = cpu_baseline(wl, n_tok, first_token=warmup * T)
+    print(json.dumps(out))
+
+
+def cpu_baseline(wl, n_tokens, first_token):
+    """The CPU oracle, as it stands, on a bounded sample of the same
+    workload: n_tokens tokens of the timed batches (generator tokens
+    first_token..), one single-token layer call each.  The experts those
+    tokens select (found with the oracle's own router, untimed) are
+    generated and quantised beforehand; the timed call routes, dequantises
+    and runs its 16 experts and combines."""
+    import concurrent.futures
+
+    import oracle
+    import synth
+    from synth.workloads import bias_for
+
+    threads = min(16, os.cpu_count() or 1)
+    wr = synth.router_bf16(wl.seed, wl.H, wl.E)
+    bias = bias_for(wl)
+    xs = [synth.x_bf16(wl.seed, 1, wl.H, t0=first_token + t) for t in range(n_tokens)]
+    need = set()
+    for x in xs:
+        ids, _ = oracle.topk_softmax(oracle.router_logits(x, wr, bias), wl.k)
+        need |= set(int(e) for e in ids[0])
+
+    def make(e):
+        return tuple(oracle.nvfp4_quantize(synth.expert_f32(wl.seed, e, m, *synth.expert_shape(m, wl.H, wl.I),
+                                                            nthreads=1)) for m in range(3))
+
+    cache = {}
+    with concurrent.futures.ThreadPoolExecutor(max_workers=threads) as ex:
+        for e, v in zip(sorted(need), ex.map(make, sorted(need))):
+            cache[e] = v
+    total = 0.0
+    for x in xs:
+        t0 = time.perf_counter()
+        oracle.moe_layer(x, cache, wl.E, wl.k, wr_bf16=wr, bias=bias, nthreads=threads)
+        total += time.perf_counter() - t0
+    return {"value": round(n_tokens / total, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_tokens} tokens of the {wl.name} workload's timed batches, one single-token oracle layer "
+                      f"call each (router, top-k, permutation, 16 experts dequantised and run in fp64, combine), "
+                      f"{threads} threads over the token's experts; expert weights pre-quantised, untimed",
+            "seconds": round(total, 2)}
+
+
+if __name__ == "__main__":
+    main()

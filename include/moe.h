@@ -114,7 +114,8 @@ moe_status moe_quantize_nvfp4(const float* w, int64_t N, int64_t K, uint8_t* q, 
  *   x              [T][H] bf16 activations, or NULL: then `logits` is an
  *                  input (fp32 [T][E]) and the router GEMM is skipped;
  *   w_router       [H][E] bf16 router weight (ignored when x is NULL);
- *   bias           [E] fp32 added to the logits, or NULL;
+ *   bias           [E] fp32 added to the logits, or NULL (ignored when x
+ *                  is NULL: given logits are used as they are);
  *   logits         [T][E] fp32: logits = x.W_r + bias (fp32 accumulation);
  *   topk_ids       [T][k] int32: the k largest logits in the order (logit
  *                  descending, expert index ascending), so ties go to the

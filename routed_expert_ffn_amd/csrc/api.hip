@@ -61,7 +61,7 @@ Layout layout(const moe_dims& d) {
     return r;
   };
   const size_t T = (size_t)d.T, H = (size_t)d.H, I = (size_t)d.I, E = (size_t)d.E, P = T * (size_t)d.k;
-  const size_t S = (size_t)moe::router_slabs(d.T, d.H, d.E), nb = (size_t)moe::perm_blocks(d.T);
+  const size_t S = (size_t)moe::router_plan(d.T, d.H, d.E).slabs, nb = (size_t)moe::perm_blocks(d.T);
   L.part = take(S * T * E * 4);
   L.logits = take(T * E * 4);
   L.ids = take(P * 4);
@@ -126,32 +126,35 @@ moe_status check_experts(const moe_experts* w) {
     moe::prof_after(kernel_id, stream);          \
   } while (0)
 
-// Enqueue routing; logits may be an input (x == NULL).
+// Enqueue routing; logits are an input when x == NULL.  When x16 is given,
+// the permutation kernels also write the fp16 copy of x the FFN reads.
 moe_status enqueue_route(const moe_dims& d, const void* x, const void* wr, const float* bias, float* logits,
                          int32_t* ids, float* w, int32_t* offsets, int32_t* sorted, int32_t* pos, void* ws,
-                         hipStream_t s) {
+                         f16* x16, hipStream_t s) {
   const Layout L = layout(d);
-  if (x) {
-    const int slabs = moe::router_slabs(d.T, d.H, d.E);
-    moe::prof_before(MOE_KERNEL_ROUTER, s);
-    hipError_t e = moe::launch_router(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wr),
-                                      at<float>(ws, L.part), d.T, d.H, d.E, slabs, s);
-    if (e != hipSuccess) return hip_fail(e, "router");
-    e = moe::launch_logits_reduce(at<float>(ws, L.part), bias, logits, d.T, d.E, slabs, s);
-    if (e != hipSuccess) return hip_fail(e, "router reduce");
-    moe::prof_after(MOE_KERNEL_ROUTER, s);
-  }
-  LAUNCH(MOE_KERNEL_TOPK, s, moe::launch_topk(logits, d.T, d.E, d.k, ids, w, s), "top-k");
+  const moe::RouterPlan rp = moe::router_plan(d.T, d.H, d.E);
+  if (x)
+    LAUNCH(MOE_KERNEL_ROUTER, s,
+           moe::launch_router(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wr),
+                              at<float>(ws, L.part), d.T, d.H, d.E, rp, s),
+           "router");
+  LAUNCH(MOE_KERNEL_TOPK, s,
+         moe::launch_topk(x ? at<float>(ws, L.part) : nullptr, rp.slabs, x ? bias : nullptr, logits, d.T, d.E, d.k,
+                          ids, w, s),
+         "top-k");
   LAUNCH(MOE_KERNEL_PERMUTE, s,
          moe::launch_permute(ids, d.T, d.E, d.k, at<uint64_t>(ws, L.masks), at<int32_t>(ws, L.counts),
                              at<int32_t>(ws, L.base), offsets, sorted, pos, at<int32_t>(ws, L.active),
-                             at<int32_t>(ws, L.nact), s),
+                             at<int32_t>(ws, L.nact), x16 ? static_cast<const uint16_t*>(x) : nullptr, x16, d.H,
+                             s),
          "permute");
   return MOE_OK;
 }
 
-moe_status enqueue_ffn(const moe_dims& d, const void* x, const int32_t* offsets, const int32_t* sorted,
-                       const moe_experts* w, float* rows, void* ws, hipStream_t s) {
+// Enqueue the two grouped GEMMs (x16, the active list and the permutation
+// are already in place).
+moe_status enqueue_ffn(const moe_dims& d, const int32_t* offsets, const int32_t* sorted, const moe_experts* w,
+                       float* rows, void* ws, hipStream_t s) {
   const Layout L = layout(d);
   moe::FfnArgs a;
   a.T = d.T;
@@ -168,8 +171,6 @@ moe_status enqueue_ffn(const moe_dims& d, const void* x, const int32_t* offsets,
   a.w = w;
   a.h = at<f16>(ws, L.h);
   a.rows = rows;
-  LAUNCH(MOE_KERNEL_CAST, s,
-         moe::launch_cast(static_cast<const uint16_t*>(x), at<f16>(ws, L.x16), (long long)d.T * d.H, s), "cast");
   LAUNCH(MOE_KERNEL_GATEUP, s, moe::launch_gateup(a, s), "gate/up");
   LAUNCH(MOE_KERNEL_DOWN, s, moe::launch_down(a, s), "down");
   return MOE_OK;
@@ -231,7 +232,7 @@ moe_status moe_route(moe_dims d, const void* x, const void* w_router, const floa
   TRY(check_ptr(pair_pos, "pair_pos"));
   TRY(check_ws(d, ws, ws_bytes));
   return enqueue_route(d, x, w_router, bias, logits, topk_ids, topk_w, expert_offsets, sorted_pairs, pair_pos, ws,
-                       (hipStream_t)stream);
+                       nullptr, (hipStream_t)stream);
 }
 
 moe_status moe_expert_ffn(moe_dims d, const void* x, const int32_t* expert_offsets, const int32_t* sorted_pairs,
@@ -246,11 +247,11 @@ moe_status moe_expert_ffn(moe_dims d, const void* x, const int32_t* expert_offse
   TRY(check_ws(d, ws, ws_bytes));
   const Layout L = layout(d);
   hipStream_t s = (hipStream_t)stream;
-  {
-    hipError_t e = moe::launch_active_list(expert_offsets, d.E, at<int32_t>(ws, L.active), at<int32_t>(ws, L.nact), s);
-    if (e != hipSuccess) return hip_fail(e, "active list");
-  }
-  return enqueue_ffn(d, x, expert_offsets, sorted_pairs, w, rows, ws, s);
+  LAUNCH(MOE_KERNEL_CAST, s, moe::launch_active_list(expert_offsets, d.E, at<int32_t>(ws, L.active),
+                                                     at<int32_t>(ws, L.nact), s), "active list");
+  LAUNCH(MOE_KERNEL_CAST, s,
+         moe::launch_cast(static_cast<const uint16_t*>(x), at<f16>(ws, L.x16), (long long)d.T * d.H, s), "cast");
+  return enqueue_ffn(d, expert_offsets, sorted_pairs, w, rows, ws, s);
 }
 
 moe_status moe_layer(moe_dims d, const void* x, const void* w_router, const float* bias, const moe_experts* w,
@@ -273,8 +274,9 @@ moe_status moe_layer(moe_dims d, const void* x, const void* w_router, const floa
   int32_t* sorted = at<int32_t>(ws, L.sorted);
   int32_t* pos = at<int32_t>(ws, L.pos);
   float* rows = at<float>(ws, L.rows);
-  TRY(enqueue_route(d, x, w_router, bias, at<float>(ws, L.logits), ids, wts, offsets, sorted, pos, ws, s));
-  TRY(enqueue_ffn(d, x, offsets, sorted, w, rows, ws, s));
+  TRY(enqueue_route(d, x, w_router, bias, at<float>(ws, L.logits), ids, wts, offsets, sorted, pos, ws,
+                    at<f16>(ws, L.x16), s));
+  TRY(enqueue_ffn(d, offsets, sorted, w, rows, ws, s));
   LAUNCH(MOE_KERNEL_COMBINE, s,
          moe::launch_combine(rows, pos, wts, d.T, d.H, d.k, static_cast<uint16_t*>(y), s), "combine");
   return MOE_OK;

@@ -9,8 +9,11 @@
 
 namespace moe {
 
-// The router's partial sums over H are split in this many slabs for T tokens.
-int router_slabs(int T, int H, int E);
+// The router's partial sums over H: slabs of slab_rows rows each.
+struct RouterPlan {
+  int slabs, slab_rows;
+};
+RouterPlan router_plan(int T, int H, int E);
 // The permutation works on blocks of 64 tokens (one wavefront each).
 inline int perm_blocks(int T) { return (T + 63) / 64; }
 // Largest number of distinct experts that T tokens can select.
@@ -24,14 +27,17 @@ void prof_before(moe_kernel k, hipStream_t s);
 void prof_after(moe_kernel k, hipStream_t s);
 
 // Launchers.  Each enqueues on `s` and returns hipGetLastError().
-hipError_t launch_router(const uint16_t* x, const uint16_t* wr, float* part, int T, int H, int E, int slabs,
-                         hipStream_t s);
-hipError_t launch_logits_reduce(const float* part, const float* bias, float* logits, int T, int E, int slabs,
-                                hipStream_t s);
-hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s);
+hipError_t launch_router(const uint16_t* x, const uint16_t* wr, float* part, int T, int H, int E,
+                         const RouterPlan& rp, hipStream_t s);
+// Sums the slab partials (part may be NULL: logits are then an input), adds
+// the bias, and selects the top k with their softmax weights.
+hipError_t launch_topk(const float* part, int slabs, const float* bias, float* logits, int T, int E, int k,
+                       int32_t* ids, float* w, hipStream_t s);
+// Offsets, permutation and active-expert list; if x is non-NULL also writes
+// the fp16 copy x16 of the activations [T][H].
 hipError_t launch_permute(const int32_t* ids, int T, int E, int k, uint64_t* masks, int32_t* counts, int32_t* base,
                           int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_pos, int32_t* active,
-                          int32_t* n_active, hipStream_t s);
+                          int32_t* n_active, const uint16_t* x, f16* x16, int H, hipStream_t s);
 hipError_t launch_active_list(const int32_t* offsets, int E, int32_t* active, int32_t* n_active, hipStream_t s);
 hipError_t launch_cast(const uint16_t* x, f16* x16, long long n, hipStream_t s);
 

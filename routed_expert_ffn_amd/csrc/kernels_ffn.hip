@@ -33,8 +33,6 @@ namespace {
 
 constexpr int FFN_THREADS = 256;
 constexpr int KCHUNK = 256;
-constexpr int GU_COLS = 32;    // h columns per gate/up block (32 gate + 32 up rows)
-constexpr int DN_COLS = 64;    // output columns per down block
 
 struct GroupedParams {
   int H, I, k;
@@ -53,156 +51,188 @@ struct GroupedParams {
   float* rows;         // down output [P][H]
 };
 
-// K loop shared by both GEMMs: accumulate the block's 64 weight rows
-// (qrow[ng] / srow[ng] point at row r of group ng) against MF 16-token
-// fragments of A rows arow[f] (nvalid rows are real), over chunks
-// c = wv, wv+4, ... of K.
+// One 256-k chunk of a wavefront's operands: per weight row group ng, 32
+// NVFP4 code bytes (64 consecutive k) and their 4 scale bytes; per token
+// fragment f, the eight A fragments of the chunk.  All of a chunk's loads are
+// issued together so the wavefront waits once per chunk, not once per MFMA.
 template <int MF>
-__device__ __forceinline__ void kloop(f32x4 (&acc)[MF][4], const uint8_t* const (&qrow)[4],
-                                      const uint8_t* const (&srow)[4], const f16* const (&arow)[MF], int K, int wv,
-                                      int g, int nvalid) {
-  const int nchunks = K / KCHUNK;
-  for (int c = wv; c < nchunks; c += 4) {
-    const int kb = c * KCHUNK + 64 * g;
-    uint4 qa[4], qb[4];
-    uint32_t sc[4];
+struct Chunk {
+  uint4 qa[4], qb[4];
+  uint32_t sc[4];
+  f16x8 a[MF][8];
+};
+
+template <int MF>
+__device__ __forceinline__ void load_b(Chunk<MF>& ch, const uint8_t* const (&qrow)[4],
+                                       const uint8_t* const (&srow)[4], int kb) {
 #pragma unroll
-    for (int ng = 0; ng < 4; ng++) {
-      qa[ng] = *reinterpret_cast<const uint4*>(qrow[ng] + kb / 2);
-      qb[ng] = *reinterpret_cast<const uint4*>(qrow[ng] + kb / 2 + 16);
-      sc[ng] = *reinterpret_cast<const uint32_t*>(srow[ng] + kb / 16);
-    }
-#pragma unroll
-    for (int s = 0; s < 8; s++) {
-      f16x8 bf[4];
-#pragma unroll
-      for (int ng = 0; ng < 4; ng++) {
-        const uint32_t codes = s < 4 ? (&qa[ng].x)[s] : (&qb[ng].x)[s - 4];
-        const f16 sig = e4m3_to_f16((sc[ng] >> (8 * (s / 2))) & 0xFFu);
-        f16x2 sig2;
-        sig2[0] = sig;
-        sig2[1] = sig;
-        bf[ng] = dequant8(codes, sig2);
-      }
-#pragma unroll
-      for (int f = 0; f < MF; f++) {
-        if (f * 16 < nvalid) {
-          const f16x8 av = load_f16x8(arow[f] + kb + 8 * s);
-#pragma unroll
-          for (int ng = 0; ng < 4; ng++) acc[f][ng] = mfma16x16x32(av, bf[ng], acc[f][ng]);
-        }
-      }
-    }
+  for (int ng = 0; ng < 4; ng++) {
+    ch.qa[ng] = *reinterpret_cast<const uint4*>(qrow[ng] + kb / 2);
+    ch.qb[ng] = *reinterpret_cast<const uint4*>(qrow[ng] + kb / 2 + 16);
+    ch.sc[ng] = *reinterpret_cast<const uint32_t*>(srow[ng] + kb / 16);
   }
 }
 
 template <int MF>
-__device__ __forceinline__ void spill_partials(float (*red)[WAVE][MF * 16], f32x4 (&acc)[MF][4], int wv, int lane) {
+__device__ __forceinline__ void load_a(Chunk<MF>& ch, const f16* const (&arow)[MF], int kb, int nvalid) {
 #pragma unroll
   for (int f = 0; f < MF; f++)
+    if (f * 16 < nvalid)
 #pragma unroll
-    for (int ng = 0; ng < 4; ng++)
+      for (int s = 0; s < 8; s++) ch.a[f][s] = load_f16x8(arow[f] + kb + 8 * s);
+}
+
+// acc[f][ng] += A fragments x dequantised weights of one chunk.  Each row
+// group is dequantised and multiplied in turn, so one B fragment is live.
+template <int MF>
+__device__ __forceinline__ void mma_chunk(f32x4 (&acc)[MF][4], const Chunk<MF>& ch, int nvalid) {
 #pragma unroll
-      for (int i = 0; i < 4; i++) red[wv][lane][(f * 4 + ng) * 4 + i] = acc[f][ng][i];
+  for (int s = 0; s < 8; s++) {
+#pragma unroll
+    for (int ng = 0; ng < 4; ng++) {
+      const uint32_t codes = s < 4 ? (&ch.qa[ng].x)[s] : (&ch.qb[ng].x)[s - 4];
+      const f16 sig = e4m3_to_f16((ch.sc[ng] >> (8 * (s / 2))) & 0xFFu);
+      f16x2 sig2;
+      sig2[0] = sig;
+      sig2[1] = sig;
+      const f16x8 bf = dequant8(codes, sig2);
+#pragma unroll
+      for (int f = 0; f < MF; f++)
+        if (f * 16 < nvalid) acc[f][ng] = mfma16x16x32(ch.a[f][s], bf, acc[f][ng]);
+    }
+  }
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
-// h[p][i] = SiLU(gs_g * (x.Wg)[i]) * (gs_u * (x.Wu)[i]) for the pairs p of
-// expert active[blockIdx.y], columns i in [32*blockIdx.x, +32).
-template <int MF>
-__global__ __launch_bounds__(FFN_THREADS) void gateup_kernel(GroupedParams p) {
-  __shared__ float red[4][WAVE][MF * 16];
+// One grouped NVFP4 GEMM over the active experts (blockIdx.y indexes the
+// active list).  A block is four wavefronts; KSPLIT consecutive wavefronts
+// share one 64-row tile and take interleaved 256-k chunks of K, so a block
+// covers 4/KSPLIT row tiles.
+//   GATEUP: a row tile is 32 columns of h: gate rows (groups 0, 1) and the
+//           same up rows (groups 2, 3); the epilogue applies the per-tensor
+//           scales and SiLU(gate) * up and stores h in fp16.
+//   down:   a row tile is 64 output columns; rows = gs_d * (h . Wd).
+// The first chunk's weight loads are issued before the token rows are
+// looked up, and each later chunk is loaded while the previous one is
+// multiplied.  Partial sums of the KSPLIT wavefronts meet in LDS and are
+// added in a fixed order.
+template <int MF, int KSPLIT, bool GATEUP, bool DB, int WAVES_PER_EU>
+__global__ __launch_bounds__(FFN_THREADS, WAVES_PER_EU) void expert_gemm_kernel(GroupedParams p) {
+  constexpr int RT = 4 / KSPLIT;
+  __shared__ float red[KSPLIT > 1 ? 4 : 1][WAVE][MF * 16];
   if ((int)blockIdx.y >= *p.n_active) return;
   const int e = p.active[blockIdx.y];
-  const int begin = p.offsets[e], end = p.offsets[e + 1];
-  const int H = p.H, I = p.I;
-  const int i0 = blockIdx.x * GU_COLS;
   const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE, r = lane % 16, g = lane / 16;
+  const int rt = wv / KSPLIT, ks = wv % KSPLIT;
+  const int K = GATEUP ? p.H : p.I;
+  const int N = GATEUP ? p.I : p.H;
+  const int tile = blockIdx.x * RT + rt;
   const uint8_t* qrow[4];
   const uint8_t* srow[4];
 #pragma unroll
   for (int ng = 0; ng < 4; ng++) {
-    const size_t row = (size_t)e * I + i0 + 16 * (ng & 1) + r;
-    qrow[ng] = (ng < 2 ? p.q0 : p.q1) + row * (H / 2);
-    srow[ng] = (ng < 2 ? p.sf0 : p.sf1) + row * (H / 16);
+    size_t row;
+    const uint8_t* qb;
+    const uint8_t* sb;
+    if (GATEUP) {
+      row = (size_t)e * N + tile * 32 + 16 * (ng & 1) + r;
+      qb = ng < 2 ? p.q0 : p.q1;
+      sb = ng < 2 ? p.sf0 : p.sf1;
+    } else {
+      row = (size_t)e * N + tile * 64 + 16 * ng + r;
+      qb = p.q0;
+      sb = p.sf0;
+    }
+    qrow[ng] = qb + row * (K / 2);
+    srow[ng] = sb + row * (K / 16);
   }
-  const float gsg = p.gs0[e], gsu = p.gs1[e];
+  const int nchunks = K / KCHUNK;
+  Chunk<MF> cur;
+  if (ks < nchunks) load_b(cur, qrow, srow, ks * KCHUNK + 64 * g);  // before the token lookups
+  const int begin = p.offsets[e], end = p.offsets[e + 1];
+  const float gsa = p.gs0[e], gsb = GATEUP ? p.gs1[e] : 0.0f;
+  bool first_pass = true;
   for (int mb = begin; mb < end; mb += MF * 16) {
     const int nvalid = end - mb;
     const f16* arow[MF];
 #pragma unroll
     for (int f = 0; f < MF; f++) {
       const int pp = min(mb + f * 16 + r, end - 1);
-      arow[f] = p.a + (size_t)(p.sorted_pairs[pp] / p.k) * H;
+      arow[f] = GATEUP ? p.a + (size_t)(p.sorted_pairs[pp] / p.k) * K : p.a + (size_t)pp * K;
     }
     f32x4 acc[MF][4];
 #pragma unroll
     for (int f = 0; f < MF; f++)
 #pragma unroll
       for (int ng = 0; ng < 4; ng++) acc[f][ng] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    kloop<MF>(acc, qrow, srow, arow, H, wv, g, nvalid);
-    spill_partials<MF>(red, acc, wv, lane);
-    __syncthreads();
-    // Outputs (f, column pair cp, lane ln, i): gate in group cp, up in cp+2.
-    for (int q = threadIdx.x; q < MF * 2 * WAVE * 4; q += FFN_THREADS) {
-      const int i = q % 4, ln = (q / 4) % WAVE, cp = (q / (4 * WAVE)) % 2, f = q / (8 * WAVE);
-      const int m = f * 16 + 4 * (ln / 16) + i;
-      if (m < nvalid) {
-        const int gi = (f * 4 + cp) * 4 + i, ui = (f * 4 + cp + 2) * 4 + i;
-        const float G = ((red[0][ln][gi] + red[1][ln][gi]) + red[2][ln][gi]) + red[3][ln][gi];
-        const float U = ((red[0][ln][ui] + red[1][ln][ui]) + red[2][ln][ui]) + red[3][ln][ui];
-        const float hv = silu(gsg * G) * (gsu * U);
-        p.h[(size_t)(mb + m) * I + i0 + cp * 16 + ln % 16] = (f16)hv;
+    if (ks < nchunks) {
+      if (!first_pass) load_b(cur, qrow, srow, ks * KCHUNK + 64 * g);
+      load_a(cur, arow, ks * KCHUNK + 64 * g, nvalid);
+    }
+    first_pass = false;
+    for (int c = ks; c < nchunks; c += KSPLIT) {
+      const int kb = c * KCHUNK + 64 * g;
+      const bool more = c + KSPLIT < nchunks;
+      if (DB) {  // load the next chunk while this one is multiplied
+        Chunk<MF> nxt;
+        if (more) {
+          load_b(nxt, qrow, srow, kb + KSPLIT * KCHUNK);
+          load_a(nxt, arow, kb + KSPLIT * KCHUNK, nvalid);
+        }
+        mma_chunk<MF>(acc, cur, nvalid);
+        if (more) cur = nxt;
+      } else {
+        mma_chunk<MF>(acc, cur, nvalid);
+        if (more) {
+          load_b(cur, qrow, srow, kb + KSPLIT * KCHUNK);
+          load_a(cur, arow, kb + KSPLIT * KCHUNK, nvalid);
+        }
       }
     }
-    __syncthreads();
-  }
-}
-
-// rows[p][n] = gs_d * (h[p].Wd)[n] for the pairs p of expert
-// active[blockIdx.y], columns n in [64*blockIdx.x, +64).
-template <int MF>
-__global__ __launch_bounds__(FFN_THREADS) void down_kernel(GroupedParams p) {
-  __shared__ float red[4][WAVE][MF * 16];
-  if ((int)blockIdx.y >= *p.n_active) return;
-  const int e = p.active[blockIdx.y];
-  const int begin = p.offsets[e], end = p.offsets[e + 1];
-  const int H = p.H, I = p.I;
-  const int n0 = blockIdx.x * DN_COLS;
-  const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE, r = lane % 16, g = lane / 16;
-  const uint8_t* qrow[4];
-  const uint8_t* srow[4];
+    if (KSPLIT > 1) {
 #pragma unroll
-  for (int ng = 0; ng < 4; ng++) {
-    const size_t row = (size_t)e * H + n0 + 16 * ng + r;
-    qrow[ng] = p.q0 + row * (I / 2);
-    srow[ng] = p.sf0 + row * (I / 16);
-  }
-  const float gsd = p.gs0[e];
-  for (int mb = begin; mb < end; mb += MF * 16) {
-    const int nvalid = end - mb;
-    const f16* arow[MF];
+      for (int f = 0; f < MF; f++)
 #pragma unroll
-    for (int f = 0; f < MF; f++) arow[f] = p.a + (size_t)min(mb + f * 16 + r, end - 1) * I;
-    f32x4 acc[MF][4];
+        for (int ng = 0; ng < 4; ng++)
 #pragma unroll
-    for (int f = 0; f < MF; f++)
+          for (int i = 0; i < 4; i++) red[wv][lane][(f * 4 + ng) * 4 + i] = acc[f][ng][i];
+      __syncthreads();
+      if (ks == 0) {
 #pragma unroll
-      for (int ng = 0; ng < 4; ng++) acc[f][ng] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    kloop<MF>(acc, qrow, srow, arow, I, wv, g, nvalid);
-    spill_partials<MF>(red, acc, wv, lane);
-    __syncthreads();
-    for (int q = threadIdx.x; q < MF * 4 * WAVE * 4; q += FFN_THREADS) {
-      const int i = q % 4, ln = (q / 4) % WAVE, ng = (q / (4 * WAVE)) % 4, f = q / (16 * WAVE);
-      const int m = f * 16 + 4 * (ln / 16) + i;
-      if (m < nvalid) {
-        const int xi = (f * 4 + ng) * 4 + i;
-        const float v = ((red[0][ln][xi] + red[1][ln][xi]) + red[2][ln][xi]) + red[3][ln][xi];
-        p.rows[(size_t)(mb + m) * H + n0 + 16 * ng + ln % 16] = gsd * v;
+        for (int f = 0; f < MF; f++)
+#pragma unroll
+          for (int ng = 0; ng < 4; ng++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+              float v = red[wv][lane][(f * 4 + ng) * 4 + i];
+#pragma unroll
+              for (int s2 = 1; s2 < KSPLIT; s2++) v += red[wv + s2][lane][(f * 4 + ng) * 4 + i];
+              acc[f][ng][i] = v;
+            }
       }
     }
-    __syncthreads();
+    if (ks == 0) {
+#pragma unroll
+      for (int f = 0; f < MF; f++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int m = f * 16 + 4 * g + i;
+          if (m < nvalid) {
+            if (GATEUP) {
+#pragma unroll
+              for (int cp = 0; cp < 2; cp++) {
+                const float hv = silu(gsa * acc[f][cp][i]) * (gsb * acc[f][cp + 2][i]);
+                p.h[(size_t)(mb + m) * N + tile * 32 + 16 * cp + r] = (f16)hv;
+              }
+            } else {
+#pragma unroll
+              for (int ng = 0; ng < 4; ng++) p.rows[(size_t)(mb + m) * N + tile * 64 + 16 * ng + r] = gsa * acc[f][ng][i];
+            }
+          }
+        }
+    }
+    if (KSPLIT > 1) __syncthreads();
   }
 }
 
@@ -232,7 +262,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 }
 
 // Fragments per pass: an expert never has more pairs than there are tokens.
-int pick_mf(int T) { return T <= 16 ? 1 : (T <= 32 ? 2 : 4); }
+// At decode sizes one 16-token fragment per pass keeps two wavefronts per
+// SIMD resident; an expert with more tokens takes several passes, the later
+// ones re-reading its weights from the caches.  Large batches use four.
+int pick_mf(int T) { return T <= 1024 ? 1 : 4; }
 
 GroupedParams base_params(const FfnArgs& a) {
   GroupedParams p{};
@@ -248,6 +281,34 @@ GroupedParams base_params(const FfnArgs& a) {
   return p;
 }
 
+// Row tiles per block: gate/up splits K over all four wavefronts (one
+// 32-column tile per block), down over two (two 64-column tiles per block).
+constexpr int GU_KSPLIT = 4;
+constexpr int DN_KSPLIT = 2;
+
+// Measured on MI355X at T = 1, 64 and 256: no register double buffer and a
+// two-wavefronts-per-SIMD register budget stream fastest.
+constexpr bool GEMM_DB = false;
+constexpr int GEMM_WAVES = 2;
+
+template <int KSPLIT, bool GATEUP>
+hipError_t launch_gemm(const GroupedParams& p, int mf, dim3 grid, hipStream_t s) {
+  switch (mf) {
+    case 1:
+      hipLaunchKernelGGL((expert_gemm_kernel<1, KSPLIT, GATEUP, GEMM_DB, GEMM_WAVES>), grid, dim3(FFN_THREADS),
+                         0, s, p);
+      break;
+    case 2:
+      hipLaunchKernelGGL((expert_gemm_kernel<2, KSPLIT, GATEUP, GEMM_DB, GEMM_WAVES>), grid, dim3(FFN_THREADS),
+                         0, s, p);
+      break;
+    default:
+      hipLaunchKernelGGL((expert_gemm_kernel<4, KSPLIT, GATEUP, GEMM_DB, 1>), grid, dim3(FFN_THREADS), 0, s, p);
+      break;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gateup(const FfnArgs& a, hipStream_t s) {
@@ -259,13 +320,8 @@ hipError_t launch_gateup(const FfnArgs& a, hipStream_t s) {
   p.q1 = a.w->up.q;
   p.sf1 = a.w->up.sf;
   p.gs1 = a.w->up.gs;
-  const dim3 grid(a.I / GU_COLS, a.max_active);
-  switch (pick_mf(a.T)) {
-    case 1: hipLaunchKernelGGL((gateup_kernel<1>), grid, dim3(FFN_THREADS), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((gateup_kernel<2>), grid, dim3(FFN_THREADS), 0, s, p); break;
-    default: hipLaunchKernelGGL((gateup_kernel<4>), grid, dim3(FFN_THREADS), 0, s, p); break;
-  }
-  return hipGetLastError();
+  const dim3 grid(a.I / (32 * (4 / GU_KSPLIT)), a.max_active);
+  return launch_gemm<GU_KSPLIT, true>(p, pick_mf(a.T), grid, s);
 }
 
 hipError_t launch_down(const FfnArgs& a, hipStream_t s) {
@@ -274,13 +330,8 @@ hipError_t launch_down(const FfnArgs& a, hipStream_t s) {
   p.q0 = a.w->down.q;
   p.sf0 = a.w->down.sf;
   p.gs0 = a.w->down.gs;
-  const dim3 grid(a.H / DN_COLS, a.max_active);
-  switch (pick_mf(a.T)) {
-    case 1: hipLaunchKernelGGL((down_kernel<1>), grid, dim3(FFN_THREADS), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((down_kernel<2>), grid, dim3(FFN_THREADS), 0, s, p); break;
-    default: hipLaunchKernelGGL((down_kernel<4>), grid, dim3(FFN_THREADS), 0, s, p); break;
-  }
-  return hipGetLastError();
+  const dim3 grid(a.H / (64 * (4 / DN_KSPLIT)), a.max_active);
+  return launch_gemm<DN_KSPLIT, false>(p, pick_mf(a.T), grid, s);
 }
 
 hipError_t launch_combine(const float* rows, const int32_t* pair_pos, const float* w, int T, int H, int k,

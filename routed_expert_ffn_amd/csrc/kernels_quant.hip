@@ -31,7 +31,13 @@ __global__ __launch_bounds__(256) void amax_kernel(const float* __restrict__ w, 
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, WAVE));
-  if (threadIdx.x % WAVE == 0) atomicMax(amax_bits, m);
+  __shared__ uint32_t wmax[256 / WAVE];
+  if (threadIdx.x % WAVE == 0) wmax[threadIdx.x / WAVE] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {  // one atomic per block
+    for (int i = 1; i < 256 / WAVE; i++) m = max(m, wmax[i]);
+    atomicMax(amax_bits, m);
+  }
 }
 
 // Nearest non-negative finite e4m3 code to t >= 0, ties to the even code;
@@ -122,7 +128,9 @@ hipError_t launch_quantize(const float* w, int64_t N, int64_t K, uint8_t* q, uin
                            hipStream_t s) {
   const long long n = (long long)N * K;
   hipLaunchKernelGGL(zero_word_kernel, dim3(1), dim3(1), 0, s, ws);
-  hipLaunchKernelGGL(amax_kernel, dim3(grid_for(n / 4)), dim3(256), 0, s, w, n / 4, ws);
+  long long ga = (n / 4 + 4095) / 4096;  // >= 16 float4 per thread
+  if (ga > 1024) ga = 1024;
+  hipLaunchKernelGGL(amax_kernel, dim3((unsigned)(ga > 0 ? ga : 1)), dim3(256), 0, s, w, n / 4, ws);
   hipLaunchKernelGGL(quant_kernel, dim3(grid_for(n / 16)), dim3(256), 0, s, w, n / 16, q, sf, gs, ws);
   return hipGetLastError();
 }

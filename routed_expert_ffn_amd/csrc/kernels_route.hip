@@ -1,6 +1,5 @@
-// Routing on gfx950: router logits, softmax + top-k at one wavefront per
-// token, and the token-to-expert permutation built from a histogram and a
-// prefix scan.
+// Routing on gfx950: router logits, softmax + top-k, and the token-to-expert
+// permutation built from a histogram and a prefix scan.
 //
 // What is computed follows "Computation and Data Movement for Inference"
 // (section 3.4 "Decode experts": the router, a small tensor, picks a few
@@ -13,84 +12,90 @@
 namespace moe {
 namespace {
 
-// ---- router logits: partial sums over slabs of H ---------------------------
-// logits[t][e] = sum_h x[t][h] * W_r[h][e] with W_r stored [H][E] (E
-// contiguous).  Each lane owns 8 consecutive experts (one 16-byte load per
-// row h) and TT tokens; the four waves of a block take interleaved rows of
-// the block's slab and are summed through LDS, then each slab writes its
-// partial [slab][T][E].  bf16 x bf16 products are exact in fp32, so only the
-// summation order differs from an exact dot product.
+// ---- router logits: 2-D tiled GEMV with slab partial sums ---------------------
+// logits[t][e] = sum_h x[t][h] * W_r[h][e], W_r stored [H][E] (E contiguous).
+// A block owns 128 experts (16 lanes x 8 experts, one 16-byte load per row)
+// and a slab of rows; lane l reads row 4*wave + l/16 of each 16-row step, so
+// one wavefront load covers four 256-byte row segments.  The 16 lanes that
+// share a column group are summed with two butterfly steps and then across
+// the four waves through LDS, in a fixed order, and the block writes one
+// partial per (slab, token, expert).  bf16 x bf16 products are exact in fp32.
 constexpr int RT_THREADS = 256;
-constexpr int RT_E_PER_BLOCK = WAVE * 8;  // 512 experts per block
+constexpr int RT_E_TILE = 128;
+constexpr int RT_ROWS_PER_STEP = 16;
 
 template <int TT>
-__global__ __launch_bounds__(RT_THREADS) void router_partial_kernel(const uint16_t* __restrict__ x,
-                                                                   const uint16_t* __restrict__ wr,
-                                                                   float* __restrict__ part, int T, int H, int E,
-                                                                   int slab_rows) {
-  __shared__ float red[4][WAVE][TT * 8];
+__global__ __launch_bounds__(RT_THREADS) void router_gemv_kernel(const uint16_t* __restrict__ x,
+                                                                const uint16_t* __restrict__ wr,
+                                                                float* __restrict__ part, int T, int H, int E,
+                                                                int slab_rows) {
+  extern __shared__ float smem[];
+  float* xs = smem;                               // [TT][slab_rows]
+  float* red = smem + TT * slab_rows;             // [4 waves][16 groups][TT * 8]
   const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE;
-  const int e0 = blockIdx.x * RT_E_PER_BLOCK + lane * 8;
-  const int t0 = blockIdx.y * TT;
-  const int h0 = blockIdx.z * slab_rows;
-  const int h1 = min(H, h0 + slab_rows);
+  const int cg = lane % 16, rr = lane / 16;
+  const int e0 = blockIdx.x * RT_E_TILE + cg * 8;
+  const int h0 = blockIdx.y * slab_rows;
+  const int t0 = blockIdx.z * TT;
+  const int rows = min(slab_rows, H - h0);
+  for (int i = threadIdx.x; i < TT * slab_rows; i += RT_THREADS) {
+    const int a = i / slab_rows, r = i % slab_rows;
+    xs[i] = (t0 + a < T && r < rows) ? bf16_to_f32(x[(size_t)(t0 + a) * H + h0 + r]) : 0.0f;
+  }
+  __syncthreads();
   float acc[TT][8];
 #pragma unroll
   for (int a = 0; a < TT; a++)
 #pragma unroll
     for (int i = 0; i < 8; i++) acc[a][i] = 0.0f;
   if (e0 < E) {
-    for (int h = h0 + wv; h < h1; h += 4) {
-      uint4 wv8 = *reinterpret_cast<const uint4*>(wr + (size_t)h * E + e0);
+    for (int r = 4 * wv + rr; r < rows; r += RT_ROWS_PER_STEP) {
+      const uint4 w8 = *reinterpret_cast<const uint4*>(wr + (size_t)(h0 + r) * E + e0);
       float wf[8];
-      wf[0] = __uint_as_float(wv8.x << 16); wf[1] = __uint_as_float(wv8.x & 0xFFFF0000u);
-      wf[2] = __uint_as_float(wv8.y << 16); wf[3] = __uint_as_float(wv8.y & 0xFFFF0000u);
-      wf[4] = __uint_as_float(wv8.z << 16); wf[5] = __uint_as_float(wv8.z & 0xFFFF0000u);
-      wf[6] = __uint_as_float(wv8.w << 16); wf[7] = __uint_as_float(wv8.w & 0xFFFF0000u);
+      wf[0] = __uint_as_float(w8.x << 16); wf[1] = __uint_as_float(w8.x & 0xFFFF0000u);
+      wf[2] = __uint_as_float(w8.y << 16); wf[3] = __uint_as_float(w8.y & 0xFFFF0000u);
+      wf[4] = __uint_as_float(w8.z << 16); wf[5] = __uint_as_float(w8.z & 0xFFFF0000u);
+      wf[6] = __uint_as_float(w8.w << 16); wf[7] = __uint_as_float(w8.w & 0xFFFF0000u);
 #pragma unroll
       for (int a = 0; a < TT; a++) {
-        if (t0 + a < T) {
-          float xv = bf16_to_f32(x[(size_t)(t0 + a) * H + h]);
+        const float xv = xs[a * slab_rows + r];
 #pragma unroll
-          for (int i = 0; i < 8; i++) acc[a][i] = fmaf(xv, wf[i], acc[a][i]);
-        }
+        for (int i = 0; i < 8; i++) acc[a][i] = fmaf(xv, wf[i], acc[a][i]);
       }
     }
   }
 #pragma unroll
   for (int a = 0; a < TT; a++)
 #pragma unroll
-    for (int i = 0; i < 8; i++) red[wv][lane][a * 8 + i] = acc[a][i];
+    for (int i = 0; i < 8; i++) {
+      float v = acc[a][i];
+      v += __shfl_xor(v, 16, WAVE);
+      v += __shfl_xor(v, 32, WAVE);
+      if (rr == 0) red[(wv * 16 + cg) * (TT * 8) + a * 8 + i] = v;
+    }
   __syncthreads();
-  // Sum the four waves in a fixed order; thread -> (token a, expert i).
-  for (int q = threadIdx.x; q < WAVE * TT * 8; q += RT_THREADS) {
-    int ln = q / (TT * 8), ai = q % (TT * 8), a = ai / 8, i = ai % 8;
-    int e = blockIdx.x * RT_E_PER_BLOCK + ln * 8 + i;
+  for (int q = threadIdx.x; q < 16 * TT * 8; q += RT_THREADS) {
+    const int g = q / (TT * 8), ai = q % (TT * 8), a = ai / 8, i = ai % 8;
+    const int e = blockIdx.x * RT_E_TILE + g * 8 + i;
     if (e < E && t0 + a < T) {
-      float s = ((red[0][ln][ai] + red[1][ln][ai]) + red[2][ln][ai]) + red[3][ln][ai];
-      part[((size_t)blockIdx.z * T + (t0 + a)) * E + e] = s;
+      const float s = ((red[(0 * 16 + g) * (TT * 8) + ai] + red[(1 * 16 + g) * (TT * 8) + ai]) +
+                       red[(2 * 16 + g) * (TT * 8) + ai]) +
+                      red[(3 * 16 + g) * (TT * 8) + ai];
+      part[((size_t)blockIdx.y * T + (t0 + a)) * E + e] = s;
     }
   }
 }
 
-// logits[t][e] = (sum over slabs, ascending) + bias[e].
-__global__ __launch_bounds__(256) void logits_reduce_kernel(const float* __restrict__ part,
-                                                           const float* __restrict__ bias,
-                                                           float* __restrict__ logits, int T, int E, int slabs) {
-  const int t = blockIdx.y;
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  if (e >= E) return;
-  float s = 0.0f;
-  for (int z = 0; z < slabs; z++) s += part[((size_t)z * T + t) * E + e];
-  if (bias) s += bias[e];
-  logits[(size_t)t * E + e] = s;
-}
-
-// ---- softmax + top-k: one wavefront per token ------------------------------
-// Selection key: a 64-bit integer whose order is (logit descending, expert
-// index ascending): the high word maps the fp32 logit to an order-preserving
-// unsigned integer (with -0 folded onto +0), the low word is ~index.
-constexpr int TOPK_MAX_PER_LANE = 16;  // E <= 1024
+// ---- logits reduction + softmax + top-k ------------------------------------------
+// A block takes TB tokens.  All 1024 threads first sum the slab partials of
+// those tokens' logits (fixed ascending slab order), add the bias and store
+// the logits; then wavefront w selects the top k of token w.
+// Selection key: a 64-bit integer ordered as (logit descending, expert index
+// ascending): the high word maps the fp32 logit to an order-preserving
+// unsigned integer (-0 folded onto +0), the low word is ~index.  Each lane
+// sorts its (up to) 16 keys, then k rounds each take the wavefront maximum
+// of the lanes' heads and pop it from the winning lane.
+constexpr int TOPK_KEYS = 16;  // E <= 1024
 
 __device__ __forceinline__ uint32_t float_order(float f) {
   uint32_t u = __float_as_uint(f == 0.0f ? 0.0f : f);
@@ -102,7 +107,7 @@ __device__ __forceinline__ float order_float(uint32_t o) {
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
-    uint64_t o = __shfl_xor(v, off, WAVE);
+    const uint64_t o = __shfl_xor(v, off, WAVE);
     v = o > v ? o : v;
   }
   return v;
@@ -113,56 +118,186 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E, int k,
-                                                  int32_t* __restrict__ ids, float* __restrict__ wout) {
-  const int lane = threadIdx.x % WAVE;
-  const int t = blockIdx.x * 4 + threadIdx.x / WAVE;
-  if (t >= T) return;  // whole wavefront leaves together
-  const float* row = logits + (size_t)t * E;
-  uint64_t key[TOPK_MAX_PER_LANE];
+__device__ __forceinline__ void cas_desc(uint64_t& a, uint64_t& b) {
+  const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
+  a = hi;
+  b = lo;
+}
+
+// Bitonic sort of 16 keys, descending.
+__device__ __forceinline__ void sort16_desc(uint64_t (&k)[TOPK_KEYS]) {
 #pragma unroll
-  for (int i = 0; i < TOPK_MAX_PER_LANE; i++) {
-    int e = lane + WAVE * i;
-    key[i] = 0;  // below every real key
-    if (e < E) key[i] = ((uint64_t)float_order(row[e]) << 32) | (uint32_t)~(uint32_t)e;
+  for (int size = 2; size <= 16; size <<= 1)
+#pragma unroll
+    for (int stride = size / 2; stride > 0; stride >>= 1)
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        const int j = i ^ stride;
+        if (j > i) {
+          if ((i & size) == 0)
+            cas_desc(k[i], k[j]);
+          else
+            cas_desc(k[j], k[i]);
+        }
+      }
+}
+
+constexpr int TOPK_THREADS = 1024;
+
+template <int TB>
+__global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(const float* __restrict__ part, int slabs,
+                                                           const float* __restrict__ bias,
+                                                           float* __restrict__ logits, int T, int E, int k,
+                                                           int32_t* __restrict__ ids, float* __restrict__ wout) {
+  __shared__ float ls[TB * 1024];
+  const int t0 = blockIdx.x * TB;
+  // Phase 1: logits of this block's tokens; the slab partials of a logit are
+  // loaded 16 at a time and added in ascending slab order.
+  for (int idx = threadIdx.x; idx < TB * E; idx += TOPK_THREADS) {
+    const int a = idx / E, e = idx % E, t = t0 + a;
+    if (t >= T) continue;
+    float v;
+    if (part) {
+      const float* p = part + (size_t)t * E + e;
+      const size_t step = (size_t)T * E;
+      v = 0.0f;
+      int z = 0;
+      for (; z + 16 <= slabs; z += 16) {
+        float b[16];
+#pragma unroll
+        for (int u = 0; u < 16; u++) b[u] = p[(size_t)(z + u) * step];
+#pragma unroll
+        for (int u = 0; u < 16; u++) v += b[u];
+      }
+      for (; z < slabs; z++) v += p[(size_t)z * step];
+      if (bias) v += bias[e];
+      logits[(size_t)t * E + e] = v;
+    } else {
+      v = logits[(size_t)t * E + e];  // logits given by the caller
+    }
+    ls[a * 1024 + e] = v;
   }
+  __syncthreads();
+  // Phase 2: wavefront w selects for token t0 + w.
+  const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE;
+  const int t = t0 + wv;
+  if (wv >= TB || t >= T) return;
+  uint64_t key[TOPK_KEYS];
+#pragma unroll
+  for (int i = 0; i < TOPK_KEYS; i++) {
+    const int e = lane + WAVE * i;
+    key[i] = e < E ? (((uint64_t)float_order(ls[wv * 1024 + e]) << 32) | (uint32_t)~(uint32_t)e) : 0ull;
+  }
+  sort16_desc(key);
   int my_id = 0;
   float my_logit = 0.0f, top = 0.0f;
   for (int j = 0; j < k; j++) {
-    uint64_t best = 0;
-#pragma unroll
-    for (int i = 0; i < TOPK_MAX_PER_LANE; i++) best = key[i] > best ? key[i] : best;
-    best = wave_max_u64(best);
+    const uint64_t best = wave_max_u64(key[0]);
     const int e = (int)~(uint32_t)best;
     const float l = order_float((uint32_t)(best >> 32));
     if (j == 0) top = l;
-    if (lane == (e % WAVE)) {
-#pragma unroll
-      for (int i = 0; i < TOPK_MAX_PER_LANE; i++)
-        if (i == e / WAVE) key[i] = 0;
-    }
     if (lane == j) {
       my_id = e;
       my_logit = l;
     }
+    const bool pop = key[0] == best;  // keys are unique: only the owner pops
+#pragma unroll
+    for (int i = 0; i < TOPK_KEYS - 1; i++) key[i] = pop ? key[i + 1] : key[i];
+    key[TOPK_KEYS - 1] = pop ? 0ull : key[TOPK_KEYS - 1];
   }
-  // w_j = exp(l_j - l_0) / sum_j' exp(l_j' - l_0): softmax restricted to the
-  // selected logits, identical to the full softmax renormalised over them.
-  float ex = lane < k ? expf(my_logit - top) : 0.0f;
-  float sum = wave_sum(ex);
+  // w_j = exp(l_j - l_0) / sum_j' exp(l_j' - l_0): the softmax restricted to
+  // the selected logits, equal to the full softmax renormalised over them.
+  const float ex = lane < k ? expf(my_logit - top) : 0.0f;
+  const float sum = wave_sum(ex);
   if (lane < k) {
     ids[(size_t)t * k + lane] = my_id;
     wout[(size_t)t * k + lane] = ex / sum;
   }
 }
 
-// ---- permutation: histogram, scan, stable scatter ----------------------------
-// Tokens are processed in blocks of 64 (one per lane).  For block b and
-// expert e, mask[b][e] has bit l set when token 64b+l selected e.  The
-// records of expert e are ordered by token, so the position of record
-// (t, j) is offsets[e] + (records of e in earlier blocks) + popcount of the
-// mask bits below lane l.  Integer work only: exact and deterministic.
+// ---- permutation ---------------------------------------------------------------
+// For a block of up to 64 tokens and expert e, mask[e] has bit l set when
+// token 64b+l selected e.  The records of expert e are ordered by token, so
+// record (t, j) goes to offsets[e] + (records of e in earlier blocks) +
+// popcount of the mask bits below l.  Integer work only: exact and
+// deterministic.
 constexpr int PERM_MAX_E = 1024;
+
+// Block-wide exclusive scan of one int per thread (blockDim.x = 1024).
+__device__ int block_exclusive_scan(int v, int* lds /*[16]*/, int* total) {
+  const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < WAVE; off <<= 1) {
+    const int o = __shfl_up(incl, off, WAVE);
+    if (lane >= off) incl += o;
+  }
+  if (lane == WAVE - 1) lds[wv] = incl;
+  __syncthreads();
+  int base = 0, all = 0;
+  for (int i = 0; i < (int)(blockDim.x / WAVE); i++) {
+    if (i < wv) base += lds[i];
+    all += lds[i];
+  }
+  __syncthreads();
+  *total = all;
+  return base + incl - v;
+}
+
+__device__ __forceinline__ void cast_rows(const uint16_t* __restrict__ x, f16* __restrict__ x16, size_t first8,
+                                         size_t n8, int tid, int nthreads) {
+  for (size_t i = first8 + tid; i < first8 + n8; i += nthreads) {
+    const uint4 v = reinterpret_cast<const uint4*>(x)[i];
+    f16x8 o;
+    o[0] = (f16)__uint_as_float(v.x << 16); o[1] = (f16)__uint_as_float(v.x & 0xFFFF0000u);
+    o[2] = (f16)__uint_as_float(v.y << 16); o[3] = (f16)__uint_as_float(v.y & 0xFFFF0000u);
+    o[4] = (f16)__uint_as_float(v.z << 16); o[5] = (f16)__uint_as_float(v.z & 0xFFFF0000u);
+    o[6] = (f16)__uint_as_float(v.w << 16); o[7] = (f16)__uint_as_float(v.w & 0xFFFF0000u);
+    reinterpret_cast<f16x8*>(x16)[i] = o;
+  }
+}
+
+// T <= 64: the whole permutation, the active-expert list and the fp16 copy
+// of the activations, in one block of 1024 threads.
+__global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
+                                                         int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ sorted_pairs,
+                                                         int32_t* __restrict__ pair_pos,
+                                                         int32_t* __restrict__ active,
+                                                         int32_t* __restrict__ n_active,
+                                                         const uint16_t* __restrict__ x, f16* __restrict__ x16,
+                                                         int H) {
+  __shared__ unsigned long long m[PERM_MAX_E];
+  __shared__ int off_s[PERM_MAX_E];
+  __shared__ int lds[16];
+  const int tid = threadIdx.x;
+  if (tid < E) m[tid] = 0ull;
+  __syncthreads();
+  for (int f = tid; f < T * k; f += 1024) atomicOr(&m[ids[f]], 1ull << (f / k));
+  __syncthreads();
+  const int cnt = tid < E ? __popcll(m[tid]) : 0;
+  int total;
+  const int off = block_exclusive_scan(cnt, lds, &total);
+  int nact;
+  const int slot = block_exclusive_scan(cnt > 0 ? 1 : 0, lds, &nact);
+  if (tid < E) {
+    off_s[tid] = off;
+    offsets[tid] = off;
+    if (cnt > 0) active[slot] = tid;
+  }
+  if (tid == 0) {
+    offsets[E] = T * k;
+    *n_active = nact;
+  }
+  __syncthreads();
+  for (int f = tid; f < T * k; f += 1024) {
+    const int t = f / k, e = ids[f];
+    const int pos = off_s[e] + __popcll(m[e] & ((1ull << t) - 1ull));
+    sorted_pairs[pos] = f;
+    pair_pos[f] = pos;
+  }
+  if (x) cast_rows(x, x16, 0, (size_t)T * H / 8, tid, 1024);
+}
 
 __global__ __launch_bounds__(WAVE) void perm_count_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
                                                          uint64_t* __restrict__ masks, int32_t* __restrict__ counts) {
@@ -180,34 +315,13 @@ __global__ __launch_bounds__(WAVE) void perm_count_kernel(const int32_t* __restr
   }
 }
 
-// Block-wide exclusive scan of one int per thread (1024 threads).
-__device__ int block_exclusive_scan(int v, int* lds /*[1024/64]*/, int* total) {
-  const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE;
-  int incl = v;
-#pragma unroll
-  for (int off = 1; off < WAVE; off <<= 1) {
-    int o = __shfl_up(incl, off, WAVE);
-    if (lane >= off) incl += o;
-  }
-  if (lane == WAVE - 1) lds[wv] = incl;
-  __syncthreads();
-  int wave_base = 0, all = 0;
-  for (int i = 0; i < (int)(blockDim.x / WAVE); i++) {
-    if (i < wv) wave_base += lds[i];
-    all += lds[i];
-  }
-  __syncthreads();
-  *total = all;
-  return wave_base + incl - v;
-}
-
-// One block of 1024 threads, thread e = expert.  Turns per-block counts into
-// absolute bases, writes offsets and the list of experts with work.
+// One block of 1024 threads, thread e = expert: per-block counts become
+// absolute bases; writes offsets and the list of experts with work.
 __global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* __restrict__ counts, int nblocks, int E,
                                                         int P, int32_t* __restrict__ base,
                                                         int32_t* __restrict__ offsets, int32_t* __restrict__ active,
                                                         int32_t* __restrict__ n_active) {
-  __shared__ int lds[1024 / WAVE];
+  __shared__ int lds[16];
   const int e = threadIdx.x;
   int running = 0;
   if (e < E)
@@ -231,30 +345,40 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* __restri
   }
 }
 
-__global__ __launch_bounds__(WAVE) void perm_scatter_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
-                                                           const uint64_t* __restrict__ masks,
-                                                           const int32_t* __restrict__ base,
-                                                           int32_t* __restrict__ sorted_pairs,
-                                                           int32_t* __restrict__ pair_pos) {
-  const int lane = threadIdx.x, b = blockIdx.x;
-  const int t = b * WAVE + lane;
-  if (t >= T) return;
-  const uint64_t below = (1ull << lane) - 1ull;
-  for (int j = 0; j < k; j++) {
-    const int f = t * k + j;
-    const int e = ids[f];
-    const int pos = base[(size_t)b * E + e] + __popcll(masks[(size_t)b * E + e] & below);
-    sorted_pairs[pos] = f;
-    pair_pos[f] = pos;
+__global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
+                                                          const uint64_t* __restrict__ masks,
+                                                          const int32_t* __restrict__ base,
+                                                          int32_t* __restrict__ sorted_pairs,
+                                                          int32_t* __restrict__ pair_pos,
+                                                          const uint16_t* __restrict__ x, f16* __restrict__ x16,
+                                                          int H) {
+  const int b = blockIdx.x;
+  if (threadIdx.x < WAVE) {
+    const int lane = threadIdx.x;
+    const int t = b * WAVE + lane;
+    if (t < T) {
+      const uint64_t below = (1ull << lane) - 1ull;
+      for (int j = 0; j < k; j++) {
+        const int f = t * k + j;
+        const int e = ids[f];
+        const int pos = base[(size_t)b * E + e] + __popcll(masks[(size_t)b * E + e] & below);
+        sorted_pairs[pos] = f;
+        pair_pos[f] = pos;
+      }
+    }
+  }
+  if (x) {
+    const int rows = min(WAVE, T - b * WAVE);
+    cast_rows(x, x16, (size_t)b * WAVE * H / 8, (size_t)rows * H / 8, threadIdx.x, 256);
   }
 }
 
 // Experts with work, from offsets alone (when the permutation comes from
-// the caller).
+// the caller), and the fp16 copy of the activations.
 __global__ __launch_bounds__(1024) void active_list_kernel(const int32_t* __restrict__ offsets, int E,
                                                           int32_t* __restrict__ active,
                                                           int32_t* __restrict__ n_active) {
-  __shared__ int lds[1024 / WAVE];
+  __shared__ int lds[16];
   const int e = threadIdx.x;
   const int flag = (e < E && offsets[e + 1] > offsets[e]) ? 1 : 0;
   int nact;
@@ -263,66 +387,73 @@ __global__ __launch_bounds__(1024) void active_list_kernel(const int32_t* __rest
   if (e == 0) *n_active = nact;
 }
 
-// ---- activations bf16 -> fp16 (exact for |x| < 65504 above 2^-14) --------
 __global__ __launch_bounds__(256) void cast_kernel(const uint16_t* __restrict__ x, f16* __restrict__ x16,
                                                   long long n8) {
-  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n8; i += (long long)gridDim.x * 256) {
-    uint4 v = reinterpret_cast<const uint4*>(x)[i];
-    f16x8 o;
-    o[0] = (f16)__uint_as_float(v.x << 16); o[1] = (f16)__uint_as_float(v.x & 0xFFFF0000u);
-    o[2] = (f16)__uint_as_float(v.y << 16); o[3] = (f16)__uint_as_float(v.y & 0xFFFF0000u);
-    o[4] = (f16)__uint_as_float(v.z << 16); o[5] = (f16)__uint_as_float(v.z & 0xFFFF0000u);
-    o[6] = (f16)__uint_as_float(v.w << 16); o[7] = (f16)__uint_as_float(v.w & 0xFFFF0000u);
-    reinterpret_cast<f16x8*>(x16)[i] = o;
-  }
+  const size_t per = 256 * 8;
+  const size_t first = (size_t)blockIdx.x * per;
+  if (first < (size_t)n8) cast_rows(x, x16, first, min((size_t)n8 - first, per), threadIdx.x, 256);
 }
+
+int router_tt(int T) { return T <= 1 ? 1 : (T <= 2 ? 2 : (T <= 4 ? 4 : 8)); }
 
 }  // namespace
 
-int router_slabs(int T, int H, int E) {
-  const int tt = T <= 1 ? 1 : 8;
-  const long long tiles = (long long)((E + RT_E_PER_BLOCK - 1) / RT_E_PER_BLOCK) * ((T + tt - 1) / tt);
-  long long s = 512 / (tiles > 0 ? tiles : 1);
-  const int max_s = H / 16;
-  if (s > max_s) s = max_s;
+RouterPlan router_plan(int T, int H, int E) {
+  RouterPlan p;
+  const int tt = router_tt(T);
+  const int tiles = ((E + RT_E_TILE - 1) / RT_E_TILE) * ((T + tt - 1) / tt);
+  int s = 512 / (tiles > 0 ? tiles : 1);
+  const int steps = H / RT_ROWS_PER_STEP;
+  if (s > steps) s = steps;
   if (s < 1) s = 1;
-  return (int)s;
+  int steps_per_slab = (steps + s - 1) / s;
+  // the block's activations slab lives in LDS: at most 64 KB
+  const int max_steps = 16384 / (tt * RT_ROWS_PER_STEP);
+  if (steps_per_slab > max_steps) steps_per_slab = max_steps;
+  p.slab_rows = steps_per_slab * RT_ROWS_PER_STEP;
+  p.slabs = (H + p.slab_rows - 1) / p.slab_rows;
+  return p;
 }
 
-hipError_t launch_router(const uint16_t* x, const uint16_t* wr, float* part, int T, int H, int E, int slabs,
-                         hipStream_t s) {
-  const int slab_rows = (H + slabs - 1) / slabs;
-  const int gx = (E + RT_E_PER_BLOCK - 1) / RT_E_PER_BLOCK;
-  if (T <= 1)
-    hipLaunchKernelGGL((router_partial_kernel<1>), dim3(gx, T, slabs), dim3(RT_THREADS), 0, s, x, wr, part, T, H, E,
-                       slab_rows);
+hipError_t launch_router(const uint16_t* x, const uint16_t* wr, float* part, int T, int H, int E,
+                         const RouterPlan& rp, hipStream_t s) {
+  const int tt = router_tt(T);
+  const dim3 grid((E + RT_E_TILE - 1) / RT_E_TILE, rp.slabs, (T + tt - 1) / tt);
+  const size_t lds = sizeof(float) * ((size_t)tt * rp.slab_rows + 4 * 16 * tt * 8);
+  switch (tt) {
+    case 1: hipLaunchKernelGGL((router_gemv_kernel<1>), grid, dim3(RT_THREADS), lds, s, x, wr, part, T, H, E, rp.slab_rows); break;
+    case 2: hipLaunchKernelGGL((router_gemv_kernel<2>), grid, dim3(RT_THREADS), lds, s, x, wr, part, T, H, E, rp.slab_rows); break;
+    case 4: hipLaunchKernelGGL((router_gemv_kernel<4>), grid, dim3(RT_THREADS), lds, s, x, wr, part, T, H, E, rp.slab_rows); break;
+    default: hipLaunchKernelGGL((router_gemv_kernel<8>), grid, dim3(RT_THREADS), lds, s, x, wr, part, T, H, E, rp.slab_rows); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const float* part, int slabs, const float* bias, float* logits, int T, int E, int k,
+                       int32_t* ids, float* w, hipStream_t s) {
+  if (T <= 64)
+    hipLaunchKernelGGL((topk_kernel<1>), dim3(T), dim3(TOPK_THREADS), 0, s, part, slabs, bias, logits, T, E, k, ids,
+                       w);
   else
-    hipLaunchKernelGGL((router_partial_kernel<8>), dim3(gx, (T + 7) / 8, slabs), dim3(RT_THREADS), 0, s, x, wr, part,
-                       T, H, E, slab_rows);
-  return hipGetLastError();
-}
-
-hipError_t launch_logits_reduce(const float* part, const float* bias, float* logits, int T, int E, int slabs,
-                                hipStream_t s) {
-  hipLaunchKernelGGL(logits_reduce_kernel, dim3((E + 255) / 256, T), dim3(256), 0, s, part, bias, logits, T, E,
-                     slabs);
-  return hipGetLastError();
-}
-
-hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s) {
-  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, ids, w);
+    hipLaunchKernelGGL((topk_kernel<4>), dim3((T + 3) / 4), dim3(TOPK_THREADS), 0, s, part, slabs, bias, logits, T,
+                       E, k, ids, w);
   return hipGetLastError();
 }
 
 hipError_t launch_permute(const int32_t* ids, int T, int E, int k, uint64_t* masks, int32_t* counts, int32_t* base,
                           int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_pos, int32_t* active,
-                          int32_t* n_active, hipStream_t s) {
+                          int32_t* n_active, const uint16_t* x, f16* x16, int H, hipStream_t s) {
+  if (T <= 64) {
+    hipLaunchKernelGGL(perm_small_kernel, dim3(1), dim3(1024), 0, s, ids, T, E, k, offsets, sorted_pairs, pair_pos,
+                       active, n_active, x, x16, H);
+    return hipGetLastError();
+  }
   const int nb = perm_blocks(T);
   hipLaunchKernelGGL(perm_count_kernel, dim3(nb), dim3(WAVE), 0, s, ids, T, E, k, masks, counts);
   hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, s, counts, nb, E, T * k, base, offsets, active,
                      n_active);
-  hipLaunchKernelGGL(perm_scatter_kernel, dim3(nb), dim3(WAVE), 0, s, ids, T, E, k, masks, base, sorted_pairs,
-                     pair_pos);
+  hipLaunchKernelGGL(perm_scatter_kernel, dim3(nb), dim3(256), 0, s, ids, T, E, k, masks, base, sorted_pairs,
+                     pair_pos, x, x16, H);
   return hipGetLastError();
 }
 
@@ -333,10 +464,8 @@ hipError_t launch_active_list(const int32_t* offsets, int E, int32_t* active, in
 
 hipError_t launch_cast(const uint16_t* x, f16* x16, long long n, hipStream_t s) {
   const long long n8 = n / 8;
-  long long g = (n8 + 255) / 256;
-  if (g > 4096) g = 4096;
-  if (g < 1) g = 1;
-  hipLaunchKernelGGL(cast_kernel, dim3((unsigned)g), dim3(256), 0, s, x, x16, n8);
+  const long long g = (n8 + 2047) / 2048;
+  hipLaunchKernelGGL(cast_kernel, dim3((unsigned)(g > 0 ? g : 1)), dim3(256), 0, s, x, x16, n8);
   return hipGetLastError();
 }
 
