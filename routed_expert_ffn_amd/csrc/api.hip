@@ -49,7 +49,8 @@ size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 // Workspace regions (byte offsets, 256-byte aligned).  moe_layer uses all of
 // them; moe_route and moe_expert_ffn use subsets of the same layout.
 struct Layout {
-  size_t part, logits, ids, w, masks, counts, base, offsets, sorted, pos, active, nact, x16, h, rows, total;
+  size_t part, logits, ids, w, masks, counts, base, offsets, sorted, pos, active, nact, mtiles, nmt, x16, h, rows,
+      total;
 };
 
 Layout layout(const moe_dims& d) {
@@ -74,6 +75,8 @@ Layout layout(const moe_dims& d) {
   L.pos = take(P * 4);
   L.active = take(E * 4);
   L.nact = take(4);
+  L.mtiles = take((size_t)moe::max_mtiles(d) * 4);
+  L.nmt = take(4);
   L.x16 = take(T * H * 2);
   L.h = take(P * I * 2);
   L.rows = take(P * H * 4);
@@ -145,8 +148,8 @@ moe_status enqueue_route(const moe_dims& d, const void* x, const void* wr, const
   LAUNCH(MOE_KERNEL_PERMUTE, s,
          moe::launch_permute(ids, d.T, d.E, d.k, at<uint64_t>(ws, L.masks), at<int32_t>(ws, L.counts),
                              at<int32_t>(ws, L.base), offsets, sorted, pos, at<int32_t>(ws, L.active),
-                             at<int32_t>(ws, L.nact), x16 ? static_cast<const uint16_t*>(x) : nullptr, x16, d.H,
-                             s),
+                             at<int32_t>(ws, L.nact), at<int32_t>(ws, L.mtiles), at<int32_t>(ws, L.nmt),
+                             x16 ? static_cast<const uint16_t*>(x) : nullptr, x16, d.H, s),
          "permute");
   return MOE_OK;
 }
@@ -168,6 +171,9 @@ moe_status enqueue_ffn(const moe_dims& d, const int32_t* offsets, const int32_t*
   a.sorted_pairs = sorted;
   a.active = at<int32_t>(ws, L.active);
   a.n_active = at<int32_t>(ws, L.nact);
+  a.mtiles = at<int32_t>(ws, L.mtiles);
+  a.n_mtiles = at<int32_t>(ws, L.nmt);
+  a.max_mtiles = moe::max_mtiles(d);
   a.w = w;
   a.h = at<f16>(ws, L.h);
   a.rows = rows;
@@ -247,8 +253,10 @@ moe_status moe_expert_ffn(moe_dims d, const void* x, const int32_t* expert_offse
   TRY(check_ws(d, ws, ws_bytes));
   const Layout L = layout(d);
   hipStream_t s = (hipStream_t)stream;
-  LAUNCH(MOE_KERNEL_CAST, s, moe::launch_active_list(expert_offsets, d.E, at<int32_t>(ws, L.active),
-                                                     at<int32_t>(ws, L.nact), s), "active list");
+  LAUNCH(MOE_KERNEL_CAST, s,
+         moe::launch_active_list(expert_offsets, d.E, at<int32_t>(ws, L.active), at<int32_t>(ws, L.nact),
+                                 at<int32_t>(ws, L.mtiles), at<int32_t>(ws, L.nmt), s),
+         "active list");
   LAUNCH(MOE_KERNEL_CAST, s,
          moe::launch_cast(static_cast<const uint16_t*>(x), at<f16>(ws, L.x16), (long long)d.T * d.H, s), "cast");
   return enqueue_ffn(d, expert_offsets, sorted_pairs, w, rows, ws, s);

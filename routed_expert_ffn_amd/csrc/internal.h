@@ -11,6 +11,7 @@ namespace moe {
 
 // The router's partial sums over H: slabs of slab_rows rows each.
 struct RouterPlan {
+  bool mfma;  // bf16 matrix-core GEMM (larger T) or the VALU GEMV
   int slabs, slab_rows;
 };
 RouterPlan router_plan(int T, int H, int E);
@@ -33,12 +34,21 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* wr, float* part, int
 // the bias, and selects the top k with their softmax weights.
 hipError_t launch_topk(const float* part, int slabs, const float* bias, float* logits, int T, int E, int k,
                        int32_t* ids, float* w, hipStream_t s);
-// Offsets, permutation and active-expert list; if x is non-NULL also writes
-// the fp16 copy x16 of the activations [T][H].
+// Offsets, permutation, active-expert list and (for T > 64) the list of
+// (expert, token tile) entries; if x is non-NULL also writes the fp16
+// copy x16 of the activations [T][H].
 hipError_t launch_permute(const int32_t* ids, int T, int E, int k, uint64_t* masks, int32_t* counts, int32_t* base,
                           int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_pos, int32_t* active,
-                          int32_t* n_active, const uint16_t* x, f16* x16, int H, hipStream_t s);
-hipError_t launch_active_list(const int32_t* offsets, int E, int32_t* active, int32_t* n_active, hipStream_t s);
+                          int32_t* n_active, int32_t* mtiles, int32_t* n_mtiles, const uint16_t* x, f16* x16,
+                          int H, hipStream_t s);
+hipError_t launch_active_list(const int32_t* offsets, int E, int32_t* active, int32_t* n_active, int32_t* mtiles,
+                              int32_t* n_mtiles, hipStream_t s);
+// Token tile of the large-batch expert GEMMs: an expert's records are split
+// evenly over ceil(n / MTILE) tiles.
+constexpr int MTILE = 224;
+
+// Upper bound on the (expert, token tile) entries of T tokens.
+inline int max_mtiles(const moe_dims& d) { return max_active(d) + (int)(((long long)d.T * d.k) / MTILE) + 1; }
 hipError_t launch_cast(const uint16_t* x, f16* x16, long long n, hipStream_t s);
 
 struct FfnArgs {
@@ -49,6 +59,9 @@ struct FfnArgs {
   const int32_t* sorted_pairs;    // [P]
   const int32_t* active;          // [max_active] expert ids with work
   const int32_t* n_active;        // [1]
+  const int32_t* mtiles;          // (expert, token tile) entries
+  const int32_t* n_mtiles;        // [1]
+  int max_mtiles;                 // grid bound on the entries
   const moe_experts* w;
   f16* h;                         // [P][I]
   float* rows;                    // [P][H]

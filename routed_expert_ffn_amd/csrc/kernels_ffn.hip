@@ -236,6 +236,442 @@ __global__ __launch_bounds__(FFN_THREADS, WAVES_PER_EU) void expert_gemm_kernel(
   }
 }
 
+// ---- large batches: 224-token x 256-row tiles on 32x32x16 matrix cores ---------
+// Work items are (expert, token tile) entries of a list built with the
+// permutation (mtiles), times the row tiles of the matrix; an expert's
+// records are split evenly over ceil(n / 224) tiles.  A block of four
+// wavefronts computes a tile of up to 224 tokens (NF = ceil(n / 32) token
+// fragments, a template parameter so the inner loop is straight-line code)
+// against 256 weight rows: wavefront w takes every token fragment against
+// its own 64 weight rows (two fragments), as v_mfma_f32_32x32x16_f16 (lane l
+// holds A[l%32][8(l/32)..+7], B[8(l/32)..+7][l%32] and D[8(i/4) + 4(l/32) +
+// i%4][l%32]).  Each weight row is thus dequantised once per block and the
+// four wavefronts carry equal work.
+//
+// K runs in chunks of 64.  Inside a chunk the sum is taken in a permuted
+// order: lane half g = l/32 in step s covers the chunk's k = 32g + 8s .. +7,
+// the same for both operands, so one lane's codes for all four steps are 16
+// contiguous bytes of the weight row.  All operands reach LDS by LDS DMA
+// (global_load_lds), which is limited by the number of cache-line requests
+// a CU keeps in flight, so every request fetches whole lines where it can:
+//   tokens:  fp16 rows of one chunk (128 bytes a row), three buffers, copied
+//            two chunks ahead;
+//   weights: the raw NVFP4 bytes of four chunks ("a span": 128 code bytes
+//            and 16 scale bytes a row), two slots, copied while the previous
+//            span is in use.
+// A 128-byte row is 8 pieces of 16 bytes, piece q of row m stored in slot
+// q ^ ((m/2) % 8), so the 16 rows that one read phase touches cover all 64
+// banks.  Each wavefront turns the raw bytes of its own weight rows into
+// exact fp16 in registers (e2m1 code times e4m3 block scale) step by step.
+//
+// DMA and waits: pair A = wavefronts 0, 1 and pair B = 2, 3.  In chunk c
+// pair A (c even) or B (c odd) copies the tokens of chunk c+2 (wavefront w
+// the token groups g with g % 2 == w % 2); in the span's chunks 1 and 2
+// pairs B and A also copy the two halves (128 rows each) of the next span.
+// A pair waits for all of its copies (vmcnt(0)) at the end of the chunk
+// after the one it issued in, when nothing else of its own is in flight; a
+// partial vmcnt wait that leaves newer DMA in flight was measured not to
+// guarantee that older DMA writes are visible in LDS, so only vmcnt(0) is
+// used.
+//
+// Gate/up tiles pair 128 gate rows with the same 128 up rows (wavefront w:
+// gate rows 32w .. and up rows 128 + 32w ..), so SiLU * up happens in
+// registers.  Items are mapped to blocks so that the row tiles of one
+// (expert, token tile) run back to back on one XCD (blocks are dealt to the
+// eight XCDs round robin): its activations stay in that XCD's L2 while the
+// weights stream once.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16 mfma32x32x16(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+constexpr int BIG_M = MTILE;    // tokens per tile (7 fragments of 32)
+constexpr int BIG_MF = BIG_M / 32;
+constexpr int BIG_N = 256;      // weight rows per tile (8 fragments of 32)
+constexpr int BIG_THREADS = 256;
+constexpr int BIG_KC = 64;      // k per chunk: 8 pieces of 8 halves per token row
+constexpr int BIG_SPAN = 4;     // chunks per raw weight span
+static_assert(BIG_M % 32 == 0 && BIG_MF <= 8, "token tile of whole fragments");
+// LDS layout (bytes)
+constexpr int BIG_TILE_BYTES = BIG_M * BIG_KC * 2;                  // tokens of one chunk
+constexpr int BIG_SPANQ_BYTES = BIG_N * BIG_SPAN * BIG_KC / 2;      // codes of one span [256][128]
+constexpr int BIG_SPANS_BYTES = BIG_N * BIG_SPAN * BIG_KC / 16;     // scales of one span [256][16]
+constexpr int BIG_OFF_A = 0;                                        // [3][224][64] fp16
+constexpr int BIG_OFF_RQ = BIG_OFF_A + 3 * BIG_TILE_BYTES;          // [2][256][128] u8
+constexpr int BIG_OFF_RS = BIG_OFF_RQ + 2 * BIG_SPANQ_BYTES;        // [2][256][16] u8
+constexpr int BIG_OFF_ROW = BIG_OFF_RS + 2 * BIG_SPANS_BYTES;       // [224] i32
+constexpr int BIG_LDS = BIG_OFF_ROW + BIG_M * 4;
+static_assert(BIG_LDS <= 160 * 1024, "LDS budget of one CU");
+
+struct BigParams {
+  GroupedParams g;
+  const int32_t* mtiles;    // entries e * 65536 + tile
+  const int32_t* n_mtiles;  // [1]
+  int n_row_tiles;          // row tiles of BIG_N weight rows per expert
+};
+
+// Barrier for LDS hand-off: this wavefront's LDS accesses and all but its
+// last N vector-memory instructions have completed when it arrives (N = 63:
+// no vector-memory wait at all).  The memory clobber keeps the compiler from
+// moving memory accesses across it, and unlike __syncthreads() it adds no
+// fence of its own.
+template <int N>
+__device__ __forceinline__ void lds_barrier_vm() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// LDS DMA of 16 (4) bytes per lane from gbase + voff to LDS address lds +
+// 16 (4) * lane, written as instructions of our own: the compiler would
+// otherwise count the copies as outstanding LDS work and wait for all LDS
+// traffic (lgkmcnt(0)) before every use of an LDS read, serialising the
+// fragment reads with the MFMAs.  Every wait for these copies is explicit
+// (lds_barrier_vm).  gbase and lds are wave-uniform (scalar registers).
+__device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
+  return (uint32_t)(size_t)(const __attribute__((address_space(3))) unsigned char*)p;
+}
+__device__ __forceinline__ void dma16(const unsigned char* gbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "s"(lds)
+               : "memory", "m0");
+}
+
+struct BigTile {
+  int e, mb, nvalid, rtile, K, N;
+};
+
+// Per-thread state of one tile.  DMA addresses are a wave-uniform base plus
+// a 32-bit per-lane byte offset, the form the DMA instruction takes directly.
+struct BigLane {
+  const unsigned char* a;  // token operand rows (x or h), uniform
+  uint32_t toff[16];       // this lane's source (row, piece): group 2j + w%2, instruction i -> 4j + i
+  int ngrp;                // token groups this wavefront copies
+  const uint8_t* q[2];     // raw codes of tile rows 0 / 128 (uniform, k = 0)
+  const uint8_t* sc[2];    // raw scales of tile rows 0 / 128
+  uint32_t qlane;          // per-lane code source offset (this wavefront's instructions)
+  uint32_t slane;          // per-lane scale source offset
+  uint32_t qstep;          // code bytes of 16 rows: two instructions of one wavefront apart
+  int aoff[4];             // per step: LDS byte offset of token row m32 in a token buffer
+  int qrow[2], srow[2];    // LDS byte offsets of this lane's weight row (fragment nf) in a span slot
+  int K;
+};
+
+// Token rows of chunk kc, groups 2j + p (j < ngrp, p = w % 2), into token
+// buffer buf.  Instruction i of group g fills rows R = 32g + 8i .. R+7; lane
+// l writes row R + l/8, slot l%8.
+__device__ __forceinline__ void dma_tokens(const BigLane& L, unsigned char* smem, int buf, int kc, int p) {
+  const unsigned char* base = L.a + 2 * (size_t)kc;
+  const uint32_t dst = lds_addr(smem + BIG_OFF_A + buf * BIG_TILE_BYTES + 32 * p * BIG_KC * 2);
+#pragma unroll
+  for (int j = 0; j < 4; j++)
+    if (j < L.ngrp) {
+#pragma unroll
+      for (int i = 0; i < 4; i++) dma16(base, L.toff[4 * j + i], dst + (64 * j + 8 * i) * BIG_KC * 2);
+    }
+}
+
+// Half h (tile rows 128h .. 128h+127) of the raw span starting at k = k0
+// into span slot `slot`, by the wavefront of parity p of the issuing pair:
+// code instructions i = p, p+2, .. < 16 cover rows 128h + 8i .. +7 (lane l:
+// row + l/8, slot l%8, the swizzled piece), scale instruction p rows
+// 128h + 64p + l (16 bytes each).
+__device__ __forceinline__ void dma_span_half(const BigLane& L, unsigned char* smem, int slot, int k0, int h, int p) {
+  const uint32_t rq = lds_addr(smem + BIG_OFF_RQ + slot * BIG_SPANQ_BYTES + 128 * h * 128 + 8 * p * 128);
+  const uint32_t rs = lds_addr(smem + BIG_OFF_RS + slot * BIG_SPANS_BYTES + 128 * h * 16 + 64 * p * 16);
+  const unsigned char* qb = L.q[h] + k0 / 2;
+#pragma unroll
+  for (int ii = 0; ii < 8; ii++) dma16(qb, L.qlane + ii * L.qstep, rq + 16 * ii * 128);
+  dma16(L.sc[h] + k0 / 16, L.slane, rs);
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Step s of one chunk: the two weight fragments, dequantised from this
+// lane's raw codes (word s) and block scale (element s/2 of the pair).
+__device__ __forceinline__ void dequant_step(f16x8 (&bv)[2], const u32x4 (&q)[2], const f16x2 (&sig)[2], int s) {
+#pragma unroll
+  for (int nf = 0; nf < 2; nf++) {
+    f16x2 s2;
+    s2[0] = sig[nf][s / 2];
+    s2[1] = sig[nf][s / 2];
+    bv[nf] = dequant8(q[nf][s], s2);
+  }
+}
+
+template <int NF>
+__device__ __forceinline__ void read_a(f16x8 (&av)[8], const unsigned char* Ab, int aoff) {
+#pragma unroll
+  for (int f = 0; f < NF; f++) av[f] = *reinterpret_cast<const f16x8*>(Ab + aoff + 32 * f * BIG_KC * 2);
+}
+
+template <int NF>
+__device__ __forceinline__ void mma_step(f32x16 (&acc)[8][2], const f16x8 (&av)[8], const f16x8 (&bv)[2]) {
+#pragma unroll
+  for (int f = 0; f < NF; f++)
+#pragma unroll
+    for (int nf = 0; nf < 2; nf++) acc[f][nf] = mfma32x32x16(av[f], bv[nf], acc[f][nf]);
+}
+
+// One wavefront per SIMD issues in order, and an MFMA blocks issue until the
+// matrix core takes it, so vector work only overlaps the matrix core when
+// it sits between MFMAs: one step's 2 NF MFMAs are spread over the next
+// step's dequantisation (about 18 vector instructions).
+template <int NF>
+__device__ __forceinline__ void interleave_mfma_valu() {
+  constexpr int per = (18 + 2 * NF - 1) / (2 * NF);
+#pragma unroll
+  for (int i = 0; i < 2 * NF; i++) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, per, 0);  // vector ALU
+  }
+}
+
+// Chunk c = 4 s + J of the tile.  TOK: a chunk c+2 exists (its tokens are
+// copied by pair J % 2); SPAN: a span s+1 exists (its halves are copied in
+// J = 1 by pair B and J = 2 by pair A).  Then the four steps, with token
+// fragments read and weights dequantised one step ahead, and the barrier,
+// at which the pair that issued in chunk c-1 waits for its DMA.
+template <int NF, int J, bool TOK, bool SPAN>
+__device__ __forceinline__ void big_chunk(const BigLane& L, f32x16 (&acc)[8][2], unsigned char* smem, int c,
+                                          int wv) {
+  const int pair = wv >> 1, par = wv & 1;
+  const int span = c / BIG_SPAN, slot = span & 1;
+  const bool tok_issuer = pair == (J & 1);
+  const bool span_issuer = (J == 1 && pair == 1) || (J == 2 && pair == 0);
+  if (TOK && tok_issuer) dma_tokens(L, smem, (c + 2) % 3, (c + 2) * BIG_KC, par);
+  if (SPAN && span_issuer) dma_span_half(L, smem, slot ^ 1, (span + 1) * BIG_SPAN * BIG_KC, J == 1 ? 0 : 1, par);
+  asm volatile("" ::: "memory");
+  const unsigned char* Ab = smem + BIG_OFF_A + (c % 3) * BIG_TILE_BYTES;
+  const unsigned char* rq = smem + BIG_OFF_RQ + slot * BIG_SPANQ_BYTES;
+  const unsigned char* rs = smem + BIG_OFF_RS + slot * BIG_SPANS_BYTES;
+  u32x4 q[2];
+  f16x2 sig[2];
+  const int g2 = (threadIdx.x % WAVE) / 32, m32 = threadIdx.x % 32;
+  const int qslot = (2 * J + g2) ^ ((m32 / 2) % 8);  // piece 2J + g of the lane's row
+#pragma unroll
+  for (int nf = 0; nf < 2; nf++) {
+    q[nf] = *reinterpret_cast<const u32x4*>(rq + L.qrow[nf] + 16 * qslot);
+    const uint32_t sp = *reinterpret_cast<const uint16_t*>(rs + L.srow[nf] + 4 * J + 2 * g2);
+    sig[nf] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sp, 1.0f, false);
+  }
+  // Steps, each fenced so that the compiler keeps the order: the token
+  // fragment reads of step s+1 are issued before the MFMAs of step s, and
+  // the dequantisation of step s+1 is interleaved with those MFMAs.
+  f16x8 a0[8], a1[8], b0[2], b1[2];
+  read_a<NF>(a0, Ab, L.aoff[0]);
+  dequant_step(b0, q, sig, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  read_a<NF>(a1, Ab, L.aoff[1]);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_step<NF>(acc, a0, b0);
+  dequant_step(b1, q, sig, 1);
+  interleave_mfma_valu<NF>();
+  __builtin_amdgcn_sched_barrier(0);
+  read_a<NF>(a0, Ab, L.aoff[2]);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_step<NF>(acc, a1, b1);
+  dequant_step(b0, q, sig, 2);
+  interleave_mfma_valu<NF>();
+  __builtin_amdgcn_sched_barrier(0);
+  read_a<NF>(a1, Ab, L.aoff[3]);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_step<NF>(acc, a0, b0);
+  dequant_step(b1, q, sig, 3);
+  interleave_mfma_valu<NF>();
+  __builtin_amdgcn_sched_barrier(0);
+  mma_step<NF>(acc, a1, b1);
+  const bool issued = (TOK && tok_issuer) || (SPAN && span_issuer);
+  if (issued)
+    lds_barrier_vm<63>();  // its copies stay in flight one more chunk
+  else
+    lds_barrier_vm<0>();
+}
+
+template <int NF, bool TOK, bool SPAN>
+__device__ __forceinline__ void big_span(const BigLane& L, f32x16 (&acc)[8][2], unsigned char* smem, int c, int wv) {
+  big_chunk<NF, 0, TOK, SPAN>(L, acc, smem, c, wv);
+  big_chunk<NF, 1, TOK, SPAN>(L, acc, smem, c + 1, wv);
+  big_chunk<NF, 2, TOK, SPAN>(L, acc, smem, c + 2, wv);
+  big_chunk<NF, 3, TOK, SPAN>(L, acc, smem, c + 3, wv);
+}
+
+template <int NF, bool GATEUP>
+__device__ __forceinline__ void big_tile(const GroupedParams& p, const BigTile& t, unsigned char* smem) {
+  const int lane = threadIdx.x % WAVE, m32 = lane % 32, g2 = lane / 32;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE), par = wv & 1;
+  const int K = t.K, nch = K / BIG_KC;
+  const int32_t* rowoff = reinterpret_cast<const int32_t*>(smem + BIG_OFF_ROW);
+  BigLane L;
+  L.K = K;
+  // token DMA: groups 2j + par; row R + l/8 of instruction (g, i) holds
+  // piece (l%8) ^ ((row/2) % 8) = (l%8) ^ (4(i%2) + l/16) in slot l%8
+  {
+    L.a = reinterpret_cast<const unsigned char*>(p.a);
+    L.ngrp = (NF - par + 1) / 2;
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const uint32_t piece = (uint32_t)((lane % 8) ^ (4 * (i % 2) + lane / 16));
+        const int r = min(32 * (2 * j + par) + 8 * i + lane / 8, BIG_M - 1);
+        L.toff[4 * j + i] = 2u * ((uint32_t)rowoff[r] * (uint32_t)K + 8u * piece);
+      }
+  }
+  // raw weight spans: tile row r is gate row rtile*128 + r (r < 128) or the
+  // same up row (r >= 128) for gate/up, row rtile*256 + r for down; a code
+  // instruction's lane l reads its row's piece (l%8) ^ (4(i%2) + l/16)
+  {
+    const size_t qrow = (size_t)(K / 2), srow = (size_t)(K / 16);
+    if (GATEUP) {
+      const size_t r0 = (size_t)t.e * t.N + t.rtile * (BIG_N / 2);
+      L.q[0] = p.q0 + r0 * qrow;
+      L.q[1] = p.q1 + r0 * qrow;
+      L.sc[0] = p.sf0 + r0 * srow;
+      L.sc[1] = p.sf1 + r0 * srow;
+    } else {
+      const size_t r0 = (size_t)t.e * t.N + t.rtile * BIG_N;
+      L.q[0] = p.q0 + r0 * qrow;
+      L.q[1] = L.q[0] + 128 * qrow;
+      L.sc[0] = p.sf0 + r0 * srow;
+      L.sc[1] = L.sc[0] + 128 * srow;
+    }
+    // this wavefront's code instructions i = par, par+2, ..: rows 8i + l/8
+    L.qlane = (uint32_t)((8 * par + lane / 8) * qrow + 16 * ((lane % 8) ^ (4 * par + lane / 16)));
+    L.qstep = (uint32_t)(16 * qrow);
+    L.slane = (uint32_t)((64 * par + lane) * srow);
+  }
+  // LDS read offsets: token row 32f + m32 (f a compile-time offset); weight
+  // fragment nf = tile rows 32w + 128nf (gate/up) or 64w + 32nf (down)
+  {
+#pragma unroll
+    for (int s = 0; s < 4; s++) {
+      const int slot = (4 * g2 + s) ^ ((m32 / 2) % 8);
+      L.aoff[s] = (m32 * BIG_KC + 8 * slot) * 2;
+    }
+#pragma unroll
+    for (int nf = 0; nf < 2; nf++) {
+      const int row = (GATEUP ? 32 * wv + 128 * nf : 64 * wv + 32 * nf) + m32;
+      L.qrow[nf] = row * 128;
+      L.srow[nf] = row * 16;
+    }
+  }
+  f32x16 acc[8][2];
+#pragma unroll
+  for (int f = 0; f < 8; f++)
+#pragma unroll
+    for (int nf = 0; nf < 2; nf++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) acc[f][nf][i] = 0.0f;
+  // prologue: pair A copies the tokens of chunk 0 and all of span 0 and
+  // waits for them; pair B copies the tokens of chunk 1 (as if issued in
+  // chunk -1) and waits at the end of chunk 0.  nch % 4 == 0, nch >= 4.
+  {
+    const int pair = wv >> 1;
+    if (pair == 0) {
+      dma_tokens(L, smem, 0, 0, par);
+      dma_span_half(L, smem, 0, 0, 0, par);
+      dma_span_half(L, smem, 0, 0, 1, par);
+      lds_barrier_vm<0>();
+    } else {
+      dma_tokens(L, smem, 1, BIG_KC, par);
+      lds_barrier_vm<63>();
+    }
+  }
+  int c = 0;
+  for (; c + BIG_SPAN < nch; c += BIG_SPAN) big_span<NF, true, true>(L, acc, smem, c, wv);
+  // the last span: tokens of chunks c+2, c+3 still to copy, no next span
+  big_chunk<NF, 0, true, false>(L, acc, smem, c, wv);
+  big_chunk<NF, 1, true, false>(L, acc, smem, c + 1, wv);
+  big_chunk<NF, 2, false, false>(L, acc, smem, c + 2, wv);
+  big_chunk<NF, 3, false, false>(L, acc, smem, c + 3, wv);
+  const float gsa = p.gs0[t.e], gsb = GATEUP ? p.gs1[t.e] : 0.0f;
+#pragma unroll
+  for (int f = 0; f < NF; f++)
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      const int m = 32 * f + 8 * (i / 4) + 4 * g2 + (i % 4);
+      if (m < t.nvalid) {
+        if (GATEUP) {
+          const float hv = silu(gsa * acc[f][0][i]) * (gsb * acc[f][1][i]);
+          p.h[(size_t)(t.mb + m) * t.N + t.rtile * (BIG_N / 2) + 32 * wv + m32] = (f16)hv;
+        } else {
+#pragma unroll
+          for (int nf = 0; nf < 2; nf++)
+            p.rows[(size_t)(t.mb + m) * t.N + t.rtile * BIG_N + 64 * wv + 32 * nf + m32] = gsa * acc[f][nf][i];
+        }
+      }
+    }
+}
+
+template <bool GATEUP>
+__global__ __launch_bounds__(BIG_THREADS, 1) void expert_gemm_big_kernel(BigParams bp) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char big_smem[];
+  int32_t* rowoff = reinterpret_cast<int32_t*>(big_smem + BIG_OFF_ROW);
+  const GroupedParams& p = bp.g;
+  const int n_items = *bp.n_mtiles * bp.n_row_tiles;
+  const int per_xcd = (n_items + 7) / 8;
+  const int slot = blockIdx.x / 8, item = (blockIdx.x % 8) * per_xcd + slot;
+  if (slot >= per_xcd || item >= n_items) return;
+  const int mt = bp.mtiles[item / bp.n_row_tiles];
+  BigTile t;
+  t.rtile = item % bp.n_row_tiles;
+  t.e = mt >> 16;
+  const int mtile = mt & 0xFFFF;
+  // an expert's n records are split evenly over ceil(n / BIG_M) tiles
+  const int n_e = p.offsets[t.e + 1] - p.offsets[t.e];
+  const int tiles = (n_e + BIG_M - 1) / BIG_M;
+  const int ts = (n_e + tiles - 1) / tiles;
+  t.mb = p.offsets[t.e] + mtile * ts;
+  t.nvalid = min(ts, n_e - mtile * ts);
+  t.K = GATEUP ? p.H : p.I;
+  t.N = GATEUP ? p.I : p.H;
+  // source row (in units of K elements) of every token row of the tile;
+  // rows past the count repeat the last row
+  for (int m = threadIdx.x; m < BIG_M; m += BIG_THREADS) {
+    const int pp = t.mb + min(m, t.nvalid - 1);
+    rowoff[m] = GATEUP ? p.sorted_pairs[pp] / p.k : pp;
+  }
+  __syncthreads();
+  switch ((t.nvalid + 31) / 32) {  // token fragments, 1 .. 7
+    case 1: big_tile<1, GATEUP>(p, t, big_smem); break;
+    case 2: big_tile<2, GATEUP>(p, t, big_smem); break;
+    case 3: big_tile<3, GATEUP>(p, t, big_smem); break;
+    case 4: big_tile<4, GATEUP>(p, t, big_smem); break;
+    case 5: big_tile<5, GATEUP>(p, t, big_smem); break;
+    case 6: big_tile<6, GATEUP>(p, t, big_smem); break;
+    default: big_tile<BIG_MF, GATEUP>(p, t, big_smem); break;
+  }
+}
+
+// Token batches from this size use the large-tile kernels when the tiles
+// divide the matrices: H and I both in row tiles (256 and 128 rows) and in
+// multiples of four chunks of 64 (the DMA rotation), i.e. H % 256 == 0 and
+// I % 256 == 0.  Otherwise the small-batch kernels run with four fragments
+// per pass.
+constexpr int BIG_MIN_T = 1024;
+// Token rows are addressed with 32-bit byte offsets: 2 T H and 2 T k I must
+// stay below 2^32.
+bool use_big(const FfnArgs& a) {
+  const long long ki = (long long)a.k * a.I, span = (long long)a.T * (a.H > ki ? a.H : ki);
+  return a.T >= BIG_MIN_T && a.I % 256 == 0 && a.H % 256 == 0 && span < (1LL << 31);
+}
+
+template <bool GATEUP>
+hipError_t launch_big(const FfnArgs& a, const GroupedParams& p, hipStream_t s) {
+  BigParams bp;
+  bp.g = p;
+  bp.mtiles = a.mtiles;
+  bp.n_mtiles = a.n_mtiles;
+  bp.n_row_tiles = GATEUP ? a.I / (BIG_N / 2) : a.H / BIG_N;
+  const size_t lds = BIG_LDS;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&expert_gemm_big_kernel<GATEUP>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const long long items = (long long)a.max_mtiles * bp.n_row_tiles;
+  const unsigned grid = (unsigned)(8 * ((items + 7) / 8));
+  hipLaunchKernelGGL((expert_gemm_big_kernel<GATEUP>), dim3(grid), dim3(BIG_THREADS), lds, s, bp);
+  return hipGetLastError();
+}
+
 // y[t][n] = bf16( sum_j w[t][j] * rows[pair_pos[t*k+j]][n] ), fp32 sum over
 // ascending j.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ rows,
@@ -320,6 +756,7 @@ hipError_t launch_gateup(const FfnArgs& a, hipStream_t s) {
   p.q1 = a.w->up.q;
   p.sf1 = a.w->up.sf;
   p.gs1 = a.w->up.gs;
+  if (use_big(a)) return launch_big<true>(a, p, s);
   const dim3 grid(a.I / (32 * (4 / GU_KSPLIT)), a.max_active);
   return launch_gemm<GU_KSPLIT, true>(p, pick_mf(a.T), grid, s);
 }
@@ -330,6 +767,7 @@ hipError_t launch_down(const FfnArgs& a, hipStream_t s) {
   p.q0 = a.w->down.q;
   p.sf0 = a.w->down.sf;
   p.gs0 = a.w->down.gs;
+  if (use_big(a)) return launch_big<false>(a, p, s);
   const dim3 grid(a.H / (64 * (4 / DN_KSPLIT)), a.max_active);
   return launch_gemm<DN_KSPLIT, false>(p, pick_mf(a.T), grid, s);
 }

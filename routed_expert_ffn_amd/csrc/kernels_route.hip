@@ -86,6 +86,76 @@ __global__ __launch_bounds__(RT_THREADS) void router_gemv_kernel(const uint16_t*
   }
 }
 
+// ---- router logits on bf16 matrix cores (T >= 32) --------------------------------
+// v_mfma_f32_16x16x32_bf16 with A = 16 tokens x 32 k (x is K-contiguous) and
+// B = 32 k x 16 experts.  W_r is stored [H][E] (experts contiguous), so each
+// lane (c = l%16, g = l/16) loads rows k0+8g .. k0+8g+7 of experts
+// e0+8c .. e0+8c+7 (eight 16-byte loads) and transposes them in registers
+// into eight 8-element k-runs, one per expert: B fragment j of MFMA j holds
+// expert e0 + 8*(l%16) + j, so eight MFMAs cover 128 experts.  One wavefront
+// computes 64 tokens x 128 experts over one slab of K; slabs write partials
+// [slab][T][E] that the top-k kernel adds in a fixed order.  bf16 products
+// are exact in fp32.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+constexpr int RM_TOKENS = 64;
+constexpr int RM_EXPERTS = 128;
+
+__global__ __launch_bounds__(WAVE) void router_mfma_kernel(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ wr,
+                                                          float* __restrict__ part, int T, int H, int E,
+                                                          int kslab) {
+  const int lane = threadIdx.x, c = lane % 16, g = lane / 16;
+  const int e0 = blockIdx.x * RM_EXPERTS, t0 = blockIdx.y * RM_TOKENS;
+  const int k_begin = blockIdx.z * kslab, k_end = min(H, k_begin + kslab);
+  const int ec = e0 + 8 * c;  // this lane's 8 experts
+  const bool e_ok = ec < E;
+  const uint16_t* arow[4];
+#pragma unroll
+  for (int f = 0; f < 4; f++) arow[f] = x + (size_t)min(t0 + 16 * f + c, T - 1) * H;
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int f = 0; f < 4; f++)
+#pragma unroll
+    for (int j = 0; j < 8; j++) acc[f][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int k0 = k_begin; k0 < k_end; k0 += 32) {
+    uint4 rw[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+      rw[i] = e_ok ? *reinterpret_cast<const uint4*>(wr + (size_t)(k0 + 8 * g + i) * E + ec) : make_uint4(0, 0, 0, 0);
+    uint4 av[4];
+#pragma unroll
+    for (int f = 0; f < 4; f++) av[f] = *reinterpret_cast<const uint4*>(arow[f] + k0 + 8 * g);
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      // column j: (w[0][j], ..., w[7][j]); w[i][j] is half j%2 of dword j/2 of row i
+      uint32_t col[4];
+#pragma unroll
+      for (int p2 = 0; p2 < 4; p2++) {
+        const uint32_t lo = (&rw[2 * p2].x)[j / 2], hi = (&rw[2 * p2 + 1].x)[j / 2];
+        col[p2] = (j & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+      }
+      const bf16x8 bfrag = __builtin_bit_cast(bf16x8, make_uint4(col[0], col[1], col[2], col[3]));
+#pragma unroll
+      for (int f = 0; f < 4; f++)
+        acc[f][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[f]), bfrag, acc[f][j], 0,
+                                                            0, 0);
+    }
+  }
+  // D[4g+i][c] of MFMA (f, j): token t0+16f+4g+i, expert e0+8c+j.
+  if (!e_ok) return;
+#pragma unroll
+  for (int f = 0; f < 4; f++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int t = t0 + 16 * f + 4 * g + i;
+      if (t < T) {
+        float* dst = part + ((size_t)blockIdx.z * T + t) * E + ec;
+        *reinterpret_cast<float4*>(dst) = make_float4(acc[f][0][i], acc[f][1][i], acc[f][2][i], acc[f][3][i]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[f][4][i], acc[f][5][i], acc[f][6][i], acc[f][7][i]);
+      }
+    }
+}
+
 // ---- logits reduction + softmax + top-k ------------------------------------------
 // A block takes TB tokens.  All 1024 threads first sum the slab partials of
 // those tokens' logits (fixed ascending slab order), add the bias and store
@@ -104,13 +174,30 @@ __device__ __forceinline__ uint32_t float_order(float f) {
 __device__ __forceinline__ float order_float(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
+// Wavefront maximum of an unsigned 32-bit value with DPP lane moves:
+// quad_perm [1,0,3,2] and [2,3,0,1], row_ror 4 and 8 leave every lane of a
+// row with the row maximum; row_bcast 15 and 31 carry it across rows, so
+// lane 63 ends with the maximum of all 64 lanes.  Lanes without a source
+// read 0, the identity of the maximum.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_move(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_move<0xb1>(v));
+  v = max(v, dpp_move<0x4e>(v));
+  v = max(v, dpp_move<0x124>(v));
+  v = max(v, dpp_move<0x128>(v));
+  v = max(v, dpp_move<0x142>(v));
+  v = max(v, dpp_move<0x143>(v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+// Maximum 64-bit key: the high words first, then the low words among the
+// lanes holding the high-word maximum.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const uint64_t o = __shfl_xor(v, off, WAVE);
-    v = o > v ? o : v;
-  }
-  return v;
+  const uint32_t hi = wave_max_u32((uint32_t)(v >> 32));
+  const uint32_t lo = wave_max_u32((uint32_t)(v >> 32) == hi ? (uint32_t)v : 0u);
+  return ((uint64_t)hi << 32) | lo;
 }
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -317,10 +404,22 @@ __global__ __launch_bounds__(WAVE) void perm_count_kernel(const int32_t* __restr
 
 // One block of 1024 threads, thread e = expert: per-block counts become
 // absolute bases; writes offsets and the list of experts with work.
+// Entries (expert, token tile) for the large-batch GEMMs: expert e with c
+// records has ceil(c / MTILE) entries e * 65536 + tile, in expert order.
+__device__ void write_mtiles(int e, int cnt, int* lds, int32_t* __restrict__ mtiles,
+                             int32_t* __restrict__ n_mtiles) {
+  const int nt = (cnt + MTILE - 1) / MTILE;
+  int total;
+  const int first = block_exclusive_scan(nt, lds, &total);
+  for (int m = 0; m < nt; m++) mtiles[first + m] = e * 65536 + m;
+  if (threadIdx.x == 0) *n_mtiles = total;
+}
+
 __global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* __restrict__ counts, int nblocks, int E,
                                                         int P, int32_t* __restrict__ base,
                                                         int32_t* __restrict__ offsets, int32_t* __restrict__ active,
-                                                        int32_t* __restrict__ n_active) {
+                                                        int32_t* __restrict__ n_active, int32_t* __restrict__ mtiles,
+                                                        int32_t* __restrict__ n_mtiles) {
   __shared__ int lds[16];
   const int e = threadIdx.x;
   int running = 0;
@@ -343,6 +442,7 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* __restri
     offsets[E] = P;
     *n_active = nact;
   }
+  write_mtiles(e, e < E ? running : 0, lds, mtiles, n_mtiles);
 }
 
 __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
@@ -377,14 +477,18 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __rest
 // the caller), and the fp16 copy of the activations.
 __global__ __launch_bounds__(1024) void active_list_kernel(const int32_t* __restrict__ offsets, int E,
                                                           int32_t* __restrict__ active,
-                                                          int32_t* __restrict__ n_active) {
+                                                          int32_t* __restrict__ n_active,
+                                                          int32_t* __restrict__ mtiles,
+                                                          int32_t* __restrict__ n_mtiles) {
   __shared__ int lds[16];
   const int e = threadIdx.x;
-  const int flag = (e < E && offsets[e + 1] > offsets[e]) ? 1 : 0;
+  const int cnt = e < E ? offsets[e + 1] - offsets[e] : 0;
+  const int flag = cnt > 0 ? 1 : 0;
   int nact;
   const int slot = block_exclusive_scan(flag, lds, &nact);
   if (flag) active[slot] = e;
   if (e == 0) *n_active = nact;
+  write_mtiles(e, cnt, lds, mtiles, n_mtiles);
 }
 
 __global__ __launch_bounds__(256) void cast_kernel(const uint16_t* __restrict__ x, f16* __restrict__ x16,
@@ -395,11 +499,25 @@ __global__ __launch_bounds__(256) void cast_kernel(const uint16_t* __restrict__ 
 }
 
 int router_tt(int T) { return T <= 1 ? 1 : (T <= 2 ? 2 : (T <= 4 ? 4 : 8)); }
+constexpr int ROUTER_MFMA_MIN_T = 32;
 
 }  // namespace
 
 RouterPlan router_plan(int T, int H, int E) {
   RouterPlan p;
+  if (T >= ROUTER_MFMA_MIN_T) {
+    // one wavefront per (128 experts, 64 tokens, K slab); aim for >= 512
+    const int tiles = ((E + RM_EXPERTS - 1) / RM_EXPERTS) * ((T + RM_TOKENS - 1) / RM_TOKENS);
+    int s = (512 + tiles - 1) / tiles;
+    const int steps = H / 32;
+    if (s > steps) s = steps;
+    if (s < 1) s = 1;
+    const int steps_per_slab = (steps + s - 1) / s;
+    p.mfma = true;
+    p.slab_rows = steps_per_slab * 32;
+    p.slabs = (H + p.slab_rows - 1) / p.slab_rows;
+    return p;
+  }
   const int tt = router_tt(T);
   const int tiles = ((E + RT_E_TILE - 1) / RT_E_TILE) * ((T + tt - 1) / tt);
   int s = 512 / (tiles > 0 ? tiles : 1);
@@ -410,6 +528,7 @@ RouterPlan router_plan(int T, int H, int E) {
   // the block's activations slab lives in LDS: at most 64 KB
   const int max_steps = 16384 / (tt * RT_ROWS_PER_STEP);
   if (steps_per_slab > max_steps) steps_per_slab = max_steps;
+  p.mfma = false;
   p.slab_rows = steps_per_slab * RT_ROWS_PER_STEP;
   p.slabs = (H + p.slab_rows - 1) / p.slab_rows;
   return p;
@@ -417,6 +536,11 @@ RouterPlan router_plan(int T, int H, int E) {
 
 hipError_t launch_router(const uint16_t* x, const uint16_t* wr, float* part, int T, int H, int E,
                          const RouterPlan& rp, hipStream_t s) {
+  if (rp.mfma) {
+    const dim3 grid((E + RM_EXPERTS - 1) / RM_EXPERTS, (T + RM_TOKENS - 1) / RM_TOKENS, rp.slabs);
+    hipLaunchKernelGGL(router_mfma_kernel, grid, dim3(WAVE), 0, s, x, wr, part, T, H, E, rp.slab_rows);
+    return hipGetLastError();
+  }
   const int tt = router_tt(T);
   const dim3 grid((E + RT_E_TILE - 1) / RT_E_TILE, rp.slabs, (T + tt - 1) / tt);
   const size_t lds = sizeof(float) * ((size_t)tt * rp.slab_rows + 4 * 16 * tt * 8);
@@ -442,7 +566,8 @@ hipError_t launch_topk(const float* part, int slabs, const float* bias, float* l
 
 hipError_t launch_permute(const int32_t* ids, int T, int E, int k, uint64_t* masks, int32_t* counts, int32_t* base,
                           int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_pos, int32_t* active,
-                          int32_t* n_active, const uint16_t* x, f16* x16, int H, hipStream_t s) {
+                          int32_t* n_active, int32_t* mtiles, int32_t* n_mtiles, const uint16_t* x, f16* x16,
+                          int H, hipStream_t s) {
   if (T <= 64) {
     hipLaunchKernelGGL(perm_small_kernel, dim3(1), dim3(1024), 0, s, ids, T, E, k, offsets, sorted_pairs, pair_pos,
                        active, n_active, x, x16, H);
@@ -451,14 +576,15 @@ hipError_t launch_permute(const int32_t* ids, int T, int E, int k, uint64_t* mas
   const int nb = perm_blocks(T);
   hipLaunchKernelGGL(perm_count_kernel, dim3(nb), dim3(WAVE), 0, s, ids, T, E, k, masks, counts);
   hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, s, counts, nb, E, T * k, base, offsets, active,
-                     n_active);
+                     n_active, mtiles, n_mtiles);
   hipLaunchKernelGGL(perm_scatter_kernel, dim3(nb), dim3(256), 0, s, ids, T, E, k, masks, base, sorted_pairs,
                      pair_pos, x, x16, H);
   return hipGetLastError();
 }
 
-hipError_t launch_active_list(const int32_t* offsets, int E, int32_t* active, int32_t* n_active, hipStream_t s) {
-  hipLaunchKernelGGL(active_list_kernel, dim3(1), dim3(1024), 0, s, offsets, E, active, n_active);
+hipError_t launch_active_list(const int32_t* offsets, int E, int32_t* active, int32_t* n_active, int32_t* mtiles,
+                              int32_t* n_mtiles, hipStream_t s) {
+  hipLaunchKernelGGL(active_list_kernel, dim3(1), dim3(1024), 0, s, offsets, E, active, n_active, mtiles, n_mtiles);
   return hipGetLastError();
 }
 

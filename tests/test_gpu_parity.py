@@ -149,10 +149,15 @@ SMALL = dict(H=512, I=256)
 
 
 @pytest.mark.parametrize("T,E,k,beta", [(1, 64, 8, None), (3, 32, 16, None), (17, 64, 8, 0.5), (65, 32, 16, 0.8),
-                                        (130, 16, 16, None), (200, 40, 4, 1.0), (33, 8, 8, None), (70, 48, 1, 0.3)])
+                                        (130, 16, 16, None), (200, 40, 4, 1.0), (33, 8, 8, None), (70, 48, 1, 0.3),
+                                        (1100, 32, 8, 0.5), (2048, 16, 4, None), (1500, 64, 16, 1.0),
+                                        (1024, 200, 2, 1.2)])
 def test_ragged_layer(T, E, k, beta):
     """Token counts that are not multiples of 16 or 64, experts with more
-    than 64 tokens (several passes), every expert selected (k = E), k = 1."""
+    than 64 tokens (several passes), every expert selected (k = E), k = 1,
+    and batches of 1024+ tokens (the 224-token tile kernels) with experts
+    holding several ragged 224-token tiles, or only a handful of tokens
+    (tiles with a single 32-token fragment)."""
     say(f"ragged T={T} E={E} k={k} beta={beta}")
     bias = None if beta is None else synth.zipf_bias(9, E, beta)
     inp = Inputs(T, SMALL["H"], SMALL["I"], E, k, seed=9, bias=bias, router_std=0.1)
@@ -161,7 +166,7 @@ def test_ragged_layer(T, E, k, beta):
     counts = np.diff(r["offsets"])
     say(f"  counts: max={counts.max()} active={np.count_nonzero(counts)}")
     ox = OracleExperts(9, SMALL["H"], SMALL["I"])
-    ref = oracle.moe_layer(inp.host_x(), ox.get(r["ids"]), E, k, logits_in=r["logits"], want_rows=True)
+    ref = oracle.moe_layer(inp.host_x(), ox.get(r["ids"]), E, k, logits_in=r["logits"], want_rows=True, nthreads=16)
     rows = inp.ffn(r["offsets"], r["sorted_pairs"])
     assert_close(rows, ref["rows"], "rows")
     y, ids, _ = inp.layer()
