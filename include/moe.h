@@ -160,7 +160,8 @@ const char* moe_last_error(void);
  * Kernels of the path, in launch order within moe_layer. */
 typedef enum {
   MOE_KERNEL_ROUTER = 0,  /* router logits (slab partials + reduction)   */
-  MOE_KERNEL_TOPK = 1,    /* softmax + top-k                             */
+  MOE_KERNEL_TOPK = 1,    /* softmax + top-k; for T <= 8 one launch that  */
+                          /* also permutes (nothing is then PERMUTE)     */
   MOE_KERNEL_PERMUTE = 2, /* histogram, scan and scatter (three kernels) */
   MOE_KERNEL_CAST = 3,    /* activations bf16 -> fp16                    */
   MOE_KERNEL_GATEUP = 4,  /* grouped gate/up GEMM + SiLU*mul             */
@@ -169,12 +170,21 @@ typedef enum {
   MOE_KERNEL_COUNT = 7
 } moe_kernel;
 
-/* While armed, each launch of `kernel` on the calling thread records
- * events[2i] before and events[2i+1] after the i-th launch (i < n_pairs) on
- * the launch stream; events are hipEvent_t handles the caller created and
- * later reads with hipEventElapsedTime.  Pass events = NULL to disarm.
- * Returns the number of pairs recorded since the last arming. */
-int moe_profile_arm(moe_kernel kernel, void** events, int n_pairs);
+/* Timing of one kernel's launches made by the calling thread.
+ * moe_profile_arm creates n_pairs (1 .. 65536) pairs of HIP events on the
+ * current device, with timing and without the system-scope fence (so that a
+ * record costs the stream next to nothing), and arms: the i-th later launch
+ * of `kernel` (i < n_pairs) records pair i around itself on its launch
+ * stream.  Arming again first releases the events of a previous arming.
+ * Returns MOE_OK, MOE_ERR_ARG (kernel or n_pairs out of range) or
+ * MOE_ERR_HIP (event creation failed; nothing is armed).
+ * moe_profile_read waits for the recorded pairs, writes the duration in
+ * milliseconds of the first min(recorded, max) launches to ms (host
+ * memory), releases the events, disarms, and returns the number written,
+ * or minus the moe_status of a failure (ms NULL or max < 0: -MOE_ERR_ARG;
+ * a HIP event call failed: -MOE_ERR_HIP). */
+moe_status moe_profile_arm(moe_kernel kernel, int n_pairs);
+int moe_profile_read(float* ms, int max);
 
 #ifdef __cplusplus
 }

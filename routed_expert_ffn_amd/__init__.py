@@ -18,7 +18,8 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_ARG", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_A
 KERNELS = {"router": 0, "topk": 1, "permute": 2, "cast": 3, "gateup": 4, "down": 5, "combine": 6}
 # Symbols include/moe.h declares.
 EXPORTS = ("moe_workspace_bytes", "moe_quantize_workspace_bytes", "moe_quantize_nvfp4", "moe_route",
-           "moe_expert_ffn", "moe_layer", "moe_status_string", "moe_last_error", "moe_profile_arm")
+           "moe_expert_ffn", "moe_layer", "moe_status_string", "moe_last_error", "moe_profile_arm",
+           "moe_profile_read")
 
 
 class MoeError(RuntimeError):
@@ -68,7 +69,9 @@ def lib():
         L.moe_last_error.restype = ctypes.c_char_p
         L.moe_last_error.argtypes = []
         L.moe_profile_arm.restype = ctypes.c_int
-        L.moe_profile_arm.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+        L.moe_profile_arm.argtypes = [ctypes.c_int, ctypes.c_int]
+        L.moe_profile_read.restype = ctypes.c_int
+        L.moe_profile_read.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_int]
         _lib = L
     return _lib
 
@@ -136,18 +139,20 @@ def moe_layer(d, x, w_router, bias, experts, y, topk_ids_out, topk_w_out, ws, st
                            _stream(stream)))
 
 
-def moe_profile_arm(kernel, events=None):
-    """Arm timing of one kernel (name or id) with a list of torch.cuda.Event
-    pairs (enable_timing=True); returns the pairs recorded since the last
-    arming.  events=None disarms."""
+def moe_profile_arm(kernel, n_pairs):
+    """Arm timing of the next n_pairs launches of one kernel (name or id) on
+    this thread; the library records its own events on the launch stream."""
     kid = KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
-    if not events:
-        return lib().moe_profile_arm(kid, None, 0)
-    for ev in events:  # torch creates the underlying hipEvent_t lazily, at the first record
-        ev.record()
-    handles = (ctypes.c_void_p * len(events))(*[ev.cuda_event for ev in events])
-    moe_profile_arm._keep = handles
-    return lib().moe_profile_arm(kid, handles, len(events) // 2)
+    _check(lib().moe_profile_arm(kid, int(n_pairs)))
+
+
+def moe_profile_read(max_launches):
+    """Durations (ms) of the launches recorded since moe_profile_arm; disarms."""
+    buf = (ctypes.c_float * max(1, int(max_launches)))()
+    n = lib().moe_profile_read(buf, int(max_launches))
+    if n < 0:
+        _check(-n)
+    return [float(buf[i]) for i in range(n)]
 
 
 # ---- device memory holders (plumbing) ------------------------------------------

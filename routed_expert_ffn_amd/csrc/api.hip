@@ -5,6 +5,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <vector>
+
 #include "internal.h"
 
 namespace {
@@ -27,9 +29,14 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct Prof {
   int kernel = -1;
-  void** events = nullptr;
-  int n_pairs = 0;
+  std::vector<hipEvent_t> events;  // 2 per launch
   int used = 0;
+  void release() {
+    for (hipEvent_t e : events) (void)hipEventDestroy(e);
+    events.clear();
+    used = 0;
+    kernel = -1;
+  }
 };
 thread_local Prof g_prof;
 
@@ -141,6 +148,15 @@ moe_status enqueue_route(const moe_dims& d, const void* x, const void* wr, const
            moe::launch_router(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wr),
                               at<float>(ws, L.part), d.T, d.H, d.E, rp, s),
            "router");
+  if (moe::route_fused(d.T)) {  // top-k and permutation in one launch, timed as top-k
+    LAUNCH(MOE_KERNEL_TOPK, s,
+           moe::launch_route_small(x ? at<float>(ws, L.part) : nullptr, rp.slabs, x ? bias : nullptr, logits, d.T,
+                                   d.E, d.k, ids, w, offsets, sorted, pos, at<int32_t>(ws, L.active),
+                                   at<int32_t>(ws, L.nact), x16 ? static_cast<const uint16_t*>(x) : nullptr, x16,
+                                   d.H, s),
+           "route");
+    return MOE_OK;
+  }
   LAUNCH(MOE_KERNEL_TOPK, s,
          moe::launch_topk(x ? at<float>(ws, L.part) : nullptr, rp.slabs, x ? bias : nullptr, logits, d.T, d.E, d.k,
                           ids, w, s),
@@ -185,13 +201,13 @@ moe_status enqueue_ffn(const moe_dims& d, const int32_t* offsets, const int32_t*
 }  // namespace
 
 void moe::prof_before(moe_kernel k, hipStream_t s) {
-  if (g_prof.events && g_prof.kernel == (int)k && g_prof.used < g_prof.n_pairs)
-    (void)hipEventRecord(static_cast<hipEvent_t>(g_prof.events[2 * g_prof.used]), s);
+  if (g_prof.kernel == (int)k && 2 * g_prof.used < (int)g_prof.events.size())
+    (void)hipEventRecord(g_prof.events[2 * g_prof.used], s);
 }
 
 void moe::prof_after(moe_kernel k, hipStream_t s) {
-  if (g_prof.events && g_prof.kernel == (int)k && g_prof.used < g_prof.n_pairs) {
-    (void)hipEventRecord(static_cast<hipEvent_t>(g_prof.events[2 * g_prof.used + 1]), s);
+  if (g_prof.kernel == (int)k && 2 * g_prof.used < (int)g_prof.events.size()) {
+    (void)hipEventRecord(g_prof.events[2 * g_prof.used + 1], s);
     g_prof.used++;
   }
 }
@@ -304,13 +320,35 @@ const char* moe_status_string(moe_status s) {
 
 const char* moe_last_error(void) { return g_err; }
 
-int moe_profile_arm(moe_kernel kernel, void** events, int n_pairs) {
-  const int used = g_prof.used;
+moe_status moe_profile_arm(moe_kernel kernel, int n_pairs) {
+  g_prof.release();
+  if ((int)kernel < 0 || (int)kernel >= MOE_KERNEL_COUNT || n_pairs < 1 || n_pairs > 65536)
+    return fail(MOE_ERR_ARG, "moe_profile_arm: kernel %d, n_pairs %d", (int)kernel, n_pairs);
+  g_prof.events.resize(2 * (size_t)n_pairs);
+  for (size_t i = 0; i < g_prof.events.size(); i++) {
+    if (hipEventCreateWithFlags(&g_prof.events[i], hipEventDisableSystemFence) != hipSuccess) {
+      g_prof.events.resize(i);
+      g_prof.release();
+      return fail(MOE_ERR_HIP, "moe_profile_arm: hipEventCreateWithFlags failed");
+    }
+  }
   g_prof.kernel = (int)kernel;
-  g_prof.events = (events && n_pairs > 0) ? events : nullptr;
-  g_prof.n_pairs = events ? n_pairs : 0;
-  g_prof.used = 0;
-  return used;
+  return MOE_OK;
+}
+
+int moe_profile_read(float* ms, int max) {
+  if (!ms || max < 0) return -(int)fail(MOE_ERR_ARG, "moe_profile_read: ms is NULL or max < 0");
+  const int n = g_prof.used < max ? g_prof.used : max;
+  int status = n;
+  for (int i = 0; i < n; i++) {
+    if (hipEventSynchronize(g_prof.events[2 * i + 1]) != hipSuccess ||
+        hipEventElapsedTime(&ms[i], g_prof.events[2 * i], g_prof.events[2 * i + 1]) != hipSuccess) {
+      status = -(int)fail(MOE_ERR_HIP, "moe_profile_read: event %d", i);
+      break;
+    }
+  }
+  g_prof.release();
+  return status;
 }
 
 }  // extern "C"

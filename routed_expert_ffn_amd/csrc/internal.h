@@ -37,6 +37,14 @@ hipError_t launch_topk(const float* part, int slabs, const float* bias, float* l
 // Offsets, permutation, active-expert list and (for T > 64) the list of
 // (expert, token tile) entries; if x is non-NULL also writes the fp16
 // copy x16 of the activations [T][H].
+// T small enough for the single-launch routing kernel.
+bool route_fused(int T);
+// Logits reduction, top-k, permutation, active list and fp16 copy of x in one
+// launch (T <= the fused limit).
+hipError_t launch_route_small(const float* part, int slabs, const float* bias, float* logits, int T, int E, int k,
+                              int32_t* ids, float* w, int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_pos,
+                              int32_t* active, int32_t* n_active, const uint16_t* x, f16* x16, int H,
+                              hipStream_t s);
 hipError_t launch_permute(const int32_t* ids, int T, int E, int k, uint64_t* masks, int32_t* counts, int32_t* base,
                           int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_pos, int32_t* active,
                           int32_t* n_active, int32_t* mtiles, int32_t* n_mtiles, const uint16_t* x, f16* x16,

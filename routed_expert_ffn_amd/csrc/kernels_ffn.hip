@@ -673,23 +673,39 @@ hipError_t launch_big(const FfnArgs& a, const GroupedParams& p, hipStream_t s) {
 }
 
 // y[t][n] = bf16( sum_j w[t][j] * rows[pair_pos[t*k+j]][n] ), fp32 sum over
-// ascending j.
+// ascending j.  A thread takes four columns; the positions and weights of 16
+// records, then their 16 row loads, are issued together before the sums.
+constexpr int COMBINE_JB = 16;
+
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ rows,
                                                      const int32_t* __restrict__ pair_pos,
                                                      const float* __restrict__ w, int H, int k,
                                                      uint16_t* __restrict__ y) {
   const int t = blockIdx.y;
-  const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
+  const int n = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (n >= H) return;
   float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
-  for (int j = 0; j < k; j++) {
-    const int pos = pair_pos[(size_t)t * k + j];
-    const float wj = w[(size_t)t * k + j];
-    const float4 v = *reinterpret_cast<const float4*>(rows + (size_t)pos * H + n);
-    a0 = fmaf(wj, v.x, a0);
-    a1 = fmaf(wj, v.y, a1);
-    a2 = fmaf(wj, v.z, a2);
-    a3 = fmaf(wj, v.w, a3);
+  for (int j0 = 0; j0 < k; j0 += COMBINE_JB) {
+    int pos[COMBINE_JB];
+    float wj[COMBINE_JB];
+#pragma unroll
+    for (int u = 0; u < COMBINE_JB; u++) {
+      const bool ok = j0 + u < k;
+      pos[u] = ok ? pair_pos[(size_t)t * k + j0 + u] : 0;
+      wj[u] = ok ? w[(size_t)t * k + j0 + u] : 0.0f;
+    }
+    float4 v[COMBINE_JB];
+#pragma unroll
+    for (int u = 0; u < COMBINE_JB; u++)
+      v[u] = j0 + u < k ? *reinterpret_cast<const float4*>(rows + (size_t)pos[u] * H + n) : make_float4(0, 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < COMBINE_JB; u++)
+      if (j0 + u < k) {
+        a0 = fmaf(wj[u], v[u].x, a0);
+        a1 = fmaf(wj[u], v[u].y, a1);
+        a2 = fmaf(wj[u], v[u].z, a2);
+        a3 = fmaf(wj[u], v[u].w, a3);
+      }
   }
   uint2 o;
   o.x = (uint32_t)f32_to_bf16(a0) | ((uint32_t)f32_to_bf16(a1) << 16);
@@ -774,7 +790,9 @@ hipError_t launch_down(const FfnArgs& a, hipStream_t s) {
 
 hipError_t launch_combine(const float* rows, const int32_t* pair_pos, const float* w, int T, int H, int k,
                           uint16_t* y, hipStream_t s) {
-  hipLaunchKernelGGL(combine_kernel, dim3((H / 4 + 255) / 256, T), dim3(256), 0, s, rows, pair_pos, w, H, k, y);
+  const int threads = T < 64 ? 64 : 256;  // few tokens: spread the columns over more CUs
+  hipLaunchKernelGGL(combine_kernel, dim3((H / 4 + threads - 1) / threads, T), dim3(threads), 0, s, rows, pair_pos, w,
+                     H, k, y);
   return hipGetLastError();
 }
 

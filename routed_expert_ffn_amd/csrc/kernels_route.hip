@@ -21,6 +21,7 @@ namespace {
 // the four waves through LDS, in a fixed order, and the block writes one
 // partial per (slab, token, expert).  bf16 x bf16 products are exact in fp32.
 constexpr int RT_THREADS = 256;
+constexpr int ROUTER_MAX_SLABS = 32;  // K slabs of the router, at most
 constexpr int RT_E_TILE = 128;
 constexpr int RT_ROWS_PER_STEP = 16;
 
@@ -49,18 +50,30 @@ __global__ __launch_bounds__(RT_THREADS) void router_gemv_kernel(const uint16_t*
 #pragma unroll
     for (int i = 0; i < 8; i++) acc[a][i] = 0.0f;
   if (e0 < E) {
-    for (int r = 4 * wv + rr; r < rows; r += RT_ROWS_PER_STEP) {
-      const uint4 w8 = *reinterpret_cast<const uint4*>(wr + (size_t)(h0 + r) * E + e0);
-      float wf[8];
-      wf[0] = __uint_as_float(w8.x << 16); wf[1] = __uint_as_float(w8.x & 0xFFFF0000u);
-      wf[2] = __uint_as_float(w8.y << 16); wf[3] = __uint_as_float(w8.y & 0xFFFF0000u);
-      wf[4] = __uint_as_float(w8.z << 16); wf[5] = __uint_as_float(w8.z & 0xFFFF0000u);
-      wf[6] = __uint_as_float(w8.w << 16); wf[7] = __uint_as_float(w8.w & 0xFFFF0000u);
+    // rows in batches of eight loads in flight, then their FMAs in row order
+    for (int r0 = 4 * wv + rr; r0 < rows; r0 += 8 * RT_ROWS_PER_STEP) {
+      uint4 w8[8];
 #pragma unroll
-      for (int a = 0; a < TT; a++) {
-        const float xv = xs[a * slab_rows + r];
+      for (int b = 0; b < 8; b++) {
+        const int r = r0 + b * RT_ROWS_PER_STEP;
+        w8[b] = r < rows ? *reinterpret_cast<const uint4*>(wr + (size_t)(h0 + r) * E + e0) : make_uint4(0, 0, 0, 0);
+      }
 #pragma unroll
-        for (int i = 0; i < 8; i++) acc[a][i] = fmaf(xv, wf[i], acc[a][i]);
+      for (int b = 0; b < 8; b++) {
+        const int r = r0 + b * RT_ROWS_PER_STEP;
+        if (r < rows) {
+          float wf[8];
+          wf[0] = __uint_as_float(w8[b].x << 16); wf[1] = __uint_as_float(w8[b].x & 0xFFFF0000u);
+          wf[2] = __uint_as_float(w8[b].y << 16); wf[3] = __uint_as_float(w8[b].y & 0xFFFF0000u);
+          wf[4] = __uint_as_float(w8[b].z << 16); wf[5] = __uint_as_float(w8[b].z & 0xFFFF0000u);
+          wf[6] = __uint_as_float(w8[b].w << 16); wf[7] = __uint_as_float(w8[b].w & 0xFFFF0000u);
+#pragma unroll
+          for (int a = 0; a < TT; a++) {
+            const float xv = xs[a * slab_rows + r];
+#pragma unroll
+            for (int i = 0; i < 8; i++) acc[a][i] = fmaf(xv, wf[i], acc[a][i]);
+          }
+        }
       }
     }
   }
@@ -231,49 +244,32 @@ __device__ __forceinline__ void sort16_desc(uint64_t (&k)[TOPK_KEYS]) {
 
 constexpr int TOPK_THREADS = 1024;
 
-template <int TB>
-__global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(const float* __restrict__ part, int slabs,
-                                                           const float* __restrict__ bias,
-                                                           float* __restrict__ logits, int T, int E, int k,
-                                                           int32_t* __restrict__ ids, float* __restrict__ wout) {
-  __shared__ float ls[TB * 1024];
-  const int t0 = blockIdx.x * TB;
-  // Phase 1: logits of this block's tokens; the slab partials of a logit are
-  // loaded 16 at a time and added in ascending slab order.
-  for (int idx = threadIdx.x; idx < TB * E; idx += TOPK_THREADS) {
-    const int a = idx / E, e = idx % E, t = t0 + a;
-    if (t >= T) continue;
-    float v;
-    if (part) {
-      const float* p = part + (size_t)t * E + e;
-      const size_t step = (size_t)T * E;
-      v = 0.0f;
-      int z = 0;
-      for (; z + 16 <= slabs; z += 16) {
-        float b[16];
+// Sum of the slab partials of one logit, in ascending slab order; the loads
+// are issued together, so a thread waits for memory once (the router plan
+// keeps the slab count at or below ROUTER_MAX_SLABS).
+__device__ __forceinline__ float sum_slabs(const float* __restrict__ p, size_t step, int slabs) {
+  float v = 0.0f;
+  for (int z0 = 0; z0 < slabs; z0 += ROUTER_MAX_SLABS) {
+    float b[ROUTER_MAX_SLABS];
 #pragma unroll
-        for (int u = 0; u < 16; u++) b[u] = p[(size_t)(z + u) * step];
+    for (int u = 0; u < ROUTER_MAX_SLABS; u++) b[u] = z0 + u < slabs ? p[(size_t)(z0 + u) * step] : 0.0f;
 #pragma unroll
-        for (int u = 0; u < 16; u++) v += b[u];
-      }
-      for (; z < slabs; z++) v += p[(size_t)z * step];
-      if (bias) v += bias[e];
-      logits[(size_t)t * E + e] = v;
-    } else {
-      v = logits[(size_t)t * E + e];  // logits given by the caller
-    }
-    ls[a * 1024 + e] = v;
+    for (int u = 0; u < ROUTER_MAX_SLABS; u++)
+      if (z0 + u < slabs) v += b[u];
   }
-  __syncthreads();
-  // Phase 2: wavefront w selects for token t0 + w.
-  const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE;
-  const int t = t0 + wv;
-  if (wv >= TB || t >= T) return;
+  return v;
+}
+
+// One wavefront: the top k of E logits (LDS) and their renormalised softmax
+// weights, written to ids[0..k) / w[0..k) (and ids_copy, if given).
+__device__ __forceinline__ void select_topk(const float* ls, int E, int k, int32_t* __restrict__ ids, float* __restrict__ w,
+                            int32_t* ids_copy) {
+  const int lane = threadIdx.x % WAVE;
   uint64_t key[TOPK_KEYS];
 #pragma unroll
   for (int i = 0; i < TOPK_KEYS; i++) {
     const int e = lane + WAVE * i;
-    key[i] = e < E ? (((uint64_t)float_order(ls[wv * 1024 + e]) << 32) | (uint32_t)~(uint32_t)e) : 0ull;
+    key[i] = e < E ? (((uint64_t)float_order(ls[e]) << 32) | (uint32_t)~(uint32_t)e) : 0ull;
   }
   sort16_desc(key);
   int my_id = 0;
@@ -297,9 +293,40 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(const float* __restr
   const float ex = lane < k ? expf(my_logit - top) : 0.0f;
   const float sum = wave_sum(ex);
   if (lane < k) {
-    ids[(size_t)t * k + lane] = my_id;
-    wout[(size_t)t * k + lane] = ex / sum;
+    ids[lane] = my_id;
+    w[lane] = ex / sum;
+    if (ids_copy) ids_copy[lane] = my_id;
   }
+}
+
+template <int TB>
+__global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(const float* __restrict__ part, int slabs,
+                                                           const float* __restrict__ bias,
+                                                           float* __restrict__ logits, int T, int E, int k,
+                                                           int32_t* __restrict__ ids, float* __restrict__ wout) {
+  __shared__ float ls[TB * 1024];
+  const int t0 = blockIdx.x * TB;
+  // Phase 1: logits of this block's tokens (slab partials added in ascending
+  // slab order, or the caller's logits).
+  for (int idx = threadIdx.x; idx < TB * E; idx += TOPK_THREADS) {
+    const int a = idx / E, e = idx % E, t = t0 + a;
+    if (t >= T) continue;
+    float v;
+    if (part) {
+      v = sum_slabs(part + (size_t)t * E + e, (size_t)T * E, slabs);
+      if (bias) v += bias[e];
+      logits[(size_t)t * E + e] = v;
+    } else {
+      v = logits[(size_t)t * E + e];  // logits given by the caller
+    }
+    ls[a * 1024 + e] = v;
+  }
+  __syncthreads();
+  // Phase 2: wavefront w selects for token t0 + w.
+  const int wv = threadIdx.x / WAVE;
+  const int t = t0 + wv;
+  if (wv >= TB || t >= T) return;
+  select_topk(ls + wv * 1024, E, k, ids + (size_t)t * k, wout + (size_t)t * k, nullptr);
 }
 
 // ---- permutation ---------------------------------------------------------------
@@ -311,7 +338,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(const float* __restr
 constexpr int PERM_MAX_E = 1024;
 
 // Block-wide exclusive scan of one int per thread (blockDim.x = 1024).
-__device__ int block_exclusive_scan(int v, int* lds /*[16]*/, int* total) {
+__device__ __forceinline__ int block_exclusive_scan(int v, int* lds /*[16]*/, int* total) {
   const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE;
   int incl = v;
 #pragma unroll
@@ -331,6 +358,124 @@ __device__ int block_exclusive_scan(int v, int* lds /*[16]*/, int* total) {
   return base + incl - v;
 }
 
+// ---- top-k of one token by a block of 1024 threads ------------------------------
+// Exact, by filtering.  Keys are (u << 32 | ~index), u = float_order(logit):
+// larger key = larger logit, then lower index.  Each of the W = E/64 full
+// wavefronts takes the j = ceil(k / W) largest of its 64 keys (j rounds of a
+// DPP wavefront maximum); tau = the k-th largest of those W*j leaders is at
+// most the k-th largest key overall (a subset's order statistic), so every
+// key of the top k is >= tau, and at least k keys are.  The keys >= tau
+// (about k for ordinary logits) are gathered into wavefront 0, one per lane,
+// and each finds its rank by comparing against all the others.  Winners are
+// placed lane = rank and weighted as in select_topk, so the results are the
+// same bit for bit.  When the leaders or the keys >= tau do not fit in 64
+// lanes (few full wavefronts, heavy ties) wavefront 0 runs select_topk.
+struct BlockTopkLds {
+  uint64_t cand[64];
+  uint64_t tau;
+  int cnt[16];
+  float out_l[64];
+  int out_e[64];
+};
+
+// Rank of this lane's key among the first n lanes' keys (wavefront 0).
+__device__ __forceinline__ int lane_rank(uint64_t mine, int n) {
+  int rank = 0;
+  for (int i = 0; i < n; i++) {
+    const uint64_t other = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(mine >> 32), i) << 32) |
+                           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mine, i);
+    rank += other > mine ? 1 : 0;
+  }
+  return rank;
+}
+
+__device__ __forceinline__ void block_topk(const float* ls, int E, int k, int32_t* __restrict__ ids,
+                                           float* __restrict__ w, int32_t* ids_copy, BlockTopkLds& S) {
+  const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
+  const uint64_t key = tid < E ? (((uint64_t)float_order(ls[tid]) << 32) | (uint32_t)~(uint32_t)tid) : 0ull;
+  const int W = E / WAVE;
+  const int j = W > 0 ? (k + W - 1) / W : 0;
+  const int n_lead = W * j;
+  bool fast = W > 0 && n_lead <= WAVE;
+  // leaders: the j largest keys of each full wavefront
+  if (fast && wv < W) {
+    uint64_t kk = key;
+    for (int r = 0; r < j; r++) {
+      const uint64_t m = wave_max_u64(kk);
+      if (kk == m) kk = 0ull;
+      if (lane == 0) S.cand[wv * j + r] = m;
+    }
+  }
+  __syncthreads();
+  if (fast && wv == 0) {
+    const uint64_t c = lane < n_lead ? S.cand[lane] : 0ull;
+    const int rank = lane_rank(c, n_lead);
+    if (lane < n_lead && rank == k - 1) S.tau = c;
+  }
+  __syncthreads();
+  const uint64_t tau = fast ? S.tau : ~0ull;
+  const bool cand = fast && key != 0ull && key >= tau;
+  const uint64_t bal = __ballot(cand);
+  if (lane == 0) S.cnt[wv] = __popcll(bal);
+  __syncthreads();
+  int base = 0, total = 0;
+  for (int i = 0; i < (int)(blockDim.x / WAVE); i++) {
+    if (i < wv) base += S.cnt[i];
+    total += S.cnt[i];
+  }
+  fast = fast && total <= WAVE;
+  if (fast && cand) S.cand[base + __popcll(bal & ((1ull << lane) - 1ull))] = key;
+  __syncthreads();
+  if (wv == 0) {
+    if (fast) {
+      const uint64_t mine = lane < total ? S.cand[lane] : 0ull;
+      const int rank = lane_rank(mine, total);
+      if (lane < total && rank < k) {
+        S.out_l[rank] = order_float((uint32_t)(mine >> 32));
+        S.out_e[rank] = (int)~(uint32_t)mine;
+      }
+      // (same wavefront: its LDS writes are read back in order)
+      const float l = lane < k ? S.out_l[lane] : 0.0f;
+      const float top = S.out_l[0];
+      const float ex = lane < k ? expf(l - top) : 0.0f;
+      const float sum = wave_sum(ex);
+      if (lane < k) {
+        const int e = S.out_e[lane];
+        ids[lane] = e;
+        w[lane] = ex / sum;
+        if (ids_copy) ids_copy[lane] = e;
+      }
+    } else {
+      select_topk(ls, E, k, ids, w, ids_copy);
+    }
+  }
+  __syncthreads();
+}
+
+// One token per block: the logits (as topk_kernel), then block_topk.
+__global__ __launch_bounds__(TOPK_THREADS) void topk_block_kernel(const float* __restrict__ part, int slabs,
+                                                                 const float* __restrict__ bias,
+                                                                 float* __restrict__ logits, int T, int E, int k,
+                                                                 int32_t* __restrict__ ids,
+                                                                 float* __restrict__ wout) {
+  __shared__ float ls[1024];
+  __shared__ BlockTopkLds tk;
+  const int t = blockIdx.x, e = threadIdx.x;
+  if (e < E) {
+    float v;
+    if (part) {
+      v = sum_slabs(part + (size_t)t * E + e, (size_t)T * E, slabs);
+      if (bias) v += bias[e];
+      logits[(size_t)t * E + e] = v;
+    } else {
+      v = logits[(size_t)t * E + e];
+    }
+    ls[e] = v;
+  }
+  __syncthreads();
+  block_topk(ls, E, k, ids + (size_t)t * k, wout + (size_t)t * k, nullptr, tk);
+}
+
 __device__ __forceinline__ void cast_rows(const uint16_t* __restrict__ x, f16* __restrict__ x16, size_t first8,
                                          size_t n8, int tid, int nthreads) {
   for (size_t i = first8 + tid; i < first8 + n8; i += nthreads) {
@@ -344,22 +489,14 @@ __device__ __forceinline__ void cast_rows(const uint16_t* __restrict__ x, f16* _
   }
 }
 
-// T <= 64: the whole permutation, the active-expert list and the fp16 copy
-// of the activations, in one block of 1024 threads.
-__global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
-                                                         int32_t* __restrict__ offsets,
-                                                         int32_t* __restrict__ sorted_pairs,
-                                                         int32_t* __restrict__ pair_pos,
-                                                         int32_t* __restrict__ active,
-                                                         int32_t* __restrict__ n_active,
-                                                         const uint16_t* __restrict__ x, f16* __restrict__ x16,
-                                                         int H) {
-  __shared__ unsigned long long m[PERM_MAX_E];
-  __shared__ int off_s[PERM_MAX_E];
-  __shared__ int lds[16];
+// The permutation of up to 64 tokens in one block of 1024 threads (thread e
+// = expert e for the counts): m and off_s are LDS arrays of E entries, m
+// zeroed by the caller before a barrier.  Also writes the active-expert list.
+__device__ __forceinline__ void permute_block(const int32_t* ids, int T, int E, int k, int32_t* __restrict__ offsets,
+                              int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_pos,
+                              int32_t* __restrict__ active, int32_t* __restrict__ n_active, unsigned long long* m,
+                              int* off_s, int* lds) {
   const int tid = threadIdx.x;
-  if (tid < E) m[tid] = 0ull;
-  __syncthreads();
   for (int f = tid; f < T * k; f += 1024) atomicOr(&m[ids[f]], 1ull << (f / k));
   __syncthreads();
   const int cnt = tid < E ? __popcll(m[tid]) : 0;
@@ -383,6 +520,67 @@ __global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t* __restr
     sorted_pairs[pos] = f;
     pair_pos[f] = pos;
   }
+}
+
+// T <= 64: the whole permutation, the active-expert list and the fp16 copy
+// of the activations, in one block of 1024 threads.
+__global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
+                                                         int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ sorted_pairs,
+                                                         int32_t* __restrict__ pair_pos,
+                                                         int32_t* __restrict__ active,
+                                                         int32_t* __restrict__ n_active,
+                                                         const uint16_t* __restrict__ x, f16* __restrict__ x16,
+                                                         int H) {
+  __shared__ unsigned long long m[PERM_MAX_E];
+  __shared__ int off_s[PERM_MAX_E];
+  __shared__ int lds[16];
+  if (threadIdx.x < E) m[threadIdx.x] = 0ull;
+  __syncthreads();
+  permute_block(ids, T, E, k, offsets, sorted_pairs, pair_pos, active, n_active, m, off_s, lds);
+  if (x) cast_rows(x, x16, 0, (size_t)T * H / 8, threadIdx.x, 1024);
+}
+
+// T <= ROUTE_SMALL_T: the whole routing in one block of 1024 threads (one
+// launch instead of three): logits from the slab partials (or the caller's
+// logits), top-k and weights (block_topk, token by token), then the
+// permutation, the active-expert list and the fp16 copy of the activations.
+constexpr int ROUTE_SMALL_T = 8;
+
+__global__ __launch_bounds__(1024) void route_small_kernel(const float* __restrict__ part, int slabs,
+                                                          const float* __restrict__ bias, float* __restrict__ logits,
+                                                          int T, int E, int k, int32_t* __restrict__ ids,
+                                                          float* __restrict__ wout, int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ sorted_pairs,
+                                                          int32_t* __restrict__ pair_pos,
+                                                          int32_t* __restrict__ active,
+                                                          int32_t* __restrict__ n_active,
+                                                          const uint16_t* __restrict__ x, f16* __restrict__ x16,
+                                                          int H) {
+  __shared__ float ls[ROUTE_SMALL_T * PERM_MAX_E];
+  __shared__ int ids_s[ROUTE_SMALL_T * 64];
+  __shared__ unsigned long long m[PERM_MAX_E];
+  __shared__ int off_s[PERM_MAX_E];
+  __shared__ int lds[16];
+  __shared__ BlockTopkLds tk;
+  const int tid = threadIdx.x;
+  for (int idx = tid; idx < T * E; idx += 1024) {
+    const int t = idx / E, e = idx % E;
+    float v;
+    if (part) {
+      v = sum_slabs(part + (size_t)t * E + e, (size_t)T * E, slabs);
+      if (bias) v += bias[e];
+      logits[(size_t)t * E + e] = v;
+    } else {
+      v = logits[(size_t)t * E + e];
+    }
+    ls[t * PERM_MAX_E + e] = v;
+  }
+  if (tid < E) m[tid] = 0ull;
+  __syncthreads();
+  for (int t = 0; t < T; t++)
+    block_topk(ls + t * PERM_MAX_E, E, k, ids + (size_t)t * k, wout + (size_t)t * k, ids_s + t * k, tk);
+  permute_block(ids_s, T, E, k, offsets, sorted_pairs, pair_pos, active, n_active, m, off_s, lds);
   if (x) cast_rows(x, x16, 0, (size_t)T * H / 8, tid, 1024);
 }
 
@@ -406,7 +604,7 @@ __global__ __launch_bounds__(WAVE) void perm_count_kernel(const int32_t* __restr
 // absolute bases; writes offsets and the list of experts with work.
 // Entries (expert, token tile) for the large-batch GEMMs: expert e with c
 // records has ceil(c / MTILE) entries e * 65536 + tile, in expert order.
-__device__ void write_mtiles(int e, int cnt, int* lds, int32_t* __restrict__ mtiles,
+__device__ __forceinline__ void write_mtiles(int e, int cnt, int* lds, int32_t* __restrict__ mtiles,
                              int32_t* __restrict__ n_mtiles) {
   const int nt = (cnt + MTILE - 1) / MTILE;
   int total;
@@ -509,6 +707,7 @@ RouterPlan router_plan(int T, int H, int E) {
     // one wavefront per (128 experts, 64 tokens, K slab); aim for >= 512
     const int tiles = ((E + RM_EXPERTS - 1) / RM_EXPERTS) * ((T + RM_TOKENS - 1) / RM_TOKENS);
     int s = (512 + tiles - 1) / tiles;
+    if (s > ROUTER_MAX_SLABS) s = ROUTER_MAX_SLABS;
     const int steps = H / 32;
     if (s > steps) s = steps;
     if (s < 1) s = 1;
@@ -521,6 +720,7 @@ RouterPlan router_plan(int T, int H, int E) {
   const int tt = router_tt(T);
   const int tiles = ((E + RT_E_TILE - 1) / RT_E_TILE) * ((T + tt - 1) / tt);
   int s = 512 / (tiles > 0 ? tiles : 1);
+  if (s > ROUTER_MAX_SLABS) s = ROUTER_MAX_SLABS;
   const int steps = H / RT_ROWS_PER_STEP;
   if (s > steps) s = steps;
   if (s < 1) s = 1;
@@ -556,11 +756,22 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* wr, float* part, int
 hipError_t launch_topk(const float* part, int slabs, const float* bias, float* logits, int T, int E, int k,
                        int32_t* ids, float* w, hipStream_t s) {
   if (T <= 64)
-    hipLaunchKernelGGL((topk_kernel<1>), dim3(T), dim3(TOPK_THREADS), 0, s, part, slabs, bias, logits, T, E, k, ids,
+    hipLaunchKernelGGL(topk_block_kernel, dim3(T), dim3(TOPK_THREADS), 0, s, part, slabs, bias, logits, T, E, k, ids,
                        w);
   else
     hipLaunchKernelGGL((topk_kernel<4>), dim3((T + 3) / 4), dim3(TOPK_THREADS), 0, s, part, slabs, bias, logits, T,
                        E, k, ids, w);
+  return hipGetLastError();
+}
+
+bool route_fused(int T) { return T <= ROUTE_SMALL_T; }
+
+hipError_t launch_route_small(const float* part, int slabs, const float* bias, float* logits, int T, int E, int k,
+                              int32_t* ids, float* w, int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_pos,
+                              int32_t* active, int32_t* n_active, const uint16_t* x, f16* x16, int H,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(1024), 0, s, part, slabs, bias, logits, T, E, k, ids, w,
+                     offsets, sorted_pairs, pair_pos, active, n_active, x, x16, H);
   return hipGetLastError();
 }
 

@@ -95,3 +95,16 @@ def test_status_strings_and_errors():
         assert L.moe_status_string(s)
     with pytest.raises(moe.MoeError):
         moe._check(2)
+
+
+def test_profile_arguments_rejected_without_hip():
+    """Out-of-range kernel ids and counts are refused before any event is
+    created; reading into NULL reports -MOE_ERR_ARG."""
+    L = moe.lib()
+    assert L.moe_profile_arm(-1, 4) == 1
+    assert L.moe_profile_arm(7, 4) == 1
+    assert L.moe_profile_arm(4, 0) == 1
+    assert L.moe_profile_arm(4, 65537) == 1
+    assert L.moe_profile_read(None, 4) == -1
+    assert L.moe_profile_read((ctypes.c_float * 1)(), -1) == -1
+    assert L.moe_profile_read((ctypes.c_float * 1)(), 1) == 0  # nothing armed: nothing recorded

@@ -220,12 +220,16 @@ def test_t_zero_is_a_no_op():
 
 
 def test_kernel_profile_hook(tiny):
-    """moe_profile_arm records events around the armed kernel's launches."""
+    """moe_profile_arm / moe_profile_read time the armed kernel's launches:
+    one duration per launch up to the armed count, then disarmed."""
     _, inp, _ = tiny
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    moe.moe_profile_arm("gateup", evs)
+    moe.moe_profile_arm("gateup", 2)
+    for _ in range(3):
+        inp.layer()
+    ms = moe.moe_profile_read(8)
+    assert len(ms) == 2 and all(0 < t < 1000 for t in ms)
     inp.layer()
+    assert moe.moe_profile_read(8) == []
+    moe.moe_profile_arm("combine", 4)
     inp.layer()
-    assert moe.moe_profile_arm("gateup", None) == 2
-    torch.cuda.synchronize()
-    assert evs[0].elapsed_time(evs[1]) > 0 and evs[2].elapsed_time(evs[3]) > 0
+    assert len(moe.moe_profile_read(1)) == 1
