@@ -27,6 +27,13 @@ def test_exports_match_header():
         assert hasattr(L, name), name
 
 
+def test_constants_match_header():
+    text = open(HEADER).read()
+    enum = dict((n.lower(), int(v)) for n, v in re.findall(r"MOE_KERNEL_([A-Z]+) = (\d+)", text))
+    enum.pop("count")
+    assert enum == moe.KERNELS
+
+
 def test_workspace_sizes():
     for wl in WORKLOADS.values():
         d = moe.dims(wl.T, wl.H, wl.I, wl.E, wl.k)
