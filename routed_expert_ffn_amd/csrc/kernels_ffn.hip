@@ -384,6 +384,7 @@ __device__ __forceinline__ void dma_span_half(const BigLane& L, unsigned char* s
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 // Step s of one chunk: the two weight fragments, dequantised from this
 // lane's raw codes (word s) and block scale (element s/2 of the pair).
@@ -494,6 +495,40 @@ __device__ __forceinline__ void big_span(const BigLane& L, f32x16 (&acc)[8][2], 
   big_chunk<NF, 3, TOK, SPAN>(L, acc, smem, c + 3, wv);
 }
 
+// 4x4 transpose across the four lanes of a quad: lane j's v[r] becomes lane
+// r's v[j].  Two exchange rounds: lanes two apart swap register pairs
+// (lane j < 2 takes registers 0, 1 of lane j + 2 into its registers 2, 3),
+// then neighbouring lanes swap single registers (even lane j takes register
+// 0 of lane j + 1 into register 1, register 2 into register 3), each a
+// quad permutation followed by a per-lane select.
+template <int CTRL>
+__device__ __forceinline__ float dpp_quad(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ void quad_transpose(float (&v)[4]) {
+  constexpr int XOR2 = 2 | (3 << 2) | (0 << 4) | (1 << 6);  // lane j reads lane j ^ 2
+  constexpr int XOR1 = 1 | (0 << 2) | (3 << 4) | (2 << 6);  // lane j reads lane j ^ 1
+  const int j = threadIdx.x & 3;
+  {
+    const float x0 = dpp_quad<XOR2>(v[0]), x1 = dpp_quad<XOR2>(v[1]);
+    const float x2 = dpp_quad<XOR2>(v[2]), x3 = dpp_quad<XOR2>(v[3]);
+    const bool lo = j < 2;
+    v[0] = lo ? v[0] : x2;
+    v[1] = lo ? v[1] : x3;
+    v[2] = lo ? x0 : v[2];
+    v[3] = lo ? x1 : v[3];
+  }
+  {
+    const float x0 = dpp_quad<XOR1>(v[0]), x1 = dpp_quad<XOR1>(v[1]);
+    const float x2 = dpp_quad<XOR1>(v[2]), x3 = dpp_quad<XOR1>(v[3]);
+    const bool even = (j & 1) == 0;
+    v[0] = even ? v[0] : x1;
+    v[1] = even ? x0 : v[1];
+    v[2] = even ? v[2] : x3;
+    v[3] = even ? x2 : v[3];
+  }
+}
+
 template <int NF, bool GATEUP>
 __device__ __forceinline__ void big_tile(const GroupedParams& p, const BigTile& t, unsigned char* smem) {
   const int lane = threadIdx.x % WAVE, m32 = lane % 32, g2 = lane / 32;
@@ -583,20 +618,39 @@ __device__ __forceinline__ void big_tile(const GroupedParams& p, const BigTile& 
   big_chunk<NF, 1, true, false>(L, acc, smem, c + 1, wv);
   big_chunk<NF, 2, false, false>(L, acc, smem, c + 2, wv);
   big_chunk<NF, 3, false, false>(L, acc, smem, c + 3, wv);
+  // Epilogue.  Accumulator registers 4q .. 4q+3 of a lane hold rows
+  // 8q + 4 g2 + 0..3 of its column m32; a quad transpose turns them into
+  // four consecutive columns (m32 & ~3 ..) of row 8q + 4 g2 + (lane & 3), so
+  // each lane stores 16 (h: 8) contiguous bytes and one store instruction
+  // covers eight row segments.
   const float gsa = p.gs0[t.e], gsb = GATEUP ? p.gs1[t.e] : 0.0f;
+  const int n4 = m32 & ~3, j4 = lane & 3;
 #pragma unroll
   for (int f = 0; f < NF; f++)
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
-      const int m = 32 * f + 8 * (i / 4) + 4 * g2 + (i % 4);
-      if (m < t.nvalid) {
-        if (GATEUP) {
-          const float hv = silu(gsa * acc[f][0][i]) * (gsb * acc[f][1][i]);
-          p.h[(size_t)(t.mb + m) * t.N + t.rtile * (BIG_N / 2) + 32 * wv + m32] = (f16)hv;
-        } else {
+    for (int q4 = 0; q4 < 4; q4++) {
+      const int m = 32 * f + 8 * q4 + 4 * g2 + j4;
+      if (GATEUP) {
+        float hv[4];
 #pragma unroll
-          for (int nf = 0; nf < 2; nf++)
-            p.rows[(size_t)(t.mb + m) * t.N + t.rtile * BIG_N + 64 * wv + 32 * nf + m32] = gsa * acc[f][nf][i];
+        for (int r = 0; r < 4; r++) hv[r] = silu(gsa * acc[f][0][4 * q4 + r]) * (gsb * acc[f][1][4 * q4 + r]);
+        quad_transpose(hv);
+        if (m < t.nvalid) {
+          f16x4 o;
+#pragma unroll
+          for (int r = 0; r < 4; r++) o[r] = (f16)hv[r];
+          *reinterpret_cast<f16x4*>(p.h + (size_t)(t.mb + m) * t.N + t.rtile * (BIG_N / 2) + 32 * wv + n4) = o;
+        }
+      } else {
+#pragma unroll
+        for (int nf = 0; nf < 2; nf++) {
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; r++) v[r] = gsa * acc[f][nf][4 * q4 + r];
+          quad_transpose(v);
+          if (m < t.nvalid)
+            *reinterpret_cast<float4*>(p.rows + (size_t)(t.mb + m) * t.N + t.rtile * BIG_N + 64 * wv + 32 * nf + n4) =
+                make_float4(v[0], v[1], v[2], v[3]);
         }
       }
     }
