@@ -9,8 +9,9 @@ tokens (the generator's next T tokens), so each step routes to different
 experts and reads their weights cold, as a decode step of a real model does.
 Prints one JSON line: whole-layer tokens/s, the dominant kernel's achieved
 bandwidth against the HBM roofline (timed with HIP events on the launch
-stream inside the timed region), and the CPU oracle timed on a bounded
-sample of the same workload.
+stream inside the timed region) and against the streaming-read rate the
+library's calibration kernel measures on the same GPU, and the CPU oracle
+timed on a bounded sample of the same workload.
 """
 import argparse
 import hashlib
@@ -50,6 +51,26 @@ def kernel_source_sha():
     for f in ("kernels_ffn.hip", "common.h"):
         h.update(open(os.path.join(ROOT, "routed_expert_ffn_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
+
+
+def stream_read_GBps(moe, torch, region_bytes=256 << 20, regions=16):
+    """What a plain streaming read reaches on this GPU: the library's
+    calibration kernel reads each of `regions` regions of `region_bytes`
+    once, in turn (the 4 GiB cycle exceeds every cache, so every read comes
+    from HBM); median over the regions."""
+    buf = torch.empty(region_bytes * regions, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(moe.STREAM_SINK_WORDS, dtype=torch.int32, device="cuda")
+    moe.moe_stream_read(buf[-region_bytes:], sink)  # first launch, not timed
+    rates = []
+    for r in range(regions):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        moe.moe_stream_read(buf[r * region_bytes:(r + 1) * region_bytes], sink)
+        b.record()
+        b.synchronize()
+        rates.append(region_bytes / (a.elapsed_time(b) * 1e-3) / 1e9)
+    del buf
+    return float(sorted(rates)[len(rates) // 2])
 
 
 def load_traffic(workload, sha):
@@ -106,6 +127,7 @@ def main():
     wts = torch.empty((n_batches, T, k), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
+    stream_peak = stream_read_GBps(moe, torch)
 
     def step(i):
         moe.moe_layer(d, xs[i * T:(i + 1) * T], wr, bias, store, y, ids[i], wts[i], ws)
@@ -150,7 +172,8 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(wl.name, sha),
                 "kernel": "gateup_kernel (grouped gate/up + SiLU*mul)",
                 "algorithmic_bytes_per_launch": int(prof_bytes), "avg_launch_ms": round(gateup_avg_ms, 5),
-                "timed_launches": n_prof}
+                "timed_launches": n_prof, "stream_read_GBps": round(stream_peak, 1),
+                "frac_of_stream_read": round(achieved / stream_peak, 4)}
     if prefill:
         gu_flops = 4 * T * k * H * I
         tf = gu_flops / (gateup_avg_ms * 1e-3) / 1e12
@@ -179,6 +202,7 @@ def main():
         "roofline": roofline,
         "layer": {"algorithmic_bytes": int(layer_bytes), "hbm_GBps": round(layer_bytes / (ms_per_step * 1e-3) / 1e9, 1),
                   "hbm_frac": round(layer_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                  "frac_of_stream_read": round(layer_bytes / (ms_per_step * 1e-3) / 1e9 / stream_peak, 4),
                   "TFLOPs": round(layer_flops / (ms_per_step * 1e-3) / 1e12, 3),
                   "distinct_experts_mean": float(distinct.mean())},
         "setup_s": round(setup_s, 2),

@@ -186,6 +186,21 @@ typedef enum {
 moe_status moe_profile_arm(moe_kernel kernel, int n_pairs);
 int moe_profile_read(float* ms, int max);
 
+/* ---- HBM read calibration ---------------------------------------------------
+ * The decode configurations are bound by reading expert weights from HBM;
+ * their achieved bandwidth is reported against the datasheet peak and
+ * against what a plain streaming read reaches on the same GPU, measured with
+ * this call.  It enqueues on `stream` one kernel that reads the `bytes`
+ * bytes at device pointer buf (16-byte aligned, bytes a positive multiple of
+ * 16) exactly once with coalesced 16-byte loads, and writes the XOR of the
+ * 32-bit words each of its blocks read to sink[0 .. blocks-1] (device
+ * memory, MOE_STREAM_SINK_WORDS words; words from `blocks` on are left
+ * untouched), so the XOR of a zeroed sink equals the XOR of the buffer.
+ * Returns MOE_OK, MOE_ERR_ARG (a NULL pointer or bytes not a positive
+ * multiple of 16), MOE_ERR_ALIGN or MOE_ERR_HIP. */
+#define MOE_STREAM_SINK_WORDS 4096
+moe_status moe_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,7 +19,9 @@ KERNELS = {"router": 0, "topk": 1, "permute": 2, "cast": 3, "gateup": 4, "down":
 # Symbols include/moe.h declares.
 EXPORTS = ("moe_workspace_bytes", "moe_quantize_workspace_bytes", "moe_quantize_nvfp4", "moe_route",
            "moe_expert_ffn", "moe_layer", "moe_status_string", "moe_last_error", "moe_profile_arm",
-           "moe_profile_read")
+           "moe_profile_read", "moe_stream_read")
+# MOE_STREAM_SINK_WORDS of moe.h
+STREAM_SINK_WORDS = 4096
 
 
 class MoeError(RuntimeError):
@@ -72,6 +74,8 @@ def lib():
         L.moe_profile_arm.argtypes = [ctypes.c_int, ctypes.c_int]
         L.moe_profile_read.restype = ctypes.c_int
         L.moe_profile_read.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_int]
+        L.moe_stream_read.restype = ctypes.c_int
+        L.moe_stream_read.argtypes = [_p, ctypes.c_size_t, _p, _p]
         _lib = L
     return _lib
 
@@ -144,6 +148,15 @@ def moe_profile_arm(kernel, n_pairs):
     this thread; the library records its own events on the launch stream."""
     kid = KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
     _check(lib().moe_profile_arm(kid, int(n_pairs)))
+
+
+def moe_stream_read(buf, sink, stream=None):
+    """Enqueue one streaming read of every byte of the device tensor buf;
+    per-block XOR words go to sink (a device tensor of at least
+    STREAM_SINK_WORDS 32-bit words)."""
+    if sink.numel() * sink.element_size() < STREAM_SINK_WORDS * 4:
+        raise ValueError("sink holds fewer than STREAM_SINK_WORDS words")
+    _check(lib().moe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)))
 
 
 def moe_profile_read(max_launches):

@@ -306,6 +306,16 @@ moe_status moe_layer(moe_dims d, const void* x, const void* w_router, const floa
   return MOE_OK;
 }
 
+moe_status moe_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink) return fail(MOE_ERR_ARG, "buf and sink must not be NULL");
+  if (bytes == 0 || bytes % 16) return fail(MOE_ERR_ARG, "bytes = %zu must be a positive multiple of 16", bytes);
+  if (!aligned16(buf)) return fail(MOE_ERR_ALIGN, "buf is not 16-byte aligned");
+  if ((uintptr_t)sink & 3u) return fail(MOE_ERR_ALIGN, "sink is not 4-byte aligned");
+  hipError_t e = moe::launch_stream_read(buf, (long long)bytes, sink, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "stream read");
+  return MOE_OK;
+}
+
 const char* moe_status_string(moe_status s) {
   switch (s) {
     case MOE_OK: return "ok";

@@ -79,6 +79,11 @@ hipError_t launch_down(const FfnArgs& a, hipStream_t s);
 hipError_t launch_combine(const float* rows, const int32_t* pair_pos, const float* w, int T, int H, int k,
                           uint16_t* y, hipStream_t s);
 
+// Streaming read of `bytes` (a multiple of 16) into at most
+// STREAM_SINK_WORDS per-block XOR words.
+constexpr int STREAM_SINK_WORDS = MOE_STREAM_SINK_WORDS;
+hipError_t launch_stream_read(const void* buf, long long bytes, uint32_t* sink, hipStream_t s);
+
 hipError_t launch_quantize(const float* w, int64_t N, int64_t K, uint8_t* q, uint8_t* sf, float* gs, uint32_t* ws,
                            hipStream_t s);
 

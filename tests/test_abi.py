@@ -115,3 +115,16 @@ def test_profile_arguments_rejected_without_hip():
     assert L.moe_profile_read(None, 4) == -1
     assert L.moe_profile_read((ctypes.c_float * 1)(), -1) == -1
     assert L.moe_profile_read((ctypes.c_float * 1)(), 1) == 0  # nothing armed: nothing recorded
+
+
+def test_stream_read_arguments_rejected_without_hip():
+    """The HBM read calibration refuses NULL pointers, sizes that are not
+    positive multiples of 16 and misaligned pointers before any launch."""
+    L = moe.lib()
+    assert L.moe_stream_read(None, 4096, 4096, None) == 1
+    assert L.moe_stream_read(4096, 4096, None, None) == 1
+    assert L.moe_stream_read(4096, 0, 4096, None) == 1
+    assert L.moe_stream_read(4096, 4100, 4096, None) == 1
+    assert L.moe_stream_read(4104, 4096, 4096, None) == 3
+    assert L.moe_stream_read(4096, 4096, 4098, None) == 3
+    assert int(re.search(r"#define MOE_STREAM_SINK_WORDS (\d+)", open(HEADER).read()).group(1)) == moe.STREAM_SINK_WORDS
