@@ -39,6 +39,7 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=None, help="tokens in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
     return ap.parse_args()
 
 
@@ -103,6 +104,7 @@ def main():
     torch.cuda.set_device(dev)
     steps, warmup = args.steps, args.warmup
     n_batches = steps + warmup
+    n_graph = 0 if args.no_graph else steps  # fresh batches for the graph replay
 
     # ---- resident inputs -------------------------------------------------------
     t_setup = time.perf_counter()
@@ -118,13 +120,13 @@ def main():
     b = bias_for(wl)
     bias = None if b is None else torch.tensor(b, device=dev)
     # one batch of T fresh tokens per step
-    xs = torch.empty((n_batches * T, H), dtype=torch.bfloat16, device=dev)
+    xs = torch.empty(((n_batches + n_graph) * T, H), dtype=torch.bfloat16, device=dev)
     synth.gpu_x_bf16(wl.seed, xs)
     d = moe.dims(T, H, I, E, k)
     ws = torch.empty(moe.moe_workspace_bytes(d), dtype=torch.uint8, device=dev)
     y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    ids = torch.empty((n_batches, T, k), dtype=torch.int32, device=dev)
-    wts = torch.empty((n_batches, T, k), dtype=torch.float32, device=dev)
+    ids = torch.empty((n_batches + n_graph, T, k), dtype=torch.int32, device=dev)
+    wts = torch.empty((n_batches + n_graph, T, k), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
     stream_peak = stream_read_GBps(moe, torch)
@@ -221,6 +223,23 @@ def main():
             ms = moe.moe_profile_read(reps)
             br[name] = round(float(np.mean(ms)), 5) if ms else None
         out["kernel_ms"] = br
+
+    # ---- HIP-graph replay (after the timed region; not part of the value) ------
+    # the same step captured once per batch into one graph, on batches no
+    # earlier step used (so the weights are read cold again), replayed once
+    if n_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(n_batches, n_batches + n_graph):
+                step(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        graph.replay()
+        b.record()
+        torch.cuda.synchronize()
+        out["graph_ms_per_step"] = round(a.elapsed_time(b) / n_graph, 5)
+        del graph
 
     if not args.no_cpu_baseline:
         n_tok = args.cpu_tokens or (8 if T <= 16 else 4)
