@@ -53,6 +53,10 @@ def lib():
         L.oracle_moe_layer.restype = ctypes.c_int
         L.oracle_moe_layer.argtypes = [_p, _c_i64, _c_i64, _c_i64, _p, _p, _p, _c_i64, ctypes.c_int, _p,
                                        ctypes.c_int, _p, _p, _p, _p, _p, _p, _p, _p]
+        L.oracle_round_bf16.restype = None
+        L.oracle_round_bf16.argtypes = [_p, _c_i64, _p]
+        L.oracle_bf16_matmul.restype = None
+        L.oracle_bf16_matmul.argtypes = [_p, _c_i64, _c_i64, _p, _c_i64, _p]
         _lib = L
     return _lib
 
@@ -197,4 +201,50 @@ def moe_layer(x_bf16, experts, E, k, wr_bf16=None, bias=None, logits_in=None, nt
     out = dict(logits=logits, ids=ids, w=w, offsets=offsets, sorted_pairs=sp, pair_pos=pp, y=y)
     if want_rows:
         out["rows"] = rows
+    return out
+
+
+# ---- latent routed-expert block (oracle.h: "latent routed-expert block") --------
+
+def round_bf16(a):
+    """Nearest bf16 bit patterns of fp64 values (ties to even)."""
+    a = _c(a, np.float64)
+    out = np.empty(a.shape, np.uint16)
+    lib().oracle_round_bf16(_ptr(a), a.size, _ptr(out))
+    return out
+
+
+def bf16_matmul(x_bf16, w_bf16):
+    """fp64 x @ W for bf16 bit patterns x [T][K] and W [K][N]."""
+    x = _c(x_bf16, np.uint16)
+    w = _c(w_bf16, np.uint16)
+    T, K = x.shape
+    K2, N = w.shape
+    assert K == K2
+    out = np.empty((T, N), np.float64)
+    lib().oracle_bf16_matmul(_ptr(x), T, K, _ptr(w), N, _ptr(out))
+    return out
+
+
+def latent_layer(x_bf16, experts, E, k, w_down_bf16, w_up_bf16, wr_bf16=None, bias=None, logits_in=None,
+                 nthreads=1, want_rows=False):
+    """K3's latent routed-expert block on model-width tokens x [T][Hm]:
+      z     = bf16(x . P_down)                 routed latent [T][H]
+      route = top-k of the router on x (the model's hidden state)
+      y_lat = bf16(moe_layer(z) with that routing)   [T][H]
+      y     = y_lat . P_up                     [T][Hm] fp64 (the GPU rounds it to bf16)
+    P_down [Hm][H] and P_up [H][Hm] are bf16, stored input-major.  The
+    roundings to bf16 are the model's activation type at the block's seams;
+    where the router reads is a reading (the pages do not say): the hidden
+    state, as the plain router of the non-latent layer does."""
+    x = _c(x_bf16, np.uint16)
+    z = round_bf16(bf16_matmul(x, w_down_bf16))
+    if logits_in is None:
+        logits_in = router_logits(x, wr_bf16, bias)
+    out = moe_layer(z, experts, E, k, logits_in=logits_in, nthreads=nthreads, want_rows=want_rows)
+    y_lat = round_bf16(out["y"])
+    out["z"] = z
+    out["y_lat"] = y_lat
+    out["y_lat_f64"] = out["y"]
+    out["y"] = bf16_matmul(y_lat, w_up_bf16)
     return out

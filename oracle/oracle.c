@@ -273,3 +273,49 @@ int oracle_moe_layer(const uint16_t* x, int64_t T, int64_t H, int64_t I, const u
   if (!logits_out) free(logits);
   return status;
 }
+
+/* ---- latent routed-expert block ---------------------------------------------- */
+
+void oracle_round_bf16(const double* in, int64_t n, uint16_t* out) {
+  for (int64_t i = 0; i < n; i++) {
+    double d = in[i];
+    if (isnan(d)) {
+      out[i] = 0x7FC0;
+      continue;
+    }
+    uint16_t sign = signbit(d) ? 0x8000 : 0;
+    double a = fabs(d);
+    /* largest fp32 <= a, then its bf16 truncation: the largest bf16 <= a */
+    float f = (float)a;
+    if ((double)f > a) f = nextafterf(f, 0.0f);
+    uint32_t fb;
+    memcpy(&fb, &f, 4);
+    uint16_t lo = (uint16_t)(fb >> 16);
+    if (lo >= 0x7F80) { /* a is at least 2^128: infinity */
+      out[i] = sign | 0x7F80;
+      continue;
+    }
+    uint16_t hi = (uint16_t)(lo + 1);
+    double vlo = bf16_to_double(lo);
+    /* the value above the largest finite bf16 is 2^128 for rounding */
+    double vhi = (hi == 0x7F80) ? ldexp(1.0, 128) : bf16_to_double(hi);
+    double dlo = a - vlo, dhi = vhi - a;
+    uint16_t r;
+    if (dlo < dhi)
+      r = lo;
+    else if (dhi < dlo)
+      r = hi;
+    else
+      r = (lo & 1) ? hi : lo;
+    out[i] = sign | r;
+  }
+}
+
+void oracle_bf16_matmul(const uint16_t* x, int64_t T, int64_t K, const uint16_t* W, int64_t N, double* out) {
+  for (int64_t t = 0; t < T; t++)
+    for (int64_t c = 0; c < N; c++) {
+      double s = 0.0;
+      for (int64_t r = 0; r < K; r++) s += bf16_to_double(x[t * K + r]) * bf16_to_double(W[r * N + c]);
+      out[t * N + c] = s;
+    }
+}

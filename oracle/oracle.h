@@ -120,6 +120,26 @@ int oracle_moe_layer(const uint16_t* x, int64_t T, int64_t H, int64_t I, const u
                      int nthreads, float* logits_out, int32_t* ids, double* w, int32_t* offsets,
                      int32_t* sorted_pairs, int32_t* pair_pos, double* rows, double* y);
 
+/* ---- latent routed-expert block (K3's LatentMoE) ----------------------------
+ * [p4] lightseek.org, "Kimi K3 optimization on GB300" (part I), sections
+ * "Routed-down projection: column sharding and latent assembly" and
+ * "Routed-up projection: sharding the post-expert tail": every MoE block
+ * projects the 7168-wide hidden state into the 3584-wide routed latent with
+ * a bf16 weight, the experts work in the latent, and a second bf16
+ * projection maps their combined output back.  [p2] "The model, as the
+ * serving system sees it" gives the experts' 3584 x 3072 shape. */
+
+/* Nearest bf16 to d (bit pattern), ties to the even pattern; a value half an
+ * ulp or more above the largest finite bf16 gives infinity; NaN gives a
+ * quiet NaN.  The two bf16 neighbours of |d| are found from its fp32
+ * neighbour below, and the nearer one is chosen by exact fp64 distances. */
+void oracle_round_bf16(const double* in, int64_t n, uint16_t* out);
+
+/* out[t][c] = sum_r x[t][r] * W[r][c] in fp64 over ascending r, with x
+ * [T][K] and W [K][N] bf16 bit patterns (W stored input-major, the
+ * transpose of the pages' [out, in] weight). */
+void oracle_bf16_matmul(const uint16_t* x, int64_t T, int64_t K, const uint16_t* W, int64_t N, double* out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -32,11 +32,13 @@ def cpu():
         L.synth_x_bf16.argtypes = [_u64, _i64, _i, _i, _p]
         L.synth_router_bf16.argtypes = [_u64, _i, _i, _f, _p]
         L.synth_expert_f32.argtypes = [_u64, _i, _i, _i, _i, _f, _p, _i]
+        L.synth_proj_bf16.argtypes = [_u64, _i, _i, _i, _f, _p]
         L.synth_zipf_bias.argtypes = [_u64, _i, ctypes.c_double, ctypes.c_double, _p]
         L.synth_popularity_perm.argtypes = [_u64, _i, _p]
         L.synth_normals_f32.argtypes = [_u64, _u64, _u64, _i64, _p]
         L.synth_round_bf16.argtypes = [_p, _i64, _p]
-        for f in (L.synth_x_bf16, L.synth_router_bf16, L.synth_expert_f32, L.synth_zipf_bias, L.synth_popularity_perm,
+        for f in (L.synth_x_bf16, L.synth_router_bf16, L.synth_expert_f32, L.synth_proj_bf16, L.synth_zipf_bias,
+                  L.synth_popularity_perm,
                   L.synth_normals_f32, L.synth_round_bf16):
             f.restype = None
         _cpu = L
@@ -52,7 +54,8 @@ def gpu():
         L.synth_gpu_x_bf16.argtypes = [_u64, _i64, _i, _i, _p, _p]
         L.synth_gpu_router_bf16.argtypes = [_u64, _i, _i, _f, _p, _p]
         L.synth_gpu_expert_f32.argtypes = [_u64, _i, _i, _i, _i, _f, _p, _p]
-        for f in (L.synth_gpu_x_bf16, L.synth_gpu_router_bf16, L.synth_gpu_expert_f32):
+        L.synth_gpu_proj_bf16.argtypes = [_u64, _i, _i, _i, _f, _p, _p]
+        for f in (L.synth_gpu_x_bf16, L.synth_gpu_router_bf16, L.synth_gpu_expert_f32, L.synth_gpu_proj_bf16):
             f.restype = ctypes.c_int
         _gpu = L
     return _gpu
@@ -82,6 +85,14 @@ def expert_f32(seed, e, m, N, K, std=WEIGHT_STD, nthreads=None):
     if nthreads is None:
         nthreads = min(16, os.cpu_count() or 1)
     cpu().synth_expert_f32(seed, e, m, N, K, std, _ptr(out), nthreads)
+    return out
+
+
+def proj_bf16(seed, which, K, N, std=WEIGHT_STD):
+    """Latent projection weights [K][N] bf16 bits: which 0 = routed-down
+    ([H_model][H]), 1 = routed-up ([H][H_model])."""
+    out = np.empty((K, N), np.uint16)
+    cpu().synth_proj_bf16(seed, which, K, N, std, _ptr(out))
     return out
 
 
@@ -140,6 +151,12 @@ def gpu_router_bf16(seed, out, std=WEIGHT_STD, stream=None):
     H, E = out.shape
     assert out.is_cuda and out.is_contiguous() and out.element_size() == 2
     _check(gpu().synth_gpu_router_bf16(seed, H, E, std, out.data_ptr(), _stream(stream)), "synth_gpu_router_bf16")
+
+
+def gpu_proj_bf16(seed, which, out, std=WEIGHT_STD, stream=None):
+    K, N = out.shape
+    assert out.is_cuda and out.is_contiguous() and out.element_size() == 2
+    _check(gpu().synth_gpu_proj_bf16(seed, which, K, N, std, out.data_ptr(), _stream(stream)), "synth_gpu_proj_bf16")
 
 
 def gpu_expert_f32(seed, e, m, out, std=WEIGHT_STD, stream=None):

@@ -18,6 +18,12 @@ void synth_router_bf16(uint64_t seed, int H, int E, float std, uint16_t* out) {
     out[i] = synth_bf16_rne(std * synth_normal(key, (uint64_t)i));
 }
 
+void synth_proj_bf16(uint64_t seed, int which, int K, int N, float std, uint16_t* out) {
+  uint64_t key = synth_key(seed, which ? SYNTH_STREAM_PROJ_UP : SYNTH_STREAM_PROJ_DOWN);
+  for (int64_t i = 0; i < (int64_t)K * N; i++)
+    out[i] = synth_bf16_rne(std * synth_normal(key, (uint64_t)i));
+}
+
 typedef struct {
   uint64_t key;
   float std;

@@ -4,6 +4,9 @@
  * Layouts (all row-major):
  *   x      [T][H]  bf16 bits, N(0,1) approx.; token t uses index (t0+t)*H + h
  *   W_r    [H][E]  bf16 bits, std * N(0,1) rounded to bf16; index h*E + e
+ *   P_d,P_u [K][N] bf16 bits, the latent routed-down ([Hm][H]) and routed-up
+ *                  ([H][Hm]) projections, std * N(0,1); index k*N + n;
+ *                  which = 0 (down) or 1 (up)
  *   W_e,m  [N][K]  fp32, std * N(0,1); index n*K + k; m = 0 gate, 1 up, 2 down
  *                  (gate/up: N = I, K = H; down: N = H, K = I)
  *   bias   [E]     fp32 expert-popularity bias (CPU only, see synth_zipf_bias)
@@ -19,6 +22,7 @@ extern "C" {
 void synth_x_bf16(uint64_t seed, int64_t t0, int T, int H, uint16_t* out);
 void synth_router_bf16(uint64_t seed, int H, int E, float std, uint16_t* out);
 void synth_expert_f32(uint64_t seed, int e, int m, int N, int K, float std, float* out, int nthreads);
+void synth_proj_bf16(uint64_t seed, int which, int K, int N, float std, uint16_t* out);
 /* Zipf-style popularity bias: b[e] = -beta * s * ln(1 + pi(e)), where pi is a
  * seeded random permutation of 0..E-1 (Fisher-Yates on the PERM stream).
  * Adding it to the router logits makes expert popularity fall off as a power
@@ -34,6 +38,7 @@ void synth_popularity_perm(uint64_t seed, int E, int32_t* pi);
 int synth_gpu_x_bf16(uint64_t seed, int64_t t0, int T, int H, uint16_t* out, void* stream);
 int synth_gpu_router_bf16(uint64_t seed, int H, int E, float std, uint16_t* out, void* stream);
 int synth_gpu_expert_f32(uint64_t seed, int e, int m, int N, int K, float std, float* out, void* stream);
+int synth_gpu_proj_bf16(uint64_t seed, int which, int K, int N, float std, uint16_t* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -32,6 +32,8 @@
 #define SYNTH_STREAM_X 1u          /* activations x[t][h]            */
 #define SYNTH_STREAM_WR 2u         /* router weights W_r[h][e]       */
 #define SYNTH_STREAM_PERM 3u       /* expert popularity permutation  */
+#define SYNTH_STREAM_PROJ_DOWN 4u  /* routed-down projection [Hm][H] */
+#define SYNTH_STREAM_PROJ_UP 5u    /* routed-up projection [H][Hm]   */
 #define SYNTH_STREAM_EXPERT0 16u   /* expert e, matrix m: 16 + 3e + m */
 
 SYNTH_FN uint64_t synth_mix64(uint64_t z) {

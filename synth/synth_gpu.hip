@@ -49,6 +49,14 @@ extern "C" int synth_gpu_router_bf16(uint64_t seed, int H, int E, float std, uin
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
+extern "C" int synth_gpu_proj_bf16(uint64_t seed, int which, int K, int N, float std, uint16_t* out, void* stream) {
+  int64_t n = (int64_t)K * N;
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(k_router, dim3(grid_for(n)), dim3(256), 0, (hipStream_t)stream,
+                     synth_key(seed, which ? SYNTH_STREAM_PROJ_UP : SYNTH_STREAM_PROJ_DOWN), n, std, out);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 extern "C" int synth_gpu_expert_f32(uint64_t seed, int e, int m, int N, int K, float std, float* out, void* stream) {
   int64_t n = (int64_t)N * K;
   if (n <= 0) return 0;

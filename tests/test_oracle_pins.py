@@ -369,3 +369,59 @@ def test_missing_selected_expert_is_an_error():
     del ex[min(used)]
     with pytest.raises(RuntimeError):
         oracle.moe_layer(x, ex, E, k, wr_bf16=wr)
+
+
+# ---- latent routed-expert block ----------------------------------------------------
+
+def test_round_bf16_golden_and_direct_from_fp64():
+    """Hand-derived bf16 patterns: ties go to the even pattern, just above a
+    tie rounds up (which a detour through fp32 would lose), overflow at half
+    an ulp above the largest finite value, subnormals, signed zeros."""
+    cases = [(1.0 + 2 ** -8, 0x3F80), (1.0 + 3 * 2 ** -8, 0x3F82), (1.0 + 2 ** -8 + 2 ** -30, 0x3F81),
+             (-(1.0 + 2 ** -8), 0xBF80), (0.0, 0x0000), (-0.0, 0x8000), ((2 - 2 ** -7) * 2.0 ** 127, 0x7F7F),
+             ((2 - 2 ** -8) * 2.0 ** 127, 0x7F80), ((2 - 2 ** -8 - 2 ** -20) * 2.0 ** 127, 0x7F7F),
+             (2.0 ** -133, 0x0001), (2.0 ** -134, 0x0000), (3 * 2.0 ** -135, 0x0001), (float("inf"), 0x7F80)]
+    got = oracle.round_bf16(np.array([v for v, _ in cases]))
+    assert [int(g) for g in got] == [want for _, want in cases]
+
+
+def test_round_bf16_matches_torch_and_generator_on_fp32_values():
+    rng = np.random.default_rng(11)
+    f = (rng.standard_normal(100000) * np.exp(rng.uniform(-60, 60, 100000))).astype(np.float32)
+    ours = oracle.round_bf16(f.astype(np.float64))
+    np.testing.assert_array_equal(ours, torch.tensor(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+    np.testing.assert_array_equal(ours, synth.round_bf16(f))
+
+
+def test_bf16_matmul_exact_on_small_integers():
+    """Integer-valued bf16 operands keep every product and partial sum exact,
+    so the fp64 result must equal the integer matrix product."""
+    rng = np.random.default_rng(12)
+    xi = rng.integers(-8, 9, (5, 96))
+    wi = rng.integers(-8, 9, (96, 40))
+    x = synth.round_bf16(xi.astype(np.float32))
+    w = synth.round_bf16(wi.astype(np.float32))
+    np.testing.assert_array_equal(oracle.bf16_matmul(x, w), (xi @ wi).astype(np.float64))
+
+
+def test_latent_layer_with_embedding_projections_is_the_plain_layer():
+    """P_down = [I; 0] (Hm = 2H) takes the first H features as the latent
+    and P_up = [I 0] writes the latent back into them: the block's output is
+    the plain layer's output on those features, rounded to bf16, and zeros."""
+    T, H, I, E, k = 5, 64, 32, 16, 4
+    Hm = 2 * H
+    x = synth.x_bf16(13, T, Hm)
+    wr = synth.router_bf16(13, Hm, E, std=0.2)
+    one = synth.round_bf16(np.ones(1, np.float32))[0]
+    pd = np.zeros((Hm, H), np.uint16)
+    pd[np.arange(H), np.arange(H)] = one
+    pu = np.zeros((H, Hm), np.uint16)
+    pu[np.arange(H), np.arange(H)] = one
+    ex = _tiny_experts(13, E, H, I)
+    lat = oracle.latent_layer(x, ex, E, k, pd, pu, wr_bf16=wr)
+    np.testing.assert_array_equal(lat["z"], x[:, :H])
+    plain = oracle.moe_layer(np.ascontiguousarray(x[:, :H]), ex, E, k,
+                             logits_in=oracle.router_logits(x, wr))
+    np.testing.assert_array_equal(lat["ids"], plain["ids"])
+    np.testing.assert_array_equal(lat["y"][:, :H], synth.bf16_to_f32(oracle.round_bf16(plain["y"])))
+    assert not lat["y"][:, H:].any()
