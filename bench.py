@@ -115,16 +115,25 @@ def main():
             synth.gpu_expert_f32(wl.seed, e, mi, buf[m])
             store.quantize_into(e, m, buf[m])
     del buf
-    wr = torch.empty((H, E), dtype=torch.bfloat16, device=dev)
+    # the latent block's tokens, router and output have the hidden width
+    Hm = wl.H_model or H
+    wr = torch.empty((Hm, E), dtype=torch.bfloat16, device=dev)
     synth.gpu_router_bf16(wl.seed, wr)
     b = bias_for(wl)
     bias = None if b is None else torch.tensor(b, device=dev)
     # one batch of T fresh tokens per step
-    xs = torch.empty(((n_batches + n_graph) * T, H), dtype=torch.bfloat16, device=dev)
+    xs = torch.empty(((n_batches + n_graph) * T, Hm), dtype=torch.bfloat16, device=dev)
     synth.gpu_x_bf16(wl.seed, xs)
     d = moe.dims(T, H, I, E, k)
-    ws = torch.empty(moe.moe_workspace_bytes(d), dtype=torch.uint8, device=dev)
-    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    if wl.H_model:
+        p_down = torch.empty((Hm, H), dtype=torch.bfloat16, device=dev)
+        p_up = torch.empty((H, Hm), dtype=torch.bfloat16, device=dev)
+        synth.gpu_proj_bf16(wl.seed, 0, p_down)
+        synth.gpu_proj_bf16(wl.seed, 1, p_up)
+        ws = torch.empty(moe.moe_latent_workspace_bytes(d, Hm), dtype=torch.uint8, device=dev)
+    else:
+        ws = torch.empty(moe.moe_workspace_bytes(d), dtype=torch.uint8, device=dev)
+    y = torch.empty((T, Hm), dtype=torch.bfloat16, device=dev)
     ids = torch.empty((n_batches + n_graph, T, k), dtype=torch.int32, device=dev)
     wts = torch.empty((n_batches + n_graph, T, k), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
@@ -132,7 +141,11 @@ def main():
     stream_peak = stream_read_GBps(moe, torch)
 
     def step(i):
-        moe.moe_layer(d, xs[i * T:(i + 1) * T], wr, bias, store, y, ids[i], wts[i], ws)
+        if wl.H_model:
+            moe.moe_latent_layer(d, Hm, p_down, p_up, xs[i * T:(i + 1) * T], wr, bias, store, y, None, ids[i], wts[i],
+                                 ws)
+        else:
+            moe.moe_layer(d, xs[i * T:(i + 1) * T], wr, bias, store, y, ids[i], wts[i], ws)
 
     for i in range(warmup):
         step(i)
@@ -161,8 +174,10 @@ def main():
     # ---- algorithmic work ------------------------------------------------------------
     ms_per_step = elapsed_ms / steps
     expert_bytes = 2 * nvfp4_bytes(I, H) + nvfp4_bytes(H, I)
-    layer_bytes = distinct.mean() * expert_bytes + H * E * 2 + 2 * T * H * 2
-    layer_flops = 2 * T * H * E + 6 * T * k * H * I
+    # latent block: plus the two projection weights; router and x, y at the hidden width
+    proj_bytes = 2 * Hm * H * 2 if wl.H_model else 0
+    layer_bytes = distinct.mean() * expert_bytes + Hm * E * 2 + 2 * T * Hm * 2 + proj_bytes
+    layer_flops = 2 * T * Hm * E + 6 * T * k * H * I + (4 * T * Hm * H if wl.H_model else 0)
     gateup_unit = 2 * nvfp4_bytes(I, H)              # one active expert's gate+up weights
     gateup_bytes = distinct * gateup_unit + T * H * 2 + T * k * I * 2
     gateup_avg_ms = float(np.mean(gateup_ms))
@@ -198,9 +213,12 @@ def main():
         "vs_baseline": None,
         "dtype": "fp16",
         "data": "synthetic",
-        "config": {"workload": f"{wl.name}: MoE layer T={T} H={H} I={I} E={E} top-{k}, NVFP4 experts, bf16 "
-                               f"activations, fresh tokens every step",
-                   "T": T, "H": H, "I": I, "E": E, "k": k, "zipf_beta": wl.beta, "seed": wl.seed},
+        "config": {"workload": (f"{wl.name}: latent MoE block, hidden {Hm} -> routed latent {H} (bf16 projections), "
+                                if wl.H_model else f"{wl.name}: MoE layer ")
+                               + f"T={T} H={H} I={I} E={E} top-{k}, NVFP4 experts, bf16 activations, fresh tokens "
+                               f"every step",
+                   "T": T, "H": H, "I": I, "E": E, "k": k, "H_model": wl.H_model, "zipf_beta": wl.beta,
+                   "seed": wl.seed},
         "roofline": roofline,
         "layer": {"algorithmic_bytes": int(layer_bytes), "hbm_GBps": round(layer_bytes / (ms_per_step * 1e-3) / 1e9, 1),
                   "hbm_frac": round(layer_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -261,9 +279,13 @@ def cpu_baseline(wl, n_tokens, first_token):
     from synth.workloads import bias_for
 
     threads = min(16, os.cpu_count() or 1)
-    wr = synth.router_bf16(wl.seed, wl.H, wl.E)
+    Hm = wl.H_model or wl.H
+    wr = synth.router_bf16(wl.seed, Hm, wl.E)
     bias = bias_for(wl)
-    xs = [synth.x_bf16(wl.seed, 1, wl.H, t0=first_token + t) for t in range(n_tokens)]
+    xs = [synth.x_bf16(wl.seed, 1, Hm, t0=first_token + t) for t in range(n_tokens)]
+    if wl.H_model:
+        p_down = synth.proj_bf16(wl.seed, 0, Hm, wl.H)
+        p_up = synth.proj_bf16(wl.seed, 1, wl.H, Hm)
     need = set()
     for x in xs:
         ids, _ = oracle.topk_softmax(oracle.router_logits(x, wr, bias), wl.k)
@@ -280,11 +302,15 @@ def cpu_baseline(wl, n_tokens, first_token):
     total = 0.0
     for x in xs:
         t0 = time.perf_counter()
-        oracle.moe_layer(x, cache, wl.E, wl.k, wr_bf16=wr, bias=bias, nthreads=threads)
+        if wl.H_model:
+            oracle.latent_layer(x, cache, wl.E, wl.k, p_down, p_up, wr_bf16=wr, bias=bias, nthreads=threads)
+        else:
+            oracle.moe_layer(x, cache, wl.E, wl.k, wr_bf16=wr, bias=bias, nthreads=threads)
         total += time.perf_counter() - t0
     return {"value": round(n_tokens / total, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{n_tokens} tokens of the {wl.name} workload's timed batches, one single-token oracle layer "
-                      f"call each (router, top-k, permutation, 16 experts dequantised and run in fp64, combine), "
+                      f"call each (router, top-k, permutation, 16 experts dequantised and run in fp64, combine"
+                      f"{', and the two latent projections' if wl.H_model else ''}), "
                       f"{threads} threads over the token's experts; expert weights pre-quantised, untimed",
             "seconds": round(total, 2)}
 

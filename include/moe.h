@@ -152,6 +152,38 @@ moe_status moe_expert_ffn(moe_dims d, const void* x, const int32_t* expert_offse
 moe_status moe_layer(moe_dims d, const void* x, const void* w_router, const float* bias, const moe_experts* w,
                      void* y, int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes, void* stream);
 
+/* ---- the latent routed-expert block (K3's LatentMoE) -------------------------
+ * lightseek.org, "Kimi K3 optimization on GB300" (part I), sections
+ * "Routed-down projection: column sharding and latent assembly" and
+ * "Routed-up projection: sharding the post-expert tail": each MoE block
+ * projects the model's hidden state (width H_model, 7168 in K3) into the
+ * routed latent (width d.H, 3584) with a bf16 weight, runs the routed
+ * experts there (I = 3072), and projects their combined output back:
+ *   z     = bf16(x . w_down)                      [T][d.H]
+ *   route = top-k of the router on x              (the hidden state)
+ *   y_lat = bf16(sum_j w_j * FFN_{id_j}(z))       as moe_layer, on z
+ *   y     = bf16(y_lat . w_up)                    [T][H_model]
+ * Projections accumulate in fp32.  Weights are stored input-major (the
+ * transpose of a [out][in] linear weight), as w_router is.
+ * MOE_KERNEL_PROJECT times each projection (its GEMM and the reduction). */
+typedef struct {
+  int32_t H_model;     /* hidden width: a positive multiple of 256 */
+  const void* w_down;  /* [H_model][H] bf16, device */
+  const void* w_up;    /* [H][H_model] bf16, device */
+} moe_latent;
+
+/* Workspace of moe_latent_layer (0 for invalid dims or H_model). */
+size_t moe_latent_workspace_bytes(moe_dims d, int32_t H_model);
+
+/* Device pointers: x [T][H_model] bf16; w_router [H_model][E] bf16; bias
+ * [E] fp32 or NULL; y [T][H_model] bf16 output; z_out [T][H] bf16 copy of
+ * the routed latent or NULL; topk_ids_out / topk_w_out as in moe_layer.
+ * lat is host memory read during the call.  Errors as moe_layer, plus
+ * MOE_ERR_ARG for a NULL lat or projection and MOE_ERR_SHAPE for H_model. */
+moe_status moe_latent_layer(moe_dims d, const moe_latent* lat, const void* x, const void* w_router, const float* bias,
+                            const moe_experts* w, void* y, void* z_out, int32_t* topk_ids_out, float* topk_w_out,
+                            void* ws, size_t ws_bytes, void* stream);
+
 const char* moe_status_string(moe_status s);
 /* Detail of the last non-OK return on the calling thread. */
 const char* moe_last_error(void);
@@ -167,7 +199,8 @@ typedef enum {
   MOE_KERNEL_GATEUP = 4,  /* grouped gate/up GEMM + SiLU*mul             */
   MOE_KERNEL_DOWN = 5,    /* grouped down GEMM                           */
   MOE_KERNEL_COMBINE = 6, /* weighted un-permute and sum                 */
-  MOE_KERNEL_COUNT = 7
+  MOE_KERNEL_PROJECT = 7, /* latent block: one bf16 projection            */
+  MOE_KERNEL_COUNT = 8
 } moe_kernel;
 
 /* Timing of one kernel's launches made by the calling thread.

@@ -15,11 +15,11 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 MOE_OK = 0
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_ARG", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_ALIGN", 4: "MOE_ERR_WORKSPACE",
                 5: "MOE_ERR_HIP"}
-KERNELS = {"router": 0, "topk": 1, "permute": 2, "cast": 3, "gateup": 4, "down": 5, "combine": 6}
+KERNELS = {"router": 0, "topk": 1, "permute": 2, "cast": 3, "gateup": 4, "down": 5, "combine": 6, "project": 7}
 # Symbols include/moe.h declares.
 EXPORTS = ("moe_workspace_bytes", "moe_quantize_workspace_bytes", "moe_quantize_nvfp4", "moe_route",
            "moe_expert_ffn", "moe_layer", "moe_status_string", "moe_last_error", "moe_profile_arm",
-           "moe_profile_read", "moe_stream_read")
+           "moe_profile_read", "moe_stream_read", "moe_latent_workspace_bytes", "moe_latent_layer")
 # MOE_STREAM_SINK_WORDS of moe.h
 STREAM_SINK_WORDS = 4096
 
@@ -41,6 +41,10 @@ class NVFP4(ctypes.Structure):
 
 class Experts(ctypes.Structure):
     _fields_ = [("gate", NVFP4), ("up", NVFP4), ("down", NVFP4)]
+
+
+class Latent(ctypes.Structure):
+    _fields_ = [("H_model", ctypes.c_int32), ("w_down", ctypes.c_void_p), ("w_up", ctypes.c_void_p)]
 
 
 _lib = None
@@ -66,6 +70,11 @@ def lib():
         L.moe_expert_ffn.argtypes = [Dims, _p, _p, _p, ctypes.POINTER(Experts), _p, _p, ctypes.c_size_t, _p]
         L.moe_layer.restype = ctypes.c_int
         L.moe_layer.argtypes = [Dims, _p, _p, _p, ctypes.POINTER(Experts), _p, _p, _p, _p, ctypes.c_size_t, _p]
+        L.moe_latent_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_latent_workspace_bytes.argtypes = [Dims, ctypes.c_int32]
+        L.moe_latent_layer.restype = ctypes.c_int
+        L.moe_latent_layer.argtypes = [Dims, ctypes.POINTER(Latent), _p, _p, _p, ctypes.POINTER(Experts), _p, _p, _p,
+                                       _p, _p, ctypes.c_size_t, _p]
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_last_error.restype = ctypes.c_char_p
@@ -141,6 +150,20 @@ def moe_layer(d, x, w_router, bias, experts, y, topk_ids_out, topk_w_out, ws, st
     _check(lib().moe_layer(d, _ptr(x), _ptr(w_router), _ptr(bias), ctypes.byref(experts.c()), _ptr(y),
                            _ptr(topk_ids_out), _ptr(topk_w_out), _ptr(ws), ws.numel() * ws.element_size(),
                            _stream(stream)))
+
+
+def moe_latent_workspace_bytes(d, H_model):
+    return lib().moe_latent_workspace_bytes(d, int(H_model))
+
+
+def moe_latent_layer(d, H_model, w_down, w_up, x, w_router, bias, experts, y, z_out, topk_ids_out, topk_w_out, ws,
+                     stream=None):
+    """The latent routed-expert block: x [T][H_model] -> y [T][H_model], with
+    the experts on the routed latent of width d.H (moe.h: moe_latent_layer)."""
+    lat = Latent(int(H_model), _ptr(w_down), _ptr(w_up))
+    _check(lib().moe_latent_layer(d, ctypes.byref(lat), _ptr(x), _ptr(w_router), _ptr(bias), ctypes.byref(experts.c()),
+                                  _ptr(y), _ptr(z_out), _ptr(topk_ids_out), _ptr(topk_w_out), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def moe_profile_arm(kernel, n_pairs):

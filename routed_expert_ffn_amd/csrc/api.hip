@@ -91,6 +91,39 @@ Layout layout(const moe_dims& d) {
   return L;
 }
 
+// moe_latent_layer: moe_layer's regions for the latent width, then the
+// router's partials over the hidden width, the projections' partials, the
+// latent z and the combined latent output.
+struct LatentLayout {
+  Layout base;
+  size_t rpart, ppart, z, ylat, total;
+};
+
+LatentLayout latent_layout(const moe_dims& d, int Hm) {
+  LatentLayout LL;
+  LL.base = layout(d);
+  size_t o = LL.base.total;
+  auto take = [&](size_t bytes) {
+    size_t r = o;
+    o += align256(bytes);
+    return r;
+  };
+  const size_t T = (size_t)d.T, H = (size_t)d.H, E = (size_t)d.E, M = (size_t)Hm;
+  LL.rpart = take((size_t)moe::router_plan(d.T, Hm, d.E).slabs * T * E * 4);
+  const size_t down = (size_t)moe::router_plan(d.T, Hm, d.H).slabs * T * H * 4;
+  const size_t up = (size_t)moe::router_plan(d.T, d.H, Hm).slabs * T * M * 4;
+  LL.ppart = take(down > up ? down : up);
+  LL.z = take(T * H * 2);
+  LL.ylat = take(T * H * 2);
+  LL.total = o;
+  return LL;
+}
+
+moe_status check_latent_width(int Hm) {
+  if (Hm <= 0 || Hm % 256) return fail(MOE_ERR_SHAPE, "H_model = %d must be a positive multiple of 256", Hm);
+  return MOE_OK;
+}
+
 template <class T>
 T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
@@ -303,6 +336,83 @@ moe_status moe_layer(moe_dims d, const void* x, const void* w_router, const floa
   TRY(enqueue_ffn(d, offsets, sorted, w, rows, ws, s));
   LAUNCH(MOE_KERNEL_COMBINE, s,
          moe::launch_combine(rows, pos, wts, d.T, d.H, d.k, static_cast<uint16_t*>(y), s), "combine");
+  return MOE_OK;
+}
+
+size_t moe_latent_workspace_bytes(moe_dims d, int32_t H_model) {
+  if (check_dims(d) != MOE_OK || check_latent_width(H_model) != MOE_OK) return 0;
+  return latent_layout(d, H_model).total;
+}
+
+moe_status moe_latent_layer(moe_dims d, const moe_latent* lat, const void* x, const void* w_router, const float* bias,
+                            const moe_experts* w, void* y, void* z_out, int32_t* topk_ids_out, float* topk_w_out,
+                            void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_dims(d));
+  if (!lat) return fail(MOE_ERR_ARG, "lat is NULL");
+  TRY(check_latent_width(lat->H_model));
+  if (d.T == 0) return MOE_OK;
+  TRY(check_ptr(lat->w_down, "w_down"));
+  TRY(check_ptr(lat->w_up, "w_up"));
+  TRY(check_ptr(x, "x"));
+  TRY(check_ptr(w_router, "w_router"));
+  TRY(check_ptr(bias, "bias", false));
+  TRY(check_experts(w));
+  TRY(check_ptr(y, "y"));
+  TRY(check_ptr(z_out, "z_out", false));
+  TRY(check_ptr(topk_ids_out, "topk_ids_out", false));
+  TRY(check_ptr(topk_w_out, "topk_w_out", false));
+  const LatentLayout LL = latent_layout(d, lat->H_model);
+  if (!ws) return fail(MOE_ERR_ARG, "workspace is NULL");
+  if (!aligned16(ws)) return fail(MOE_ERR_ALIGN, "workspace is not 16-byte aligned");
+  if (ws_bytes < LL.total) return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, LL.total);
+  const Layout& L = LL.base;
+  hipStream_t s = (hipStream_t)stream;
+  const int T = d.T, H = d.H, Hm = lat->H_model, E = d.E, k = d.k;
+  int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, L.ids);
+  float* wts = topk_w_out ? topk_w_out : at<float>(ws, L.w);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* sorted = at<int32_t>(ws, L.sorted);
+  int32_t* pos = at<int32_t>(ws, L.pos);
+  f16* x16 = at<f16>(ws, L.x16);
+  uint16_t* z = z_out ? static_cast<uint16_t*>(z_out) : at<uint16_t>(ws, LL.z);
+  uint16_t* ylat = at<uint16_t>(ws, LL.ylat);
+  float* rpart = at<float>(ws, LL.rpart);
+  float* ppart = at<float>(ws, LL.ppart);
+  // router on the hidden state
+  const moe::RouterPlan rp = moe::router_plan(T, Hm, E);
+  LAUNCH(MOE_KERNEL_ROUTER, s,
+         moe::launch_router(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router), rpart, T, Hm, E,
+                            rp, s),
+         "router");
+  // routed-down projection: the latent in bf16 and its fp16 copy for the experts
+  LAUNCH(MOE_KERNEL_PROJECT, s,
+         moe::launch_projection(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(lat->w_down), ppart, T,
+                                Hm, H, moe::router_plan(T, Hm, H), z, x16, s),
+         "routed-down projection");
+  // top-k and permutation on the router's partials (x16 is already in place)
+  if (moe::route_fused(T)) {
+    LAUNCH(MOE_KERNEL_TOPK, s,
+           moe::launch_route_small(rpart, rp.slabs, bias, at<float>(ws, L.logits), T, E, k, ids, wts, offsets, sorted,
+                                   pos, at<int32_t>(ws, L.active), at<int32_t>(ws, L.nact), nullptr, nullptr, H, s),
+           "route");
+  } else {
+    LAUNCH(MOE_KERNEL_TOPK, s,
+           moe::launch_topk(rpart, rp.slabs, bias, at<float>(ws, L.logits), T, E, k, ids, wts, s), "top-k");
+    LAUNCH(MOE_KERNEL_PERMUTE, s,
+           moe::launch_permute(ids, T, E, k, at<uint64_t>(ws, L.masks), at<int32_t>(ws, L.counts),
+                               at<int32_t>(ws, L.base), offsets, sorted, pos, at<int32_t>(ws, L.active),
+                               at<int32_t>(ws, L.nact), at<int32_t>(ws, L.mtiles), at<int32_t>(ws, L.nmt), nullptr,
+                               nullptr, H, s),
+           "permute");
+  }
+  float* rows = at<float>(ws, L.rows);
+  TRY(enqueue_ffn(d, offsets, sorted, w, rows, ws, s));
+  LAUNCH(MOE_KERNEL_COMBINE, s, moe::launch_combine(rows, pos, wts, T, H, k, ylat, s), "combine");
+  // routed-up projection back to the hidden width
+  LAUNCH(MOE_KERNEL_PROJECT, s,
+         moe::launch_projection(ylat, static_cast<const uint16_t*>(lat->w_up), ppart, T, H, Hm,
+                                moe::router_plan(T, H, Hm), static_cast<uint16_t*>(y), nullptr, s),
+         "routed-up projection");
   return MOE_OK;
 }
 

@@ -84,6 +84,11 @@ hipError_t launch_combine(const float* rows, const int32_t* pair_pos, const floa
 constexpr int STREAM_SINK_WORDS = MOE_STREAM_SINK_WORDS;
 hipError_t launch_stream_read(const void* buf, long long bytes, uint32_t* sink, hipStream_t s);
 
+// x [T][K] . w [K][N] (bf16, input-major) into out [T][N] bf16 and, if
+// out16 is non-NULL, its fp16 copy; part holds rp.slabs * T * N fp32.
+hipError_t launch_projection(const uint16_t* x, const uint16_t* w, float* part, int T, int K, int N,
+                             const RouterPlan& rp, uint16_t* out, f16* out16, hipStream_t s);
+
 hipError_t launch_quantize(const float* w, int64_t N, int64_t K, uint8_t* q, uint8_t* sf, float* gs, uint32_t* ws,
                            hipStream_t s);
 

@@ -13,6 +13,13 @@ I, E experts, top-k) and the input recipe:
              speculative verify T=256: per-expert counts 0..~40 (0.29: max 39)
              prefill chunk T=8192:     up to ~4x the mean count (0.17: 4.00x)
            The tiny and single-user cases carry no bias.
+The latent workloads are K3's LatentMoE block (lightseek.org, "Kimi K3
+optimization on GB300", part I): tokens of the hidden width H_model = 7168,
+experts in the 3584-wide routed latent with I = 3072 ([p2] "The model, as
+the serving system sees it"), and the two projections
+  P_down [H_model][H], P_up [H][H_model] ~ N(0, 0.02) rounded to bf16
+                                          (streams PROJ_DOWN, PROJ_UP);
+the router reads the hidden state, so W_r is [H_model][E].
 The normal variate is the Irwin-Hall sum of twelve uniforms (synth_def.h).
 """
 from dataclasses import dataclass
@@ -30,6 +37,7 @@ class Workload:
     beta: Optional[float] = None  # Zipf bias strength; None = no bias
     seed: int = 0
     zipf_s: float = 1.1
+    H_model: Optional[int] = None  # latent block: hidden width (the experts run at H)
 
     @property
     def P(self):
@@ -42,6 +50,11 @@ WORKLOADS = {
     "decode_64": Workload("decode_64", T=64, H=7168, I=2048, beta=0.10),
     "verify_256": Workload("verify_256", T=256, H=7168, I=2048, beta=0.29),
     "prefill_8192": Workload("prefill_8192", T=8192, H=7168, I=2048, beta=0.17),
+    # the latent block at K3's shapes (NEXT: the pages' actual model)
+    "latent_tiny": Workload("latent_tiny", T=8, H=512, I=256, H_model=1024),
+    "latent_decode_1": Workload("latent_decode_1", T=1, H=3584, I=3072, H_model=7168),
+    "latent_decode_64": Workload("latent_decode_64", T=64, H=3584, I=3072, beta=0.10, H_model=7168),
+    "latent_prefill_8192": Workload("latent_prefill_8192", T=8192, H=3584, I=3072, beta=0.17, H_model=7168),
 }
 
 

@@ -109,7 +109,7 @@ def test_profile_arguments_rejected_without_hip():
     created; reading into NULL reports -MOE_ERR_ARG."""
     L = moe.lib()
     assert L.moe_profile_arm(-1, 4) == 1
-    assert L.moe_profile_arm(7, 4) == 1
+    assert L.moe_profile_arm(8, 4) == 1
     assert L.moe_profile_arm(4, 0) == 1
     assert L.moe_profile_arm(4, 65537) == 1
     assert L.moe_profile_read(None, 4) == -1
@@ -128,3 +128,20 @@ def test_stream_read_arguments_rejected_without_hip():
     assert L.moe_stream_read(4104, 4096, 4096, None) == 3
     assert L.moe_stream_read(4096, 4096, 4098, None) == 3
     assert int(re.search(r"#define MOE_STREAM_SINK_WORDS (\d+)", open(HEADER).read()).group(1)) == moe.STREAM_SINK_WORDS
+
+
+def test_latent_workspace_and_validation_without_hip():
+    """The latent block's workspace covers the plain layer's, and bad widths
+    or NULL projections are refused before any launch."""
+    d = moe.dims(8, 3584, 3072, 896, 16)
+    assert moe.moe_latent_workspace_bytes(d, 7168) > moe.moe_workspace_bytes(d)
+    assert moe.moe_latent_workspace_bytes(d, 7000) == 0
+    assert moe.moe_latent_workspace_bytes(d, 0) == 0
+    L = moe.lib()
+    ex = moe.Experts()
+    lat = moe.Latent(7168, None, None)
+    args = (ctypes.byref(ex), 4096, 4096, None, None, None, 4096, 1 << 40, None)
+    assert L.moe_latent_layer(d, None, 4096, 4096, None, *args) == 1
+    assert L.moe_latent_layer(d, ctypes.byref(lat), 4096, 4096, None, *args) == 1
+    bad = moe.Latent(100, 4096, 4096)
+    assert L.moe_latent_layer(d, ctypes.byref(bad), 4096, 4096, None, *args) == 2
