@@ -248,3 +248,24 @@ def latent_layer(x_bf16, experts, E, k, w_down_bf16, w_up_bf16, wr_bf16=None, bi
     out["y_lat_f64"] = out["y"]
     out["y"] = bf16_matmul(y_lat, w_up_bf16)
     return out
+
+
+# ---- one share of the experts (expert parallelism) ---------------------------------
+
+def layer_share(out, base, count, k):
+    """The part of the layer that the experts [base, base + count) compute,
+    from a moe_layer(..., want_rows=True) result: served[t][j] = whether
+    record (t, j) selected one of them, and y_partial[t] = sum over those j of
+    w[t][j] * rows[pos(t, j)] in fp64 over ascending j.  al-engr.com Kimi-K3
+    plan, "What has to be built - and the discovery that changed it" (a mask
+    on the router's chosen ids, a local expert offset) and "Track A" (a
+    worker returns rows plus the ids it served)."""
+    ids, w, rows, pos = out["ids"], out["w"], out["rows"], out["pair_pos"]
+    T = ids.shape[0]
+    served = (ids >= base) & (ids < base + count)
+    y = np.zeros((T, rows.shape[1]), np.float64)
+    for t in range(T):
+        for j in range(k):
+            if served[t, j]:
+                y[t] += w[t, j] * rows[pos[t * k + j]]
+    return served.astype(np.uint8), y

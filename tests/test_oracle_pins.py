@@ -425,3 +425,20 @@ def test_latent_layer_with_embedding_projections_is_the_plain_layer():
     np.testing.assert_array_equal(lat["ids"], plain["ids"])
     np.testing.assert_array_equal(lat["y"][:, :H], synth.bf16_to_f32(oracle.round_bf16(plain["y"])))
     assert not lat["y"][:, H:].any()
+
+
+def test_layer_shares_partition_the_layer():
+    """Shares that partition the experts: their served masks are disjoint and
+    cover every record, and their partial outputs add up to the layer's
+    output (to fp64 rounding; exactly where a token's experts all fall in
+    one share)."""
+    T, H, I, E, k = 6, 64, 32, 16, 4
+    x = synth.x_bf16(14, T, H)
+    wr = synth.router_bf16(14, H, E, std=0.3)
+    out = oracle.moe_layer(x, _tiny_experts(14, E, H, I), E, k, wr_bf16=wr, want_rows=True)
+    parts = [oracle.layer_share(out, b, c, k) for b, c in [(0, 5), (5, 1), (6, 10)]]
+    np.testing.assert_array_equal(sum(p[0].astype(int) for p in parts), np.ones((T, k), int))
+    total = sum(p[1] for p in parts)
+    np.testing.assert_allclose(total, out["y"], rtol=1e-13, atol=1e-15)
+    whole = oracle.layer_share(out, 0, E, k)
+    assert whole[0].all() and np.array_equal(whole[1], out["y"])
