@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
+    ap.add_argument("--ep", type=int, default=1,
+                    help="time one device's share of an expert-parallel split into this many equal shares "
+                         "(the first E/ep experts; routing still over all E)")
     return ap.parse_args()
 
 
@@ -108,9 +111,13 @@ def main():
 
     # ---- resident inputs -------------------------------------------------------
     t_setup = time.perf_counter()
-    store = moe.ExpertStore(E, H, I, device=dev)
+    if args.ep < 1 or E % args.ep or (args.ep > 1 and wl.H_model):
+        print(json.dumps({"error": "--ep must divide E (and the latent block has no share path)"}))
+        sys.exit(2)
+    share = E // args.ep  # experts held here: 0 .. share-1
+    store = moe.ExpertStore(share, H, I, device=dev)
     buf = {m: torch.empty(store.shape(m), dtype=torch.float32, device=dev) for m in store.MATS}
-    for e in range(E):
+    for e in range(share):
         for mi, m in enumerate(store.MATS):
             synth.gpu_expert_f32(wl.seed, e, mi, buf[m])
             store.quantize_into(e, m, buf[m])
@@ -133,7 +140,7 @@ def main():
         ws = torch.empty(moe.moe_latent_workspace_bytes(d, Hm), dtype=torch.uint8, device=dev)
     else:
         ws = torch.empty(moe.moe_workspace_bytes(d), dtype=torch.uint8, device=dev)
-    y = torch.empty((T, Hm), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((T, Hm), dtype=torch.float32 if args.ep > 1 else torch.bfloat16, device=dev)
     ids = torch.empty((n_batches + n_graph, T, k), dtype=torch.int32, device=dev)
     wts = torch.empty((n_batches + n_graph, T, k), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
@@ -141,7 +148,9 @@ def main():
     stream_peak = stream_read_GBps(moe, torch)
 
     def step(i):
-        if wl.H_model:
+        if args.ep > 1:
+            moe.moe_layer_share(d, 0, share, xs[i * T:(i + 1) * T], wr, bias, store, y, None, ids[i], wts[i], ws)
+        elif wl.H_model:
             moe.moe_latent_layer(d, Hm, p_down, p_up, xs[i * T:(i + 1) * T], wr, bias, store, y, None, ids[i], wts[i],
                                  ws)
         else:
@@ -169,17 +178,20 @@ def main():
     assert len(gateup_ms) == n_prof
 
     ids_np = ids.cpu().numpy()
-    distinct = np.array([len(np.unique(ids_np[i])) for i in range(warmup, n_batches)])
+    # distinct active experts per step (of this device's share)
+    distinct = np.array([len(np.unique(ids_np[i][ids_np[i] < share])) for i in range(warmup, n_batches)])
 
     # ---- algorithmic work ------------------------------------------------------------
     ms_per_step = elapsed_ms / steps
     expert_bytes = 2 * nvfp4_bytes(I, H) + nvfp4_bytes(H, I)
     # latent block: plus the two projection weights; router and x, y at the hidden width
     proj_bytes = 2 * Hm * H * 2 if wl.H_model else 0
-    layer_bytes = distinct.mean() * expert_bytes + Hm * E * 2 + 2 * T * Hm * 2 + proj_bytes
-    layer_flops = 2 * T * Hm * E + 6 * T * k * H * I + (4 * T * Hm * H if wl.H_model else 0)
+    y_bytes = T * Hm * (4 if args.ep > 1 else 2)
+    layer_bytes = distinct.mean() * expert_bytes + Hm * E * 2 + T * Hm * 2 + y_bytes + proj_bytes
+    local_pairs = np.mean([np.count_nonzero(ids_np[i] < share) for i in range(warmup, n_batches)])
+    layer_flops = 2 * T * Hm * E + 6 * local_pairs * H * I + (4 * T * Hm * H if wl.H_model else 0)
     gateup_unit = 2 * nvfp4_bytes(I, H)              # one active expert's gate+up weights
-    gateup_bytes = distinct * gateup_unit + T * H * 2 + T * k * I * 2
+    gateup_bytes = distinct * gateup_unit + T * H * 2 + local_pairs * I * 2
     gateup_avg_ms = float(np.mean(gateup_ms))
     prof_bytes = float(np.mean(gateup_bytes[:n_prof]))  # the steps whose launches were timed
     achieved = prof_bytes / (gateup_avg_ms * 1e-3) / 1e9
@@ -192,7 +204,7 @@ def main():
                 "timed_launches": n_prof, "stream_read_GBps": round(stream_peak, 1),
                 "frac_of_stream_read": round(achieved / stream_peak, 4)}
     if prefill:
-        gu_flops = 4 * T * k * H * I
+        gu_flops = 4 * local_pairs * H * I
         tf = gu_flops / (gateup_avg_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(tf, 1), "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(tf / FP16_MFMA_PEAK_TFLOPS, 4), "traffic": load_traffic(wl.name, sha),
@@ -218,7 +230,7 @@ def main():
                                + f"T={T} H={H} I={I} E={E} top-{k}, NVFP4 experts, bf16 activations, fresh tokens "
                                f"every step",
                    "T": T, "H": H, "I": I, "E": E, "k": k, "H_model": wl.H_model, "zipf_beta": wl.beta,
-                   "seed": wl.seed},
+                   "seed": wl.seed, "expert_share": f"experts 0..{share - 1} of {E}" if args.ep > 1 else None},
         "roofline": roofline,
         "layer": {"algorithmic_bytes": int(layer_bytes), "hbm_GBps": round(layer_bytes / (ms_per_step * 1e-3) / 1e9, 1),
                   "hbm_frac": round(layer_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -259,7 +271,7 @@ def main():
         out["graph_ms_per_step"] = round(a.elapsed_time(b) / n_graph, 5)
         del graph
 
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.ep == 1:
         n_tok = args.cpu_tokens or (8 if T <= 16 else 4)
         out["cpu_baseline"] = cpu_baseline(wl, n_tok, first_token=warmup * T)
     print(json.dumps(out))

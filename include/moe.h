@@ -44,7 +44,9 @@
  *     H and I multiples of 256, 0 <= T and T*k < 2^31.  T = 0 is a no-op
  *     returning MOE_OK once the dimensions are valid (pointers are then not
  *     examined).
- *   - Pointers must be 16-byte aligned.
+ *   - Pointers must be 16-byte aligned, except the per-tensor scales gs
+ *     of moe_nvfp4 (4-byte aligned, so that a share of a store can point
+ *     into it) and the uint8 outputs.
  *   - Activations (x) must be finite with |x| < 65504, and so must the
  *     intermediate h = SiLU(x.W_gate)*(x.W_up): the expert GEMMs run on
  *     fp16 matrix cores (the NVFP4 products are exact in fp16; see the
@@ -151,6 +153,43 @@ moe_status moe_expert_ffn(moe_dims d, const void* x, const int32_t* expert_offse
  *   the routing (NULL to skip). */
 moe_status moe_layer(moe_dims d, const void* x, const void* w_router, const float* bias, const moe_experts* w,
                      void* y, int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- one share of the experts (expert parallelism) ---------------------------
+ * al-engr.com Kimi-K3 plan, section "What has to be built - and the
+ * discovery that changed it": splitting one model's experts across devices
+ * takes a mask on the router's chosen ids and a routed kernel that takes a
+ * local expert offset; section "Track A": an expert worker takes global
+ * expert ids and returns rows plus the ids it actually served, so that every
+ * token's experts are accounted for exactly once.  Here a share is the
+ * contiguous range [base, base + count) of the E experts, and its store
+ * holds those count experts only (store entry i is expert base + i).
+ * Routing (moe_route, or the routing inside moe_layer_share) is over all E
+ * experts, unchanged. */
+typedef struct {
+  int32_t base, count;
+} moe_expert_share;
+
+/* moe_expert_ffn for one share: rows[p] for the records p of the share's
+ * experts, which are the contiguous range expert_offsets[base] ..
+ * expert_offsets[base + count) of the sorted order; other rows are left as
+ * they were.  w holds the share's count experts.  Errors as moe_expert_ffn,
+ * plus MOE_ERR_SHAPE for a share that is empty or not inside [0, E). */
+moe_status moe_expert_ffn_share(moe_dims d, moe_expert_share share, const void* x, const int32_t* expert_offsets,
+                                const int32_t* sorted_pairs, const moe_experts* w, float* rows, void* ws,
+                                size_t ws_bytes, void* stream);
+
+/* moe_layer for one share: routing over all E experts, the share's experts
+ * on their records, and (device pointers)
+ *   y_partial [T][H] fp32: sum, over ascending j with topk_ids[t][j] in the
+ *             share, of topk_w[t][j] * FFN_{topk_ids[t][j]}(x[t]), in fp32;
+ *   served    [T][k] uint8 or NULL: 1 where this share computed record
+ *             (t, j), else 0 (summed over a partition of the experts: all 1).
+ * The partials of shares that partition the experts add up to moe_layer's
+ * sum; rounding that total to bf16 is left to the caller (after the
+ * reduction across devices).  Workspace as moe_layer. */
+moe_status moe_layer_share(moe_dims d, moe_expert_share share, const void* x, const void* w_router, const float* bias,
+                           const moe_experts* w, float* y_partial, uint8_t* served, int32_t* topk_ids_out,
+                           float* topk_w_out, void* ws, size_t ws_bytes, void* stream);
 
 /* ---- the latent routed-expert block (K3's LatentMoE) -------------------------
  * lightseek.org, "Kimi K3 optimization on GB300" (part I), sections

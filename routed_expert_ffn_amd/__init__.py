@@ -19,7 +19,8 @@ KERNELS = {"router": 0, "topk": 1, "permute": 2, "cast": 3, "gateup": 4, "down":
 # Symbols include/moe.h declares.
 EXPORTS = ("moe_workspace_bytes", "moe_quantize_workspace_bytes", "moe_quantize_nvfp4", "moe_route",
            "moe_expert_ffn", "moe_layer", "moe_status_string", "moe_last_error", "moe_profile_arm",
-           "moe_profile_read", "moe_stream_read", "moe_latent_workspace_bytes", "moe_latent_layer")
+           "moe_profile_read", "moe_stream_read", "moe_latent_workspace_bytes", "moe_latent_layer",
+           "moe_expert_ffn_share", "moe_layer_share")
 # MOE_STREAM_SINK_WORDS of moe.h
 STREAM_SINK_WORDS = 4096
 
@@ -41,6 +42,10 @@ class NVFP4(ctypes.Structure):
 
 class Experts(ctypes.Structure):
     _fields_ = [("gate", NVFP4), ("up", NVFP4), ("down", NVFP4)]
+
+
+class Share(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_int32), ("count", ctypes.c_int32)]
 
 
 class Latent(ctypes.Structure):
@@ -70,6 +75,12 @@ def lib():
         L.moe_expert_ffn.argtypes = [Dims, _p, _p, _p, ctypes.POINTER(Experts), _p, _p, ctypes.c_size_t, _p]
         L.moe_layer.restype = ctypes.c_int
         L.moe_layer.argtypes = [Dims, _p, _p, _p, ctypes.POINTER(Experts), _p, _p, _p, _p, ctypes.c_size_t, _p]
+        L.moe_expert_ffn_share.restype = ctypes.c_int
+        L.moe_expert_ffn_share.argtypes = [Dims, Share, _p, _p, _p, ctypes.POINTER(Experts), _p, _p, ctypes.c_size_t,
+                                           _p]
+        L.moe_layer_share.restype = ctypes.c_int
+        L.moe_layer_share.argtypes = [Dims, Share, _p, _p, _p, ctypes.POINTER(Experts), _p, _p, _p, _p, _p,
+                                      ctypes.c_size_t, _p]
         L.moe_latent_workspace_bytes.restype = ctypes.c_size_t
         L.moe_latent_workspace_bytes.argtypes = [Dims, ctypes.c_int32]
         L.moe_latent_layer.restype = ctypes.c_int
@@ -152,6 +163,23 @@ def moe_layer(d, x, w_router, bias, experts, y, topk_ids_out, topk_w_out, ws, st
                            _stream(stream)))
 
 
+def moe_expert_ffn_share(d, base, count, x, expert_offsets, sorted_pairs, experts, rows, ws, stream=None):
+    """moe_expert_ffn for the share [base, base + count) of the experts;
+    `experts` holds that share (e.g. ExpertStore.share(base, count))."""
+    _check(lib().moe_expert_ffn_share(d, Share(int(base), int(count)), _ptr(x), _ptr(expert_offsets),
+                                      _ptr(sorted_pairs), ctypes.byref(experts.c()), _ptr(rows), _ptr(ws),
+                                      ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_layer_share(d, base, count, x, w_router, bias, experts, y_partial, served, topk_ids_out, topk_w_out, ws,
+                    stream=None):
+    """moe_layer for one share of the experts: fp32 partial output and the
+    records it served (moe.h: moe_layer_share)."""
+    _check(lib().moe_layer_share(d, Share(int(base), int(count)), _ptr(x), _ptr(w_router), _ptr(bias),
+                                 ctypes.byref(experts.c()), _ptr(y_partial), _ptr(served), _ptr(topk_ids_out),
+                                 _ptr(topk_w_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
 def moe_latent_workspace_bytes(d, H_model):
     return lib().moe_latent_workspace_bytes(d, int(H_model))
 
@@ -227,5 +255,25 @@ class ExpertStore:
         self._c = Experts(*mats)
         return self._c
 
+    def share(self, base, count):
+        """The store of experts base .. base+count-1 alone (entry i = expert
+        base + i): views into this store, as one device's share would hold."""
+        return _StoreShare(self, base, count)
+
     def nbytes_per_expert(self):
         return sum(q[0].numel() + sf[0].numel() + 4 for q, sf, _ in self.t.values())
+
+
+class _StoreShare:
+    def __init__(self, store, base, count):
+        if base < 0 or count < 1 or base + count > store.E:
+            raise ValueError("share outside the store")
+        self.store, self.base, self.count = store, base, count
+
+    def c(self):
+        mats = []
+        for m in ExpertStore.MATS:
+            q, sf, gs = self.store.t[m]
+            mats.append(NVFP4(q[self.base].data_ptr(), sf[self.base].data_ptr(), gs[self.base:].data_ptr()))
+        self._c = Experts(*mats)
+        return self._c

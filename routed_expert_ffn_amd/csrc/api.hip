@@ -149,8 +149,9 @@ moe_status check_experts(const moe_experts* w) {
   const char* names[3] = {"gate", "up", "down"};
   for (int i = 0; i < 3; i++) {
     if (!m[i]->q || !m[i]->sf || !m[i]->gs) return fail(MOE_ERR_ARG, "%s weights have a NULL pointer", names[i]);
-    if (!aligned16(m[i]->q) || !aligned16(m[i]->sf) || !aligned16(m[i]->gs))
-      return fail(MOE_ERR_ALIGN, "%s weights are not 16-byte aligned", names[i]);
+    if (!aligned16(m[i]->q) || !aligned16(m[i]->sf))
+      return fail(MOE_ERR_ALIGN, "%s codes or scales are not 16-byte aligned", names[i]);
+    if ((uintptr_t)m[i]->gs & 3u) return fail(MOE_ERR_ALIGN, "%s per-tensor scales are not 4-byte aligned", names[i]);
   }
   return MOE_OK;
 }
@@ -206,7 +207,7 @@ moe_status enqueue_route(const moe_dims& d, const void* x, const void* wr, const
 // Enqueue the two grouped GEMMs (x16, the active list and the permutation
 // are already in place).
 moe_status enqueue_ffn(const moe_dims& d, const int32_t* offsets, const int32_t* sorted, const moe_experts* w,
-                       float* rows, void* ws, hipStream_t s) {
+                       float* rows, void* ws, hipStream_t s, int e_base = 0) {
   const Layout L = layout(d);
   moe::FfnArgs a;
   a.T = d.T;
@@ -214,6 +215,7 @@ moe_status enqueue_ffn(const moe_dims& d, const int32_t* offsets, const int32_t*
   a.I = d.I;
   a.E = d.E;
   a.k = d.k;
+  a.e_base = e_base;
   a.max_active = moe::max_active(d);
   a.x16 = at<f16>(ws, L.x16);
   a.offsets = offsets;
@@ -230,6 +232,36 @@ moe_status enqueue_ffn(const moe_dims& d, const int32_t* offsets, const int32_t*
   LAUNCH(MOE_KERNEL_DOWN, s, moe::launch_down(a, s), "down");
   return MOE_OK;
 }
+
+moe_status expert_ffn_range(moe_dims d, int lo, int hi, const void* x, const int32_t* expert_offsets,
+                            const int32_t* sorted_pairs, const moe_experts* w, float* rows, void* ws, size_t ws_bytes,
+                            void* stream) {
+  TRY(check_dims(d));
+  if (d.T == 0) return MOE_OK;
+  TRY(check_ptr(x, "x"));
+  TRY(check_ptr(expert_offsets, "expert_offsets"));
+  TRY(check_ptr(sorted_pairs, "sorted_pairs"));
+  TRY(check_experts(w));
+  TRY(check_ptr(rows, "rows"));
+  TRY(check_ws(d, ws, ws_bytes));
+  const Layout L = layout(d);
+  hipStream_t s = (hipStream_t)stream;
+  LAUNCH(MOE_KERNEL_CAST, s,
+         moe::launch_active_list(expert_offsets, d.E, lo, hi, at<int32_t>(ws, L.active), at<int32_t>(ws, L.nact),
+                                 at<int32_t>(ws, L.mtiles), at<int32_t>(ws, L.nmt), s),
+         "active list");
+  LAUNCH(MOE_KERNEL_CAST, s,
+         moe::launch_cast(static_cast<const uint16_t*>(x), at<f16>(ws, L.x16), (long long)d.T * d.H, s), "cast");
+  return enqueue_ffn(d, expert_offsets, sorted_pairs, w, rows, ws, s, lo);
+}
+
+moe_status check_share(const moe_dims& d, moe_expert_share sh) {
+  if (sh.base < 0 || sh.count < 1 || sh.base > d.E - sh.count)
+    return fail(MOE_ERR_SHAPE, "share [%d, %d + %d) is not a non-empty range of the %d experts", sh.base, sh.base,
+                sh.count, d.E);
+  return MOE_OK;
+}
+
 
 }  // namespace
 
@@ -292,23 +324,52 @@ moe_status moe_route(moe_dims d, const void* x, const void* w_router, const floa
 
 moe_status moe_expert_ffn(moe_dims d, const void* x, const int32_t* expert_offsets, const int32_t* sorted_pairs,
                           const moe_experts* w, float* rows, void* ws, size_t ws_bytes, void* stream) {
+  return expert_ffn_range(d, 0, d.E, x, expert_offsets, sorted_pairs, w, rows, ws, ws_bytes, stream);
+}
+
+moe_status moe_expert_ffn_share(moe_dims d, moe_expert_share share, const void* x, const int32_t* expert_offsets,
+                                const int32_t* sorted_pairs, const moe_experts* w, float* rows, void* ws,
+                                size_t ws_bytes, void* stream) {
   TRY(check_dims(d));
+  TRY(check_share(d, share));
+  return expert_ffn_range(d, share.base, share.base + share.count, x, expert_offsets, sorted_pairs, w, rows, ws,
+                          ws_bytes, stream);
+}
+
+moe_status moe_layer_share(moe_dims d, moe_expert_share share, const void* x, const void* w_router, const float* bias,
+                           const moe_experts* w, float* y_partial, uint8_t* served, int32_t* topk_ids_out,
+                           float* topk_w_out, void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_dims(d));
+  TRY(check_share(d, share));
   if (d.T == 0) return MOE_OK;
   TRY(check_ptr(x, "x"));
-  TRY(check_ptr(expert_offsets, "expert_offsets"));
-  TRY(check_ptr(sorted_pairs, "sorted_pairs"));
+  TRY(check_ptr(w_router, "w_router"));
+  TRY(check_ptr(bias, "bias", false));
   TRY(check_experts(w));
-  TRY(check_ptr(rows, "rows"));
+  TRY(check_ptr(y_partial, "y_partial"));
+  TRY(check_ptr(topk_ids_out, "topk_ids_out", false));
+  TRY(check_ptr(topk_w_out, "topk_w_out", false));
   TRY(check_ws(d, ws, ws_bytes));
   const Layout L = layout(d);
   hipStream_t s = (hipStream_t)stream;
-  LAUNCH(MOE_KERNEL_CAST, s,
-         moe::launch_active_list(expert_offsets, d.E, at<int32_t>(ws, L.active), at<int32_t>(ws, L.nact),
+  const int lo = share.base, hi = share.base + share.count;
+  int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, L.ids);
+  float* wts = topk_w_out ? topk_w_out : at<float>(ws, L.w);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* sorted = at<int32_t>(ws, L.sorted);
+  int32_t* pos = at<int32_t>(ws, L.pos);
+  float* rows = at<float>(ws, L.rows);
+  TRY(enqueue_route(d, x, w_router, bias, at<float>(ws, L.logits), ids, wts, offsets, sorted, pos, ws,
+                    at<f16>(ws, L.x16), s));
+  // the share's experts only: its active list and tile entries replace the routing's
+  LAUNCH(MOE_KERNEL_PERMUTE, s,
+         moe::launch_active_list(offsets, d.E, lo, hi, at<int32_t>(ws, L.active), at<int32_t>(ws, L.nact),
                                  at<int32_t>(ws, L.mtiles), at<int32_t>(ws, L.nmt), s),
          "active list");
-  LAUNCH(MOE_KERNEL_CAST, s,
-         moe::launch_cast(static_cast<const uint16_t*>(x), at<f16>(ws, L.x16), (long long)d.T * d.H, s), "cast");
-  return enqueue_ffn(d, expert_offsets, sorted_pairs, w, rows, ws, s);
+  TRY(enqueue_ffn(d, offsets, sorted, w, rows, ws, s, lo));
+  LAUNCH(MOE_KERNEL_COMBINE, s,
+         moe::launch_combine_share(rows, pos, wts, ids, lo, hi, d.T, d.H, d.k, y_partial, served, s), "combine");
+  return MOE_OK;
 }
 
 moe_status moe_layer(moe_dims d, const void* x, const void* w_router, const float* bias, const moe_experts* w,

@@ -49,8 +49,9 @@ hipError_t launch_permute(const int32_t* ids, int T, int E, int k, uint64_t* mas
                           int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_pos, int32_t* active,
                           int32_t* n_active, int32_t* mtiles, int32_t* n_mtiles, const uint16_t* x, f16* x16,
                           int H, hipStream_t s);
-hipError_t launch_active_list(const int32_t* offsets, int E, int32_t* active, int32_t* n_active, int32_t* mtiles,
-                              int32_t* n_mtiles, hipStream_t s);
+// Active list and (expert, token tile) entries of the experts in [lo, hi).
+hipError_t launch_active_list(const int32_t* offsets, int E, int lo, int hi, int32_t* active, int32_t* n_active,
+                              int32_t* mtiles, int32_t* n_mtiles, hipStream_t s);
 // Token tile of the large-batch expert GEMMs: an expert's records are split
 // evenly over ceil(n / MTILE) tiles.
 constexpr int MTILE = 224;
@@ -61,6 +62,7 @@ hipError_t launch_cast(const uint16_t* x, f16* x16, long long n, hipStream_t s);
 
 struct FfnArgs {
   int T, H, I, E, k;
+  int e_base;                     // first expert of the store (weights of e at e - e_base)
   int max_active;                 // grid bound on the number of active experts
   const f16* x16;                 // [T][H]
   const int32_t* offsets;         // [E+1]
@@ -78,6 +80,11 @@ hipError_t launch_gateup(const FfnArgs& a, hipStream_t s);
 hipError_t launch_down(const FfnArgs& a, hipStream_t s);
 hipError_t launch_combine(const float* rows, const int32_t* pair_pos, const float* w, int T, int H, int k,
                           uint16_t* y, hipStream_t s);
+// One share of the experts: only records whose expert is in [lo, hi) are
+// summed, into fp32 partial outputs; served[t*k+j] (may be NULL) = 1 for
+// those records, 0 for the others.
+hipError_t launch_combine_share(const float* rows, const int32_t* pair_pos, const float* w, const int32_t* ids,
+                                int lo, int hi, int T, int H, int k, float* y, uint8_t* served, hipStream_t s);
 
 // Streaming read of `bytes` (a multiple of 16) into at most
 // STREAM_SINK_WORDS per-block XOR words.

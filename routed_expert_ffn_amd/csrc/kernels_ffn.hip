@@ -36,6 +36,7 @@ constexpr int KCHUNK = 256;
 
 struct GroupedParams {
   int H, I, k;
+  int e_base;          // expert e's weights are entry e - e_base of the store
   const int32_t* offsets;
   const int32_t* sorted_pairs;
   const int32_t* active;
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(FFN_THREADS, WAVES_PER_EU) void expert_gemm_kernel(
   constexpr int RT = 4 / KSPLIT;
   __shared__ float red[KSPLIT > 1 ? 4 : 1][WAVE][MF * 16];
   if ((int)blockIdx.y >= *p.n_active) return;
-  const int e = p.active[blockIdx.y];
+  const int e = p.active[blockIdx.y], el = e - p.e_base;
   const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE, r = lane % 16, g = lane / 16;
   const int rt = wv / KSPLIT, ks = wv % KSPLIT;
   const int K = GATEUP ? p.H : p.I;
@@ -136,11 +137,11 @@ __global__ __launch_bounds__(FFN_THREADS, WAVES_PER_EU) void expert_gemm_kernel(
     const uint8_t* qb;
     const uint8_t* sb;
     if (GATEUP) {
-      row = (size_t)e * N + tile * 32 + 16 * (ng & 1) + r;
+      row = (size_t)el * N + tile * 32 + 16 * (ng & 1) + r;
       qb = ng < 2 ? p.q0 : p.q1;
       sb = ng < 2 ? p.sf0 : p.sf1;
     } else {
-      row = (size_t)e * N + tile * 64 + 16 * ng + r;
+      row = (size_t)el * N + tile * 64 + 16 * ng + r;
       qb = p.q0;
       sb = p.sf0;
     }
@@ -151,7 +152,7 @@ __global__ __launch_bounds__(FFN_THREADS, WAVES_PER_EU) void expert_gemm_kernel(
   Chunk<MF> cur;
   if (ks < nchunks) load_b(cur, qrow, srow, ks * KCHUNK + 64 * g);  // before the token lookups
   const int begin = p.offsets[e], end = p.offsets[e + 1];
-  const float gsa = p.gs0[e], gsb = GATEUP ? p.gs1[e] : 0.0f;
+  const float gsa = p.gs0[el], gsb = GATEUP ? p.gs1[el] : 0.0f;
   bool first_pass = true;
   for (int mb = begin; mb < end; mb += MF * 16) {
     const int nvalid = end - mb;
@@ -557,13 +558,13 @@ __device__ __forceinline__ void big_tile(const GroupedParams& p, const BigTile& 
   {
     const size_t qrow = (size_t)(K / 2), srow = (size_t)(K / 16);
     if (GATEUP) {
-      const size_t r0 = (size_t)t.e * t.N + t.rtile * (BIG_N / 2);
+      const size_t r0 = (size_t)(t.e - p.e_base) * t.N + t.rtile * (BIG_N / 2);
       L.q[0] = p.q0 + r0 * qrow;
       L.q[1] = p.q1 + r0 * qrow;
       L.sc[0] = p.sf0 + r0 * srow;
       L.sc[1] = p.sf1 + r0 * srow;
     } else {
-      const size_t r0 = (size_t)t.e * t.N + t.rtile * BIG_N;
+      const size_t r0 = (size_t)(t.e - p.e_base) * t.N + t.rtile * BIG_N;
       L.q[0] = p.q0 + r0 * qrow;
       L.q[1] = L.q[0] + 128 * qrow;
       L.sc[0] = p.sf0 + r0 * srow;
@@ -623,7 +624,7 @@ __device__ __forceinline__ void big_tile(const GroupedParams& p, const BigTile& 
   // four consecutive columns (m32 & ~3 ..) of row 8q + 4 g2 + (lane & 3), so
   // each lane stores 16 (h: 8) contiguous bytes and one store instruction
   // covers eight row segments.
-  const float gsa = p.gs0[t.e], gsb = GATEUP ? p.gs1[t.e] : 0.0f;
+  const float gsa = p.gs0[t.e - p.e_base], gsb = GATEUP ? p.gs1[t.e - p.e_base] : 0.0f;
   const int n4 = m32 & ~3, j4 = lane & 3;
 #pragma unroll
   for (int f = 0; f < NF; f++)
@@ -767,6 +768,39 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   *reinterpret_cast<uint2*>(y + (size_t)t * H + n) = o;
 }
 
+// One share of the experts ([lo, hi)): as combine_kernel, but only records
+// whose expert lies in the share are summed, in ascending j, into fp32
+// partial outputs, and block 0 of each token writes which records it
+// served.  The partials of shares that partition the experts add up to the
+// whole layer's sum.
+__global__ __launch_bounds__(256) void combine_share_kernel(const float* __restrict__ rows,
+                                                           const int32_t* __restrict__ pair_pos,
+                                                           const float* __restrict__ w,
+                                                           const int32_t* __restrict__ ids, int lo, int hi, int H,
+                                                           int k, float* __restrict__ y,
+                                                           uint8_t* __restrict__ served) {
+  const int t = blockIdx.y;
+  if (served && blockIdx.x == 0)
+    for (int j = threadIdx.x; j < k; j += blockDim.x) {
+      const int e = ids[(size_t)t * k + j];
+      served[(size_t)t * k + j] = (e >= lo && e < hi) ? 1 : 0;
+    }
+  const int n = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (n >= H) return;
+  float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int j = 0; j < k; j++) {
+    const int e = ids[(size_t)t * k + j];
+    if (e < lo || e >= hi) continue;
+    const float wj = w[(size_t)t * k + j];
+    const float4 v = *reinterpret_cast<const float4*>(rows + (size_t)pair_pos[(size_t)t * k + j] * H + n);
+    a.x = fmaf(wj, v.x, a.x);
+    a.y = fmaf(wj, v.y, a.y);
+    a.z = fmaf(wj, v.z, a.z);
+    a.w = fmaf(wj, v.w, a.w);
+  }
+  *reinterpret_cast<float4*>(y + (size_t)t * H + n) = a;
+}
+
 // Fragments per pass: an expert never has more pairs than there are tokens.
 // At decode sizes one 16-token fragment per pass keeps two wavefronts per
 // SIMD resident; an expert with more tokens takes several passes, the later
@@ -778,6 +812,7 @@ GroupedParams base_params(const FfnArgs& a) {
   p.H = a.H;
   p.I = a.I;
   p.k = a.k;
+  p.e_base = a.e_base;
   p.offsets = a.offsets;
   p.sorted_pairs = a.sorted_pairs;
   p.active = a.active;
@@ -840,6 +875,14 @@ hipError_t launch_down(const FfnArgs& a, hipStream_t s) {
   if (use_big(a)) return launch_big<false>(a, p, s);
   const dim3 grid(a.H / (64 * (4 / DN_KSPLIT)), a.max_active);
   return launch_gemm<DN_KSPLIT, false>(p, pick_mf(a.T), grid, s);
+}
+
+hipError_t launch_combine_share(const float* rows, const int32_t* pair_pos, const float* w, const int32_t* ids,
+                                int lo, int hi, int T, int H, int k, float* y, uint8_t* served, hipStream_t s) {
+  const int threads = T < 64 ? 64 : 256;
+  hipLaunchKernelGGL(combine_share_kernel, dim3((H / 4 + threads - 1) / threads, T), dim3(threads), 0, s, rows,
+                     pair_pos, w, ids, lo, hi, H, k, y, served);
+  return hipGetLastError();
 }
 
 hipError_t launch_combine(const float* rows, const int32_t* pair_pos, const float* w, int T, int H, int k,

@@ -671,16 +671,17 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __rest
   }
 }
 
-// Experts with work, from offsets alone (when the permutation comes from
-// the caller), and the fp16 copy of the activations.
-__global__ __launch_bounds__(1024) void active_list_kernel(const int32_t* __restrict__ offsets, int E,
+// Experts in [lo, hi) with work and their (expert, token tile) entries,
+// from offsets alone (when the permutation comes from the caller, or when
+// only one share of the experts runs here).
+__global__ __launch_bounds__(1024) void active_list_kernel(const int32_t* __restrict__ offsets, int E, int lo, int hi,
                                                           int32_t* __restrict__ active,
                                                           int32_t* __restrict__ n_active,
                                                           int32_t* __restrict__ mtiles,
                                                           int32_t* __restrict__ n_mtiles) {
   __shared__ int lds[16];
   const int e = threadIdx.x;
-  const int cnt = e < E ? offsets[e + 1] - offsets[e] : 0;
+  const int cnt = (e < E && e >= lo && e < hi) ? offsets[e + 1] - offsets[e] : 0;
   const int flag = cnt > 0 ? 1 : 0;
   int nact;
   const int slot = block_exclusive_scan(flag, lds, &nact);
@@ -793,9 +794,10 @@ hipError_t launch_permute(const int32_t* ids, int T, int E, int k, uint64_t* mas
   return hipGetLastError();
 }
 
-hipError_t launch_active_list(const int32_t* offsets, int E, int32_t* active, int32_t* n_active, int32_t* mtiles,
-                              int32_t* n_mtiles, hipStream_t s) {
-  hipLaunchKernelGGL(active_list_kernel, dim3(1), dim3(1024), 0, s, offsets, E, active, n_active, mtiles, n_mtiles);
+hipError_t launch_active_list(const int32_t* offsets, int E, int lo, int hi, int32_t* active, int32_t* n_active,
+                              int32_t* mtiles, int32_t* n_mtiles, hipStream_t s) {
+  hipLaunchKernelGGL(active_list_kernel, dim3(1), dim3(1024), 0, s, offsets, E, lo, hi, active, n_active, mtiles,
+                     n_mtiles);
   return hipGetLastError();
 }
 

@@ -145,3 +145,16 @@ def test_latent_workspace_and_validation_without_hip():
     assert L.moe_latent_layer(d, ctypes.byref(lat), 4096, 4096, None, *args) == 1
     bad = moe.Latent(100, 4096, 4096)
     assert L.moe_latent_layer(d, ctypes.byref(bad), 4096, 4096, None, *args) == 2
+
+
+def test_share_validation_without_hip():
+    """Shares that are empty or leave [0, E) are refused before any launch."""
+    L = moe.lib()
+    d = moe.dims(8, 512, 256, 64, 8)
+    ex = moe.Experts()
+    ws_bytes = moe.moe_workspace_bytes(d)
+    for base, count in [(-1, 4), (0, 0), (60, 8), (64, 1)]:
+        sh = moe.Share(base, count)
+        assert L.moe_layer_share(d, sh, FAKE, FAKE, None, ctypes.byref(ex), FAKE, None, None, None, FAKE, ws_bytes,
+                                 None) == 2
+        assert L.moe_expert_ffn_share(d, sh, FAKE, FAKE, FAKE, ctypes.byref(ex), FAKE, FAKE, ws_bytes, None) == 2
