@@ -269,3 +269,36 @@ def layer_share(out, base, count, k):
             if served[t, j]:
                 y[t] += w[t, j] * rows[pos[t * k + j]]
     return served.astype(np.uint8), y
+
+
+# ---- shared experts (every token uses them) ------------------------------------------
+
+def shared_experts(x_bf16, w_gate_up_bf16, w_down_bf16, count, I):
+    """Dense bf16 SwiGLU experts that every token uses, summed (fp64):
+    for shared expert s, g = x . Wgu[:, 2sI : 2sI+I], u = x . Wgu[:, 2sI+I :
+    2sI+2I], h = bf16(SiLU(g) * u), out += h . Wd[sI : sI+I, :].  Weights are
+    bf16 and stored input-major (Wgu [H][count*2I], Wd [count*I][H]); h is
+    rounded to bf16, the dense module's activation type, before the down
+    projection.  [p1] section 3.3: every token uses the 2 shared experts,
+    whose output joins the routed experts' in the layer's sum; [p2]
+    "Precision: what is stored in which format": shared experts are bf16."""
+    gu = bf16_matmul(x_bf16, w_gate_up_bf16)
+    T = gu.shape[0]
+    h = np.empty((T, count * I), np.float64)
+    for s in range(count):
+        g = gu[:, 2 * s * I:2 * s * I + I]
+        u = gu[:, 2 * s * I + I:2 * s * I + 2 * I]
+        h[:, s * I:(s + 1) * I] = g / (1.0 + np.exp(-g)) * u
+    return bf16_matmul(round_bf16(h), w_down_bf16)
+
+
+def layer_with_shared(x_bf16, experts, E, k, w_gate_up_bf16, w_down_bf16, count, I_shared, wr_bf16=None, bias=None,
+                      logits_in=None, nthreads=1, want_rows=False):
+    """The routed layer plus its shared experts: y = routed sum + shared sum
+    (fp64; the GPU rounds the total to bf16 once)."""
+    out = moe_layer(x_bf16, experts, E, k, wr_bf16=wr_bf16, bias=bias, logits_in=logits_in, nthreads=nthreads,
+                    want_rows=want_rows)
+    out["y_routed"] = out["y"]
+    out["y_shared"] = shared_experts(x_bf16, w_gate_up_bf16, w_down_bf16, count, I_shared)
+    out["y"] = out["y_routed"] + out["y_shared"]
+    return out

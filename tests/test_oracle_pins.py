@@ -442,3 +442,47 @@ def test_layer_shares_partition_the_layer():
     np.testing.assert_allclose(total, out["y"], rtol=1e-13, atol=1e-15)
     whole = oracle.layer_share(out, 0, E, k)
     assert whole[0].all() and np.array_equal(whole[1], out["y"])
+
+
+# ---- shared experts -------------------------------------------------------------------
+
+def _shared_weights(seed, H, I, count):
+    wgu = synth.round_bf16((np.random.default_rng(seed).standard_normal((H, 2 * count * I)) * 0.1).astype(np.float32))
+    wd = synth.round_bf16((np.random.default_rng(seed + 1).standard_normal((count * I, H)) * 0.1).astype(np.float32))
+    return wgu, wd
+
+
+def test_shared_experts_match_torch_float64():
+    """Against torch's float64 matmuls and SiLU (another implementation of the
+    products), with the oracle's bf16 rounding of h shared by both."""
+    T, H, I, count = 5, 64, 48, 2
+    x = synth.x_bf16(15, T, H)
+    wgu, wd = _shared_weights(15, H, I, count)
+    f = lambda a: torch.tensor(synth.bf16_to_f32(a).astype(np.float64))
+    gu = f(x) @ f(wgu)
+    hs = []
+    for s in range(count):
+        g, u = gu[:, 2 * s * I:2 * s * I + I], gu[:, 2 * s * I + I:2 * s * I + 2 * I]
+        hs.append(torch.nn.functional.silu(g) * u)
+    h = f(oracle.round_bf16(torch.cat(hs, 1).numpy()))
+    ref = (h @ f(wd)).numpy()
+    np.testing.assert_allclose(oracle.shared_experts(x, wgu, wd, count, I), ref, rtol=1e-12, atol=1e-12)
+
+
+def test_shared_experts_are_additive_and_vanish():
+    """Two shared experts give the sum of each alone; zero input gives zero
+    (SiLU(0) = 0); zero down weights leave the routed layer unchanged."""
+    T, H, I = 4, 64, 32
+    x = synth.x_bf16(16, T, H)
+    wgu, wd = _shared_weights(16, H, I, 2)
+    both = oracle.shared_experts(x, wgu, wd, 2, I)
+    one = oracle.shared_experts(x, np.ascontiguousarray(wgu[:, :2 * I]), np.ascontiguousarray(wd[:I]), 1, I)
+    two = oracle.shared_experts(x, np.ascontiguousarray(wgu[:, 2 * I:]), np.ascontiguousarray(wd[I:]), 1, I)
+    np.testing.assert_allclose(both, one + two, rtol=1e-13, atol=1e-13)
+    assert not oracle.shared_experts(np.zeros_like(x), wgu, wd, 2, I).any()
+    E, k = 16, 4
+    wr = synth.router_bf16(16, H, E, std=0.3)
+    ex = _tiny_experts(16, E, H, I)
+    plain = oracle.moe_layer(x, ex, E, k, wr_bf16=wr)
+    with_zero = oracle.layer_with_shared(x, ex, E, k, wgu, np.zeros_like(wd), 2, I, wr_bf16=wr)
+    np.testing.assert_array_equal(with_zero["y"], plain["y"])
