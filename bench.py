@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
+    ap.add_argument("--shared", type=int, default=0,
+                    help="add this many bf16 shared experts (width I) that every token uses")
     ap.add_argument("--ep", type=int, default=1,
                     help="time one device's share of an expert-parallel split into this many equal shares "
                          "(the first E/ep experts; routing still over all E)")
@@ -111,8 +113,8 @@ def main():
 
     # ---- resident inputs -------------------------------------------------------
     t_setup = time.perf_counter()
-    if args.ep < 1 or E % args.ep or (args.ep > 1 and wl.H_model):
-        print(json.dumps({"error": "--ep must divide E (and the latent block has no share path)"}))
+    if args.ep < 1 or E % args.ep or (args.ep > 1 and wl.H_model) or (args.shared and (wl.H_model or args.ep > 1)):
+        print(json.dumps({"error": "--ep must divide E; --ep and --shared go with the plain layer only, not together"}))
         sys.exit(2)
     share = E // args.ep  # experts held here: 0 .. share-1
     store = moe.ExpertStore(share, H, I, device=dev)
@@ -138,6 +140,12 @@ def main():
         synth.gpu_proj_bf16(wl.seed, 0, p_down)
         synth.gpu_proj_bf16(wl.seed, 1, p_up)
         ws = torch.empty(moe.moe_latent_workspace_bytes(d, Hm), dtype=torch.uint8, device=dev)
+    elif args.shared:
+        sh_gu = torch.empty((H, args.shared * 2 * I), dtype=torch.bfloat16, device=dev)
+        sh_dn = torch.empty((args.shared * I, H), dtype=torch.bfloat16, device=dev)
+        synth.gpu_proj_bf16(wl.seed, 2, sh_gu)
+        synth.gpu_proj_bf16(wl.seed, 3, sh_dn)
+        ws = torch.empty(moe.moe_layer_shared_workspace_bytes(d, args.shared, I), dtype=torch.uint8, device=dev)
     else:
         ws = torch.empty(moe.moe_workspace_bytes(d), dtype=torch.uint8, device=dev)
     y = torch.empty((T, Hm), dtype=torch.float32 if args.ep > 1 else torch.bfloat16, device=dev)
@@ -150,6 +158,9 @@ def main():
     def step(i):
         if args.ep > 1:
             moe.moe_layer_share(d, 0, share, xs[i * T:(i + 1) * T], wr, bias, store, y, None, ids[i], wts[i], ws)
+        elif args.shared:
+            moe.moe_layer_shared(d, args.shared, I, sh_gu, sh_dn, xs[i * T:(i + 1) * T], wr, bias, store, y, ids[i],
+                                 wts[i], ws)
         elif wl.H_model:
             moe.moe_latent_layer(d, Hm, p_down, p_up, xs[i * T:(i + 1) * T], wr, bias, store, y, None, ids[i], wts[i],
                                  ws)
@@ -186,10 +197,12 @@ def main():
     expert_bytes = 2 * nvfp4_bytes(I, H) + nvfp4_bytes(H, I)
     # latent block: plus the two projection weights; router and x, y at the hidden width
     proj_bytes = 2 * Hm * H * 2 if wl.H_model else 0
+    proj_bytes += args.shared * 3 * H * I * 2  # bf16 shared experts
     y_bytes = T * Hm * (4 if args.ep > 1 else 2)
     layer_bytes = distinct.mean() * expert_bytes + Hm * E * 2 + T * Hm * 2 + y_bytes + proj_bytes
     local_pairs = np.mean([np.count_nonzero(ids_np[i] < share) for i in range(warmup, n_batches)])
-    layer_flops = 2 * T * Hm * E + 6 * local_pairs * H * I + (4 * T * Hm * H if wl.H_model else 0)
+    layer_flops = (2 * T * Hm * E + 6 * local_pairs * H * I + (4 * T * Hm * H if wl.H_model else 0)
+                   + 6 * T * args.shared * H * I)
     gateup_unit = 2 * nvfp4_bytes(I, H)              # one active expert's gate+up weights
     gateup_bytes = distinct * gateup_unit + T * H * 2 + local_pairs * I * 2
     gateup_avg_ms = float(np.mean(gateup_ms))
@@ -230,7 +243,8 @@ def main():
                                + f"T={T} H={H} I={I} E={E} top-{k}, NVFP4 experts, bf16 activations, fresh tokens "
                                f"every step",
                    "T": T, "H": H, "I": I, "E": E, "k": k, "H_model": wl.H_model, "zipf_beta": wl.beta,
-                   "seed": wl.seed, "expert_share": f"experts 0..{share - 1} of {E}" if args.ep > 1 else None},
+                   "seed": wl.seed, "expert_share": f"experts 0..{share - 1} of {E}" if args.ep > 1 else None,
+                   "shared_experts": args.shared},
         "roofline": roofline,
         "layer": {"algorithmic_bytes": int(layer_bytes), "hbm_GBps": round(layer_bytes / (ms_per_step * 1e-3) / 1e9, 1),
                   "hbm_frac": round(layer_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -271,7 +285,7 @@ def main():
         out["graph_ms_per_step"] = round(a.elapsed_time(b) / n_graph, 5)
         del graph
 
-    if not args.no_cpu_baseline and args.ep == 1:
+    if not args.no_cpu_baseline and args.ep == 1 and not args.shared:
         n_tok = args.cpu_tokens or (8 if T <= 16 else 4)
         out["cpu_baseline"] = cpu_baseline(wl, n_tok, first_token=warmup * T)
     print(json.dumps(out))

@@ -154,6 +154,35 @@ moe_status moe_expert_ffn(moe_dims d, const void* x, const int32_t* expert_offse
 moe_status moe_layer(moe_dims d, const void* x, const void* w_router, const float* bias, const moe_experts* w,
                      void* y, int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes, void* stream);
 
+/* ---- shared experts ------------------------------------------------------------
+ * wpnews.pro, "Serving Kimi K3 End to End", section 3.3: every token also
+ * uses the model's 2 shared experts, whose output joins the MoE layer's sum;
+ * "Serving Kimi-K3 ... with 8xB300 GPUs", "Precision: what is stored in which
+ * format": they are kept in bf16.  Each shared expert s is a dense SwiGLU
+ * FFN of intermediate width I: g, u = x . Wgu (columns 2sI .. 2sI+I-1 and
+ * 2sI+I .. 2sI+2I-1), h = bf16(SiLU(g) * u) (g, u accumulated in fp32),
+ * out_s = h . Wd (rows sI .. sI+I-1), accumulated in fp32. */
+typedef struct {
+  int32_t count;          /* shared experts (K3: 2), >= 1 */
+  int32_t I;              /* intermediate width of each: a positive multiple of 256 */
+  const void* w_gate_up;  /* [H][count*2*I] bf16, device, input-major */
+  const void* w_down;     /* [count*I][H] bf16, device, input-major */
+} moe_shared;
+
+/* Workspace of moe_layer_shared (0 for invalid dims or shared experts). */
+size_t moe_layer_shared_workspace_bytes(moe_dims d, const moe_shared* shared);
+
+/* moe_layer plus the shared experts (device pointers as moe_layer; shared
+ * is host memory read during the call):
+ *   y[t] = bf16( sum_j topk_w[t][j] * FFN_{topk_ids[t][j]}(x[t]) + sum_s out_s(x[t]) ),
+ * the routed sum in fp32 over ascending j, then the shared experts' fp32
+ * output, rounded once.  MOE_KERNEL_SHARED times the shared experts' launches.
+ * Errors as moe_layer, plus MOE_ERR_ARG (NULL shared or weights) and
+ * MOE_ERR_SHAPE (count < 1 or I not a positive multiple of 256). */
+moe_status moe_layer_shared(moe_dims d, const moe_shared* shared, const void* x, const void* w_router,
+                            const float* bias, const moe_experts* w, void* y, int32_t* topk_ids_out, float* topk_w_out,
+                            void* ws, size_t ws_bytes, void* stream);
+
 /* ---- one share of the experts (expert parallelism) ---------------------------
  * al-engr.com Kimi-K3 plan, section "What has to be built - and the
  * discovery that changed it": splitting one model's experts across devices
@@ -239,7 +268,8 @@ typedef enum {
   MOE_KERNEL_DOWN = 5,    /* grouped down GEMM                           */
   MOE_KERNEL_COMBINE = 6, /* weighted un-permute and sum                 */
   MOE_KERNEL_PROJECT = 7, /* latent block: one bf16 projection            */
-  MOE_KERNEL_COUNT = 8
+  MOE_KERNEL_SHARED = 8,  /* shared experts: gate/up + SwiGLU, then down  */
+  MOE_KERNEL_COUNT = 9
 } moe_kernel;
 
 /* Timing of one kernel's launches made by the calling thread.

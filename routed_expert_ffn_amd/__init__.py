@@ -15,12 +15,13 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 MOE_OK = 0
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_ARG", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_ALIGN", 4: "MOE_ERR_WORKSPACE",
                 5: "MOE_ERR_HIP"}
-KERNELS = {"router": 0, "topk": 1, "permute": 2, "cast": 3, "gateup": 4, "down": 5, "combine": 6, "project": 7}
+KERNELS = {"router": 0, "topk": 1, "permute": 2, "cast": 3, "gateup": 4, "down": 5, "combine": 6, "project": 7,
+           "shared": 8}
 # Symbols include/moe.h declares.
 EXPORTS = ("moe_workspace_bytes", "moe_quantize_workspace_bytes", "moe_quantize_nvfp4", "moe_route",
            "moe_expert_ffn", "moe_layer", "moe_status_string", "moe_last_error", "moe_profile_arm",
            "moe_profile_read", "moe_stream_read", "moe_latent_workspace_bytes", "moe_latent_layer",
-           "moe_expert_ffn_share", "moe_layer_share")
+           "moe_expert_ffn_share", "moe_layer_share", "moe_layer_shared_workspace_bytes", "moe_layer_shared")
 # MOE_STREAM_SINK_WORDS of moe.h
 STREAM_SINK_WORDS = 4096
 
@@ -46,6 +47,11 @@ class Experts(ctypes.Structure):
 
 class Share(ctypes.Structure):
     _fields_ = [("base", ctypes.c_int32), ("count", ctypes.c_int32)]
+
+
+class Shared(ctypes.Structure):
+    _fields_ = [("count", ctypes.c_int32), ("I", ctypes.c_int32), ("w_gate_up", ctypes.c_void_p),
+                ("w_down", ctypes.c_void_p)]
 
 
 class Latent(ctypes.Structure):
@@ -81,6 +87,11 @@ def lib():
         L.moe_layer_share.restype = ctypes.c_int
         L.moe_layer_share.argtypes = [Dims, Share, _p, _p, _p, ctypes.POINTER(Experts), _p, _p, _p, _p, _p,
                                       ctypes.c_size_t, _p]
+        L.moe_layer_shared_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_layer_shared_workspace_bytes.argtypes = [Dims, ctypes.POINTER(Shared)]
+        L.moe_layer_shared.restype = ctypes.c_int
+        L.moe_layer_shared.argtypes = [Dims, ctypes.POINTER(Shared), _p, _p, _p, ctypes.POINTER(Experts), _p, _p, _p, _p,
+                                       ctypes.c_size_t, _p]
         L.moe_latent_workspace_bytes.restype = ctypes.c_size_t
         L.moe_latent_workspace_bytes.argtypes = [Dims, ctypes.c_int32]
         L.moe_latent_layer.restype = ctypes.c_int
@@ -178,6 +189,20 @@ def moe_layer_share(d, base, count, x, w_router, bias, experts, y_partial, serve
     _check(lib().moe_layer_share(d, Share(int(base), int(count)), _ptr(x), _ptr(w_router), _ptr(bias),
                                  ctypes.byref(experts.c()), _ptr(y_partial), _ptr(served), _ptr(topk_ids_out),
                                  _ptr(topk_w_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_layer_shared_workspace_bytes(d, count, I):
+    return lib().moe_layer_shared_workspace_bytes(d, ctypes.byref(Shared(int(count), int(I), None, None)))
+
+
+def moe_layer_shared(d, count, I, w_gate_up, w_down, x, w_router, bias, experts, y, topk_ids_out, topk_w_out, ws,
+                     stream=None):
+    """moe_layer plus `count` bf16 shared experts of width I (moe.h:
+    moe_layer_shared); w_gate_up [H][count*2I], w_down [count*I][H]."""
+    sh = Shared(int(count), int(I), _ptr(w_gate_up), _ptr(w_down))
+    _check(lib().moe_layer_shared(d, ctypes.byref(sh), _ptr(x), _ptr(w_router), _ptr(bias), ctypes.byref(experts.c()),
+                                  _ptr(y), _ptr(topk_ids_out), _ptr(topk_w_out), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def moe_latent_workspace_bytes(d, H_model):

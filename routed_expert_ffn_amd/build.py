@@ -12,7 +12,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["api.hip", "kernels_route.hip", "kernels_ffn.hip", "kernels_quant.hip", "kernels_stream.hip",
-           "kernels_latent.hip"]
+           "kernels_dense.hip"]
 # Packed-fp32 instructions are kept out of the device code on purpose.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

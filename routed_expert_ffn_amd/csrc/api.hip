@@ -119,6 +119,41 @@ LatentLayout latent_layout(const moe_dims& d, int Hm) {
   return LL;
 }
 
+// moe_layer_shared: moe_layer's regions, then the shared experts' gate/up
+// partials, their hidden layer and their down partials.
+struct SharedLayout {
+  Layout base;
+  size_t gupart, h, dpart, total;
+  int gu_slabs, d_slabs;
+};
+
+SharedLayout shared_layout(const moe_dims& d, const moe_shared& sh) {
+  SharedLayout SL;
+  SL.base = layout(d);
+  size_t o = SL.base.total;
+  auto take = [&](size_t bytes) {
+    size_t r = o;
+    o += align256(bytes);
+    return r;
+  };
+  const int width = sh.count * sh.I;
+  const size_t T = (size_t)d.T;
+  SL.gu_slabs = moe::router_plan(d.T, d.H, 2 * width).slabs;
+  SL.d_slabs = moe::router_plan(d.T, width, d.H).slabs;
+  SL.gupart = take((size_t)SL.gu_slabs * T * 2 * width * 4);
+  SL.h = take(T * width * 2);
+  SL.dpart = take((size_t)SL.d_slabs * T * d.H * 4);
+  SL.total = o;
+  return SL;
+}
+
+moe_status check_shared(const moe_shared* sh) {
+  if (!sh) return fail(MOE_ERR_ARG, "shared is NULL");
+  if (sh->count < 1 || sh->count > 64) return fail(MOE_ERR_SHAPE, "shared count = %d must be in [1, 64]", sh->count);
+  if (sh->I <= 0 || sh->I % 256) return fail(MOE_ERR_SHAPE, "shared I = %d must be a positive multiple of 256", sh->I);
+  return MOE_OK;
+}
+
 moe_status check_latent_width(int Hm) {
   if (Hm <= 0 || Hm % 256) return fail(MOE_ERR_SHAPE, "H_model = %d must be a positive multiple of 256", Hm);
   return MOE_OK;
@@ -397,6 +432,59 @@ moe_status moe_layer(moe_dims d, const void* x, const void* w_router, const floa
   TRY(enqueue_ffn(d, offsets, sorted, w, rows, ws, s));
   LAUNCH(MOE_KERNEL_COMBINE, s,
          moe::launch_combine(rows, pos, wts, d.T, d.H, d.k, static_cast<uint16_t*>(y), s), "combine");
+  return MOE_OK;
+}
+
+size_t moe_layer_shared_workspace_bytes(moe_dims d, const moe_shared* shared) {
+  if (check_dims(d) != MOE_OK || check_shared(shared) != MOE_OK) return 0;
+  return shared_layout(d, *shared).total;
+}
+
+moe_status moe_layer_shared(moe_dims d, const moe_shared* shared, const void* x, const void* w_router,
+                            const float* bias, const moe_experts* w, void* y, int32_t* topk_ids_out, float* topk_w_out,
+                            void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_dims(d));
+  TRY(check_shared(shared));
+  if (d.T == 0) return MOE_OK;
+  TRY(check_ptr(shared->w_gate_up, "shared w_gate_up"));
+  TRY(check_ptr(shared->w_down, "shared w_down"));
+  TRY(check_ptr(x, "x"));
+  TRY(check_ptr(w_router, "w_router"));
+  TRY(check_ptr(bias, "bias", false));
+  TRY(check_experts(w));
+  TRY(check_ptr(y, "y"));
+  TRY(check_ptr(topk_ids_out, "topk_ids_out", false));
+  TRY(check_ptr(topk_w_out, "topk_w_out", false));
+  const SharedLayout SL = shared_layout(d, *shared);
+  if (!ws) return fail(MOE_ERR_ARG, "workspace is NULL");
+  if (!aligned16(ws)) return fail(MOE_ERR_ALIGN, "workspace is not 16-byte aligned");
+  if (ws_bytes < SL.total) return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, SL.total);
+  const Layout& L = SL.base;
+  hipStream_t s = (hipStream_t)stream;
+  const int T = d.T, H = d.H, width = shared->count * shared->I;
+  int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, L.ids);
+  float* wts = topk_w_out ? topk_w_out : at<float>(ws, L.w);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* sorted = at<int32_t>(ws, L.sorted);
+  int32_t* pos = at<int32_t>(ws, L.pos);
+  float* rows = at<float>(ws, L.rows);
+  uint16_t* h = at<uint16_t>(ws, SL.h);
+  float* dpart = at<float>(ws, SL.dpart);
+  TRY(enqueue_route(d, x, w_router, bias, at<float>(ws, L.logits), ids, wts, offsets, sorted, pos, ws,
+                    at<f16>(ws, L.x16), s));
+  TRY(enqueue_ffn(d, offsets, sorted, w, rows, ws, s));
+  // the shared experts on every token: hidden layer, then the down partials
+  LAUNCH(MOE_KERNEL_SHARED, s,
+         moe::launch_shared_hidden(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(shared->w_gate_up),
+                                   at<float>(ws, SL.gupart), T, H, shared->count, shared->I,
+                                   moe::router_plan(T, H, 2 * width), h, s),
+         "shared experts, gate/up");
+  LAUNCH(MOE_KERNEL_SHARED, s,
+         moe::launch_router(h, static_cast<const uint16_t*>(shared->w_down), dpart, T, width, H,
+                            moe::router_plan(T, width, H), s),
+         "shared experts, down");
+  LAUNCH(MOE_KERNEL_COMBINE, s,
+         moe::launch_combine(rows, pos, wts, T, H, d.k, static_cast<uint16_t*>(y), s, dpart, SL.d_slabs), "combine");
   return MOE_OK;
 }
 

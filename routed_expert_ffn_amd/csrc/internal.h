@@ -78,8 +78,9 @@ struct FfnArgs {
 };
 hipError_t launch_gateup(const FfnArgs& a, hipStream_t s);
 hipError_t launch_down(const FfnArgs& a, hipStream_t s);
+// add (may be NULL): add_slabs fp32 partials [T][H] added after the routed sum.
 hipError_t launch_combine(const float* rows, const int32_t* pair_pos, const float* w, int T, int H, int k,
-                          uint16_t* y, hipStream_t s);
+                          uint16_t* y, hipStream_t s, const float* add = nullptr, int add_slabs = 0);
 // One share of the experts: only records whose expert is in [lo, hi) are
 // summed, into fp32 partial outputs; served[t*k+j] (may be NULL) = 1 for
 // those records, 0 for the others.
@@ -95,6 +96,11 @@ hipError_t launch_stream_read(const void* buf, long long bytes, uint32_t* sink, 
 // out16 is non-NULL, its fp16 copy; part holds rp.slabs * T * N fp32.
 hipError_t launch_projection(const uint16_t* x, const uint16_t* w, float* part, int T, int K, int N,
                              const RouterPlan& rp, uint16_t* out, f16* out16, hipStream_t s);
+
+// Shared experts' hidden layer: h [T][count*I] bf16 from x [T][H] and the
+// gate/up weights [H][count*2I]; part holds rp.slabs * T * 2*count*I fp32.
+hipError_t launch_shared_hidden(const uint16_t* x, const uint16_t* w_gate_up, float* part, int T, int H, int count,
+                                int I, const RouterPlan& rp, uint16_t* h, hipStream_t s);
 
 hipError_t launch_quantize(const float* w, int64_t N, int64_t K, uint8_t* q, uint8_t* sf, float* gs, uint32_t* ws,
                            hipStream_t s);

@@ -727,15 +727,18 @@ hipError_t launch_big(const FfnArgs& a, const GroupedParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// y[t][n] = bf16( sum_j w[t][j] * rows[pair_pos[t*k+j]][n] ), fp32 sum over
-// ascending j.  A thread takes four columns; the positions and weights of 16
-// records, then their 16 row loads, are issued together before the sums.
+// y[t][n] = bf16( sum_j w[t][j] * rows[pair_pos[t*k+j]][n] (+ add) ), fp32
+// sum over ascending j, then (when add is given) the add_slabs partials
+// add[s][t][n] in order: the shared experts' output.  A thread takes four
+// columns; the positions and weights of 16 records, then their 16 row loads,
+// are issued together before the sums.
 constexpr int COMBINE_JB = 16;
 
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ rows,
                                                      const int32_t* __restrict__ pair_pos,
                                                      const float* __restrict__ w, int H, int k,
-                                                     uint16_t* __restrict__ y) {
+                                                     uint16_t* __restrict__ y, const float* __restrict__ add,
+                                                     int add_slabs, long long add_stride) {
   const int t = blockIdx.y;
   const int n = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (n >= H) return;
@@ -762,6 +765,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
         a3 = fmaf(wj[u], v[u].w, a3);
       }
   }
+  if (add)
+    for (int s = 0; s < add_slabs; s++) {
+      const float4 v = *reinterpret_cast<const float4*>(add + (size_t)s * add_stride + (size_t)t * H + n);
+      a0 += v.x;
+      a1 += v.y;
+      a2 += v.z;
+      a3 += v.w;
+    }
   uint2 o;
   o.x = (uint32_t)f32_to_bf16(a0) | ((uint32_t)f32_to_bf16(a1) << 16);
   o.y = (uint32_t)f32_to_bf16(a2) | ((uint32_t)f32_to_bf16(a3) << 16);
@@ -886,10 +897,10 @@ hipError_t launch_combine_share(const float* rows, const int32_t* pair_pos, cons
 }
 
 hipError_t launch_combine(const float* rows, const int32_t* pair_pos, const float* w, int T, int H, int k,
-                          uint16_t* y, hipStream_t s) {
+                          uint16_t* y, hipStream_t s, const float* add, int add_slabs) {
   const int threads = T < 64 ? 64 : 256;  // few tokens: spread the columns over more CUs
   hipLaunchKernelGGL(combine_kernel, dim3((H / 4 + threads - 1) / threads, T), dim3(threads), 0, s, rows, pair_pos, w,
-                     H, k, y);
+                     H, k, y, add, add_slabs, (long long)T * H);
   return hipGetLastError();
 }
 

@@ -89,8 +89,9 @@ def expert_f32(seed, e, m, N, K, std=WEIGHT_STD, nthreads=None):
 
 
 def proj_bf16(seed, which, K, N, std=WEIGHT_STD):
-    """Latent projection weights [K][N] bf16 bits: which 0 = routed-down
-    ([H_model][H]), 1 = routed-up ([H][H_model])."""
+    """Dense bf16 weights [K][N] (bits): which 0 = latent routed-down
+    ([H_model][H]), 1 = routed-up ([H][H_model]), 2 = shared experts'
+    gate/up ([H][count*2I]), 3 = their down ([count*I][H])."""
     out = np.empty((K, N), np.uint16)
     cpu().synth_proj_bf16(seed, which, K, N, std, _ptr(out))
     return out

@@ -19,7 +19,7 @@ void synth_router_bf16(uint64_t seed, int H, int E, float std, uint16_t* out) {
 }
 
 void synth_proj_bf16(uint64_t seed, int which, int K, int N, float std, uint16_t* out) {
-  uint64_t key = synth_key(seed, which ? SYNTH_STREAM_PROJ_UP : SYNTH_STREAM_PROJ_DOWN);
+  uint64_t key = synth_key(seed, (uint64_t)SYNTH_STREAM_PROJ_DOWN + (uint64_t)which);
   for (int64_t i = 0; i < (int64_t)K * N; i++)
     out[i] = synth_bf16_rne(std * synth_normal(key, (uint64_t)i));
 }

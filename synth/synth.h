@@ -4,9 +4,10 @@
  * Layouts (all row-major):
  *   x      [T][H]  bf16 bits, N(0,1) approx.; token t uses index (t0+t)*H + h
  *   W_r    [H][E]  bf16 bits, std * N(0,1) rounded to bf16; index h*E + e
- *   P_d,P_u [K][N] bf16 bits, the latent routed-down ([Hm][H]) and routed-up
- *                  ([H][Hm]) projections, std * N(0,1); index k*N + n;
- *                  which = 0 (down) or 1 (up)
+ *   P       [K][N] bf16 bits, std * N(0,1), index k*N + n, dense bf16
+ *                  weights by `which`: 0 the latent routed-down projection
+ *                  [Hm][H], 1 the routed-up projection [H][Hm], 2 the shared
+ *                  experts' gate/up [H][count*2I], 3 their down [count*I][H]
  *   W_e,m  [N][K]  fp32, std * N(0,1); index n*K + k; m = 0 gate, 1 up, 2 down
  *                  (gate/up: N = I, K = H; down: N = H, K = I)
  *   bias   [E]     fp32 expert-popularity bias (CPU only, see synth_zipf_bias)

@@ -34,6 +34,8 @@
 #define SYNTH_STREAM_PERM 3u       /* expert popularity permutation  */
 #define SYNTH_STREAM_PROJ_DOWN 4u  /* routed-down projection [Hm][H] */
 #define SYNTH_STREAM_PROJ_UP 5u    /* routed-up projection [H][Hm]   */
+#define SYNTH_STREAM_SHARED_GU 6u  /* shared experts' gate/up [H][2cI] */
+#define SYNTH_STREAM_SHARED_D 7u   /* shared experts' down [cI][H]    */
 #define SYNTH_STREAM_EXPERT0 16u   /* expert e, matrix m: 16 + 3e + m */
 
 SYNTH_FN uint64_t synth_mix64(uint64_t z) {

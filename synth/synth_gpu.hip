@@ -53,7 +53,7 @@ extern "C" int synth_gpu_proj_bf16(uint64_t seed, int which, int K, int N, float
   int64_t n = (int64_t)K * N;
   if (n <= 0) return 0;
   hipLaunchKernelGGL(k_router, dim3(grid_for(n)), dim3(256), 0, (hipStream_t)stream,
-                     synth_key(seed, which ? SYNTH_STREAM_PROJ_UP : SYNTH_STREAM_PROJ_DOWN), n, std, out);
+                     synth_key(seed, (uint64_t)SYNTH_STREAM_PROJ_DOWN + (uint64_t)which), n, std, out);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -41,6 +41,21 @@ def assert_close(got, ref, what, max_abs=MAX_ABS, rel=REL_L2):
     assert a <= max_abs and r <= rel, f"{what}: max_abs={a:.3e} rel_l2={r:.3e}"
 
 
+def assert_close_bf16_out(got, ref, what):
+    """A bf16 output against the oracle's fp64 value: relative L2 within
+    REL_L2, and each element within MAX_ABS or one bf16 unit of its
+    magnitude, whichever is larger (at |y| >= 4 the output's own rounding to
+    bf16 alone reaches half a unit, 1.6e-2, and one unit past 8 exceeds
+    MAX_ABS)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    unit = np.ldexp(1.0, np.frexp(np.abs(ref))[1] - 8)
+    worst = float(np.max(np.abs(got - ref) / np.maximum(MAX_ABS, unit)))
+    a, r = errors(got, ref)
+    say(f"  {what}: max_abs={a:.3e} (worst {worst:.2f} of its allowance) rel_l2={r:.3e}")
+    assert worst <= 1.0 and r <= REL_L2, f"{what}: worst {worst:.2f}, rel_l2={r:.3e}"
+
+
 def build_store(E, H, I, seed, experts=None):
     """NVFP4 store on the GPU: fp32 weights from the GPU generator, quantised
     by moe_quantize_nvfp4 (experts outside `experts` are left zero)."""

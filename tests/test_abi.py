@@ -109,7 +109,7 @@ def test_profile_arguments_rejected_without_hip():
     created; reading into NULL reports -MOE_ERR_ARG."""
     L = moe.lib()
     assert L.moe_profile_arm(-1, 4) == 1
-    assert L.moe_profile_arm(8, 4) == 1
+    assert L.moe_profile_arm(len(moe.KERNELS), 4) == 1
     assert L.moe_profile_arm(4, 0) == 1
     assert L.moe_profile_arm(4, 65537) == 1
     assert L.moe_profile_read(None, 4) == -1
@@ -158,3 +158,16 @@ def test_share_validation_without_hip():
         assert L.moe_layer_share(d, sh, FAKE, FAKE, None, ctypes.byref(ex), FAKE, None, None, None, FAKE, ws_bytes,
                                  None) == 2
         assert L.moe_expert_ffn_share(d, sh, FAKE, FAKE, FAKE, ctypes.byref(ex), FAKE, FAKE, ws_bytes, None) == 2
+
+
+def test_shared_workspace_and_validation_without_hip():
+    d = moe.dims(8, 512, 256, 64, 8)
+    assert moe.moe_layer_shared_workspace_bytes(d, 2, 256) > moe.moe_workspace_bytes(d)
+    assert moe.moe_layer_shared_workspace_bytes(d, 0, 256) == 0
+    assert moe.moe_layer_shared_workspace_bytes(d, 2, 100) == 0
+    L = moe.lib()
+    ex = moe.Experts()
+    args = (FAKE, FAKE, None, ctypes.byref(ex), FAKE, None, None, FAKE, 1 << 40, None)
+    assert L.moe_layer_shared(d, None, *args) == 1
+    assert L.moe_layer_shared(d, ctypes.byref(moe.Shared(2, 256, None, None)), *args) == 1
+    assert L.moe_layer_shared(d, ctypes.byref(moe.Shared(2, 300, FAKE, FAKE)), *args) == 2

@@ -24,7 +24,7 @@ if torch.cuda.is_available():
     import routed_expert_ffn_amd as moe
     import synth
     from synth.workloads import WORKLOADS, bias_for
-    from tests.gpu_helpers import DEV, MAX_ABS, REL_L2, OracleExperts, build_store, say, to_np
+    from tests.gpu_helpers import DEV, OracleExperts, assert_close_bf16_out, build_store, say, to_np
 
 
 class LatentCase:
@@ -101,13 +101,7 @@ def compare(case, rows, y, z, ids, logits, ex):
                               logits_in=logits[rows], nthreads=16)
     np.testing.assert_array_equal(ids[rows], ref["ids"])
     check_z(z[rows], ref["z"], x, pd)
-    got, want = y[rows], ref["y"]
-    unit = np.ldexp(1.0, np.frexp(np.abs(want))[1] - 8)
-    allowed = np.maximum(MAX_ABS, unit)
-    worst = float(np.max(np.abs(got - want) / allowed))
-    rel = float(np.linalg.norm(got - want) / np.linalg.norm(want))
-    say(f"  y: max_abs={np.abs(got - want).max():.3e} (worst {worst:.2f} of its allowance) rel_l2={rel:.3e}")
-    assert worst <= 1.0 and rel <= REL_L2
+    assert_close_bf16_out(y[rows], ref["y"], "y")
     return ref
 
 
