@@ -145,8 +145,10 @@ moe_status moe_route(moe_dims d, const void* x, const void* w_router, const floa
 moe_status moe_expert_ffn(moe_dims d, const void* x, const int32_t* expert_offsets, const int32_t* sorted_pairs,
                           const moe_experts* w, float* rows, void* ws, size_t ws_bytes, void* stream);
 
-/* The whole layer: y[t] = sum_j topk_w[t][j] * FFN_{topk_ids[t][j]}(x[t]),
- * summed in fp32 over ascending j and rounded to bf16 (device pointers):
+/* The whole layer: y[t] = sum_j topk_w[t][j] * FFN_{topk_ids[t][j]}(x[t]):
+ * each weighted term is stored in fp16 (|term| < 65504), the terms are
+ * summed in fp32 over ascending j and the sum is rounded to bf16 (device
+ * pointers):
  *   x [T][H] bf16, w_router [H][E] bf16, bias [E] fp32 or NULL,
  *   y [T][H] bf16 output,
  *   topk_ids_out [T][k] int32 / topk_w_out [T][k] fp32: optional copies of

@@ -242,7 +242,8 @@ moe_status enqueue_route(const moe_dims& d, const void* x, const void* wr, const
 // Enqueue the two grouped GEMMs (x16, the active list and the permutation
 // are already in place).
 moe_status enqueue_ffn(const moe_dims& d, const int32_t* offsets, const int32_t* sorted, const moe_experts* w,
-                       float* rows, void* ws, hipStream_t s, int e_base = 0) {
+                       float* rows, void* ws, hipStream_t s, int e_base = 0, f16* rows16 = nullptr,
+                       const float* pair_w = nullptr) {
   const Layout L = layout(d);
   moe::FfnArgs a;
   a.T = d.T;
@@ -263,6 +264,8 @@ moe_status enqueue_ffn(const moe_dims& d, const int32_t* offsets, const int32_t*
   a.w = w;
   a.h = at<f16>(ws, L.h);
   a.rows = rows;
+  a.rows16 = rows16;
+  a.pair_w = pair_w;
   LAUNCH(MOE_KERNEL_GATEUP, s, moe::launch_gateup(a, s), "gate/up");
   LAUNCH(MOE_KERNEL_DOWN, s, moe::launch_down(a, s), "down");
   return MOE_OK;
@@ -429,9 +432,11 @@ moe_status moe_layer(moe_dims d, const void* x, const void* w_router, const floa
   float* rows = at<float>(ws, L.rows);
   TRY(enqueue_route(d, x, w_router, bias, at<float>(ws, L.logits), ids, wts, offsets, sorted, pos, ws,
                     at<f16>(ws, L.x16), s));
-  TRY(enqueue_ffn(d, offsets, sorted, w, rows, ws, s));
-  LAUNCH(MOE_KERNEL_COMBINE, s,
-         moe::launch_combine(rows, pos, wts, d.T, d.H, d.k, static_cast<uint16_t*>(y), s), "combine");
+  // the down GEMM writes each record's row times its routing weight in fp16
+  f16* rows16 = at<f16>(ws, L.rows);
+  TRY(enqueue_ffn(d, offsets, sorted, w, rows, ws, s, 0, rows16, wts));
+  LAUNCH(MOE_KERNEL_COMBINE, s, moe::launch_combine16(rows16, pos, d.T, d.H, d.k, static_cast<uint16_t*>(y), s),
+         "combine");
   return MOE_OK;
 }
 
@@ -472,7 +477,8 @@ moe_status moe_layer_shared(moe_dims d, const moe_shared* shared, const void* x,
   float* dpart = at<float>(ws, SL.dpart);
   TRY(enqueue_route(d, x, w_router, bias, at<float>(ws, L.logits), ids, wts, offsets, sorted, pos, ws,
                     at<f16>(ws, L.x16), s));
-  TRY(enqueue_ffn(d, offsets, sorted, w, rows, ws, s));
+  f16* rows16 = at<f16>(ws, L.rows);
+  TRY(enqueue_ffn(d, offsets, sorted, w, rows, ws, s, 0, rows16, wts));
   // the shared experts on every token: hidden layer, then the down partials
   LAUNCH(MOE_KERNEL_SHARED, s,
          moe::launch_shared_hidden(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(shared->w_gate_up),
@@ -484,7 +490,7 @@ moe_status moe_layer_shared(moe_dims d, const moe_shared* shared, const void* x,
                             moe::router_plan(T, width, H), s),
          "shared experts, down");
   LAUNCH(MOE_KERNEL_COMBINE, s,
-         moe::launch_combine(rows, pos, wts, T, H, d.k, static_cast<uint16_t*>(y), s, dpart, SL.d_slabs), "combine");
+         moe::launch_combine16(rows16, pos, T, H, d.k, static_cast<uint16_t*>(y), s, dpart, SL.d_slabs), "combine");
   return MOE_OK;
 }
 
@@ -555,8 +561,9 @@ moe_status moe_latent_layer(moe_dims d, const moe_latent* lat, const void* x, co
            "permute");
   }
   float* rows = at<float>(ws, L.rows);
-  TRY(enqueue_ffn(d, offsets, sorted, w, rows, ws, s));
-  LAUNCH(MOE_KERNEL_COMBINE, s, moe::launch_combine(rows, pos, wts, T, H, k, ylat, s), "combine");
+  f16* rows16 = at<f16>(ws, L.rows);
+  TRY(enqueue_ffn(d, offsets, sorted, w, rows, ws, s, 0, rows16, wts));
+  LAUNCH(MOE_KERNEL_COMBINE, s, moe::launch_combine16(rows16, pos, T, H, k, ylat, s), "combine");
   // routed-up projection back to the hidden width
   LAUNCH(MOE_KERNEL_PROJECT, s,
          moe::launch_projection(ylat, static_cast<const uint16_t*>(lat->w_up), ppart, T, H, Hm,

@@ -74,13 +74,17 @@ struct FfnArgs {
   int max_mtiles;                 // grid bound on the entries
   const moe_experts* w;
   f16* h;                         // [P][I]
-  float* rows;                    // [P][H]
+  float* rows;                    // [P][H] fp32, unweighted (when rows16 is NULL)
+  f16* rows16;                    // or [P][H] fp16, times the record's routing weight
+  const float* pair_w;            // routing weights [T*k] for rows16
 };
 hipError_t launch_gateup(const FfnArgs& a, hipStream_t s);
 hipError_t launch_down(const FfnArgs& a, hipStream_t s);
-// add (may be NULL): add_slabs fp32 partials [T][H] added after the routed sum.
-hipError_t launch_combine(const float* rows, const int32_t* pair_pos, const float* w, int T, int H, int k,
-                          uint16_t* y, hipStream_t s, const float* add = nullptr, int add_slabs = 0);
+// Combine of weighted fp16 rows: y = bf16(sum_j rows16[pos(t,j)] (+ add)),
+// add (may be NULL) being add_slabs fp32 partials [T][H] summed after the
+// records (the shared experts' output).
+hipError_t launch_combine16(const f16* rows, const int32_t* pair_pos, int T, int H, int k, uint16_t* y, hipStream_t s,
+                            const float* add = nullptr, int add_slabs = 0);
 // One share of the experts: only records whose expert is in [lo, hi) are
 // summed, into fp32 partial outputs; served[t*k+j] (may be NULL) = 1 for
 // those records, 0 for the others.

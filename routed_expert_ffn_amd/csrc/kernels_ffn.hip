@@ -49,7 +49,9 @@ struct GroupedParams {
   const uint8_t* sf1;
   const float* gs1;
   f16* h;              // gate/up output [P][I]
-  float* rows;         // down output [P][H]
+  float* rows;         // down output [P][H], fp32 unweighted (when rows16 is NULL)
+  f16* rows16;         // or: down output [P][H] fp16, each row times its routing weight
+  const float* pair_w; //     the routing weights [T*k], indexed by record (sorted_pairs[p])
 };
 
 // One 256-k chunk of a wavefront's operands: per weight row group ng, 32
@@ -226,6 +228,11 @@ __global__ __launch_bounds__(FFN_THREADS, WAVES_PER_EU) void expert_gemm_kernel(
                 const float hv = silu(gsa * acc[f][cp][i]) * (gsb * acc[f][cp + 2][i]);
                 p.h[(size_t)(mb + m) * N + tile * 32 + 16 * cp + r] = (f16)hv;
               }
+            } else if (p.rows16) {
+              const float ws = p.pair_w[p.sorted_pairs[mb + m]] * gsa;
+#pragma unroll
+              for (int ng = 0; ng < 4; ng++)
+                p.rows16[(size_t)(mb + m) * N + tile * 64 + 16 * ng + r] = (f16)(ws * acc[f][ng][i]);
             } else {
 #pragma unroll
               for (int ng = 0; ng < 4; ng++) p.rows[(size_t)(mb + m) * N + tile * 64 + 16 * ng + r] = gsa * acc[f][ng][i];
@@ -302,7 +309,8 @@ constexpr int BIG_OFF_A = 0;                                        // [3][224][
 constexpr int BIG_OFF_RQ = BIG_OFF_A + 3 * BIG_TILE_BYTES;          // [2][256][128] u8
 constexpr int BIG_OFF_RS = BIG_OFF_RQ + 2 * BIG_SPANQ_BYTES;        // [2][256][16] u8
 constexpr int BIG_OFF_ROW = BIG_OFF_RS + 2 * BIG_SPANS_BYTES;       // [224] i32
-constexpr int BIG_LDS = BIG_OFF_ROW + BIG_M * 4;
+constexpr int BIG_OFF_RW = BIG_OFF_ROW + BIG_M * 4;                 // [224] f32 routing weights (down, fp16 rows)
+constexpr int BIG_LDS = BIG_OFF_RW + BIG_M * 4;
 static_assert(BIG_LDS <= 160 * 1024, "LDS budget of one CU");
 
 struct BigParams {
@@ -643,15 +651,25 @@ __device__ __forceinline__ void big_tile(const GroupedParams& p, const BigTile& 
           *reinterpret_cast<f16x4*>(p.h + (size_t)(t.mb + m) * t.N + t.rtile * (BIG_N / 2) + 32 * wv + n4) = o;
         }
       } else {
+        // fp16 rows carry the routing weight of their record
+        const float ws = p.rows16 ? reinterpret_cast<const float*>(smem + BIG_OFF_RW)[min(m, BIG_M - 1)] : 1.0f;
 #pragma unroll
         for (int nf = 0; nf < 2; nf++) {
           float v[4];
 #pragma unroll
           for (int r = 0; r < 4; r++) v[r] = gsa * acc[f][nf][4 * q4 + r];
           quad_transpose(v);
-          if (m < t.nvalid)
-            *reinterpret_cast<float4*>(p.rows + (size_t)(t.mb + m) * t.N + t.rtile * BIG_N + 64 * wv + 32 * nf + n4) =
-                make_float4(v[0], v[1], v[2], v[3]);
+          if (m < t.nvalid) {
+            const size_t at = (size_t)(t.mb + m) * t.N + t.rtile * BIG_N + 64 * wv + 32 * nf + n4;
+            if (p.rows16) {
+              f16x4 o;
+#pragma unroll
+              for (int r = 0; r < 4; r++) o[r] = (f16)(ws * v[r]);
+              *reinterpret_cast<f16x4*>(p.rows16 + at) = o;
+            } else {
+              *reinterpret_cast<float4*>(p.rows + at) = make_float4(v[0], v[1], v[2], v[3]);
+            }
+          }
         }
       }
     }
@@ -684,6 +702,7 @@ __global__ __launch_bounds__(BIG_THREADS, 1) void expert_gemm_big_kernel(BigPara
   for (int m = threadIdx.x; m < BIG_M; m += BIG_THREADS) {
     const int pp = t.mb + min(m, t.nvalid - 1);
     rowoff[m] = GATEUP ? p.sorted_pairs[pp] / p.k : pp;
+    if (!GATEUP && p.rows16) reinterpret_cast<float*>(big_smem + BIG_OFF_RW)[m] = p.pair_w[p.sorted_pairs[pp]];
   }
   __syncthreads();
   switch ((t.nvalid + 31) / 32) {  // token fragments, 1 .. 7
@@ -727,42 +746,38 @@ hipError_t launch_big(const FfnArgs& a, const GroupedParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// y[t][n] = bf16( sum_j w[t][j] * rows[pair_pos[t*k+j]][n] (+ add) ), fp32
-// sum over ascending j, then (when add is given) the add_slabs partials
-// add[s][t][n] in order: the shared experts' output.  A thread takes four
-// columns; the positions and weights of 16 records, then their 16 row loads,
-// are issued together before the sums.
+// Combine: the positions (and weights) of 16 records, then their 16 row
+// loads, are issued together before the sums.
 constexpr int COMBINE_JB = 16;
 
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ rows,
-                                                     const int32_t* __restrict__ pair_pos,
-                                                     const float* __restrict__ w, int H, int k,
-                                                     uint16_t* __restrict__ y, const float* __restrict__ add,
-                                                     int add_slabs, long long add_stride) {
+// y[t][n] = bf16( sum_j rows16[pair_pos[t*k+j]][n] (+ add) ): the rows
+// already carry their routing weights; fp32 sum over ascending j, then the
+// add_slabs partials in order.  Four columns per thread, 16 records' loads
+// issued together.
+__global__ __launch_bounds__(256) void combine16_kernel(const f16* __restrict__ rows, const int32_t* __restrict__ pair_pos,
+                                                       int H, int k, uint16_t* __restrict__ y,
+                                                       const float* __restrict__ add, int add_slabs,
+                                                       long long add_stride) {
+  typedef _Float16 h4 __attribute__((ext_vector_type(4)));
   const int t = blockIdx.y;
   const int n = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (n >= H) return;
   float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
   for (int j0 = 0; j0 < k; j0 += COMBINE_JB) {
     int pos[COMBINE_JB];
-    float wj[COMBINE_JB];
 #pragma unroll
-    for (int u = 0; u < COMBINE_JB; u++) {
-      const bool ok = j0 + u < k;
-      pos[u] = ok ? pair_pos[(size_t)t * k + j0 + u] : 0;
-      wj[u] = ok ? w[(size_t)t * k + j0 + u] : 0.0f;
-    }
-    float4 v[COMBINE_JB];
+    for (int u = 0; u < COMBINE_JB; u++) pos[u] = j0 + u < k ? pair_pos[(size_t)t * k + j0 + u] : 0;
+    h4 v[COMBINE_JB];
 #pragma unroll
     for (int u = 0; u < COMBINE_JB; u++)
-      v[u] = j0 + u < k ? *reinterpret_cast<const float4*>(rows + (size_t)pos[u] * H + n) : make_float4(0, 0, 0, 0);
+      v[u] = j0 + u < k ? *reinterpret_cast<const h4*>(rows + (size_t)pos[u] * H + n) : h4{};
 #pragma unroll
     for (int u = 0; u < COMBINE_JB; u++)
       if (j0 + u < k) {
-        a0 = fmaf(wj[u], v[u].x, a0);
-        a1 = fmaf(wj[u], v[u].y, a1);
-        a2 = fmaf(wj[u], v[u].z, a2);
-        a3 = fmaf(wj[u], v[u].w, a3);
+        a0 += (float)v[u][0];
+        a1 += (float)v[u][1];
+        a2 += (float)v[u][2];
+        a3 += (float)v[u][3];
       }
   }
   if (add)
@@ -779,7 +794,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   *reinterpret_cast<uint2*>(y + (size_t)t * H + n) = o;
 }
 
-// One share of the experts ([lo, hi)): as combine_kernel, but only records
+// One share of the experts ([lo, hi)): fp32 unweighted rows; only records
 // whose expert lies in the share are summed, in ascending j, into fp32
 // partial outputs, and block 0 of each token writes which records it
 // served.  The partials of shares that partition the experts add up to the
@@ -830,6 +845,8 @@ GroupedParams base_params(const FfnArgs& a) {
   p.n_active = a.n_active;
   p.h = a.h;
   p.rows = a.rows;
+  p.rows16 = a.rows16;
+  p.pair_w = a.pair_w;
   return p;
 }
 
@@ -888,6 +905,14 @@ hipError_t launch_down(const FfnArgs& a, hipStream_t s) {
   return launch_gemm<DN_KSPLIT, false>(p, pick_mf(a.T), grid, s);
 }
 
+hipError_t launch_combine16(const f16* rows, const int32_t* pair_pos, int T, int H, int k, uint16_t* y, hipStream_t s,
+                            const float* add, int add_slabs) {
+  const int threads = T < 64 ? 64 : 256;
+  hipLaunchKernelGGL(combine16_kernel, dim3((H / 4 + threads - 1) / threads, T), dim3(threads), 0, s, rows, pair_pos, H,
+                     k, y, add, add_slabs, (long long)T * H);
+  return hipGetLastError();
+}
+
 hipError_t launch_combine_share(const float* rows, const int32_t* pair_pos, const float* w, const int32_t* ids,
                                 int lo, int hi, int T, int H, int k, float* y, uint8_t* served, hipStream_t s) {
   const int threads = T < 64 ? 64 : 256;
@@ -896,12 +921,5 @@ hipError_t launch_combine_share(const float* rows, const int32_t* pair_pos, cons
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const float* rows, const int32_t* pair_pos, const float* w, int T, int H, int k,
-                          uint16_t* y, hipStream_t s, const float* add, int add_slabs) {
-  const int threads = T < 64 ? 64 : 256;  // few tokens: spread the columns over more CUs
-  hipLaunchKernelGGL(combine_kernel, dim3((H / 4 + threads - 1) / threads, T), dim3(threads), 0, s, rows, pair_pos, w,
-                     H, k, y, add, add_slabs, (long long)T * H);
-  return hipGetLastError();
-}
 
 }  // namespace moe
