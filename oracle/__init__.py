@@ -53,6 +53,12 @@ def lib():
         L.oracle_moe_layer.restype = ctypes.c_int
         L.oracle_moe_layer.argtypes = [_p, _c_i64, _c_i64, _c_i64, _p, _p, _p, _c_i64, ctypes.c_int, _p,
                                        ctypes.c_int, _p, _p, _p, _p, _p, _p, _p, _p]
+        L.oracle_e8m0_value.restype = ctypes.c_double
+        L.oracle_e8m0_value.argtypes = [ctypes.c_uint8]
+        L.oracle_mxfp4_quantize.restype = None
+        L.oracle_mxfp4_quantize.argtypes = [_p, _c_i64, _c_i64, _p, _p]
+        L.oracle_mxfp4_dequantize.restype = None
+        L.oracle_mxfp4_dequantize.argtypes = [_p, _p, _c_i64, _c_i64, _p]
         L.oracle_round_bf16.restype = None
         L.oracle_round_bf16.argtypes = [_p, _c_i64, _p]
         L.oracle_bf16_matmul.restype = None
@@ -157,7 +163,8 @@ def swiglu_token(gate, up, down, x_row_bf16):
 
 
 class _Expert(ctypes.Structure):
-    _fields_ = [("q", ctypes.c_void_p * 3), ("sf", ctypes.c_void_p * 3), ("gs", ctypes.c_float * 3)]
+    _fields_ = [("q", ctypes.c_void_p * 3), ("sf", ctypes.c_void_p * 3), ("gs", ctypes.c_float * 3),
+                ("format", ctypes.c_int32)]
 
 
 def moe_layer(x_bf16, experts, E, k, wr_bf16=None, bias=None, logits_in=None, nthreads=1, want_rows=False):
@@ -178,6 +185,7 @@ def moe_layer(x_bf16, experts, E, k, wr_bf16=None, bias=None, logits_in=None, nt
             s.q[m] = q.ctypes.data
             s.sf[m] = sf.ctypes.data
             s.gs[m] = float(mats[m].gs)
+        s.format = getattr(mats[0], "format", 0)
         keep.append(s)
         structs[e] = ctypes.pointer(s)
     wr = None if wr_bf16 is None else _c(wr_bf16, np.uint16)
@@ -301,4 +309,39 @@ def layer_with_shared(x_bf16, experts, E, k, w_gate_up_bf16, w_down_bf16, count,
     out["y_routed"] = out["y"]
     out["y_shared"] = shared_experts(x_bf16, w_gate_up_bf16, w_down_bf16, count, I_shared)
     out["y"] = out["y_routed"] + out["y_shared"]
+    return out
+
+
+# ---- MXFP4 (oracle.h: "MXFP4 weight store") --------------------------------------
+
+def e8m0_value(s):
+    return lib().oracle_e8m0_value(int(s))
+
+
+class MXFP4:
+    """q [N][K/2] e2m1 codes, sf [N][K/32] e8m0 scales; no per-tensor scale."""
+    format = 1
+    gs = 1.0
+
+    def __init__(self, q, sf):
+        self.q, self.sf = q, sf
+
+    @property
+    def shape(self):
+        return self.q.shape[0], self.q.shape[1] * 2
+
+
+def mxfp4_quantize(w):
+    w = _c(w, np.float32)
+    N, K = w.shape
+    q = np.empty((N, K // 2), np.uint8)
+    sf = np.empty((N, K // 32), np.uint8)
+    lib().oracle_mxfp4_quantize(_ptr(w), N, K, _ptr(q), _ptr(sf))
+    return MXFP4(q, sf)
+
+
+def mxfp4_dequantize(m):
+    N, K = m.shape
+    out = np.empty((N, K), np.float64)
+    lib().oracle_mxfp4_dequantize(_ptr(_c(m.q, np.uint8)), _ptr(_c(m.sf, np.uint8)), N, K, _ptr(out))
     return out

@@ -101,6 +101,49 @@ void oracle_nvfp4_dequantize(const uint8_t* q, const uint8_t* sf, float gs, int6
     }
 }
 
+/* ---- MXFP4 ---------------------------------------------------------------- */
+
+double oracle_e8m0_value(uint8_t s) { return s == 255 ? NAN : ldexp(1.0, (int)s - 127); }
+
+void oracle_mxfp4_quantize(const float* w, int64_t N, int64_t K, uint8_t* q, uint8_t* sf) {
+  memset(q, 0, (size_t)(N * (K / 2)));
+  for (int64_t n = 0; n < N; n++) {
+    for (int64_t b = 0; b < K / 32; b++) {
+      const float* blk = w + n * K + 32 * b;
+      float bmax = 0.0f;
+      for (int i = 0; i < 32; i++) {
+        float a = fabsf(blk[i]);
+        if (a > bmax) bmax = a;
+      }
+      if (bmax == 0.0f) {
+        sf[n * (K / 32) + b] = 0;
+        continue;
+      }
+      int e2;
+      frexp((double)bmax, &e2); /* bmax = m * 2^e2, m in [0.5, 1): floor(log2) = e2 - 1 */
+      int s = (e2 - 1) - 2 + 127;
+      if (s < 0) s = 0;
+      if (s > 254) s = 254;
+      sf[n * (K / 32) + b] = (uint8_t)s;
+      double x = oracle_e8m0_value((uint8_t)s);
+      for (int i = 0; i < 32; i++) {
+        uint8_t code = oracle_e2m1_round(fabs((double)blk[i]) / x);
+        if (blk[i] < 0.0f && code != 0) code |= 8;
+        int64_t k = 32 * b + i;
+        q[n * (K / 2) + k / 2] |= (uint8_t)(code << (4 * (k & 1)));
+      }
+    }
+  }
+}
+
+void oracle_mxfp4_dequantize(const uint8_t* q, const uint8_t* sf, int64_t N, int64_t K, double* w) {
+  for (int64_t n = 0; n < N; n++)
+    for (int64_t k = 0; k < K; k++) {
+      uint8_t code = (q[n * (K / 2) + k / 2] >> (4 * (k & 1))) & 15;
+      w[n * K + k] = oracle_e2m1_value(code) * oracle_e8m0_value(sf[n * (K / 32) + k / 32]);
+    }
+}
+
 /* ---- router -------------------------------------------------------------- */
 
 static double bf16_to_double(uint16_t b) {
@@ -220,9 +263,15 @@ static void* expert_bucket_worker(void* arg) {
       u = (double*)malloc(sizeof(double) * (size_t)(I * H));
       d = (double*)malloc(sizeof(double) * (size_t)(H * I));
     }
-    oracle_nvfp4_dequantize(ex->q[0], ex->sf[0], ex->gs[0], I, H, g);
-    oracle_nvfp4_dequantize(ex->q[1], ex->sf[1], ex->gs[1], I, H, u);
-    oracle_nvfp4_dequantize(ex->q[2], ex->sf[2], ex->gs[2], H, I, d);
+    if (ex->format == 1) {
+      oracle_mxfp4_dequantize(ex->q[0], ex->sf[0], I, H, g);
+      oracle_mxfp4_dequantize(ex->q[1], ex->sf[1], I, H, u);
+      oracle_mxfp4_dequantize(ex->q[2], ex->sf[2], H, I, d);
+    } else {
+      oracle_nvfp4_dequantize(ex->q[0], ex->sf[0], ex->gs[0], I, H, g);
+      oracle_nvfp4_dequantize(ex->q[1], ex->sf[1], ex->gs[1], I, H, u);
+      oracle_nvfp4_dequantize(ex->q[2], ex->sf[2], ex->gs[2], H, I, d);
+    }
     for (int32_t p = begin; p < end; p++) {
       int64_t t = j->sorted_pairs[p] / j->k;
       oracle_swiglu_token(g, u, d, j->x + t * H, H, I, j->rows + (int64_t)p * H);

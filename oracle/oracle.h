@@ -58,6 +58,28 @@ void oracle_nvfp4_quantize(const float* w, int64_t N, int64_t K, uint8_t* q, uin
 /* w[n][k] = e2m1(q) * sigma * gs, exact in fp64. */
 void oracle_nvfp4_dequantize(const uint8_t* q, const uint8_t* sf, float gs, int64_t N, int64_t K, double* w);
 
+/* ---- MXFP4 weight store (the OCP microscaling format) ------------------------
+ * [p2] "Number formats on Blackwell": MXFP4 carries an 8-bit power-of-two
+ * scale per 32 values (Moonshot trained K3's experts in it); the OCP
+ * Microscaling Formats (MX) v1.0 specification defines it: E8M0 scale byte
+ * X = 2^(s - 127) (255 is NaN), elements e2m1.  Layout as NVFP4 but with
+ *   sf [N][K/32]  e8m0 scale of the 32 consecutive k of one row,
+ * and no per-tensor scale.  K must be a multiple of 32. */
+
+/* E8M0 value: 2^(s - 127); s = 255 is NaN. */
+double oracle_e8m0_value(uint8_t s);
+
+/* Quantise, following the specification's conversion: per block, with
+ * amax the largest |w| (fp32), the shared exponent is
+ * floor(log2(amax)) - 2 (2 = the largest e2m1 exponent), clamped to the
+ * E8M0 range; each element is the nearest e2m1 to w / X (ties to the even
+ * code), clamped to 6; a block of zeros gets scale byte 0 and zero codes.
+ * Division by the power of two X is exact. */
+void oracle_mxfp4_quantize(const float* w, int64_t N, int64_t K, uint8_t* q, uint8_t* sf);
+
+/* w[n][k] = e2m1(q) * e8m0(sf), exact in fp64. */
+void oracle_mxfp4_dequantize(const uint8_t* q, const uint8_t* sf, int64_t N, int64_t K, double* w);
+
 /* ---- router -------------------------------------------------------------- */
 /* logits[t][e] = fp32( sum_h x[t][h] * W_r[h][e] + bias[e] ), the sum in fp64
  * over ascending h.  x [T][H] and W_r [H][E] are bf16 bit patterns; bias may
@@ -92,6 +114,7 @@ typedef struct {
   const uint8_t* q[3];
   const uint8_t* sf[3];
   float gs[3];
+  int32_t format; /* 0: NVFP4 (sf e4m3 per 16, gs used); 1: MXFP4 (sf e8m0 per 32, gs unused) */
 } oracle_expert_nvfp4;
 
 /* One token through one expert, weights already dequantised (fp64):

@@ -486,3 +486,100 @@ def test_shared_experts_are_additive_and_vanish():
     plain = oracle.moe_layer(x, ex, E, k, wr_bf16=wr)
     with_zero = oracle.layer_with_shared(x, ex, E, k, wgu, np.zeros_like(wd), 2, I, wr_bf16=wr)
     np.testing.assert_array_equal(with_zero["y"], plain["y"])
+
+
+# ---- MXFP4 (the OCP microscaling format) ----------------------------------------------
+
+def e8m0_torch(codes):
+    with np.errstate(invalid="ignore"):  # code 255 decodes to NaN
+        return torch.tensor(np.asarray(codes, np.uint8)).view(torch.float8_e8m0fnu).float().numpy().astype(np.float64)
+
+
+def _mx_dequant_independent(m):
+    N, K = m.shape
+    codes = np.empty((N, K), np.uint8)
+    codes[:, 0::2] = m.q & 15
+    codes[:, 1::2] = m.q >> 4
+    return np.vectorize(E2M1_TABLE.get)(codes) * np.repeat(e8m0_torch(m.sf), 32, axis=1), codes
+
+
+def test_e8m0_decode_matches_torch():
+    ref = e8m0_torch(np.arange(256))
+    for s in range(256):
+        v = oracle.e8m0_value(s)
+        assert (np.isnan(v) and np.isnan(ref[s])) or v == ref[s], s
+
+
+def test_mxfp4_golden_blocks():
+    """Hand-derived: a block whose largest value is 7 gets X = 2^(2-2) = 1
+    (scale byte 127) and 7 clamps to 6; a block whose largest value is 0.3
+    gets X = 2^(-2-2) (byte 123) and 0.3 / X = 4.8 rounds to 4; a zero
+    block gets byte 0 and zero codes."""
+    w = np.zeros((3, 32), np.float32)
+    w[0, 5] = 7.0
+    w[0, 6] = -1.25  # 1.25 is a tie between 1 and 1.5: even code 1.0
+    w[1, 0] = 0.3
+    w[1, 1] = 0.09375  # 1.5 * 2^-4: exactly code 1.5
+    m = oracle.mxfp4_quantize(w)
+    assert list(m.sf[:, 0]) == [127, 123, 0]
+    deq = oracle.mxfp4_dequantize(m)
+    assert deq[0, 5] == 6.0 and deq[0, 6] == -1.0
+    assert deq[1, 0] == 4 * 2.0 ** -4 and deq[1, 1] == 0.09375
+    assert not deq[2].any()
+
+
+def test_mxfp4_grid_round_trip_is_bit_exact():
+    """Blocks of e2m1 grid values times 2^s whose largest magnitude is 4 or 6
+    times 2^s come back exactly, with scale byte 127 + s."""
+    rng = np.random.default_rng(17)
+    N, K = 8, 256
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    codes = rng.integers(0, 16, (N, K))
+    vals = np.where(codes >= 8, -1, 1) * grid[codes % 8]
+    s = rng.integers(-20, 20, (N, K // 32))
+    for n in range(N):
+        for b in range(K // 32):
+            vals[n, 32 * b] = (4.0 if (n + b) % 2 else 6.0) * (1 if vals[n, 32 * b] >= 0 else -1)
+    w = (vals * np.repeat(2.0 ** s, 32, axis=1)).astype(np.float32)
+    m = oracle.mxfp4_quantize(w)
+    np.testing.assert_array_equal(m.sf, (127 + s).astype(np.uint8))
+    np.testing.assert_array_equal(oracle.mxfp4_dequantize(m), w.astype(np.float64))
+    deq, _ = _mx_dequant_independent(m)
+    np.testing.assert_array_equal(deq, w.astype(np.float64))
+
+
+def test_mxfp4_random_is_nearest_on_grid():
+    """Random weights: each scale is 2^(floor(log2 blockmax) - 2) and each
+    code the nearest e2m1 point to |w| / X (clamped to 6), ties to even."""
+    w = synth.expert_f32(0, 6, 0, 32, 256)
+    m = oracle.mxfp4_quantize(w)
+    bmax = np.abs(w).reshape(32, 8, 32).max(axis=2).astype(np.float64)
+    np.testing.assert_array_equal(m.sf.astype(int), np.floor(np.log2(bmax)).astype(int) - 2 + 127)
+    deq, codes = _mx_dequant_independent(m)
+    np.testing.assert_array_equal(oracle.mxfp4_dequantize(m), deq)
+    x = np.repeat(e8m0_torch(m.sf), 32, axis=1)
+    r = np.abs(w).astype(np.float64) / x
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    dist = np.abs(r[..., None] - grid)
+    best = dist.min(axis=-1)
+    got = np.abs(deq) / x
+    assert np.all(np.abs(r - got) <= best + 1e-15)
+
+
+def test_layer_with_mxfp4_experts_matches_numpy():
+    """The layer on MXFP4 experts equals the numpy layer on independently
+    dequantised weights (the same checks as the NVFP4 brute force)."""
+    T, H, I, E, k = 3, 64, 32, 8, 2
+    x = synth.x_bf16(18, T, H)
+    wr = synth.router_bf16(18, H, E, std=0.3)
+    ex = {e: tuple(oracle.mxfp4_quantize(synth.expert_f32(18, e, m, *synth.expert_shape(m, H, I))) for m in range(3))
+          for e in range(E)}
+    out = oracle.moe_layer(x, ex, E, k, wr_bf16=wr)
+    xf = synth.bf16_to_f32(x).astype(np.float64)
+    y = np.zeros((T, H))
+    for t in range(T):
+        for j in range(k):
+            g, u, d = [_mx_dequant_independent(mm)[0] for mm in ex[int(out["ids"][t, j])]]
+            a, b = xf[t] @ g.T, xf[t] @ u.T
+            y[t] += out["w"][t, j] * ((a / (1 + np.exp(-a)) * b) @ d.T)
+    np.testing.assert_allclose(out["y"], y, rtol=1e-11, atol=1e-13)
