@@ -40,6 +40,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
+    ap.add_argument("--format", choices=("nvfp4", "mxfp4"), default="nvfp4", help="expert weight format")
     ap.add_argument("--shared", type=int, default=0,
                     help="add this many bf16 shared experts (width I) that every token uses")
     ap.add_argument("--ep", type=int, default=1,
@@ -50,6 +51,10 @@ def parse():
 
 def nvfp4_bytes(N, K):
     return N * (K // 2) + N * (K // 16) + 4
+
+
+def mxfp4_bytes(N, K):
+    return N * (K // 2) + N * (K // 32) + 4
 
 
 def kernel_source_sha():
@@ -117,7 +122,7 @@ def main():
         print(json.dumps({"error": "--ep must divide E; --ep and --shared go with the plain layer only, not together"}))
         sys.exit(2)
     share = E // args.ep  # experts held here: 0 .. share-1
-    store = moe.ExpertStore(share, H, I, device=dev)
+    store = moe.ExpertStore(share, H, I, device=dev, fmt=args.format)
     buf = {m: torch.empty(store.shape(m), dtype=torch.float32, device=dev) for m in store.MATS}
     for e in range(share):
         for mi, m in enumerate(store.MATS):
@@ -194,7 +199,8 @@ def main():
 
     # ---- algorithmic work ------------------------------------------------------------
     ms_per_step = elapsed_ms / steps
-    expert_bytes = 2 * nvfp4_bytes(I, H) + nvfp4_bytes(H, I)
+    mat_bytes = mxfp4_bytes if args.format == "mxfp4" else nvfp4_bytes
+    expert_bytes = 2 * mat_bytes(I, H) + mat_bytes(H, I)
     # latent block: plus the two projection weights; router and x, y at the hidden width
     proj_bytes = 2 * Hm * H * 2 if wl.H_model else 0
     proj_bytes += args.shared * 3 * H * I * 2  # bf16 shared experts
@@ -203,7 +209,7 @@ def main():
     local_pairs = np.mean([np.count_nonzero(ids_np[i] < share) for i in range(warmup, n_batches)])
     layer_flops = (2 * T * Hm * E + 6 * local_pairs * H * I + (4 * T * Hm * H if wl.H_model else 0)
                    + 6 * T * args.shared * H * I)
-    gateup_unit = 2 * nvfp4_bytes(I, H)              # one active expert's gate+up weights
+    gateup_unit = 2 * mat_bytes(I, H)                # one active expert's gate+up weights
     gateup_bytes = distinct * gateup_unit + T * H * 2 + local_pairs * I * 2
     gateup_avg_ms = float(np.mean(gateup_ms))
     prof_bytes = float(np.mean(gateup_bytes[:n_prof]))  # the steps whose launches were timed
@@ -240,11 +246,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": (f"{wl.name}: latent MoE block, hidden {Hm} -> routed latent {H} (bf16 projections), "
                                 if wl.H_model else f"{wl.name}: MoE layer ")
-                               + f"T={T} H={H} I={I} E={E} top-{k}, NVFP4 experts, bf16 activations, fresh tokens "
+                               + f"T={T} H={H} I={I} E={E} top-{k}, {args.format.upper()} experts, bf16 activations, fresh tokens "
                                f"every step",
                    "T": T, "H": H, "I": I, "E": E, "k": k, "H_model": wl.H_model, "zipf_beta": wl.beta,
                    "seed": wl.seed, "expert_share": f"experts 0..{share - 1} of {E}" if args.ep > 1 else None,
-                   "shared_experts": args.shared},
+                   "shared_experts": args.shared, "weight_format": args.format},
         "roofline": roofline,
         "layer": {"algorithmic_bytes": int(layer_bytes), "hbm_GBps": round(layer_bytes / (ms_per_step * 1e-3) / 1e9, 1),
                   "hbm_frac": round(layer_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -285,7 +291,7 @@ def main():
         out["graph_ms_per_step"] = round(a.elapsed_time(b) / n_graph, 5)
         del graph
 
-    if not args.no_cpu_baseline and args.ep == 1 and not args.shared:
+    if not args.no_cpu_baseline and args.ep == 1 and not args.shared and args.format == "nvfp4":
         n_tok = args.cpu_tokens or (8 if T <= 16 else 4)
         out["cpu_baseline"] = cpu_baseline(wl, n_tok, first_token=warmup * T)
     print(json.dumps(out))

@@ -89,9 +89,26 @@ typedef struct {
   const float* gs;
 } moe_nvfp4;
 
-/* gate and up: N = I, K = H.  down: N = H, K = I.  All device pointers. */
+/* Weight formats of a store.  MXFP4 (the OCP microscaling format; [p2]
+ * "Number formats on Blackwell": K3's experts were trained in it) uses the
+ * same moe_nvfp4 fields with
+ *   sf [E][N][K/32] e8m0 scale 2^(sf - 127) of 32 consecutive k of a row
+ *                   (255, NaN, is out of contract),
+ *   gs [E]          a power of two 2^r per matrix: the fp16 dequantisation
+ *                   computes e2m1 * 2^(sf - 127 - r), exact for block scales
+ *                   within 2^8 .. 2^-23 of 2^r, and gs is multiplied back in
+ *                   fp32.  moe_quantize_mxfp4 sets r = smax - 135 (smax the
+ *                   largest scale byte), which keeps every block within 31
+ *                   binades of the largest exact.
+ * Dequantised weight: W[n][k] = e2m1(q) * 2^(sf - 127).  MXFP4 stores run on
+ * the small-batch GEMMs at every batch size. */
+typedef enum { MOE_FMT_NVFP4 = 0, MOE_FMT_MXFP4 = 1 } moe_weight_format;
+
+/* gate and up: N = I, K = H.  down: N = H, K = I.  All device pointers.
+ * format: a moe_weight_format (0, NVFP4, when left zero). */
 typedef struct {
   moe_nvfp4 gate, up, down;
+  int32_t format;
 } moe_experts;
 
 /* Bytes of device workspace that moe_route, moe_expert_ffn and moe_layer
@@ -110,6 +127,17 @@ size_t moe_workspace_bytes(moe_dims d);
  * moe_quantize_workspace_bytes() bytes. */
 size_t moe_quantize_workspace_bytes(void);
 moe_status moe_quantize_nvfp4(const float* w, int64_t N, int64_t K, uint8_t* q, uint8_t* sf, float* gs, void* ws,
+                              size_t ws_bytes, void* stream);
+
+/* Quantise one fp32 matrix w[N][K] (device) to MXFP4 (device outputs q
+ * [N][K/2], sf [N][K/32], gs [1]), following the OCP MX specification's
+ * conversion: per 32-element block along K, with blockmax the largest |w|,
+ * sf = floor(log2(blockmax)) - 2 + 127 clamped to 0 .. 254 (X = 2^(sf-127));
+ * code = nearest e2m1 to |w| / X, ties to the even code, clamped to 6; a
+ * zero block gets sf = 0 and zero codes.  gs = 2^(smax - 135), smax the
+ * scale of the matrix's largest |w| (see moe_weight_format).  Needs
+ * K % 32 == 0, N >= 1 and a workspace as moe_quantize_nvfp4. */
+moe_status moe_quantize_mxfp4(const float* w, int64_t N, int64_t K, uint8_t* q, uint8_t* sf, float* gs, void* ws,
                               size_t ws_bytes, void* stream);
 
 /* Route T tokens (device pointers):

@@ -21,7 +21,9 @@ KERNELS = {"router": 0, "topk": 1, "permute": 2, "cast": 3, "gateup": 4, "down":
 EXPORTS = ("moe_workspace_bytes", "moe_quantize_workspace_bytes", "moe_quantize_nvfp4", "moe_route",
            "moe_expert_ffn", "moe_layer", "moe_status_string", "moe_last_error", "moe_profile_arm",
            "moe_profile_read", "moe_stream_read", "moe_latent_workspace_bytes", "moe_latent_layer",
-           "moe_expert_ffn_share", "moe_layer_share", "moe_layer_shared_workspace_bytes", "moe_layer_shared")
+           "moe_expert_ffn_share", "moe_layer_share", "moe_layer_shared_workspace_bytes", "moe_layer_shared",
+           "moe_quantize_mxfp4")
+FORMATS = {"nvfp4": 0, "mxfp4": 1}  # moe_weight_format
 # MOE_STREAM_SINK_WORDS of moe.h
 STREAM_SINK_WORDS = 4096
 
@@ -42,7 +44,7 @@ class NVFP4(ctypes.Structure):
 
 
 class Experts(ctypes.Structure):
-    _fields_ = [("gate", NVFP4), ("up", NVFP4), ("down", NVFP4)]
+    _fields_ = [("gate", NVFP4), ("up", NVFP4), ("down", NVFP4), ("format", ctypes.c_int32)]
 
 
 class Share(ctypes.Structure):
@@ -75,6 +77,8 @@ def lib():
         L.moe_quantize_workspace_bytes.argtypes = []
         L.moe_quantize_nvfp4.restype = ctypes.c_int
         L.moe_quantize_nvfp4.argtypes = [_p, ctypes.c_int64, ctypes.c_int64, _p, _p, _p, _p, ctypes.c_size_t, _p]
+        L.moe_quantize_mxfp4.restype = ctypes.c_int
+        L.moe_quantize_mxfp4.argtypes = [_p, ctypes.c_int64, ctypes.c_int64, _p, _p, _p, _p, ctypes.c_size_t, _p]
         L.moe_route.restype = ctypes.c_int
         L.moe_route.argtypes = [Dims, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]
         L.moe_expert_ffn.restype = ctypes.c_int
@@ -153,6 +157,12 @@ def moe_quantize_workspace_bytes():
 def moe_quantize_nvfp4(w, q, sf, gs, ws, stream=None):
     N, K = w.shape
     _check(lib().moe_quantize_nvfp4(_ptr(w), N, K, _ptr(q), _ptr(sf), _ptr(gs), _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_quantize_mxfp4(w, q, sf, gs, ws, stream=None):
+    N, K = w.shape
+    _check(lib().moe_quantize_mxfp4(_ptr(w), N, K, _ptr(q), _ptr(sf), _ptr(gs), _ptr(ws),
                                     ws.numel() * ws.element_size(), _stream(stream)))
 
 
@@ -247,20 +257,22 @@ def moe_profile_read(max_launches):
 # ---- device memory holders (plumbing) ------------------------------------------
 
 class ExpertStore:
-    """NVFP4 weights of E experts, stacked per matrix, resident in HBM:
-    q [E][N][K/2] u8, sf [E][N][K/16] u8, gs [E] fp32 for gate/up (N = I,
-    K = H) and down (N = H, K = I)."""
+    """Weights of E experts, stacked per matrix, resident in HBM: q
+    [E][N][K/2] u8, sf [E][N][K/16] (NVFP4) or [E][N][K/32] (MXFP4) u8, gs [E]
+    fp32 for gate/up (N = I, K = H) and down (N = H, K = I)."""
 
     MATS = ("gate", "up", "down")
 
-    def __init__(self, E, H, I, device="cuda"):
+    def __init__(self, E, H, I, device="cuda", fmt="nvfp4"):
         import torch
         self.E, self.H, self.I = E, H, I
+        self.format = FORMATS[fmt]
+        blk = 32 if self.format == FORMATS["mxfp4"] else 16
         self.t = {}
         for m in self.MATS:
             N, K = self.shape(m)
             self.t[m] = (torch.empty((E, N, K // 2), dtype=torch.uint8, device=device),
-                         torch.empty((E, N, K // 16), dtype=torch.uint8, device=device),
+                         torch.empty((E, N, K // blk), dtype=torch.uint8, device=device),
                          torch.empty((E,), dtype=torch.float32, device=device))
         self._qws = torch.empty(max(256, moe_quantize_workspace_bytes()), dtype=torch.uint8, device=device)
 
@@ -268,16 +280,17 @@ class ExpertStore:
         return (self.I, self.H) if m in ("gate", "up") else (self.H, self.I)
 
     def quantize_into(self, e, m, w_f32, stream=None):
-        """Quantise fp32 w [N][K] (device) with moe_quantize_nvfp4 into expert e."""
+        """Quantise fp32 w [N][K] (device) into expert e in the store's format."""
         q, sf, gs = self.t[m]
-        moe_quantize_nvfp4(w_f32, q[e], sf[e], gs[e:e + 1], self._qws, stream)
+        quant = moe_quantize_mxfp4 if self.format == FORMATS["mxfp4"] else moe_quantize_nvfp4
+        quant(w_f32, q[e], sf[e], gs[e:e + 1], self._qws, stream)
 
     def c(self):
         mats = []
         for m in self.MATS:
             q, sf, gs = self.t[m]
             mats.append(NVFP4(q.data_ptr(), sf.data_ptr(), gs.data_ptr()))
-        self._c = Experts(*mats)
+        self._c = Experts(*mats, self.format)
         return self._c
 
     def share(self, base, count):
@@ -300,5 +313,5 @@ class _StoreShare:
         for m in ExpertStore.MATS:
             q, sf, gs = self.store.t[m]
             mats.append(NVFP4(q[self.base].data_ptr(), sf[self.base].data_ptr(), gs[self.base:].data_ptr()))
-        self._c = Experts(*mats)
+        self._c = Experts(*mats, self.store.format)
         return self._c

@@ -180,6 +180,8 @@ moe_status check_ptr(const void* p, const char* name, bool required = true) {
 
 moe_status check_experts(const moe_experts* w) {
   if (!w) return fail(MOE_ERR_ARG, "experts struct is NULL");
+  if (w->format != MOE_FMT_NVFP4 && w->format != MOE_FMT_MXFP4)
+    return fail(MOE_ERR_ARG, "experts format = %d is not a moe_weight_format", (int)w->format);
   const moe_nvfp4* m[3] = {&w->gate, &w->up, &w->down};
   const char* names[3] = {"gate", "up", "down"};
   for (int i = 0; i < 3; i++) {
@@ -324,10 +326,12 @@ size_t moe_workspace_bytes(moe_dims d) {
 
 size_t moe_quantize_workspace_bytes(void) { return 256; }
 
-moe_status moe_quantize_nvfp4(const float* w, int64_t N, int64_t K, uint8_t* q, uint8_t* sf, float* gs, void* ws,
-                              size_t ws_bytes, void* stream) {
-  if (N < 1 || K < 16 || K % 16) return fail(MOE_ERR_SHAPE, "N = %lld, K = %lld: need N >= 1 and K a multiple of 16",
-                                             (long long)N, (long long)K);
+static moe_status quantize_any(bool mx, const float* w, int64_t N, int64_t K, uint8_t* q, uint8_t* sf, float* gs, void* ws,
+                               size_t ws_bytes, void* stream) {
+  const int blk = mx ? 32 : 16;
+  if (N < 1 || K < blk || K % blk)
+    return fail(MOE_ERR_SHAPE, "N = %lld, K = %lld: need N >= 1 and K a multiple of %d", (long long)N, (long long)K,
+                blk);
   TRY(check_ptr(w, "w"));
   TRY(check_ptr(q, "q"));
   if (!sf || !gs) return fail(MOE_ERR_ARG, "sf or gs is NULL");
@@ -336,9 +340,20 @@ moe_status moe_quantize_nvfp4(const float* w, int64_t N, int64_t K, uint8_t* q, 
   if ((uintptr_t)ws & 3u) return fail(MOE_ERR_ALIGN, "workspace is not 4-byte aligned");
   if (ws_bytes < moe_quantize_workspace_bytes())
     return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, moe_quantize_workspace_bytes());
-  hipError_t e = moe::launch_quantize(w, N, K, q, sf, gs, static_cast<uint32_t*>(ws), (hipStream_t)stream);
+  hipError_t e = mx ? moe::launch_quantize_mx(w, N, K, q, sf, gs, static_cast<uint32_t*>(ws), (hipStream_t)stream)
+                    : moe::launch_quantize(w, N, K, q, sf, gs, static_cast<uint32_t*>(ws), (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "quantize");
   return MOE_OK;
+}
+
+moe_status moe_quantize_nvfp4(const float* w, int64_t N, int64_t K, uint8_t* q, uint8_t* sf, float* gs, void* ws,
+                              size_t ws_bytes, void* stream) {
+  return quantize_any(false, w, N, K, q, sf, gs, ws, ws_bytes, stream);
+}
+
+moe_status moe_quantize_mxfp4(const float* w, int64_t N, int64_t K, uint8_t* q, uint8_t* sf, float* gs, void* ws,
+                              size_t ws_bytes, void* stream) {
+  return quantize_any(true, w, N, K, q, sf, gs, ws, ws_bytes, stream);
 }
 
 moe_status moe_route(moe_dims d, const void* x, const void* w_router, const float* bias, float* logits,

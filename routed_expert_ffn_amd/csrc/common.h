@@ -25,6 +25,20 @@ __device__ __forceinline__ f16 e4m3_to_f16(uint32_t byte) {
   return v[0];
 }
 
+// Eight e2m1 codes times a power of two: the conversion's scale operand is
+// applied through its exponent, which is exact for an MXFP4 block scale
+// (the products stay within fp16 for scales within 2^8 .. 2^-23 of 1).
+__device__ __forceinline__ f16x8 dequant8_pow2(uint32_t codes, float scale) {
+  f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, scale, 0);
+  f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, scale, 1);
+  f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, scale, 2);
+  f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, scale, 3);
+  f16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
 // Eight e2m1 codes (one dword, element 0 in the low nibble) times the block
 // scale sigma, as eight fp16.  The hardware conversion with a unit scale
 // gives the plain e2m1 values; the product e2m1 * e4m3 needs at most six

@@ -108,5 +108,7 @@ hipError_t launch_shared_hidden(const uint16_t* x, const uint16_t* w_gate_up, fl
 
 hipError_t launch_quantize(const float* w, int64_t N, int64_t K, uint8_t* q, uint8_t* sf, float* gs, uint32_t* ws,
                            hipStream_t s);
+hipError_t launch_quantize_mx(const float* w, int64_t N, int64_t K, uint8_t* q, uint8_t* sf, float* gs, uint32_t* ws,
+                              hipStream_t s);
 
 }  // namespace moe

@@ -65,14 +65,19 @@ struct Chunk {
   f16x8 a[MF][8];
 };
 
-template <int MF>
+// Weight formats: NVFP4 (e4m3 scale per 16 k, 4 scale bytes per 64 codes)
+// and MXFP4 (e8m0 power-of-two scale per 32 k, 2 bytes per 64 codes).
+enum WeightFmt { FMT_NV = 0, FMT_MX = 1 };
+
+template <int MF, int FMT = FMT_NV>
 __device__ __forceinline__ void load_b(Chunk<MF>& ch, const uint8_t* const (&qrow)[4],
                                        const uint8_t* const (&srow)[4], int kb) {
 #pragma unroll
   for (int ng = 0; ng < 4; ng++) {
     ch.qa[ng] = *reinterpret_cast<const uint4*>(qrow[ng] + kb / 2);
     ch.qb[ng] = *reinterpret_cast<const uint4*>(qrow[ng] + kb / 2 + 16);
-    ch.sc[ng] = *reinterpret_cast<const uint32_t*>(srow[ng] + kb / 16);
+    ch.sc[ng] = FMT == FMT_MX ? (uint32_t)*reinterpret_cast<const uint16_t*>(srow[ng] + kb / 32)
+                              : *reinterpret_cast<const uint32_t*>(srow[ng] + kb / 16);
   }
 }
 
@@ -87,18 +92,28 @@ __device__ __forceinline__ void load_a(Chunk<MF>& ch, const f16* const (&arow)[M
 
 // acc[f][ng] += A fragments x dequantised weights of one chunk.  Each row
 // group is dequantised and multiplied in turn, so one B fragment is live.
-template <int MF>
-__device__ __forceinline__ void mma_chunk(f32x4 (&acc)[MF][4], const Chunk<MF>& ch, int nvalid) {
+// MXFP4: step s's codes share the scale byte s/4; the conversion applies
+// 2^(scale - 127 - roff[ng]) itself (roff: the matrix's per-tensor power of
+// two, applied back in fp32 with gs).
+template <int MF, int FMT = FMT_NV>
+__device__ __forceinline__ void mma_chunk(f32x4 (&acc)[MF][4], const Chunk<MF>& ch, int nvalid,
+                                          const int (&roff)[4]) {
 #pragma unroll
   for (int s = 0; s < 8; s++) {
 #pragma unroll
     for (int ng = 0; ng < 4; ng++) {
       const uint32_t codes = s < 4 ? (&ch.qa[ng].x)[s] : (&ch.qb[ng].x)[s - 4];
-      const f16 sig = e4m3_to_f16((ch.sc[ng] >> (8 * (s / 2))) & 0xFFu);
-      f16x2 sig2;
-      sig2[0] = sig;
-      sig2[1] = sig;
-      const f16x8 bf = dequant8(codes, sig2);
+      f16x8 bf;
+      if (FMT == FMT_MX) {
+        const int sb = (int)((ch.sc[ng] >> (8 * (s / 4))) & 0xFFu);
+        bf = dequant8_pow2(codes, __builtin_ldexpf(1.0f, sb - 127 - roff[ng]));
+      } else {
+        const f16 sig = e4m3_to_f16((ch.sc[ng] >> (8 * (s / 2))) & 0xFFu);
+        f16x2 sig2;
+        sig2[0] = sig;
+        sig2[1] = sig;
+        bf = dequant8(codes, sig2);
+      }
 #pragma unroll
       for (int f = 0; f < MF; f++)
         if (f * 16 < nvalid) acc[f][ng] = mfma16x16x32(ch.a[f][s], bf, acc[f][ng]);
@@ -120,7 +135,7 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 // looked up, and each later chunk is loaded while the previous one is
 // multiplied.  Partial sums of the KSPLIT wavefronts meet in LDS and are
 // added in a fixed order.
-template <int MF, int KSPLIT, bool GATEUP, bool DB, int WAVES_PER_EU>
+template <int MF, int KSPLIT, bool GATEUP, bool DB, int WAVES_PER_EU, int FMT>
 __global__ __launch_bounds__(FFN_THREADS, WAVES_PER_EU) void expert_gemm_kernel(GroupedParams p) {
   constexpr int RT = 4 / KSPLIT;
   __shared__ float red[KSPLIT > 1 ? 4 : 1][WAVE][MF * 16];
@@ -148,13 +163,21 @@ __global__ __launch_bounds__(FFN_THREADS, WAVES_PER_EU) void expert_gemm_kernel(
       sb = p.sf0;
     }
     qrow[ng] = qb + row * (K / 2);
-    srow[ng] = sb + row * (K / 16);
+    srow[ng] = sb + row * (K / (FMT == FMT_MX ? 32 : 16));
   }
   const int nchunks = K / KCHUNK;
   Chunk<MF> cur;
-  if (ks < nchunks) load_b(cur, qrow, srow, ks * KCHUNK + 64 * g);  // before the token lookups
+  if (ks < nchunks) load_b<MF, FMT>(cur, qrow, srow, ks * KCHUNK + 64 * g);  // before the token lookups
   const int begin = p.offsets[e], end = p.offsets[e + 1];
   const float gsa = p.gs0[el], gsb = GATEUP ? p.gs1[el] : 0.0f;
+  // MXFP4: gs = 2^r (frexp exponent r + 1); the block scales are divided by it
+  int roff[4];
+  {
+    const int r0 = FMT == FMT_MX ? __builtin_amdgcn_frexp_expf(gsa) - 1 : 0;
+    const int r1 = FMT == FMT_MX && GATEUP ? __builtin_amdgcn_frexp_expf(gsb) - 1 : 0;
+#pragma unroll
+    for (int ng = 0; ng < 4; ng++) roff[ng] = GATEUP && ng >= 2 ? r1 : r0;
+  }
   bool first_pass = true;
   for (int mb = begin; mb < end; mb += MF * 16) {
     const int nvalid = end - mb;
@@ -170,7 +193,7 @@ __global__ __launch_bounds__(FFN_THREADS, WAVES_PER_EU) void expert_gemm_kernel(
 #pragma unroll
       for (int ng = 0; ng < 4; ng++) acc[f][ng] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     if (ks < nchunks) {
-      if (!first_pass) load_b(cur, qrow, srow, ks * KCHUNK + 64 * g);
+      if (!first_pass) load_b<MF, FMT>(cur, qrow, srow, ks * KCHUNK + 64 * g);
       load_a(cur, arow, ks * KCHUNK + 64 * g, nvalid);
     }
     first_pass = false;
@@ -180,15 +203,15 @@ __global__ __launch_bounds__(FFN_THREADS, WAVES_PER_EU) void expert_gemm_kernel(
       if (DB) {  // load the next chunk while this one is multiplied
         Chunk<MF> nxt;
         if (more) {
-          load_b(nxt, qrow, srow, kb + KSPLIT * KCHUNK);
+          load_b<MF, FMT>(nxt, qrow, srow, kb + KSPLIT * KCHUNK);
           load_a(nxt, arow, kb + KSPLIT * KCHUNK, nvalid);
         }
-        mma_chunk<MF>(acc, cur, nvalid);
+        mma_chunk<MF, FMT>(acc, cur, nvalid, roff);
         if (more) cur = nxt;
       } else {
-        mma_chunk<MF>(acc, cur, nvalid);
+        mma_chunk<MF, FMT>(acc, cur, nvalid, roff);
         if (more) {
-          load_b(cur, qrow, srow, kb + KSPLIT * KCHUNK);
+          load_b<MF, FMT>(cur, qrow, srow, kb + KSPLIT * KCHUNK);
           load_a(cur, arow, kb + KSPLIT * KCHUNK, nvalid);
         }
       }
@@ -724,9 +747,12 @@ __global__ __launch_bounds__(BIG_THREADS, 1) void expert_gemm_big_kernel(BigPara
 constexpr int BIG_MIN_T = 1024;
 // Token rows are addressed with 32-bit byte offsets: 2 T H and 2 T k I must
 // stay below 2^32.
+// The large-tile kernels read NVFP4 only; MXFP4 runs on the small-batch
+// kernels at every size.
 bool use_big(const FfnArgs& a) {
   const long long ki = (long long)a.k * a.I, span = (long long)a.T * (a.H > ki ? a.H : ki);
-  return a.T >= BIG_MIN_T && a.I % 256 == 0 && a.H % 256 == 0 && span < (1LL << 31);
+  return a.w->format == MOE_FMT_NVFP4 && a.T >= BIG_MIN_T && a.I % 256 == 0 && a.H % 256 == 0 &&
+         span < (1LL << 31);
 }
 
 template <bool GATEUP>
@@ -860,22 +886,24 @@ constexpr int DN_KSPLIT = 2;
 constexpr bool GEMM_DB = false;
 constexpr int GEMM_WAVES = 2;
 
-template <int KSPLIT, bool GATEUP>
-hipError_t launch_gemm(const GroupedParams& p, int mf, dim3 grid, hipStream_t s) {
+template <int KSPLIT, bool GATEUP, int FMT>
+hipError_t launch_gemm_fmt(const GroupedParams& p, int mf, dim3 grid, hipStream_t s) {
   switch (mf) {
     case 1:
-      hipLaunchKernelGGL((expert_gemm_kernel<1, KSPLIT, GATEUP, GEMM_DB, GEMM_WAVES>), grid, dim3(FFN_THREADS),
-                         0, s, p);
-      break;
-    case 2:
-      hipLaunchKernelGGL((expert_gemm_kernel<2, KSPLIT, GATEUP, GEMM_DB, GEMM_WAVES>), grid, dim3(FFN_THREADS),
+      hipLaunchKernelGGL((expert_gemm_kernel<1, KSPLIT, GATEUP, GEMM_DB, GEMM_WAVES, FMT>), grid, dim3(FFN_THREADS),
                          0, s, p);
       break;
     default:
-      hipLaunchKernelGGL((expert_gemm_kernel<4, KSPLIT, GATEUP, GEMM_DB, 1>), grid, dim3(FFN_THREADS), 0, s, p);
+      hipLaunchKernelGGL((expert_gemm_kernel<4, KSPLIT, GATEUP, GEMM_DB, 1, FMT>), grid, dim3(FFN_THREADS), 0, s, p);
       break;
   }
   return hipGetLastError();
+}
+
+template <int KSPLIT, bool GATEUP>
+hipError_t launch_gemm(const GroupedParams& p, int mf, dim3 grid, hipStream_t s, int fmt) {
+  return fmt == MOE_FMT_MXFP4 ? launch_gemm_fmt<KSPLIT, GATEUP, FMT_MX>(p, mf, grid, s)
+                              : launch_gemm_fmt<KSPLIT, GATEUP, FMT_NV>(p, mf, grid, s);
 }
 
 }  // namespace
@@ -891,7 +919,7 @@ hipError_t launch_gateup(const FfnArgs& a, hipStream_t s) {
   p.gs1 = a.w->up.gs;
   if (use_big(a)) return launch_big<true>(a, p, s);
   const dim3 grid(a.I / (32 * (4 / GU_KSPLIT)), a.max_active);
-  return launch_gemm<GU_KSPLIT, true>(p, pick_mf(a.T), grid, s);
+  return launch_gemm<GU_KSPLIT, true>(p, pick_mf(a.T), grid, s, a.w->format);
 }
 
 hipError_t launch_down(const FfnArgs& a, hipStream_t s) {
@@ -902,7 +930,7 @@ hipError_t launch_down(const FfnArgs& a, hipStream_t s) {
   p.gs0 = a.w->down.gs;
   if (use_big(a)) return launch_big<false>(a, p, s);
   const dim3 grid(a.H / (64 * (4 / DN_KSPLIT)), a.max_active);
-  return launch_gemm<DN_KSPLIT, false>(p, pick_mf(a.T), grid, s);
+  return launch_gemm<DN_KSPLIT, false>(p, pick_mf(a.T), grid, s, a.w->format);
 }
 
 hipError_t launch_combine16(const f16* rows, const int32_t* pair_pos, int T, int H, int k, uint16_t* y, hipStream_t s,

@@ -115,6 +115,55 @@ __global__ __launch_bounds__(256) void quant_kernel(const float* __restrict__ w,
   }
 }
 
+// ---- MXFP4 (OCP microscaling: e8m0 power-of-two scale per 32 elements) -------
+// floor(log2(a)) of a finite a > 0, subnormals included.
+__device__ __forceinline__ int floor_log2(float a) { return __builtin_amdgcn_frexp_expf(a) - 1; }
+
+// One thread per 32-element block: scale byte s = floor(log2(blockmax)) - 2
+// + 127 clamped to 0..254 (a zero block: 0), codes = e2m1_rne(|w| / 2^(s-127))
+// clamped to 6 (the division by a power of two is exact); the first thread
+// also writes gs = 2^(smax - 135) from the matrix's largest |w|.
+__global__ __launch_bounds__(256) void quant_mx_kernel(const float* __restrict__ w, long long nblk,
+                                                      uint8_t* __restrict__ q, uint8_t* __restrict__ sf,
+                                                      float* __restrict__ gs_out,
+                                                      const uint32_t* __restrict__ amax_bits) {
+  const long long first = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (first == 0) {
+    const float amax = __uint_as_float(*amax_bits);
+    const int smax = amax > 0.0f ? min(max(floor_log2(amax) - 2 + 127, 0), 254) : 0;
+    *gs_out = __builtin_ldexpf(1.0f, smax - 135);
+  }
+  for (long long b = first; b < nblk; b += (long long)gridDim.x * 256) {
+    const float4* src = reinterpret_cast<const float4*>(w) + 8 * b;
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const float4 t = src[i];
+      v[4 * i] = t.x;
+      v[4 * i + 1] = t.y;
+      v[4 * i + 2] = t.z;
+      v[4 * i + 3] = t.w;
+    }
+    float bmax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; i++) bmax = fmaxf(bmax, fabsf(v[i]));
+    uint32_t words[4] = {0u, 0u, 0u, 0u};
+    int s = 0;
+    if (bmax > 0.0f) {
+      s = min(max(floor_log2(bmax) - 2 + 127, 0), 254);
+      const float inv = __builtin_ldexpf(1.0f, 127 - s);  // 1 / X, a power of two
+#pragma unroll
+      for (int i = 0; i < 32; i++) {
+        uint32_t c = e2m1_code_rne(fabsf(v[i]) * inv);
+        if (v[i] < 0.0f && c != 0u) c |= 8u;
+        words[i / 8] |= c << (4 * (i % 8));
+      }
+    }
+    reinterpret_cast<uint4*>(q)[b] = make_uint4(words[0], words[1], words[2], words[3]);
+    sf[b] = (uint8_t)s;
+  }
+}
+
 unsigned grid_for(long long n) {
   long long g = (n + 255) / 256;
   if (g > 8192) g = 8192;
@@ -132,6 +181,17 @@ hipError_t launch_quantize(const float* w, int64_t N, int64_t K, uint8_t* q, uin
   if (ga > 1024) ga = 1024;
   hipLaunchKernelGGL(amax_kernel, dim3((unsigned)(ga > 0 ? ga : 1)), dim3(256), 0, s, w, n / 4, ws);
   hipLaunchKernelGGL(quant_kernel, dim3(grid_for(n / 16)), dim3(256), 0, s, w, n / 16, q, sf, gs, ws);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_mx(const float* w, int64_t N, int64_t K, uint8_t* q, uint8_t* sf, float* gs, uint32_t* ws,
+                              hipStream_t s) {
+  const long long n = (long long)N * K;
+  hipLaunchKernelGGL(zero_word_kernel, dim3(1), dim3(1), 0, s, ws);
+  long long ga = (n / 4 + 4095) / 4096;
+  if (ga > 1024) ga = 1024;
+  hipLaunchKernelGGL(amax_kernel, dim3((unsigned)(ga > 0 ? ga : 1)), dim3(256), 0, s, w, n / 4, ws);
+  hipLaunchKernelGGL(quant_mx_kernel, dim3(grid_for(n / 32)), dim3(256), 0, s, w, n / 32, q, sf, gs, ws);
   return hipGetLastError();
 }
 

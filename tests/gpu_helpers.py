@@ -56,10 +56,11 @@ def assert_close_bf16_out(got, ref, what):
     assert worst <= 1.0 and r <= REL_L2, f"{what}: worst {worst:.2f}, rel_l2={r:.3e}"
 
 
-def build_store(E, H, I, seed, experts=None):
-    """NVFP4 store on the GPU: fp32 weights from the GPU generator, quantised
-    by moe_quantize_nvfp4 (experts outside `experts` are left zero)."""
-    store = moe.ExpertStore(E, H, I, device=DEV)
+def build_store(E, H, I, seed, experts=None, fmt="nvfp4"):
+    """NVFP4 (or MXFP4) store on the GPU: fp32 weights from the GPU
+    generator, quantised by the library (experts outside `experts` are left
+    zero)."""
+    store = moe.ExpertStore(E, H, I, device=DEV, fmt=fmt)
     for m in store.MATS:
         for t in store.t[m]:
             t.zero_()
@@ -75,13 +76,14 @@ def build_store(E, H, I, seed, experts=None):
 class OracleExperts:
     """Experts generated and quantised on the CPU by the oracle, on demand."""
 
-    def __init__(self, seed, H, I):
+    def __init__(self, seed, H, I, fmt="nvfp4"):
         self.seed, self.H, self.I = seed, H, I
+        self.quant = oracle.mxfp4_quantize if fmt == "mxfp4" else oracle.nvfp4_quantize
         self.cache = {}
 
     def _make(self, e):
-        return tuple(oracle.nvfp4_quantize(synth.expert_f32(self.seed, e, m, *synth.expert_shape(m, self.H, self.I),
-                                                            nthreads=1)) for m in range(3))
+        return tuple(self.quant(synth.expert_f32(self.seed, e, m, *synth.expert_shape(m, self.H, self.I), nthreads=1))
+                     for m in range(3))
 
     def get(self, ids):
         need = sorted(set(int(e) for e in np.ravel(ids)) - set(self.cache))

@@ -171,3 +171,15 @@ def test_shared_workspace_and_validation_without_hip():
     assert L.moe_layer_shared(d, None, *args) == 1
     assert L.moe_layer_shared(d, ctypes.byref(moe.Shared(2, 256, None, None)), *args) == 1
     assert L.moe_layer_shared(d, ctypes.byref(moe.Shared(2, 300, FAKE, FAKE)), *args) == 2
+
+
+def test_mxfp4_quantize_and_format_validation_without_hip():
+    L = moe.lib()
+    ws = moe.moe_quantize_workspace_bytes()
+    assert L.moe_quantize_mxfp4(FAKE, 4, 48, FAKE, FAKE, FAKE, FAKE, ws, None) == 2  # K % 32
+    assert L.moe_quantize_mxfp4(FAKE, 0, 64, FAKE, FAKE, FAKE, FAKE, ws, None) == 2
+    d = moe.dims(8, 512, 256, 64, 8)
+    nv = moe.NVFP4(FAKE, FAKE, FAKE)
+    ex = moe.Experts(nv, nv, nv, 5)
+    rows_ws = moe.moe_workspace_bytes(d)
+    assert L.moe_expert_ffn(d, FAKE, FAKE, FAKE, ctypes.byref(ex), FAKE, FAKE, rows_ws, None) == 1
