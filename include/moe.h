@@ -100,8 +100,8 @@ typedef struct {
  *                   fp32.  moe_quantize_mxfp4 sets r = smax - 135 (smax the
  *                   largest scale byte), which keeps every block within 31
  *                   binades of the largest exact.
- * Dequantised weight: W[n][k] = e2m1(q) * 2^(sf - 127).  MXFP4 stores run on
- * the small-batch GEMMs at every batch size. */
+ * Dequantised weight: W[n][k] = e2m1(q) * 2^(sf - 127).  Every entry point
+ * and GEMM variant takes either format. */
 typedef enum { MOE_FMT_NVFP4 = 0, MOE_FMT_MXFP4 = 1 } moe_weight_format;
 
 /* gate and up: N = I, K = H.  down: N = H, K = I.  All device pointers.

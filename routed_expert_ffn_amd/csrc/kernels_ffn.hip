@@ -366,6 +366,10 @@ __device__ __forceinline__ void dma16(const unsigned char* gbase, uint32_t voff,
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "s"(lds)
                : "memory", "m0");
 }
+__device__ __forceinline__ void dma4(const unsigned char* gbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(gbase), "s"(lds)
+               : "memory", "m0");
+}
 
 struct BigTile {
   int e, mb, nvalid, rtile, K, N;
@@ -381,6 +385,8 @@ struct BigLane {
   const uint8_t* sc[2];    // raw scales of tile rows 0 / 128
   uint32_t qlane;          // per-lane code source offset (this wavefront's instructions)
   uint32_t slane;          // per-lane scale source offset
+  uint32_t sstep;          // MXFP4: scale bytes of 32 rows (the second scale instruction)
+  int roff[2];             // MXFP4: power of two r of gs for fragment nf's matrix
   uint32_t qstep;          // code bytes of 16 rows: two instructions of one wavefront apart
   int aoff[4];             // per step: LDS byte offset of token row m32 in a token buffer
   int qrow[2], srow[2];    // LDS byte offsets of this lane's weight row (fragment nf) in a span slot
@@ -405,28 +411,44 @@ __device__ __forceinline__ void dma_tokens(const BigLane& L, unsigned char* smem
 // into span slot `slot`, by the wavefront of parity p of the issuing pair:
 // code instructions i = p, p+2, .. < 16 cover rows 128h + 8i .. +7 (lane l:
 // row + l/8, slot l%8, the swizzled piece), scale instruction p rows
-// 128h + 64p + l (16 bytes each).
+// 128h + 64p + l (16 bytes each).  MXFP4 has 8 scale bytes per row and span,
+// stored [256][8]: two 4-byte instructions, rows 128h + 64p + 32i + l/2,
+// bytes 4(l%2).
+template <int FMT>
 __device__ __forceinline__ void dma_span_half(const BigLane& L, unsigned char* smem, int slot, int k0, int h, int p) {
   const uint32_t rq = lds_addr(smem + BIG_OFF_RQ + slot * BIG_SPANQ_BYTES + 128 * h * 128 + 8 * p * 128);
-  const uint32_t rs = lds_addr(smem + BIG_OFF_RS + slot * BIG_SPANS_BYTES + 128 * h * 16 + 64 * p * 16);
   const unsigned char* qb = L.q[h] + k0 / 2;
 #pragma unroll
   for (int ii = 0; ii < 8; ii++) dma16(qb, L.qlane + ii * L.qstep, rq + 16 * ii * 128);
-  dma16(L.sc[h] + k0 / 16, L.slane, rs);
+  if (FMT == FMT_MX) {
+    const uint32_t rs = lds_addr(smem + BIG_OFF_RS + slot * BIG_SPANS_BYTES + 128 * h * 8 + 64 * p * 8);
+    dma4(L.sc[h] + k0 / 32, L.slane, rs);
+    dma4(L.sc[h] + k0 / 32, L.slane + L.sstep, rs + 32 * 8);
+  } else {
+    const uint32_t rs = lds_addr(smem + BIG_OFF_RS + slot * BIG_SPANS_BYTES + 128 * h * 16 + 64 * p * 16);
+    dma16(L.sc[h] + k0 / 16, L.slane, rs);
+  }
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 // Step s of one chunk: the two weight fragments, dequantised from this
-// lane's raw codes (word s) and block scale (element s/2 of the pair).
-__device__ __forceinline__ void dequant_step(f16x8 (&bv)[2], const u32x4 (&q)[2], const f16x2 (&sig)[2], int s) {
+// lane's raw codes (word s) and block scale (NVFP4: element s/2 of the pair
+// in sig; MXFP4: the one power of two in pw, the lane's 32 k being one block).
+template <int FMT>
+__device__ __forceinline__ void dequant_step(f16x8 (&bv)[2], const u32x4 (&q)[2], const f16x2 (&sig)[2],
+                                             const float (&pw)[2], int s) {
 #pragma unroll
   for (int nf = 0; nf < 2; nf++) {
-    f16x2 s2;
-    s2[0] = sig[nf][s / 2];
-    s2[1] = sig[nf][s / 2];
-    bv[nf] = dequant8(q[nf][s], s2);
+    if (FMT == FMT_MX) {
+      bv[nf] = dequant8_pow2(q[nf][s], pw[nf]);
+    } else {
+      f16x2 s2;
+      s2[0] = sig[nf][s / 2];
+      s2[1] = sig[nf][s / 2];
+      bv[nf] = dequant8(q[nf][s], s2);
+    }
   }
 }
 
@@ -463,7 +485,7 @@ __device__ __forceinline__ void interleave_mfma_valu() {
 // J = 1 by pair B and J = 2 by pair A).  Then the four steps, with token
 // fragments read and weights dequantised one step ahead, and the barrier,
 // at which the pair that issued in chunk c-1 waits for its DMA.
-template <int NF, int J, bool TOK, bool SPAN>
+template <int NF, int J, bool TOK, bool SPAN, int FMT>
 __device__ __forceinline__ void big_chunk(const BigLane& L, f32x16 (&acc)[8][2], unsigned char* smem, int c,
                                           int wv) {
   const int pair = wv >> 1, par = wv & 1;
@@ -471,44 +493,51 @@ __device__ __forceinline__ void big_chunk(const BigLane& L, f32x16 (&acc)[8][2],
   const bool tok_issuer = pair == (J & 1);
   const bool span_issuer = (J == 1 && pair == 1) || (J == 2 && pair == 0);
   if (TOK && tok_issuer) dma_tokens(L, smem, (c + 2) % 3, (c + 2) * BIG_KC, par);
-  if (SPAN && span_issuer) dma_span_half(L, smem, slot ^ 1, (span + 1) * BIG_SPAN * BIG_KC, J == 1 ? 0 : 1, par);
+  if (SPAN && span_issuer)
+    dma_span_half<FMT>(L, smem, slot ^ 1, (span + 1) * BIG_SPAN * BIG_KC, J == 1 ? 0 : 1, par);
   asm volatile("" ::: "memory");
   const unsigned char* Ab = smem + BIG_OFF_A + (c % 3) * BIG_TILE_BYTES;
   const unsigned char* rq = smem + BIG_OFF_RQ + slot * BIG_SPANQ_BYTES;
   const unsigned char* rs = smem + BIG_OFF_RS + slot * BIG_SPANS_BYTES;
   u32x4 q[2];
   f16x2 sig[2];
+  float pw[2];
   const int g2 = (threadIdx.x % WAVE) / 32, m32 = threadIdx.x % 32;
   const int qslot = (2 * J + g2) ^ ((m32 / 2) % 8);  // piece 2J + g of the lane's row
 #pragma unroll
   for (int nf = 0; nf < 2; nf++) {
     q[nf] = *reinterpret_cast<const u32x4*>(rq + L.qrow[nf] + 16 * qslot);
-    const uint32_t sp = *reinterpret_cast<const uint16_t*>(rs + L.srow[nf] + 4 * J + 2 * g2);
-    sig[nf] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sp, 1.0f, false);
+    if (FMT == FMT_MX) {
+      const int sb = *(rs + L.srow[nf] + 2 * J + g2);  // the block of k = 64J + 32g2 ..
+      pw[nf] = __builtin_ldexpf(1.0f, sb - 127 - L.roff[nf]);
+    } else {
+      const uint32_t sp = *reinterpret_cast<const uint16_t*>(rs + L.srow[nf] + 4 * J + 2 * g2);
+      sig[nf] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sp, 1.0f, false);
+    }
   }
   // Steps, each fenced so that the compiler keeps the order: the token
   // fragment reads of step s+1 are issued before the MFMAs of step s, and
   // the dequantisation of step s+1 is interleaved with those MFMAs.
   f16x8 a0[8], a1[8], b0[2], b1[2];
   read_a<NF>(a0, Ab, L.aoff[0]);
-  dequant_step(b0, q, sig, 0);
+  dequant_step<FMT>(b0, q, sig, pw, 0);
   __builtin_amdgcn_sched_barrier(0);
   read_a<NF>(a1, Ab, L.aoff[1]);
   __builtin_amdgcn_sched_barrier(0);
   mma_step<NF>(acc, a0, b0);
-  dequant_step(b1, q, sig, 1);
+  dequant_step<FMT>(b1, q, sig, pw, 1);
   interleave_mfma_valu<NF>();
   __builtin_amdgcn_sched_barrier(0);
   read_a<NF>(a0, Ab, L.aoff[2]);
   __builtin_amdgcn_sched_barrier(0);
   mma_step<NF>(acc, a1, b1);
-  dequant_step(b0, q, sig, 2);
+  dequant_step<FMT>(b0, q, sig, pw, 2);
   interleave_mfma_valu<NF>();
   __builtin_amdgcn_sched_barrier(0);
   read_a<NF>(a1, Ab, L.aoff[3]);
   __builtin_amdgcn_sched_barrier(0);
   mma_step<NF>(acc, a0, b0);
-  dequant_step(b1, q, sig, 3);
+  dequant_step<FMT>(b1, q, sig, pw, 3);
   interleave_mfma_valu<NF>();
   __builtin_amdgcn_sched_barrier(0);
   mma_step<NF>(acc, a1, b1);
@@ -519,12 +548,12 @@ __device__ __forceinline__ void big_chunk(const BigLane& L, f32x16 (&acc)[8][2],
     lds_barrier_vm<0>();
 }
 
-template <int NF, bool TOK, bool SPAN>
+template <int NF, bool TOK, bool SPAN, int FMT>
 __device__ __forceinline__ void big_span(const BigLane& L, f32x16 (&acc)[8][2], unsigned char* smem, int c, int wv) {
-  big_chunk<NF, 0, TOK, SPAN>(L, acc, smem, c, wv);
-  big_chunk<NF, 1, TOK, SPAN>(L, acc, smem, c + 1, wv);
-  big_chunk<NF, 2, TOK, SPAN>(L, acc, smem, c + 2, wv);
-  big_chunk<NF, 3, TOK, SPAN>(L, acc, smem, c + 3, wv);
+  big_chunk<NF, 0, TOK, SPAN, FMT>(L, acc, smem, c, wv);
+  big_chunk<NF, 1, TOK, SPAN, FMT>(L, acc, smem, c + 1, wv);
+  big_chunk<NF, 2, TOK, SPAN, FMT>(L, acc, smem, c + 2, wv);
+  big_chunk<NF, 3, TOK, SPAN, FMT>(L, acc, smem, c + 3, wv);
 }
 
 // 4x4 transpose across the four lanes of a quad: lane j's v[r] becomes lane
@@ -561,7 +590,7 @@ __device__ __forceinline__ void quad_transpose(float (&v)[4]) {
   }
 }
 
-template <int NF, bool GATEUP>
+template <int NF, bool GATEUP, int FMT>
 __device__ __forceinline__ void big_tile(const GroupedParams& p, const BigTile& t, unsigned char* smem) {
   const int lane = threadIdx.x % WAVE, m32 = lane % 32, g2 = lane / 32;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE), par = wv & 1;
@@ -587,7 +616,7 @@ __device__ __forceinline__ void big_tile(const GroupedParams& p, const BigTile& 
   // same up row (r >= 128) for gate/up, row rtile*256 + r for down; a code
   // instruction's lane l reads its row's piece (l%8) ^ (4(i%2) + l/16)
   {
-    const size_t qrow = (size_t)(K / 2), srow = (size_t)(K / 16);
+    const size_t qrow = (size_t)(K / 2), srow = (size_t)(K / (FMT == FMT_MX ? 32 : 16));
     if (GATEUP) {
       const size_t r0 = (size_t)(t.e - p.e_base) * t.N + t.rtile * (BIG_N / 2);
       L.q[0] = p.q0 + r0 * qrow;
@@ -604,7 +633,17 @@ __device__ __forceinline__ void big_tile(const GroupedParams& p, const BigTile& 
     // this wavefront's code instructions i = par, par+2, ..: rows 8i + l/8
     L.qlane = (uint32_t)((8 * par + lane / 8) * qrow + 16 * ((lane % 8) ^ (4 * par + lane / 16)));
     L.qstep = (uint32_t)(16 * qrow);
-    L.slane = (uint32_t)((64 * par + lane) * srow);
+    if (FMT == FMT_MX) {
+      L.slane = (uint32_t)((64 * par + lane / 2) * srow + 4 * (lane % 2));
+      L.sstep = (uint32_t)(32 * srow);
+      const float g0 = p.gs0[t.e - p.e_base], g1 = GATEUP ? p.gs1[t.e - p.e_base] : g0;
+      L.roff[0] = __builtin_amdgcn_frexp_expf(g0) - 1;  // fragment 0: gate rows (gate/up) or rows 64w..
+      L.roff[1] = __builtin_amdgcn_frexp_expf(GATEUP ? g1 : g0) - 1;
+    } else {
+      L.slane = (uint32_t)((64 * par + lane) * srow);
+      L.sstep = 0;
+      L.roff[0] = L.roff[1] = 0;
+    }
   }
   // LDS read offsets: token row 32f + m32 (f a compile-time offset); weight
   // fragment nf = tile rows 32w + 128nf (gate/up) or 64w + 32nf (down)
@@ -618,7 +657,7 @@ __device__ __forceinline__ void big_tile(const GroupedParams& p, const BigTile& 
     for (int nf = 0; nf < 2; nf++) {
       const int row = (GATEUP ? 32 * wv + 128 * nf : 64 * wv + 32 * nf) + m32;
       L.qrow[nf] = row * 128;
-      L.srow[nf] = row * 16;
+      L.srow[nf] = row * (FMT == FMT_MX ? 8 : 16);
     }
   }
   f32x16 acc[8][2];
@@ -635,8 +674,8 @@ __device__ __forceinline__ void big_tile(const GroupedParams& p, const BigTile& 
     const int pair = wv >> 1;
     if (pair == 0) {
       dma_tokens(L, smem, 0, 0, par);
-      dma_span_half(L, smem, 0, 0, 0, par);
-      dma_span_half(L, smem, 0, 0, 1, par);
+      dma_span_half<FMT>(L, smem, 0, 0, 0, par);
+      dma_span_half<FMT>(L, smem, 0, 0, 1, par);
       lds_barrier_vm<0>();
     } else {
       dma_tokens(L, smem, 1, BIG_KC, par);
@@ -644,12 +683,12 @@ __device__ __forceinline__ void big_tile(const GroupedParams& p, const BigTile& 
     }
   }
   int c = 0;
-  for (; c + BIG_SPAN < nch; c += BIG_SPAN) big_span<NF, true, true>(L, acc, smem, c, wv);
+  for (; c + BIG_SPAN < nch; c += BIG_SPAN) big_span<NF, true, true, FMT>(L, acc, smem, c, wv);
   // the last span: tokens of chunks c+2, c+3 still to copy, no next span
-  big_chunk<NF, 0, true, false>(L, acc, smem, c, wv);
-  big_chunk<NF, 1, true, false>(L, acc, smem, c + 1, wv);
-  big_chunk<NF, 2, false, false>(L, acc, smem, c + 2, wv);
-  big_chunk<NF, 3, false, false>(L, acc, smem, c + 3, wv);
+  big_chunk<NF, 0, true, false, FMT>(L, acc, smem, c, wv);
+  big_chunk<NF, 1, true, false, FMT>(L, acc, smem, c + 1, wv);
+  big_chunk<NF, 2, false, false, FMT>(L, acc, smem, c + 2, wv);
+  big_chunk<NF, 3, false, false, FMT>(L, acc, smem, c + 3, wv);
   // Epilogue.  Accumulator registers 4q .. 4q+3 of a lane hold rows
   // 8q + 4 g2 + 0..3 of its column m32; a quad transpose turns them into
   // four consecutive columns (m32 & ~3 ..) of row 8q + 4 g2 + (lane & 3), so
@@ -698,7 +737,7 @@ __device__ __forceinline__ void big_tile(const GroupedParams& p, const BigTile& 
     }
 }
 
-template <bool GATEUP>
+template <bool GATEUP, int FMT>
 __global__ __launch_bounds__(BIG_THREADS, 1) void expert_gemm_big_kernel(BigParams bp) {
   extern __shared__ __attribute__((aligned(16))) unsigned char big_smem[];
   int32_t* rowoff = reinterpret_cast<int32_t*>(big_smem + BIG_OFF_ROW);
@@ -729,13 +768,13 @@ __global__ __launch_bounds__(BIG_THREADS, 1) void expert_gemm_big_kernel(BigPara
   }
   __syncthreads();
   switch ((t.nvalid + 31) / 32) {  // token fragments, 1 .. 7
-    case 1: big_tile<1, GATEUP>(p, t, big_smem); break;
-    case 2: big_tile<2, GATEUP>(p, t, big_smem); break;
-    case 3: big_tile<3, GATEUP>(p, t, big_smem); break;
-    case 4: big_tile<4, GATEUP>(p, t, big_smem); break;
-    case 5: big_tile<5, GATEUP>(p, t, big_smem); break;
-    case 6: big_tile<6, GATEUP>(p, t, big_smem); break;
-    default: big_tile<BIG_MF, GATEUP>(p, t, big_smem); break;
+    case 1: big_tile<1, GATEUP, FMT>(p, t, big_smem); break;
+    case 2: big_tile<2, GATEUP, FMT>(p, t, big_smem); break;
+    case 3: big_tile<3, GATEUP, FMT>(p, t, big_smem); break;
+    case 4: big_tile<4, GATEUP, FMT>(p, t, big_smem); break;
+    case 5: big_tile<5, GATEUP, FMT>(p, t, big_smem); break;
+    case 6: big_tile<6, GATEUP, FMT>(p, t, big_smem); break;
+    default: big_tile<BIG_MF, GATEUP, FMT>(p, t, big_smem); break;
   }
 }
 
@@ -747,29 +786,31 @@ __global__ __launch_bounds__(BIG_THREADS, 1) void expert_gemm_big_kernel(BigPara
 constexpr int BIG_MIN_T = 1024;
 // Token rows are addressed with 32-bit byte offsets: 2 T H and 2 T k I must
 // stay below 2^32.
-// The large-tile kernels read NVFP4 only; MXFP4 runs on the small-batch
-// kernels at every size.
 bool use_big(const FfnArgs& a) {
   const long long ki = (long long)a.k * a.I, span = (long long)a.T * (a.H > ki ? a.H : ki);
-  return a.w->format == MOE_FMT_NVFP4 && a.T >= BIG_MIN_T && a.I % 256 == 0 && a.H % 256 == 0 &&
-         span < (1LL << 31);
+  return a.T >= BIG_MIN_T && a.I % 256 == 0 && a.H % 256 == 0 && span < (1LL << 31);
 }
 
-template <bool GATEUP>
-hipError_t launch_big(const FfnArgs& a, const GroupedParams& p, hipStream_t s) {
+template <bool GATEUP, int FMT>
+hipError_t launch_big_fmt(const FfnArgs& a, const GroupedParams& p, hipStream_t s) {
   BigParams bp;
   bp.g = p;
   bp.mtiles = a.mtiles;
   bp.n_mtiles = a.n_mtiles;
   bp.n_row_tiles = GATEUP ? a.I / (BIG_N / 2) : a.H / BIG_N;
   const size_t lds = BIG_LDS;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&expert_gemm_big_kernel<GATEUP>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&expert_gemm_big_kernel<GATEUP, FMT>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const long long items = (long long)a.max_mtiles * bp.n_row_tiles;
   const unsigned grid = (unsigned)(8 * ((items + 7) / 8));
-  hipLaunchKernelGGL((expert_gemm_big_kernel<GATEUP>), dim3(grid), dim3(BIG_THREADS), lds, s, bp);
+  hipLaunchKernelGGL((expert_gemm_big_kernel<GATEUP, FMT>), dim3(grid), dim3(BIG_THREADS), lds, s, bp);
   return hipGetLastError();
+}
+
+template <bool GATEUP>
+hipError_t launch_big(const FfnArgs& a, const GroupedParams& p, hipStream_t s) {
+  return a.w->format == MOE_FMT_MXFP4 ? launch_big_fmt<GATEUP, FMT_MX>(a, p, s) : launch_big_fmt<GATEUP, FMT_NV>(a, p, s);
 }
 
 // Combine: the positions (and weights) of 16 records, then their 16 row
