@@ -988,10 +988,11 @@ GroupedParams base_params(const FfnArgs& a) {
   return p;
 }
 
-// Row tiles per block: gate/up splits K over all four wavefronts (one
-// 32-column tile per block), down over two (two 64-column tiles per block).
-constexpr int GU_KSPLIT = 4;
-constexpr int DN_KSPLIT = 2;
+// Row tiles per block: gate/up splits K over two wavefronts (two 32-column
+// tiles per block); down does not split K (four 64-column tiles per block).
+// Measured on MI355X at T = 1, 64 and 256 against splits of 1, 2 and 4.
+constexpr int GU_KSPLIT = 2;
+constexpr int DN_KSPLIT = 1;
 
 // Measured on MI355X at T = 1, 64 and 256: a two-wavefronts-per-SIMD
 // register budget streams fastest.
