@@ -539,26 +539,81 @@ __device__ __forceinline__ void mma_step(f32x16 (&acc)[8][2], const f16x8 (&av)[
 
 // One wavefront per SIMD issues in order, and an MFMA blocks issue until the
 // matrix core takes it, so vector work only overlaps the matrix core when
-// it sits between MFMAs: one step's 2 NF MFMAs are spread over the next
-// step's dequantisation (about 18 vector instructions).
-template <int NF>
+// it sits between MFMAs: a step's 2 NF MFMAs are spread over the next
+// step's dequantisation (about 18 vector instructions), the first LEAD of
+// them with no vector work between them (time for LDS reads to land).
+// The next step's NDS token-fragment reads are spread over the first MFMAs
+// as well, one after each, rather than issued in a burst that can fill the
+// LDS command queue and hold up the next MFMA's issue.
+template <int NF, int LEAD = 0, int NDS = 0>
 __device__ __forceinline__ void interleave_mfma_valu() {
-  constexpr int per = (18 + 2 * NF - 1) / (2 * NF);
+  constexpr int rest = 2 * NF - LEAD;
+  constexpr int per = (20 + rest - 1) / rest;
 #pragma unroll
   for (int i = 0; i < 2 * NF; i++) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, per, 0);  // vector ALU
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // one MFMA
+    if (i < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+    if (i >= LEAD) __builtin_amdgcn_sched_group_barrier(0x002, per, 0);  // vector ALU
+  }
+}
+
+// What a wavefront carries from one chunk into the next: step 0's token
+// fragments (a) and dequantised weights (b), and the chunk's raw codes (q)
+// and block scales (sp raw, sig / pw converted) for the later steps.
+struct BigStep {
+  f16x8 a[8];
+  f16x8 b[2];
+  u32x4 q[2];
+  uint32_t sp[2];
+  f16x2 sig[2];
+  float pw[2];
+};
+
+// LDS reads of chunk J (of the span in slot `slot`): this lane's 16 code
+// bytes of each weight fragment and their scale bytes.
+template <int J, int FMT>
+__device__ __forceinline__ void read_chunk_b(const BigLane& L, const unsigned char* smem, int slot, BigStep& st) {
+  const unsigned char* rq = smem + BIG_OFF_RQ + slot * BIG_SPANQ_BYTES;
+  const unsigned char* rs = smem + BIG_OFF_RS + slot * BIG_SPANS_BYTES;
+  const int g2 = (threadIdx.x % WAVE) / 32, m32 = threadIdx.x % 32;
+  const int qslot = (2 * J + g2) ^ ((m32 / 2) % 8);  // piece 2J + g of the lane's row
+#pragma unroll
+  for (int nf = 0; nf < 2; nf++) {
+    st.q[nf] = *reinterpret_cast<const u32x4*>(rq + L.qrow[nf] + 16 * qslot);
+    if (FMT == FMT_MX)
+      st.sp[nf] = *(rs + L.srow[nf] + 2 * J + g2);  // the block of k = 64J + 32g2 ..
+    else
+      st.sp[nf] = *reinterpret_cast<const uint16_t*>(rs + L.srow[nf] + 4 * J + 2 * g2);
+  }
+}
+
+// The scale bytes as the dequantisation takes them.
+template <int FMT>
+__device__ __forceinline__ void convert_scales(const BigLane& L, BigStep& st) {
+#pragma unroll
+  for (int nf = 0; nf < 2; nf++) {
+    if (FMT == FMT_MX)
+      st.pw[nf] = __builtin_ldexpf(1.0f, (int)st.sp[nf] - 127 - L.roff[nf]);
+    else
+      st.sig[nf] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(st.sp[nf], 1.0f, false);
   }
 }
 
 // Chunk c = 4 s + J of the tile.  TOK: a chunk c+2 exists (its tokens are
 // copied by pair J % 2); SPAN: a span s+1 exists (its halves are copied in
-// J = 1 by pair B and J = 2 by pair A).  Then the four steps, with token
-// fragments read and weights dequantised one step ahead, and the barrier,
-// at which the pair that issued in chunk c-1 waits for its DMA.
-template <int NF, int J, bool TOK, bool SPAN, int FMT>
-__device__ __forceinline__ void big_chunk(const BigLane& L, f32x16 (&acc)[8][2], unsigned char* smem, int c,
-                                          int wv) {
+// J = 1 by pair B and J = 2 by pair A); NEXT: a chunk c+1 exists.  On entry
+// st holds step 0 of chunk c (token fragments read, weights dequantised)
+// and chunk c's codes and scales; on return the same for chunk c+1.  Token
+// fragments are read and weights dequantised one step ahead.  The barrier,
+// at which the pair that issued in chunk c-1 waits for its DMA, sits between
+// steps 2 and 3: after it the wavefront reads chunk c+1's codes, scales and
+// first token fragments, and dequantises its first weights, while step 3's
+// MFMAs run, so the matrix cores do not idle at the chunk boundary.  (Every
+// read of chunk c's token buffer has completed at the barrier, which is what
+// lets the next chunk's DMA overwrite it.)
+template <int NF, int J, bool TOK, bool SPAN, bool NEXT, int FMT>
+__device__ __forceinline__ void big_chunk(const BigLane& L, f32x16 (&acc)[8][2], unsigned char* smem, int c, int wv,
+                                          BigStep& st) {
   const int pair = wv >> 1, par = wv & 1;
   const int span = c / BIG_SPAN, slot = span & 1;
   const bool tok_issuer = pair == (J & 1);
@@ -568,63 +623,54 @@ __device__ __forceinline__ void big_chunk(const BigLane& L, f32x16 (&acc)[8][2],
     dma_span_half<FMT>(L, smem, slot ^ 1, (span + 1) * BIG_SPAN * BIG_KC, J == 1 ? 0 : 1, par);
   asm volatile("" ::: "memory");
   const unsigned char* Ab = smem + BIG_OFF_A + (c % 3) * BIG_TILE_BYTES;
-  const unsigned char* rq = smem + BIG_OFF_RQ + slot * BIG_SPANQ_BYTES;
-  const unsigned char* rs = smem + BIG_OFF_RS + slot * BIG_SPANS_BYTES;
-  u32x4 q[2];
-  f16x2 sig[2];
-  float pw[2];
-  const int g2 = (threadIdx.x % WAVE) / 32, m32 = threadIdx.x % 32;
-  const int qslot = (2 * J + g2) ^ ((m32 / 2) % 8);  // piece 2J + g of the lane's row
-#pragma unroll
-  for (int nf = 0; nf < 2; nf++) {
-    q[nf] = *reinterpret_cast<const u32x4*>(rq + L.qrow[nf] + 16 * qslot);
-    if (FMT == FMT_MX) {
-      const int sb = *(rs + L.srow[nf] + 2 * J + g2);  // the block of k = 64J + 32g2 ..
-      pw[nf] = __builtin_ldexpf(1.0f, sb - 127 - L.roff[nf]);
-    } else {
-      const uint32_t sp = *reinterpret_cast<const uint16_t*>(rs + L.srow[nf] + 4 * J + 2 * g2);
-      sig[nf] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sp, 1.0f, false);
-    }
-  }
-  // Steps, each fenced so that the compiler keeps the order: the token
-  // fragment reads of step s+1 are issued before the MFMAs of step s, and
-  // the dequantisation of step s+1 is interleaved with those MFMAs.
-  f16x8 a0[8], a1[8], b0[2], b1[2];
-  read_a<NF>(a0, Ab, L.aoff[0]);
-  dequant_step<FMT>(b0, q, sig, pw, 0);
-  __builtin_amdgcn_sched_barrier(0);
+  // Steps, each fenced so that the compiler keeps the order.
+  f16x8 a1[8], b1[2];
+  mma_step<NF>(acc, st.a, st.b);
   read_a<NF>(a1, Ab, L.aoff[1]);
-  __builtin_amdgcn_sched_barrier(0);
-  mma_step<NF>(acc, a0, b0);
-  dequant_step<FMT>(b1, q, sig, pw, 1);
-  interleave_mfma_valu<NF>();
-  __builtin_amdgcn_sched_barrier(0);
-  read_a<NF>(a0, Ab, L.aoff[2]);
+  dequant_step<FMT>(b1, st.q, st.sig, st.pw, 1);
+  interleave_mfma_valu<NF, 0, NF>();
   __builtin_amdgcn_sched_barrier(0);
   mma_step<NF>(acc, a1, b1);
-  dequant_step<FMT>(b0, q, sig, pw, 2);
-  interleave_mfma_valu<NF>();
+  read_a<NF>(st.a, Ab, L.aoff[2]);
+  dequant_step<FMT>(st.b, st.q, st.sig, st.pw, 2);
+  interleave_mfma_valu<NF, 0, NF>();
   __builtin_amdgcn_sched_barrier(0);
+  mma_step<NF>(acc, st.a, st.b);
   read_a<NF>(a1, Ab, L.aoff[3]);
+  dequant_step<FMT>(b1, st.q, st.sig, st.pw, 3);
+  interleave_mfma_valu<NF, 0, NF>();
   __builtin_amdgcn_sched_barrier(0);
-  mma_step<NF>(acc, a0, b0);
-  dequant_step<FMT>(b1, q, sig, pw, 3);
-  interleave_mfma_valu<NF>();
-  __builtin_amdgcn_sched_barrier(0);
-  mma_step<NF>(acc, a1, b1);
+  // (step 3's weights are computed here, beside step 2's MFMAs; without this
+  // the compiler sinks them past the barrier's branch)
+  asm volatile("" : "+v"(b1[0]), "+v"(b1[1]));
   const bool issued = (TOK && tok_issuer) || (SPAN && span_issuer);
   if (issued)
     lds_barrier_vm<63>();  // its copies stay in flight one more chunk
   else
     lds_barrier_vm<0>();
+  if (NEXT) {
+    constexpr int JN = (J + 1) % BIG_SPAN;
+    read_chunk_b<JN, FMT>(L, smem, JN == 0 ? slot ^ 1 : slot, st);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_step<NF>(acc, a1, b1);
+    read_a<NF>(st.a, smem + BIG_OFF_A + ((c + 1) % 3) * BIG_TILE_BYTES, L.aoff[0]);
+    convert_scales<FMT>(L, st);
+    dequant_step<FMT>(st.b, st.q, st.sig, st.pw, 0);
+    interleave_mfma_valu<NF, NF, NF>();
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" : "+v"(st.b[0]), "+v"(st.b[1]));  // (kept beside step 3's MFMAs)
+  } else {
+    mma_step<NF>(acc, a1, b1);
+  }
 }
 
 template <int NF, bool TOK, bool SPAN, int FMT>
-__device__ __forceinline__ void big_span(const BigLane& L, f32x16 (&acc)[8][2], unsigned char* smem, int c, int wv) {
-  big_chunk<NF, 0, TOK, SPAN, FMT>(L, acc, smem, c, wv);
-  big_chunk<NF, 1, TOK, SPAN, FMT>(L, acc, smem, c + 1, wv);
-  big_chunk<NF, 2, TOK, SPAN, FMT>(L, acc, smem, c + 2, wv);
-  big_chunk<NF, 3, TOK, SPAN, FMT>(L, acc, smem, c + 3, wv);
+__device__ __forceinline__ void big_span(const BigLane& L, f32x16 (&acc)[8][2], unsigned char* smem, int c, int wv,
+                                         BigStep& st) {
+  big_chunk<NF, 0, TOK, SPAN, true, FMT>(L, acc, smem, c, wv, st);
+  big_chunk<NF, 1, TOK, SPAN, true, FMT>(L, acc, smem, c + 1, wv, st);
+  big_chunk<NF, 2, TOK, SPAN, true, FMT>(L, acc, smem, c + 2, wv, st);
+  big_chunk<NF, 3, TOK, SPAN, true, FMT>(L, acc, smem, c + 3, wv, st);
 }
 
 // 4x4 transpose across the four lanes of a quad: lane j's v[r] becomes lane
@@ -753,13 +799,19 @@ __device__ __forceinline__ void big_tile(const GroupedParams& p, const BigTile& 
       lds_barrier_vm<63>();
     }
   }
+  // chunk 0's codes, scales and step 0
+  BigStep st;
+  read_chunk_b<0, FMT>(L, smem, 0, st);
+  read_a<NF>(st.a, smem + BIG_OFF_A, L.aoff[0]);
+  convert_scales<FMT>(L, st);
+  dequant_step<FMT>(st.b, st.q, st.sig, st.pw, 0);
   int c = 0;
-  for (; c + BIG_SPAN < nch; c += BIG_SPAN) big_span<NF, true, true, FMT>(L, acc, smem, c, wv);
+  for (; c + BIG_SPAN < nch; c += BIG_SPAN) big_span<NF, true, true, FMT>(L, acc, smem, c, wv, st);
   // the last span: tokens of chunks c+2, c+3 still to copy, no next span
-  big_chunk<NF, 0, true, false, FMT>(L, acc, smem, c, wv);
-  big_chunk<NF, 1, true, false, FMT>(L, acc, smem, c + 1, wv);
-  big_chunk<NF, 2, false, false, FMT>(L, acc, smem, c + 2, wv);
-  big_chunk<NF, 3, false, false, FMT>(L, acc, smem, c + 3, wv);
+  big_chunk<NF, 0, true, false, true, FMT>(L, acc, smem, c, wv, st);
+  big_chunk<NF, 1, true, false, true, FMT>(L, acc, smem, c + 1, wv, st);
+  big_chunk<NF, 2, false, false, true, FMT>(L, acc, smem, c + 2, wv, st);
+  big_chunk<NF, 3, false, false, false, FMT>(L, acc, smem, c + 3, wv, st);
   // Epilogue.  Accumulator registers 4q .. 4q+3 of a lane hold rows
   // 8q + 4 g2 + 0..3 of its column m32; a quad transpose turns them into
   // four consecutive columns (m32 & ~3 ..) of row 8q + 4 g2 + (lane & 3), so
