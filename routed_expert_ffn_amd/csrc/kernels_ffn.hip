@@ -77,7 +77,9 @@ __device__ __forceinline__ void load_b(Chunk<MF>& ch, const uint8_t* const (&qro
   }
 }
 
-// Block scales of a group of four consecutive chunks c .. c+3.  Lane (r, g)
+// Block scales of a group of four consecutive chunks c .. c+3 (c a multiple
+// of 4, so that a row's scale bytes of the group are one aligned 64-byte
+// (MXFP4: 32-byte) piece whichever wavefront loads them).  Lane (r, g)
 // of the wavefront (r = lane % 16, g = lane / 16) needs, in each chunk, the
 // scale word of its own 64-k quarter g (NVFP4: 4 bytes, MXFP4: 2) for its row
 // of every row group.  Loading those words one chunk at a time costs one
@@ -137,14 +139,11 @@ __device__ __forceinline__ void sq_transpose(uint32_t (&sq)[4][4]) {
   }
 }
 
-// The next chunk of the group moves into word 0.
-__device__ __forceinline__ void sq_shift(uint32_t (&sq)[4][4]) {
+// This lane's scale words of chunk c (of the group loaded for c & ~3).
+__device__ __forceinline__ void sq_pick(uint32_t (&w)[4], const uint32_t (&sq)[4][4], int c) {
+  const int i = c & 3;
 #pragma unroll
-  for (int ng = 0; ng < 4; ng++) {
-    sq[ng][0] = sq[ng][1];
-    sq[ng][1] = sq[ng][2];
-    sq[ng][2] = sq[ng][3];
-  }
+  for (int ng = 0; ng < 4; ng++) w[ng] = i == 0 ? sq[ng][0] : i == 1 ? sq[ng][1] : i == 2 ? sq[ng][2] : sq[ng][3];
 }
 
 template <int MF>
@@ -162,7 +161,7 @@ __device__ __forceinline__ void load_a(Chunk<MF>& ch, const f16* const (&arow)[M
 // 2^(scale - 127 - roff[ng]) itself (roff: the matrix's per-tensor power of
 // two, applied back in fp32 with gs).
 template <int MF, int FMT = FMT_NV>
-__device__ __forceinline__ void mma_chunk(f32x4 (&acc)[MF][4], const Chunk<MF>& ch, const uint32_t (&sq)[4][4],
+__device__ __forceinline__ void mma_chunk(f32x4 (&acc)[MF][4], const Chunk<MF>& ch, const uint32_t (&sw)[4],
                                           int nvalid, const int (&roff)[4]) {
 #pragma unroll
   for (int s = 0; s < 8; s++) {
@@ -171,10 +170,10 @@ __device__ __forceinline__ void mma_chunk(f32x4 (&acc)[MF][4], const Chunk<MF>& 
       const uint32_t codes = s < 4 ? (&ch.qa[ng].x)[s] : (&ch.qb[ng].x)[s - 4];
       f16x8 bf;
       if (FMT == FMT_MX) {
-        const int sb = (int)((sq[ng][0] >> (8 * (s / 4))) & 0xFFu);
+        const int sb = (int)((sw[ng] >> (8 * (s / 4))) & 0xFFu);
         bf = dequant8_pow2(codes, __builtin_ldexpf(1.0f, sb - 127 - roff[ng]));
       } else {
-        const f16 sig = e4m3_to_f16((sq[ng][0] >> (8 * (s / 2))) & 0xFFu);
+        const f16 sig = e4m3_to_f16((sw[ng] >> (8 * (s / 2))) & 0xFFu);
         f16x2 sig2;
         sig2[0] = sig;
         sig2[1] = sig;
@@ -240,7 +239,7 @@ __global__ __launch_bounds__(FFN_THREADS, WAVES_PER_EU) void expert_gemm_kernel(
   uint32_t sq[4][4];
   if (c_lo < c_hi) {  // before the token lookups
     load_b(cur, qrow, c_lo * KCHUNK + 64 * g);
-    load_sq<FMT>(sq, srow, c_lo, nchunks, g);
+    load_sq<FMT>(sq, srow, c_lo & ~3, nchunks, g);
   }
   const int begin = p.offsets[e], end = p.offsets[e + 1];
   const float gsa = p.gs0[el], gsb = GATEUP ? p.gs1[el] : 0.0f;
@@ -269,21 +268,20 @@ __global__ __launch_bounds__(FFN_THREADS, WAVES_PER_EU) void expert_gemm_kernel(
     if (c_lo < c_hi) {
       if (!first_pass) {
         load_b(cur, qrow, c_lo * KCHUNK + 64 * g);
-        load_sq<FMT>(sq, srow, c_lo, nchunks, g);
+        load_sq<FMT>(sq, srow, c_lo & ~3, nchunks, g);
       }
       load_a(cur, arow, c_lo * KCHUNK + 64 * g, nvalid);
     }
     first_pass = false;
     for (int c = c_lo; c < c_hi; c++) {
-      if (((c - c_lo) & 3) == 0) sq_transpose<FMT>(sq);
-      mma_chunk<MF, FMT>(acc, cur, sq, nvalid, roff);
+      if (c == c_lo || (c & 3) == 0) sq_transpose<FMT>(sq);
+      uint32_t sw[4];
+      sq_pick(sw, sq, c);
+      mma_chunk<MF, FMT>(acc, cur, sw, nvalid, roff);
       if (c + 1 < c_hi) {
         const int kb = (c + 1) * KCHUNK + 64 * g;
         load_b(cur, qrow, kb);
-        if (((c + 1 - c_lo) & 3) == 0)
-          load_sq<FMT>(sq, srow, c + 1, nchunks, g);
-        else
-          sq_shift(sq);
+        if (((c + 1) & 3) == 0) load_sq<FMT>(sq, srow, c + 1, nchunks, g);
         load_a(cur, arow, kb, nvalid);
       }
     }
