@@ -54,6 +54,34 @@ struct GroupedParams {
   const float* pair_w; //     the routing weights [T*k], indexed by record (sorted_pairs[p])
 };
 
+// Barrier for LDS hand-off: this wavefront's LDS accesses and all but its
+// last N vector-memory instructions have completed when it arrives (N = 63:
+// no vector-memory wait at all).  The memory clobber keeps the compiler from
+// moving memory accesses across it, and unlike __syncthreads() it adds no
+// fence of its own.
+template <int N>
+__device__ __forceinline__ void lds_barrier_vm() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// LDS DMA of 16 (4) bytes per lane from gbase + voff to LDS address lds +
+// 16 (4) * lane, written as instructions of our own: the compiler would
+// otherwise count the copies as outstanding LDS work and wait for all LDS
+// traffic (lgkmcnt(0)) before every use of an LDS read, serialising the
+// fragment reads with the MFMAs.  Every wait for these copies is explicit
+// (lds_barrier_vm).  gbase and lds are wave-uniform (scalar registers).
+__device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
+  return (uint32_t)(size_t)(const __attribute__((address_space(3))) unsigned char*)p;
+}
+__device__ __forceinline__ void dma16(const unsigned char* gbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const unsigned char* gbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(gbase), "s"(lds)
+               : "memory", "m0");
+}
+
 // One 256-k chunk of a wavefront's operands: per weight row group ng, 32
 // NVFP4 code bytes (64 consecutive k); per token fragment f, the eight A
 // fragments of the chunk.  All of a chunk's loads are issued together so the
@@ -146,6 +174,34 @@ __device__ __forceinline__ void sq_pick(uint32_t (&w)[4], const uint32_t (&sq)[4
   for (int ng = 0; ng < 4; ng++) w[ng] = i == 0 ? sq[ng][0] : i == 1 ? sq[ng][1] : i == 2 ? sq[ng][2] : sq[ng][3];
 }
 
+// Scales staged in LDS.  A block's weight rows are consecutive in each
+// matrix, so the block scales of all of them are one contiguous piece per
+// matrix (gate/up: the gate rows and the same up rows; down: the rows).  The
+// block copies these pieces into LDS once, as 16-byte-per-lane LDS DMA over
+// whole lines, and each wavefront then reads its words chunk by chunk.  Read
+// from memory in 64-byte pieces per row and group of four chunks instead,
+// every 128-byte line was fetched twice: its two halves are read some
+// microseconds apart, and by then the L2 no longer holds it.
+__device__ __forceinline__ void stage_scales(unsigned char* lds, const uint8_t* src, int bytes, int wv, int lane) {
+  // src is the same in every lane (one block's piece); the DMA takes it in scalar registers
+  const uint64_t sa = (uint64_t)(size_t)src;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)sa), hi = __builtin_amdgcn_readfirstlane((uint32_t)(sa >> 32));
+  src = reinterpret_cast<const uint8_t*>((size_t)(((uint64_t)hi << 32) | lo));
+  const uint32_t dst = lds_addr(lds);
+  for (int i = __builtin_amdgcn_readfirstlane(wv); i * 1024 < bytes; i += FFN_THREADS / WAVE)
+    if (i * 1024 + 16 * lane < bytes) dma16(src, (uint32_t)(i * 1024 + 16 * lane), dst + (uint32_t)(i * 1024));
+}
+
+// This lane's scale words of chunk c from the staged rows (byte offsets lsrow).
+template <int FMT>
+__device__ __forceinline__ void staged_words(uint32_t (&w)[4], const unsigned char* lds, const int (&lsrow)[4], int c,
+                                             int g) {
+#pragma unroll
+  for (int ng = 0; ng < 4; ng++)
+    w[ng] = FMT == FMT_MX ? (uint32_t)*reinterpret_cast<const uint16_t*>(lds + lsrow[ng] + 8 * c + 2 * g)
+                          : *reinterpret_cast<const uint32_t*>(lds + lsrow[ng] + 16 * c + 4 * g);
+}
+
 template <int MF>
 __device__ __forceinline__ void load_a(Chunk<MF>& ch, const f16* const (&arow)[MF], int kb, int nvalid) {
 #pragma unroll
@@ -202,10 +258,11 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 // looked up; each later chunk's loads are issued once the previous chunk has
 // been multiplied.  Partial sums of the KSPLIT wavefronts meet in LDS and
 // are added in a fixed order.
-template <int MF, int KSPLIT, bool GATEUP, int WAVES_PER_EU, int FMT>
+template <int MF, int KSPLIT, bool GATEUP, int WAVES_PER_EU, int FMT, bool SLDS>
 __global__ __launch_bounds__(FFN_THREADS, WAVES_PER_EU) void expert_gemm_kernel(GroupedParams p) {
   constexpr int RT = 4 / KSPLIT;
   __shared__ float red[KSPLIT > 1 ? 4 : 1][WAVE][MF * 16];
+  extern __shared__ __align__(16) unsigned char staged[];
   if ((int)blockIdx.y >= *p.n_active) return;
   const int e = p.active[blockIdx.y], el = e - p.e_base;
   const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE, r = lane % 16, g = lane / 16;
@@ -235,11 +292,26 @@ __global__ __launch_bounds__(FFN_THREADS, WAVES_PER_EU) void expert_gemm_kernel(
   const int nchunks = K / KCHUNK;
   const int per = (nchunks + KSPLIT - 1) / KSPLIT;
   const int c_lo = min(ks * per, nchunks), c_hi = min(c_lo + per, nchunks);
+  // staged scales: this lane's rows within the block's pieces
+  const int SB = K / (FMT == FMT_MX ? 32 : 16);
+  int lsrow[4];
+  if (SLDS) {
+    const size_t r0 = (size_t)el * N + (size_t)blockIdx.x * RT * (GATEUP ? 32 : 64);
+    if (GATEUP) {
+      stage_scales(staged, p.sf0 + r0 * SB, RT * 32 * SB, wv, lane);
+      stage_scales(staged + RT * 32 * SB, p.sf1 + r0 * SB, RT * 32 * SB, wv, lane);
+    } else {
+      stage_scales(staged, p.sf0 + r0 * SB, RT * 64 * SB, wv, lane);
+    }
+#pragma unroll
+    for (int ng = 0; ng < 4; ng++)
+      lsrow[ng] = GATEUP ? ((ng >> 1) * RT * 32 + rt * 32 + 16 * (ng & 1) + r) * SB : (rt * 64 + 16 * ng + r) * SB;
+  }
   Chunk<MF> cur;
   uint32_t sq[4][4];
   if (c_lo < c_hi) {  // before the token lookups
     load_b(cur, qrow, c_lo * KCHUNK + 64 * g);
-    load_sq<FMT>(sq, srow, c_lo & ~3, nchunks, g);
+    if (!SLDS) load_sq<FMT>(sq, srow, c_lo & ~3, nchunks, g);
   }
   const int begin = p.offsets[e], end = p.offsets[e + 1];
   const float gsa = p.gs0[el], gsb = GATEUP ? p.gs1[el] : 0.0f;
@@ -268,20 +340,29 @@ __global__ __launch_bounds__(FFN_THREADS, WAVES_PER_EU) void expert_gemm_kernel(
     if (c_lo < c_hi) {
       if (!first_pass) {
         load_b(cur, qrow, c_lo * KCHUNK + 64 * g);
-        load_sq<FMT>(sq, srow, c_lo & ~3, nchunks, g);
+        if (!SLDS) load_sq<FMT>(sq, srow, c_lo & ~3, nchunks, g);
       }
       load_a(cur, arow, c_lo * KCHUNK + 64 * g, nvalid);
     }
+    uint32_t sw[4];
+    if (SLDS) {
+      if (first_pass) lds_barrier_vm<0>();  // the staged scales (and chunk c_lo) have landed
+      if (c_lo < c_hi) staged_words<FMT>(sw, staged, lsrow, c_lo, g);
+    }
     first_pass = false;
     for (int c = c_lo; c < c_hi; c++) {
-      if (c == c_lo || (c & 3) == 0) sq_transpose<FMT>(sq);
-      uint32_t sw[4];
-      sq_pick(sw, sq, c);
+      if (!SLDS) {
+        if (c == c_lo || (c & 3) == 0) sq_transpose<FMT>(sq);
+        sq_pick(sw, sq, c);
+      }
       mma_chunk<MF, FMT>(acc, cur, sw, nvalid, roff);
       if (c + 1 < c_hi) {
         const int kb = (c + 1) * KCHUNK + 64 * g;
         load_b(cur, qrow, kb);
-        if (((c + 1) & 3) == 0) load_sq<FMT>(sq, srow, c + 1, nchunks, g);
+        if (SLDS)
+          staged_words<FMT>(sw, staged, lsrow, c + 1, g);
+        else if (((c + 1) & 3) == 0)
+          load_sq<FMT>(sq, srow, c + 1, nchunks, g);
         load_a(cur, arow, kb, nvalid);
       }
     }
@@ -411,34 +492,6 @@ struct BigParams {
   const int32_t* n_mtiles;  // [1]
   int n_row_tiles;          // row tiles of BIG_N weight rows per expert
 };
-
-// Barrier for LDS hand-off: this wavefront's LDS accesses and all but its
-// last N vector-memory instructions have completed when it arrives (N = 63:
-// no vector-memory wait at all).  The memory clobber keeps the compiler from
-// moving memory accesses across it, and unlike __syncthreads() it adds no
-// fence of its own.
-template <int N>
-__device__ __forceinline__ void lds_barrier_vm() {
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
-}
-
-// LDS DMA of 16 (4) bytes per lane from gbase + voff to LDS address lds +
-// 16 (4) * lane, written as instructions of our own: the compiler would
-// otherwise count the copies as outstanding LDS work and wait for all LDS
-// traffic (lgkmcnt(0)) before every use of an LDS read, serialising the
-// fragment reads with the MFMAs.  Every wait for these copies is explicit
-// (lds_barrier_vm).  gbase and lds are wave-uniform (scalar registers).
-__device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
-  return (uint32_t)(size_t)(const __attribute__((address_space(3))) unsigned char*)p;
-}
-__device__ __forceinline__ void dma16(const unsigned char* gbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "s"(lds)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const unsigned char* gbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(gbase), "s"(lds)
-               : "memory", "m0");
-}
 
 struct BigTile {
   int e, mb, nvalid, rtile, K, N;
@@ -1048,17 +1101,30 @@ constexpr int DN_KSPLIT = 1;
 // register budget streams fastest.
 constexpr int GEMM_WAVES = 2;
 
-template <int KSPLIT, bool GATEUP, int FMT>
-hipError_t launch_gemm_fmt(const GroupedParams& p, int mf, dim3 grid, hipStream_t s) {
-  switch (mf) {
-    case 1:
-      hipLaunchKernelGGL((expert_gemm_kernel<1, KSPLIT, GATEUP, GEMM_WAVES, FMT>), grid, dim3(FFN_THREADS), 0, s, p);
-      break;
-    default:
-      hipLaunchKernelGGL((expert_gemm_kernel<4, KSPLIT, GATEUP, 1, FMT>), grid, dim3(FFN_THREADS), 0, s, p);
-      break;
+// Block scales are staged in LDS when a block's piece (4/KSPLIT row tiles of
+// 64 rows) fits in STAGE_MAX bytes: K up to 8192 for gate/up and 4096 for
+// down with NVFP4.  Larger K reads them from memory in groups of four chunks.
+constexpr int STAGE_MAX = 64 * 1024;
+
+template <int MF, int KSPLIT, bool GATEUP, int WAVES, int FMT>
+hipError_t launch_gemm_stage(const GroupedParams& p, dim3 grid, hipStream_t s) {
+  const int K = GATEUP ? p.H : p.I;
+  const int bytes = (4 / KSPLIT) * 64 * (K / (FMT == FMT_MX ? 32 : 16));
+  if (bytes <= STAGE_MAX) {
+    const void* f = reinterpret_cast<const void*>(&expert_gemm_kernel<MF, KSPLIT, GATEUP, WAVES, FMT, true>);
+    const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, STAGE_MAX);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((expert_gemm_kernel<MF, KSPLIT, GATEUP, WAVES, FMT, true>), grid, dim3(FFN_THREADS), bytes, s, p);
+  } else {
+    hipLaunchKernelGGL((expert_gemm_kernel<MF, KSPLIT, GATEUP, WAVES, FMT, false>), grid, dim3(FFN_THREADS), 0, s, p);
   }
   return hipGetLastError();
+}
+
+template <int KSPLIT, bool GATEUP, int FMT>
+hipError_t launch_gemm_fmt(const GroupedParams& p, int mf, dim3 grid, hipStream_t s) {
+  return mf == 1 ? launch_gemm_stage<1, KSPLIT, GATEUP, GEMM_WAVES, FMT>(p, grid, s)
+                 : launch_gemm_stage<4, KSPLIT, GATEUP, 1, FMT>(p, grid, s);
 }
 
 template <int KSPLIT, bool GATEUP>
