@@ -175,6 +175,26 @@ def test_ragged_layer(T, E, k, beta):
     assert_close(y, ref["y"], "y")
 
 
+@pytest.mark.parametrize("H,I,fmt,T", [(8448, 256, "nvfp4", 8), (512, 4352, "nvfp4", 300), (512, 8448, "mxfp4", 40)])
+def test_wide_k_scales_from_memory(H, I, fmt, T):
+    """K beyond what a block can stage of its block scales in LDS (gate/up K
+    over 8192, down K over 4096 for NVFP4, twice that for MXFP4): those GEMMs
+    read the scales from memory in groups of four chunks, the others stage
+    them; experts with one and with several 16-token passes."""
+    say(f"wide K H={H} I={I} {fmt} T={T}")
+    E, k = 8, 4
+    store = build_store(E, H, I, 12, fmt=fmt)
+    inp = Inputs(T, H, I, E, k, seed=12, store=store, router_std=0.1)
+    r = inp.route()
+    ox = OracleExperts(12, H, I, fmt=fmt)
+    ref = oracle.moe_layer(inp.host_x(), ox.get(r["ids"]), E, k, logits_in=r["logits"], want_rows=True, nthreads=16)
+    rows = inp.ffn(r["offsets"], r["sorted_pairs"])
+    assert_close(rows, ref["rows"], "rows")
+    y, ids, _ = inp.layer()
+    np.testing.assert_array_equal(ids, ref["ids"])
+    assert_close(y, ref["y"], "y")
+
+
 def test_route_ties_logits_in():
     """Constructed fp32 logits with exact ties (all equal, +-0, duplicated
     values): the selection must follow (logit desc, index asc) bit-exactly."""
