@@ -24,6 +24,7 @@ constexpr int RT_THREADS = 256;
 constexpr int ROUTER_MAX_SLABS = 32;  // K slabs of the router, at most
 constexpr int RT_E_TILE = 128;
 constexpr int RT_ROWS_PER_STEP = 16;
+constexpr int RT_BATCH = 16;  // weight rows per thread in flight
 
 template <int TT>
 __global__ __launch_bounds__(RT_THREADS) void router_gemv_kernel(const uint16_t* __restrict__ x,
@@ -39,6 +40,20 @@ __global__ __launch_bounds__(RT_THREADS) void router_gemv_kernel(const uint16_t*
   const int h0 = blockIdx.y * slab_rows;
   const int t0 = blockIdx.z * TT;
   const int rows = min(slab_rows, H - h0);
+  // Rows in batches of RT_BATCH loads in flight, then their FMAs in row
+  // order.  The first batch is issued before the activations are staged (it
+  // does not depend on them), so a slab of up to RT_BATCH * 16 rows costs
+  // one memory round trip for the weights, overlapped with the one for x.
+  uint4 w8[RT_BATCH];
+  const bool active = e0 < E;
+  auto load_batch = [&](int r0) {
+#pragma unroll
+    for (int b = 0; b < RT_BATCH; b++) {
+      const int r = r0 + b * RT_ROWS_PER_STEP;
+      w8[b] = r < rows ? *reinterpret_cast<const uint4*>(wr + (size_t)(h0 + r) * E + e0) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  if (active) load_batch(4 * wv + rr);
   for (int i = threadIdx.x; i < TT * slab_rows; i += RT_THREADS) {
     const int a = i / slab_rows, r = i % slab_rows;
     xs[i] = (t0 + a < T && r < rows) ? bf16_to_f32(x[(size_t)(t0 + a) * H + h0 + r]) : 0.0f;
@@ -49,17 +64,11 @@ __global__ __launch_bounds__(RT_THREADS) void router_gemv_kernel(const uint16_t*
   for (int a = 0; a < TT; a++)
 #pragma unroll
     for (int i = 0; i < 8; i++) acc[a][i] = 0.0f;
-  if (e0 < E) {
-    // rows in batches of eight loads in flight, then their FMAs in row order
-    for (int r0 = 4 * wv + rr; r0 < rows; r0 += 8 * RT_ROWS_PER_STEP) {
-      uint4 w8[8];
+  if (active) {
+    for (int r0 = 4 * wv + rr; r0 < rows; r0 += RT_BATCH * RT_ROWS_PER_STEP) {
+      if (r0 != 4 * wv + rr) load_batch(r0);
 #pragma unroll
-      for (int b = 0; b < 8; b++) {
-        const int r = r0 + b * RT_ROWS_PER_STEP;
-        w8[b] = r < rows ? *reinterpret_cast<const uint4*>(wr + (size_t)(h0 + r) * E + e0) : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int b = 0; b < 8; b++) {
+      for (int b = 0; b < RT_BATCH; b++) {
         const int r = r0 + b * RT_ROWS_PER_STEP;
         if (r < rows) {
           float wf[8];
