@@ -19,13 +19,15 @@
 // multiply applies the e4m3 block scale (exact, see common.h).  The fp32
 // per-tensor scale is applied once per output.
 //
-// Loads.  A block owns 64 weight rows (4 groups of 16).  Per 256-k chunk,
-// lane (r = l%16, g = l/16) reads 32 bytes (64 codes) of row r at k offset
-// 64g and the 4 scale bytes of those 64 codes, so each row's 128-byte span
-// of the chunk is read whole by one wavefront.  Code dword s (k = 64g+8s..)
-// is exactly the B fragment of MFMA step s, so the k order inside an MFMA is
-// permuted consistently for A and B.  The four wavefronts of a block take
-// interleaved chunks of K and are reduced through LDS in a fixed order.
+// Loads.  A wavefront owns 64 weight rows (4 groups of 16).  Per 256-k
+// chunk, lane (r = l%16, g = l/16) reads 32 bytes (64 codes) of row r at k
+// offset 64g and uses the 4 scale bytes of those 64 codes, so each row's
+// 128-byte span of the chunk is read whole by one wavefront.  Code dword s
+// (k = 64g+8s..) is exactly the B fragment of MFMA step s, so the k order
+// inside an MFMA is permuted consistently for A and B.  The wavefronts that
+// share rows split K into contiguous ranges and are reduced through LDS in a
+// fixed order; the block scales of all the block's rows are staged in LDS
+// once.
 #include "internal.h"
 
 namespace moe {
@@ -248,8 +250,9 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 // active list).  A block is four wavefronts; KSPLIT consecutive wavefronts
 // share one 64-row tile and each takes a contiguous range of its 256-k
 // chunks, so a block covers 4/KSPLIT row tiles.  (Contiguous ranges let one
-// scale load serve four chunks; they read about 3% slower than interleaved
-// chunks, far less than the scale loads save.)
+// grouped scale load serve four chunks; they read about 3% slower than
+// interleaved chunks, far less than per-chunk scale loads cost.)  SLDS: the
+// block scales are staged in LDS (dynamic shared memory) at the start.
 //   GATEUP: a row tile is 32 columns of h: gate rows (groups 0, 1) and the
 //           same up rows (groups 2, 3); the epilogue applies the per-tensor
 //           scales and SiLU(gate) * up and stores h in fp16.
