@@ -15,6 +15,7 @@ timed on a bounded sample of the same workload.
 """
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -57,10 +58,21 @@ def mxfp4_bytes(N, K):
     return N * (K // 2) + N * (K // 32) + 4
 
 
-def kernel_source_sha():
+def code_text(src):
+    """Source text without comments and whitespace: what the compiler sees
+    of it (string literals in these files hold no comment markers)."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return "".join(src.split())
+
+
+def kernel_source_sha(sources=None):
+    """Identifies the GEMM kernels' code (comments and layout excluded), so
+    that counter records taken on it are used only while it is unchanged."""
     h = hashlib.sha256()
     for f in ("kernels_ffn.hip", "common.h"):
-        h.update(open(os.path.join(ROOT, "routed_expert_ffn_amd", "csrc", f), "rb").read())
+        text = sources[f] if sources else open(os.path.join(ROOT, "routed_expert_ffn_amd", "csrc", f)).read()
+        h.update(code_text(text).encode())
     return h.hexdigest()[:16]
 
 
