@@ -98,12 +98,62 @@ struct Chunk {
 // and MXFP4 (e8m0 power-of-two scale per 32 k, 2 bytes per 64 codes).
 enum WeightFmt { FMT_NV = 0, FMT_MX = 1 };
 
-template <int MF>
-__device__ __forceinline__ void load_b(Chunk<MF>& ch, const uint8_t* const (&qrow)[4], int kb) {
+// Codes of chunk c.  The MFMA wants lane (r, g) = (l%16, l/16) to hold
+// pieces 2g and 2g+1 (16 bytes each) of row r of its 16-row group, but
+// loads in that shape cover half of each 128-byte line per instruction.
+// Instead each instruction covers 8 whole lines: lane l loads piece l/8 of
+// row l%8 (qa) and of row 8 + l%8 (qb), as non-temporal loads (the codes
+// are read once).  Measured on a cold 252 MiB read: 6.1 TB/s this way
+// against 5.2-5.4 TB/s for any half-line or cached pattern.
+// codes_to_fragments then moves the pieces into place.
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_nt16(const uint8_t* p) {
+  const u32x4v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// R8 = false keeps the fragment shape (lane (r, g) loads bytes 32g .. 32g+31
+// of row r), which stays faster for the down GEMM when experts take several
+// 16-token passes over their weights (measured at 64 and 256 tokens).
+template <int MF, bool R8>
+__device__ __forceinline__ void load_b(Chunk<MF>& ch, const uint8_t* const (&grp)[4], int c, size_t row_bytes) {
+  const int lane = threadIdx.x % WAVE;
 #pragma unroll
   for (int ng = 0; ng < 4; ng++) {
-    ch.qa[ng] = *reinterpret_cast<const uint4*>(qrow[ng] + kb / 2);
-    ch.qb[ng] = *reinterpret_cast<const uint4*>(qrow[ng] + kb / 2 + 16);
+    if (R8) {
+      const uint8_t* p = grp[ng] + (size_t)(lane % 8) * row_bytes + 128 * (size_t)c + 16 * (lane / 8);
+      ch.qa[ng] = load_nt16(p);
+      ch.qb[ng] = load_nt16(p + 8 * row_bytes);
+    } else {
+      const uint8_t* p = grp[ng] + (size_t)(lane % 16) * row_bytes + 128 * (size_t)c + 32 * (lane / 16);
+      ch.qa[ng] = *reinterpret_cast<const uint4*>(p);
+      ch.qb[ng] = *reinterpret_cast<const uint4*>(p + 16);
+    }
+  }
+}
+
+// Lane l = r + 16g holds in qa piece l/8 of row l%8: for r < 8 that is its
+// own piece 2g of row r, for r >= 8 piece 2g+1 of row r-8, which lane l-8
+// needs; in qb piece l/8 of row 8 + l%8: for r >= 8 its own piece 2g+1 of
+// row r, for r < 8 piece 2g of row r+8, which lane l+8 needs.  One exchange
+// between lanes 8 apart in each row of 16 puts piece 2g in qa and piece
+// 2g+1 in qb everywhere: a DPP row rotation by 8 whose bank mask writes only
+// the lanes that take the moved word (banks 0-1 = lanes 0-7 of a row, banks
+// 2-3 = lanes 8-15), two instructions per word, both reading the words as
+// loaded.
+template <int BANKS>
+__device__ __forceinline__ uint32_t from_lane8_apart(uint32_t keep, uint32_t src) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)keep, (int)src, 0x128, 0xF, BANKS, false);  // row_ror:8
+}
+__device__ __forceinline__ void codes_to_fragments(uint4& qa, uint4& qb) {
+  uint32_t* a = &qa.x;
+  uint32_t* b = &qb.x;
+#pragma unroll
+  for (int d = 0; d < 4; d++) {
+    const uint32_t na = from_lane8_apart<0xC>(a[d], b[d]);  // lanes 8-15: qb of lane - 8
+    const uint32_t nb = from_lane8_apart<0x3>(b[d], a[d]);  // lanes 0-7: qa of lane + 8
+    a[d] = na;
+    b[d] = nb;
   }
 }
 
@@ -218,9 +268,12 @@ __device__ __forceinline__ void load_a(Chunk<MF>& ch, const f16* const (&arow)[M
 // MXFP4: step s's codes share the scale byte s/4; the conversion applies
 // 2^(scale - 127 - roff[ng]) itself (roff: the matrix's per-tensor power of
 // two, applied back in fp32 with gs).
-template <int MF, int FMT = FMT_NV>
-__device__ __forceinline__ void mma_chunk(f32x4 (&acc)[MF][4], const Chunk<MF>& ch, const uint32_t (&sw)[4],
+template <int MF, int FMT, bool R8>
+__device__ __forceinline__ void mma_chunk(f32x4 (&acc)[MF][4], Chunk<MF>& ch, const uint32_t (&sw)[4],
                                           int nvalid, const int (&roff)[4]) {
+  if (R8)
+#pragma unroll
+    for (int ng = 0; ng < 4; ng++) codes_to_fragments(ch.qa[ng], ch.qb[ng]);
 #pragma unroll
   for (int s = 0; s < 8; s++) {
 #pragma unroll
@@ -261,7 +314,7 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 // looked up; each later chunk's loads are issued once the previous chunk has
 // been multiplied.  Partial sums of the KSPLIT wavefronts meet in LDS and
 // are added in a fixed order.
-template <int MF, int KSPLIT, bool GATEUP, int WAVES_PER_EU, int FMT, bool SLDS>
+template <int MF, int KSPLIT, bool GATEUP, int WAVES_PER_EU, int FMT, bool SLDS, bool R8>
 __global__ __launch_bounds__(FFN_THREADS, WAVES_PER_EU) void expert_gemm_kernel(GroupedParams p) {
   constexpr int RT = 4 / KSPLIT;
   __shared__ float red[KSPLIT > 1 ? 4 : 1][WAVE][MF * 16];
@@ -273,8 +326,8 @@ __global__ __launch_bounds__(FFN_THREADS, WAVES_PER_EU) void expert_gemm_kernel(
   const int K = GATEUP ? p.H : p.I;
   const int N = GATEUP ? p.I : p.H;
   const int tile = blockIdx.x * RT + rt;
-  const uint8_t* qrow[4];
-  const uint8_t* srow[4];
+  const uint8_t* qrow[4];  // codes: first row of each 16-row group
+  const uint8_t* srow[4];  // scales: this lane's row
 #pragma unroll
   for (int ng = 0; ng < 4; ng++) {
     size_t row;
@@ -289,9 +342,10 @@ __global__ __launch_bounds__(FFN_THREADS, WAVES_PER_EU) void expert_gemm_kernel(
       qb = p.q0;
       sb = p.sf0;
     }
-    qrow[ng] = qb + row * (K / 2);
+    qrow[ng] = qb + (row - r) * (K / 2);  // row 0 of the lane's 16-row group
     srow[ng] = sb + row * (K / (FMT == FMT_MX ? 32 : 16));
   }
+  const size_t row_bytes = (size_t)(K / 2);
   const int nchunks = K / KCHUNK;
   const int per = (nchunks + KSPLIT - 1) / KSPLIT;
   const int c_lo = min(ks * per, nchunks), c_hi = min(c_lo + per, nchunks);
@@ -313,7 +367,7 @@ __global__ __launch_bounds__(FFN_THREADS, WAVES_PER_EU) void expert_gemm_kernel(
   Chunk<MF> cur;
   uint32_t sq[4][4];
   if (c_lo < c_hi) {  // before the token lookups
-    load_b(cur, qrow, c_lo * KCHUNK + 64 * g);
+    load_b<MF, R8>(cur, qrow, c_lo, row_bytes);
     if (!SLDS) load_sq<FMT>(sq, srow, c_lo & ~3, nchunks, g);
   }
   const int begin = p.offsets[e], end = p.offsets[e + 1];
@@ -342,7 +396,7 @@ __global__ __launch_bounds__(FFN_THREADS, WAVES_PER_EU) void expert_gemm_kernel(
       for (int ng = 0; ng < 4; ng++) acc[f][ng] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     if (c_lo < c_hi) {
       if (!first_pass) {
-        load_b(cur, qrow, c_lo * KCHUNK + 64 * g);
+        load_b<MF, R8>(cur, qrow, c_lo, row_bytes);
         if (!SLDS) load_sq<FMT>(sq, srow, c_lo & ~3, nchunks, g);
       }
       load_a(cur, arow, c_lo * KCHUNK + 64 * g, nvalid);
@@ -358,10 +412,10 @@ __global__ __launch_bounds__(FFN_THREADS, WAVES_PER_EU) void expert_gemm_kernel(
         if (c == c_lo || (c & 3) == 0) sq_transpose<FMT>(sq);
         sq_pick(sw, sq, c);
       }
-      mma_chunk<MF, FMT>(acc, cur, sw, nvalid, roff);
+      mma_chunk<MF, FMT, R8>(acc, cur, sw, nvalid, roff);
       if (c + 1 < c_hi) {
         const int kb = (c + 1) * KCHUNK + 64 * g;
-        load_b(cur, qrow, kb);
+        load_b<MF, R8>(cur, qrow, c + 1, row_bytes);
         if (SLDS)
           staged_words<FMT>(sw, staged, lsrow, c + 1, g);
         else if (((c + 1) & 3) == 0)
@@ -1109,31 +1163,36 @@ constexpr int GEMM_WAVES = 2;
 // down with NVFP4.  Larger K reads them from memory in groups of four chunks.
 constexpr int STAGE_MAX = 64 * 1024;
 
-template <int MF, int KSPLIT, bool GATEUP, int WAVES, int FMT>
+template <int MF, int KSPLIT, bool GATEUP, int WAVES, int FMT, bool R8>
 hipError_t launch_gemm_stage(const GroupedParams& p, dim3 grid, hipStream_t s) {
   const int K = GATEUP ? p.H : p.I;
   const int bytes = (4 / KSPLIT) * 64 * (K / (FMT == FMT_MX ? 32 : 16));
   if (bytes <= STAGE_MAX) {
-    const void* f = reinterpret_cast<const void*>(&expert_gemm_kernel<MF, KSPLIT, GATEUP, WAVES, FMT, true>);
+    const void* f = reinterpret_cast<const void*>(&expert_gemm_kernel<MF, KSPLIT, GATEUP, WAVES, FMT, true, R8>);
     const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, STAGE_MAX);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((expert_gemm_kernel<MF, KSPLIT, GATEUP, WAVES, FMT, true>), grid, dim3(FFN_THREADS), bytes, s, p);
+    hipLaunchKernelGGL((expert_gemm_kernel<MF, KSPLIT, GATEUP, WAVES, FMT, true, R8>), grid, dim3(FFN_THREADS), bytes,
+                       s, p);
   } else {
-    hipLaunchKernelGGL((expert_gemm_kernel<MF, KSPLIT, GATEUP, WAVES, FMT, false>), grid, dim3(FFN_THREADS), 0, s, p);
+    hipLaunchKernelGGL((expert_gemm_kernel<MF, KSPLIT, GATEUP, WAVES, FMT, false, R8>), grid, dim3(FFN_THREADS), 0, s,
+                       p);
   }
   return hipGetLastError();
 }
 
+// Code loads in whole lines (R8) for gate/up at every small batch, and for
+// down while every expert has at most 16 records (one token pass): T <= 16.
 template <int KSPLIT, bool GATEUP, int FMT>
-hipError_t launch_gemm_fmt(const GroupedParams& p, int mf, dim3 grid, hipStream_t s) {
-  return mf == 1 ? launch_gemm_stage<1, KSPLIT, GATEUP, GEMM_WAVES, FMT>(p, grid, s)
-                 : launch_gemm_stage<4, KSPLIT, GATEUP, 1, FMT>(p, grid, s);
+hipError_t launch_gemm_fmt(const GroupedParams& p, int mf, int T, dim3 grid, hipStream_t s) {
+  if (mf != 1) return launch_gemm_stage<4, KSPLIT, GATEUP, 1, FMT, false>(p, grid, s);
+  return GATEUP || T <= 16 ? launch_gemm_stage<1, KSPLIT, GATEUP, GEMM_WAVES, FMT, true>(p, grid, s)
+                           : launch_gemm_stage<1, KSPLIT, GATEUP, GEMM_WAVES, FMT, false>(p, grid, s);
 }
 
 template <int KSPLIT, bool GATEUP>
-hipError_t launch_gemm(const GroupedParams& p, int mf, dim3 grid, hipStream_t s, int fmt) {
-  return fmt == MOE_FMT_MXFP4 ? launch_gemm_fmt<KSPLIT, GATEUP, FMT_MX>(p, mf, grid, s)
-                              : launch_gemm_fmt<KSPLIT, GATEUP, FMT_NV>(p, mf, grid, s);
+hipError_t launch_gemm(const GroupedParams& p, int mf, int T, dim3 grid, hipStream_t s, int fmt) {
+  return fmt == MOE_FMT_MXFP4 ? launch_gemm_fmt<KSPLIT, GATEUP, FMT_MX>(p, mf, T, grid, s)
+                              : launch_gemm_fmt<KSPLIT, GATEUP, FMT_NV>(p, mf, T, grid, s);
 }
 
 }  // namespace
@@ -1149,7 +1208,7 @@ hipError_t launch_gateup(const FfnArgs& a, hipStream_t s) {
   p.gs1 = a.w->up.gs;
   if (use_big(a)) return launch_big<true>(a, p, s);
   const dim3 grid(a.I / (32 * (4 / GU_KSPLIT)), a.max_active);
-  return launch_gemm<GU_KSPLIT, true>(p, pick_mf(a.T), grid, s, a.w->format);
+  return launch_gemm<GU_KSPLIT, true>(p, pick_mf(a.T), a.T, grid, s, a.w->format);
 }
 
 hipError_t launch_down(const FfnArgs& a, hipStream_t s) {
@@ -1160,7 +1219,7 @@ hipError_t launch_down(const FfnArgs& a, hipStream_t s) {
   p.gs0 = a.w->down.gs;
   if (use_big(a)) return launch_big<false>(a, p, s);
   const dim3 grid(a.H / (64 * (4 / DN_KSPLIT)), a.max_active);
-  return launch_gemm<DN_KSPLIT, false>(p, pick_mf(a.T), grid, s, a.w->format);
+  return launch_gemm<DN_KSPLIT, false>(p, pick_mf(a.T), a.T, grid, s, a.w->format);
 }
 
 hipError_t launch_combine16(const f16* rows, const int32_t* pair_pos, int T, int H, int k, uint16_t* y, hipStream_t s,
