@@ -4,7 +4,9 @@
 // datasheet figure).  Block b reads a contiguous segment; wavefront w of the
 // block reads the segment's 1 KB pieces w, w+4, w+8, ... (one 16-byte load
 // per lane, a whole 1 KB per instruction), four pieces in flight; each block
-// folds what it read into one word (XOR), so no load can be dropped.
+// folds what it read into one word (XOR), so no load can be dropped.  The
+// loads are non-temporal, like the expert GEMMs' code loads: on a cold
+// 252 MiB read they reach about 6.0 TB/s against 5.2-5.4 TB/s cached.
 #include "internal.h"
 
 namespace moe {
@@ -12,6 +14,12 @@ namespace {
 
 constexpr int STREAM_THREADS = 256;
 constexpr int STREAM_U = 4;  // pieces in flight per wavefront
+
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_nt(const uint4* q) {
+  const u32x4v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(q));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
 
 __global__ __launch_bounds__(STREAM_THREADS) void stream_read_kernel(const uint4* __restrict__ p, long long n16,
                                                                    long long per16, uint32_t* __restrict__ sink) {
@@ -24,7 +32,7 @@ __global__ __launch_bounds__(STREAM_THREADS) void stream_read_kernel(const uint4
 #pragma unroll
     for (int u = 0; u < STREAM_U; u++) {
       const long long i = (piece + 4 * u) * WAVE + lane;
-      v[u] = i < end ? p[i] : make_uint4(0, 0, 0, 0);
+      v[u] = i < end ? load_nt(p + i) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < STREAM_U; u++) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
