@@ -208,7 +208,7 @@ moe_status check_experts(const moe_experts* w) {
   } while (0)
 
 // Enqueue routing; logits are an input when x == NULL.  When x16 is given,
-// the permutation kernels also write the fp16 copy of x the FFN reads.
+// the router also writes the fp16 copy of x the FFN reads.
 moe_status enqueue_route(const moe_dims& d, const void* x, const void* wr, const float* bias, float* logits,
                          int32_t* ids, float* w, int32_t* offsets, int32_t* sorted, int32_t* pos, void* ws,
                          f16* x16, hipStream_t s) {
@@ -217,14 +217,13 @@ moe_status enqueue_route(const moe_dims& d, const void* x, const void* wr, const
   if (x)
     LAUNCH(MOE_KERNEL_ROUTER, s,
            moe::launch_router(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wr),
-                              at<float>(ws, L.part), d.T, d.H, d.E, rp, s),
+                              at<float>(ws, L.part), d.T, d.H, d.E, rp, s, x16),
            "router");
   if (moe::route_fused(d.T)) {  // top-k and permutation in one launch, timed as top-k
     LAUNCH(MOE_KERNEL_TOPK, s,
            moe::launch_route_small(x ? at<float>(ws, L.part) : nullptr, rp.slabs, x ? bias : nullptr, logits, d.T,
                                    d.E, d.k, ids, w, offsets, sorted, pos, at<int32_t>(ws, L.active),
-                                   at<int32_t>(ws, L.nact), x16 ? static_cast<const uint16_t*>(x) : nullptr, x16,
-                                   d.H, s),
+                                   at<int32_t>(ws, L.nact), s),
            "route");
     return MOE_OK;
   }
@@ -235,8 +234,7 @@ moe_status enqueue_route(const moe_dims& d, const void* x, const void* wr, const
   LAUNCH(MOE_KERNEL_PERMUTE, s,
          moe::launch_permute(ids, d.T, d.E, d.k, at<uint64_t>(ws, L.masks), at<int32_t>(ws, L.counts),
                              at<int32_t>(ws, L.base), offsets, sorted, pos, at<int32_t>(ws, L.active),
-                             at<int32_t>(ws, L.nact), at<int32_t>(ws, L.mtiles), at<int32_t>(ws, L.nmt),
-                             x16 ? static_cast<const uint16_t*>(x) : nullptr, x16, d.H, s),
+                             at<int32_t>(ws, L.nact), at<int32_t>(ws, L.mtiles), at<int32_t>(ws, L.nmt), s),
          "permute");
   return MOE_OK;
 }
@@ -563,7 +561,7 @@ moe_status moe_latent_layer(moe_dims d, const moe_latent* lat, const void* x, co
   if (moe::route_fused(T)) {
     LAUNCH(MOE_KERNEL_TOPK, s,
            moe::launch_route_small(rpart, rp.slabs, bias, at<float>(ws, L.logits), T, E, k, ids, wts, offsets, sorted,
-                                   pos, at<int32_t>(ws, L.active), at<int32_t>(ws, L.nact), nullptr, nullptr, H, s),
+                                   pos, at<int32_t>(ws, L.active), at<int32_t>(ws, L.nact), s),
            "route");
   } else {
     LAUNCH(MOE_KERNEL_TOPK, s,
@@ -571,8 +569,7 @@ moe_status moe_latent_layer(moe_dims d, const moe_latent* lat, const void* x, co
     LAUNCH(MOE_KERNEL_PERMUTE, s,
            moe::launch_permute(ids, T, E, k, at<uint64_t>(ws, L.masks), at<int32_t>(ws, L.counts),
                                at<int32_t>(ws, L.base), offsets, sorted, pos, at<int32_t>(ws, L.active),
-                               at<int32_t>(ws, L.nact), at<int32_t>(ws, L.mtiles), at<int32_t>(ws, L.nmt), nullptr,
-                               nullptr, H, s),
+                               at<int32_t>(ws, L.nact), at<int32_t>(ws, L.mtiles), at<int32_t>(ws, L.nmt), s),
            "permute");
   }
   float* rows = at<float>(ws, L.rows);

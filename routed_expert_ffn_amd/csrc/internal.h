@@ -28,27 +28,25 @@ void prof_before(moe_kernel k, hipStream_t s);
 void prof_after(moe_kernel k, hipStream_t s);
 
 // Launchers.  Each enqueues on `s` and returns hipGetLastError().
+// With x16 non-NULL the router also writes the fp16 copy of x [T][H].
 hipError_t launch_router(const uint16_t* x, const uint16_t* wr, float* part, int T, int H, int E,
-                         const RouterPlan& rp, hipStream_t s);
+                         const RouterPlan& rp, hipStream_t s, f16* x16 = nullptr);
 // Sums the slab partials (part may be NULL: logits are then an input), adds
 // the bias, and selects the top k with their softmax weights.
 hipError_t launch_topk(const float* part, int slabs, const float* bias, float* logits, int T, int E, int k,
                        int32_t* ids, float* w, hipStream_t s);
 // Offsets, permutation, active-expert list and (for T > 64) the list of
-// (expert, token tile) entries; if x is non-NULL also writes the fp16
-// copy x16 of the activations [T][H].
+// (expert, token tile) entries.
 // T small enough for the single-launch routing kernel.
 bool route_fused(int T);
-// Logits reduction, top-k, permutation, active list and fp16 copy of x in one
-// launch (T <= the fused limit).
+// Logits reduction, top-k, permutation and active list in one launch (T <=
+// the fused limit).
 hipError_t launch_route_small(const float* part, int slabs, const float* bias, float* logits, int T, int E, int k,
                               int32_t* ids, float* w, int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_pos,
-                              int32_t* active, int32_t* n_active, const uint16_t* x, f16* x16, int H,
-                              hipStream_t s);
+                              int32_t* active, int32_t* n_active, hipStream_t s);
 hipError_t launch_permute(const int32_t* ids, int T, int E, int k, uint64_t* masks, int32_t* counts, int32_t* base,
                           int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_pos, int32_t* active,
-                          int32_t* n_active, int32_t* mtiles, int32_t* n_mtiles, const uint16_t* x, f16* x16,
-                          int H, hipStream_t s);
+                          int32_t* n_active, int32_t* mtiles, int32_t* n_mtiles, hipStream_t s);
 // Active list and (expert, token tile) entries of the experts in [lo, hi).
 hipError_t launch_active_list(const int32_t* offsets, int E, int lo, int hi, int32_t* active, int32_t* n_active,
                               int32_t* mtiles, int32_t* n_mtiles, hipStream_t s);

@@ -30,7 +30,7 @@ template <int TT>
 __global__ __launch_bounds__(RT_THREADS) void router_gemv_kernel(const uint16_t* __restrict__ x,
                                                                 const uint16_t* __restrict__ wr,
                                                                 float* __restrict__ part, int T, int H, int E,
-                                                                int slab_rows) {
+                                                                int slab_rows, f16* __restrict__ x16) {
   extern __shared__ float smem[];
   float* xs = smem;                               // [TT][slab_rows]
   float* red = smem + TT * slab_rows;             // [4 waves][16 groups][TT * 8]
@@ -54,9 +54,14 @@ __global__ __launch_bounds__(RT_THREADS) void router_gemv_kernel(const uint16_t*
     }
   };
   if (active) load_batch(4 * wv + rr);
+  // the blocks of the first expert tile also write the fp16 copy of their
+  // slab of x (bf16 -> fp32 exact, then the fp16 rounding)
+  const bool cast = x16 != nullptr && blockIdx.x == 0;
   for (int i = threadIdx.x; i < TT * slab_rows; i += RT_THREADS) {
     const int a = i / slab_rows, r = i % slab_rows;
-    xs[i] = (t0 + a < T && r < rows) ? bf16_to_f32(x[(size_t)(t0 + a) * H + h0 + r]) : 0.0f;
+    const bool in = t0 + a < T && r < rows;
+    xs[i] = in ? bf16_to_f32(x[(size_t)(t0 + a) * H + h0 + r]) : 0.0f;
+    if (cast && in) x16[(size_t)(t0 + a) * H + h0 + r] = (f16)xs[i];
   }
   __syncthreads();
   float acc[TT][8];
@@ -125,7 +130,7 @@ constexpr int RM_EXPERTS = 128;
 __global__ __launch_bounds__(WAVE) void router_mfma_kernel(const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ wr,
                                                           float* __restrict__ part, int T, int H, int E,
-                                                          int kslab) {
+                                                          int kslab, f16* __restrict__ x16) {
   const int lane = threadIdx.x, c = lane % 16, g = lane / 16;
   const int e0 = blockIdx.x * RM_EXPERTS, t0 = blockIdx.y * RM_TOKENS;
   const int k_begin = blockIdx.z * kslab, k_end = min(H, k_begin + kslab);
@@ -147,6 +152,21 @@ __global__ __launch_bounds__(WAVE) void router_mfma_kernel(const uint16_t* __res
     uint4 av[4];
 #pragma unroll
     for (int f = 0; f < 4; f++) av[f] = *reinterpret_cast<const uint4*>(arow[f] + k0 + 8 * g);
+    // the fp16 copy of x: each 32-k step of a (token tile, slab) is written
+    // by one of its expert tiles, in turn
+    if (x16 != nullptr && ((k0 - k_begin) / 32) % gridDim.x == blockIdx.x) {
+#pragma unroll
+      for (int f = 0; f < 4; f++)
+        if (t0 + 16 * f + c < T) {
+          const uint4 v = av[f];
+          f16x8 o;
+          o[0] = (f16)__uint_as_float(v.x << 16); o[1] = (f16)__uint_as_float(v.x & 0xFFFF0000u);
+          o[2] = (f16)__uint_as_float(v.y << 16); o[3] = (f16)__uint_as_float(v.y & 0xFFFF0000u);
+          o[4] = (f16)__uint_as_float(v.z << 16); o[5] = (f16)__uint_as_float(v.z & 0xFFFF0000u);
+          o[6] = (f16)__uint_as_float(v.w << 16); o[7] = (f16)__uint_as_float(v.w & 0xFFFF0000u);
+          *reinterpret_cast<f16x8*>(x16 + (size_t)(t0 + 16 * f + c) * H + k0 + 8 * g) = o;
+        }
+    }
 #pragma unroll
     for (int j = 0; j < 8; j++) {
       // column j: (w[0][j], ..., w[7][j]); w[i][j] is half j%2 of dword j/2 of row i
@@ -308,12 +328,114 @@ __device__ __forceinline__ void select_topk(const float* ls, int E, int k, int32
   }
 }
 
+// ---- top-k of one token by one wavefront, by filtering ---------------------------
+// Lane l owns the experts e = l + 64 i; hi(e) = float_order(logit e), and the
+// full key is (hi << 32 | ~e).
+//   1. m_l = the largest hi of lane l's experts (0 for a lane without any:
+//      every finite logit maps above 0);
+//   2. tau = the k-th largest of the 64 lane maxima, found as the smallest
+//      maximum that fewer than k maxima exceed.  At least k lanes hold a key
+//      with hi >= tau, so at least k keys have hi >= tau, and since a larger
+//      hi means a larger key, every key of the top k has hi >= tau;
+//   3. the keys with hi >= tau (the candidates, a few more than k for
+//      ordinary logits) are gathered in LDS in ascending expert order, one
+//      ballot per i;
+//   4. a candidate's rank is the number of larger candidates (keys are
+//      unique: the index is part of the key).
+// Winners are placed at lane = rank and weighted as in select_topk, so the
+// results are the same bit for bit.  More than 64 candidates (heavy ties)
+// fall back to select_topk.  No block barrier is involved: the lanes of a
+// wavefront exchange values through LDS, whose operations complete in issue
+// order for one wavefront.
+struct WaveTopkLds {
+  uint64_t cand[WAVE];
+  uint32_t m[WAVE];
+  float out_l[WAVE];
+  int out_e[WAVE];
+};
+
+// Keeps the compiler from moving this wavefront's LDS accesses across.
+__device__ __forceinline__ void wave_lds_order() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
+
+__device__ __forceinline__ void wave_topk(const float* ls, int E, int k, int32_t* __restrict__ ids,
+                                          float* __restrict__ w, int32_t* ids_copy, WaveTopkLds& S) {
+  const int lane = threadIdx.x % WAVE;
+  const int n = (E + WAVE - 1) / WAVE;
+  // ls holds 1024 entries: all reads are issued together, the ones past E
+  // are discarded
+  float lv[TOPK_KEYS];
+#pragma unroll
+  for (int i = 0; i < TOPK_KEYS; i++) lv[i] = ls[lane + WAVE * i];
+  uint32_t hi[TOPK_KEYS];
+  uint32_t m = 0u;
+#pragma unroll
+  for (int i = 0; i < TOPK_KEYS; i++) {
+    hi[i] = (i < n && lane + WAVE * i < E) ? float_order(lv[i]) : 0u;
+    m = max(m, hi[i]);
+  }
+  S.m[lane] = m;
+  wave_lds_order();
+  int above = 0;
+#pragma unroll
+  for (int j = 0; j < WAVE; j += 4) {
+    const uint4 q = *reinterpret_cast<const uint4*>(&S.m[j]);
+    above += (q.x > m ? 1 : 0) + (q.y > m ? 1 : 0) + (q.z > m ? 1 : 0) + (q.w > m ? 1 : 0);
+  }
+  // smallest maximum with fewer than k maxima above it (a max of inverted values)
+  const uint32_t tau = ~wave_max_u32(above < k ? ~m : 0u);
+  int total = 0;
+#pragma unroll
+  for (int i = 0; i < TOPK_KEYS; i++) {
+    if (i < n) {
+      const bool c = hi[i] >= tau;
+      const uint64_t b = __ballot(c);
+      const int below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+      const int pos = total + below;
+      if (c && pos < WAVE) S.cand[pos] = ((uint64_t)hi[i] << 32) | (uint32_t)~(uint32_t)(lane + WAVE * i);
+      total += __popcll(b);
+    }
+  }
+  if (total > WAVE) {
+    select_topk(ls, E, k, ids, w, ids_copy);
+    return;
+  }
+  wave_lds_order();
+  const uint64_t mine = lane < total ? S.cand[lane] : 0ull;
+  int rank = 0;
+  for (int j0 = 0; j0 < total; j0 += 16) {  // 16 keys (8 reads) at a time, all 64 slots in bounds
+    uint4 q[8];
+#pragma unroll
+    for (int u = 0; u < 8; u++) q[u] = *reinterpret_cast<const uint4*>(&S.cand[j0 + 2 * u]);
+#pragma unroll
+    for (int u = 0; u < 8; u++) {
+      const uint64_t a = ((uint64_t)q[u].y << 32) | q[u].x, b = ((uint64_t)q[u].w << 32) | q[u].z;
+      rank += (j0 + 2 * u < total && a > mine ? 1 : 0) + (j0 + 2 * u + 1 < total && b > mine ? 1 : 0);
+    }
+  }
+  if (lane < total && rank < k) {
+    S.out_l[rank] = order_float((uint32_t)(mine >> 32));
+    S.out_e[rank] = (int)~(uint32_t)mine;
+  }
+  wave_lds_order();
+  const float l = lane < k ? S.out_l[lane] : 0.0f;
+  const float top = S.out_l[0];
+  const float ex = lane < k ? expf(l - top) : 0.0f;
+  const float sum = wave_sum(ex);
+  if (lane < k) {
+    const int e = S.out_e[lane];
+    ids[lane] = e;
+    w[lane] = ex / sum;
+    if (ids_copy) ids_copy[lane] = e;
+  }
+}
+
 template <int TB>
 __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(const float* __restrict__ part, int slabs,
                                                            const float* __restrict__ bias,
                                                            float* __restrict__ logits, int T, int E, int k,
                                                            int32_t* __restrict__ ids, float* __restrict__ wout) {
   __shared__ float ls[TB * 1024];
+  __shared__ __attribute__((aligned(16))) WaveTopkLds tk[TB];
   const int t0 = blockIdx.x * TB;
   // Phase 1: logits of this block's tokens (slab partials added in ascending
   // slab order, or the caller's logits).
@@ -335,7 +457,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(const float* __restr
   const int wv = threadIdx.x / WAVE;
   const int t = t0 + wv;
   if (wv >= TB || t >= T) return;
-  select_topk(ls + wv * 1024, E, k, ids + (size_t)t * k, wout + (size_t)t * k, nullptr);
+  wave_topk(ls + wv * 1024, E, k, ids + (size_t)t * k, wout + (size_t)t * k, nullptr, tk[wv]);
 }
 
 // ---- permutation ---------------------------------------------------------------
@@ -346,129 +468,60 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(const float* __restr
 // deterministic.
 constexpr int PERM_MAX_E = 1024;
 
-// Block-wide exclusive scan of one int per thread (blockDim.x = 1024).
+// Inclusive scan over the 64 lanes with DPP lane moves: three row shifts
+// (1, 2, 3) of the input give each lane the sum of its quad-aligned run of
+// four; shifts by 4 and 8 (upper banks only) complete each row of 16; row
+// broadcasts 15 and 31 carry the row totals into the rows above.  Lanes
+// without a source add 0.
+template <int CTRL, int ROW_MASK = 0xf, int BANK_MASK = 0xf>
+__device__ __forceinline__ int dpp_int(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, BANK_MASK, false);
+}
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  int v = x + dpp_int<0x111>(x);
+  v += dpp_int<0x112>(x);
+  v += dpp_int<0x113>(x);
+  v += dpp_int<0x114, 0xf, 0xe>(v);
+  v += dpp_int<0x118, 0xf, 0xc>(v);
+  v += dpp_int<0x142, 0xa, 0xf>(v);
+  v += dpp_int<0x143, 0xc, 0xf>(v);
+  return v;
+}
+
+// Block-wide exclusive scan of one int per thread (blockDim.x = 1024, lds
+// 16-byte aligned).
 __device__ __forceinline__ int block_exclusive_scan(int v, int* lds /*[16]*/, int* total) {
   const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE;
-  int incl = v;
-#pragma unroll
-  for (int off = 1; off < WAVE; off <<= 1) {
-    const int o = __shfl_up(incl, off, WAVE);
-    if (lane >= off) incl += o;
-  }
+  const int incl = wave_inclusive_scan(v);
   if (lane == WAVE - 1) lds[wv] = incl;
   __syncthreads();
+  int4 q[4];
+#pragma unroll
+  for (int u = 0; u < 4; u++) q[u] = reinterpret_cast<const int4*>(lds)[u];
   int base = 0, all = 0;
-  for (int i = 0; i < (int)(blockDim.x / WAVE); i++) {
-    if (i < wv) base += lds[i];
-    all += lds[i];
+#pragma unroll
+  for (int u = 0; u < 4; u++) {
+    const int t[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      base += 4 * u + r < wv ? t[r] : 0;
+      all += t[r];
+    }
   }
   __syncthreads();
   *total = all;
   return base + incl - v;
 }
 
-// ---- top-k of one token by a block of 1024 threads ------------------------------
-// Exact, by filtering.  Keys are (u << 32 | ~index), u = float_order(logit):
-// larger key = larger logit, then lower index.  Each of the W = E/64 full
-// wavefronts takes the j = ceil(k / W) largest of its 64 keys (j rounds of a
-// DPP wavefront maximum); tau = the k-th largest of those W*j leaders is at
-// most the k-th largest key overall (a subset's order statistic), so every
-// key of the top k is >= tau, and at least k keys are.  The keys >= tau
-// (about k for ordinary logits) are gathered into wavefront 0, one per lane,
-// and each finds its rank by comparing against all the others.  Winners are
-// placed lane = rank and weighted as in select_topk, so the results are the
-// same bit for bit.  When the leaders or the keys >= tau do not fit in 64
-// lanes (few full wavefronts, heavy ties) wavefront 0 runs select_topk.
-struct BlockTopkLds {
-  uint64_t cand[64];
-  uint64_t tau;
-  int cnt[16];
-  float out_l[64];
-  int out_e[64];
-};
-
-// Rank of this lane's key among the first n lanes' keys (wavefront 0).
-__device__ __forceinline__ int lane_rank(uint64_t mine, int n) {
-  int rank = 0;
-  for (int i = 0; i < n; i++) {
-    const uint64_t other = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(mine >> 32), i) << 32) |
-                           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mine, i);
-    rank += other > mine ? 1 : 0;
-  }
-  return rank;
-}
-
-__device__ __forceinline__ void block_topk(const float* ls, int E, int k, int32_t* __restrict__ ids,
-                                           float* __restrict__ w, int32_t* ids_copy, BlockTopkLds& S) {
-  const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
-  const uint64_t key = tid < E ? (((uint64_t)float_order(ls[tid]) << 32) | (uint32_t)~(uint32_t)tid) : 0ull;
-  const int W = E / WAVE;
-  const int j = W > 0 ? (k + W - 1) / W : 0;
-  const int n_lead = W * j;
-  bool fast = W > 0 && n_lead <= WAVE;
-  // leaders: the j largest keys of each full wavefront
-  if (fast && wv < W) {
-    uint64_t kk = key;
-    for (int r = 0; r < j; r++) {
-      const uint64_t m = wave_max_u64(kk);
-      if (kk == m) kk = 0ull;
-      if (lane == 0) S.cand[wv * j + r] = m;
-    }
-  }
-  __syncthreads();
-  if (fast && wv == 0) {
-    const uint64_t c = lane < n_lead ? S.cand[lane] : 0ull;
-    const int rank = lane_rank(c, n_lead);
-    if (lane < n_lead && rank == k - 1) S.tau = c;
-  }
-  __syncthreads();
-  const uint64_t tau = fast ? S.tau : ~0ull;
-  const bool cand = fast && key != 0ull && key >= tau;
-  const uint64_t bal = __ballot(cand);
-  if (lane == 0) S.cnt[wv] = __popcll(bal);
-  __syncthreads();
-  int base = 0, total = 0;
-  for (int i = 0; i < (int)(blockDim.x / WAVE); i++) {
-    if (i < wv) base += S.cnt[i];
-    total += S.cnt[i];
-  }
-  fast = fast && total <= WAVE;
-  if (fast && cand) S.cand[base + __popcll(bal & ((1ull << lane) - 1ull))] = key;
-  __syncthreads();
-  if (wv == 0) {
-    if (fast) {
-      const uint64_t mine = lane < total ? S.cand[lane] : 0ull;
-      const int rank = lane_rank(mine, total);
-      if (lane < total && rank < k) {
-        S.out_l[rank] = order_float((uint32_t)(mine >> 32));
-        S.out_e[rank] = (int)~(uint32_t)mine;
-      }
-      // (same wavefront: its LDS writes are read back in order)
-      const float l = lane < k ? S.out_l[lane] : 0.0f;
-      const float top = S.out_l[0];
-      const float ex = lane < k ? expf(l - top) : 0.0f;
-      const float sum = wave_sum(ex);
-      if (lane < k) {
-        const int e = S.out_e[lane];
-        ids[lane] = e;
-        w[lane] = ex / sum;
-        if (ids_copy) ids_copy[lane] = e;
-      }
-    } else {
-      select_topk(ls, E, k, ids, w, ids_copy);
-    }
-  }
-  __syncthreads();
-}
-
-// One token per block: the logits (as topk_kernel), then block_topk.
+// One token per block: the logits (as topk_kernel), then wave_topk by
+// wavefront 0.
 __global__ __launch_bounds__(TOPK_THREADS) void topk_block_kernel(const float* __restrict__ part, int slabs,
                                                                  const float* __restrict__ bias,
                                                                  float* __restrict__ logits, int T, int E, int k,
                                                                  int32_t* __restrict__ ids,
                                                                  float* __restrict__ wout) {
   __shared__ float ls[1024];
-  __shared__ BlockTopkLds tk;
+  __shared__ __attribute__((aligned(16))) WaveTopkLds tk;
   const int t = blockIdx.x, e = threadIdx.x;
   if (e < E) {
     float v;
@@ -482,7 +535,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_block_kernel(const float* _
     ls[e] = v;
   }
   __syncthreads();
-  block_topk(ls, E, k, ids + (size_t)t * k, wout + (size_t)t * k, nullptr, tk);
+  if (threadIdx.x < WAVE) wave_topk(ls, E, k, ids + (size_t)t * k, wout + (size_t)t * k, nullptr, tk);
 }
 
 __device__ __forceinline__ void cast_rows(const uint16_t* __restrict__ x, f16* __restrict__ x16, size_t first8,
@@ -509,10 +562,10 @@ __device__ __forceinline__ void permute_block(const int32_t* ids, int T, int E, 
   for (int f = tid; f < T * k; f += 1024) atomicOr(&m[ids[f]], 1ull << (f / k));
   __syncthreads();
   const int cnt = tid < E ? __popcll(m[tid]) : 0;
-  int total;
-  const int off = block_exclusive_scan(cnt, lds, &total);
-  int nact;
-  const int slot = block_exclusive_scan(cnt > 0 ? 1 : 0, lds, &nact);
+  // offsets (< T k <= 4096) and active slots (< E <= 1024) in one scan
+  int packed_total;
+  const int packed = block_exclusive_scan(cnt + (cnt > 0 ? 1 << 16 : 0), lds, &packed_total);
+  const int off = packed & 0xFFFF, slot = packed >> 16, nact = packed_total >> 16;
   if (tid < E) {
     off_s[tid] = off;
     offsets[tid] = off;
@@ -531,29 +584,26 @@ __device__ __forceinline__ void permute_block(const int32_t* ids, int T, int E, 
   }
 }
 
-// T <= 64: the whole permutation, the active-expert list and the fp16 copy
-// of the activations, in one block of 1024 threads.
+// T <= 64: the whole permutation and the active-expert list, in one block of
+// 1024 threads.
 __global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
                                                          int32_t* __restrict__ offsets,
                                                          int32_t* __restrict__ sorted_pairs,
                                                          int32_t* __restrict__ pair_pos,
                                                          int32_t* __restrict__ active,
-                                                         int32_t* __restrict__ n_active,
-                                                         const uint16_t* __restrict__ x, f16* __restrict__ x16,
-                                                         int H) {
+                                                         int32_t* __restrict__ n_active) {
   __shared__ unsigned long long m[PERM_MAX_E];
   __shared__ int off_s[PERM_MAX_E];
-  __shared__ int lds[16];
+  __shared__ __attribute__((aligned(16))) int lds[16];
   if (threadIdx.x < E) m[threadIdx.x] = 0ull;
   __syncthreads();
   permute_block(ids, T, E, k, offsets, sorted_pairs, pair_pos, active, n_active, m, off_s, lds);
-  if (x) cast_rows(x, x16, 0, (size_t)T * H / 8, threadIdx.x, 1024);
 }
 
 // T <= ROUTE_SMALL_T: the whole routing in one block of 1024 threads (one
 // launch instead of three): logits from the slab partials (or the caller's
-// logits), top-k and weights (block_topk, token by token), then the
-// permutation, the active-expert list and the fp16 copy of the activations.
+// logits), top-k and weights (wave_topk, wavefront t for token t), then the
+// permutation and the active-expert list.
 constexpr int ROUTE_SMALL_T = 8;
 
 __global__ __launch_bounds__(1024) void route_small_kernel(const float* __restrict__ part, int slabs,
@@ -563,15 +613,13 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const float* __restri
                                                           int32_t* __restrict__ sorted_pairs,
                                                           int32_t* __restrict__ pair_pos,
                                                           int32_t* __restrict__ active,
-                                                          int32_t* __restrict__ n_active,
-                                                          const uint16_t* __restrict__ x, f16* __restrict__ x16,
-                                                          int H) {
+                                                          int32_t* __restrict__ n_active) {
   __shared__ float ls[ROUTE_SMALL_T * PERM_MAX_E];
   __shared__ int ids_s[ROUTE_SMALL_T * 64];
   __shared__ unsigned long long m[PERM_MAX_E];
   __shared__ int off_s[PERM_MAX_E];
-  __shared__ int lds[16];
-  __shared__ BlockTopkLds tk;
+  __shared__ __attribute__((aligned(16))) int lds[16];
+  __shared__ __attribute__((aligned(16))) WaveTopkLds tk[ROUTE_SMALL_T];
   const int tid = threadIdx.x;
   for (int idx = tid; idx < T * E; idx += 1024) {
     const int t = idx / E, e = idx % E;
@@ -587,10 +635,11 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const float* __restri
   }
   if (tid < E) m[tid] = 0ull;
   __syncthreads();
-  for (int t = 0; t < T; t++)
-    block_topk(ls + t * PERM_MAX_E, E, k, ids + (size_t)t * k, wout + (size_t)t * k, ids_s + t * k, tk);
+  const int wv = tid / WAVE;
+  if (wv < T)
+    wave_topk(ls + wv * PERM_MAX_E, E, k, ids + (size_t)wv * k, wout + (size_t)wv * k, ids_s + wv * k, tk[wv]);
+  __syncthreads();
   permute_block(ids_s, T, E, k, offsets, sorted_pairs, pair_pos, active, n_active, m, off_s, lds);
-  if (x) cast_rows(x, x16, 0, (size_t)T * H / 8, tid, 1024);
 }
 
 __global__ __launch_bounds__(WAVE) void perm_count_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
@@ -627,13 +676,20 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* __restri
                                                         int32_t* __restrict__ offsets, int32_t* __restrict__ active,
                                                         int32_t* __restrict__ n_active, int32_t* __restrict__ mtiles,
                                                         int32_t* __restrict__ n_mtiles) {
-  __shared__ int lds[16];
+  __shared__ __attribute__((aligned(16))) int lds[16];
   const int e = threadIdx.x;
   int running = 0;
   if (e < E)
-    for (int b = 0; b < nblocks; b++) {
-      base[(size_t)b * E + e] = running;
-      running += counts[(size_t)b * E + e];
+    for (int b0 = 0; b0 < nblocks; b0 += 16) {  // 16 loads in flight
+      int c[16];
+#pragma unroll
+      for (int u = 0; u < 16; u++) c[u] = b0 + u < nblocks ? counts[(size_t)(b0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 16; u++)
+        if (b0 + u < nblocks) {
+          base[(size_t)(b0 + u) * E + e] = running;
+          running += c[u];
+        }
     }
   int total;
   const int off = block_exclusive_scan(e < E ? running : 0, lds, &total);
@@ -652,13 +708,11 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* __restri
   write_mtiles(e, e < E ? running : 0, lds, mtiles, n_mtiles);
 }
 
-__global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
+__global__ __launch_bounds__(WAVE) void perm_scatter_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
                                                           const uint64_t* __restrict__ masks,
                                                           const int32_t* __restrict__ base,
                                                           int32_t* __restrict__ sorted_pairs,
-                                                          int32_t* __restrict__ pair_pos,
-                                                          const uint16_t* __restrict__ x, f16* __restrict__ x16,
-                                                          int H) {
+                                                          int32_t* __restrict__ pair_pos) {
   const int b = blockIdx.x;
   if (threadIdx.x < WAVE) {
     const int lane = threadIdx.x;
@@ -674,10 +728,6 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __rest
       }
     }
   }
-  if (x) {
-    const int rows = min(WAVE, T - b * WAVE);
-    cast_rows(x, x16, (size_t)b * WAVE * H / 8, (size_t)rows * H / 8, threadIdx.x, 256);
-  }
 }
 
 // Experts in [lo, hi) with work and their (expert, token tile) entries,
@@ -688,7 +738,7 @@ __global__ __launch_bounds__(1024) void active_list_kernel(const int32_t* __rest
                                                           int32_t* __restrict__ n_active,
                                                           int32_t* __restrict__ mtiles,
                                                           int32_t* __restrict__ n_mtiles) {
-  __shared__ int lds[16];
+  __shared__ __attribute__((aligned(16))) int lds[16];
   const int e = threadIdx.x;
   const int cnt = (e < E && e >= lo && e < hi) ? offsets[e + 1] - offsets[e] : 0;
   const int flag = cnt > 0 ? 1 : 0;
@@ -745,20 +795,20 @@ RouterPlan router_plan(int T, int H, int E) {
 }
 
 hipError_t launch_router(const uint16_t* x, const uint16_t* wr, float* part, int T, int H, int E,
-                         const RouterPlan& rp, hipStream_t s) {
+                         const RouterPlan& rp, hipStream_t s, f16* x16) {
   if (rp.mfma) {
     const dim3 grid((E + RM_EXPERTS - 1) / RM_EXPERTS, (T + RM_TOKENS - 1) / RM_TOKENS, rp.slabs);
-    hipLaunchKernelGGL(router_mfma_kernel, grid, dim3(WAVE), 0, s, x, wr, part, T, H, E, rp.slab_rows);
+    hipLaunchKernelGGL(router_mfma_kernel, grid, dim3(WAVE), 0, s, x, wr, part, T, H, E, rp.slab_rows, x16);
     return hipGetLastError();
   }
   const int tt = router_tt(T);
   const dim3 grid((E + RT_E_TILE - 1) / RT_E_TILE, rp.slabs, (T + tt - 1) / tt);
   const size_t lds = sizeof(float) * ((size_t)tt * rp.slab_rows + 4 * 16 * tt * 8);
   switch (tt) {
-    case 1: hipLaunchKernelGGL((router_gemv_kernel<1>), grid, dim3(RT_THREADS), lds, s, x, wr, part, T, H, E, rp.slab_rows); break;
-    case 2: hipLaunchKernelGGL((router_gemv_kernel<2>), grid, dim3(RT_THREADS), lds, s, x, wr, part, T, H, E, rp.slab_rows); break;
-    case 4: hipLaunchKernelGGL((router_gemv_kernel<4>), grid, dim3(RT_THREADS), lds, s, x, wr, part, T, H, E, rp.slab_rows); break;
-    default: hipLaunchKernelGGL((router_gemv_kernel<8>), grid, dim3(RT_THREADS), lds, s, x, wr, part, T, H, E, rp.slab_rows); break;
+    case 1: hipLaunchKernelGGL((router_gemv_kernel<1>), grid, dim3(RT_THREADS), lds, s, x, wr, part, T, H, E, rp.slab_rows, x16); break;
+    case 2: hipLaunchKernelGGL((router_gemv_kernel<2>), grid, dim3(RT_THREADS), lds, s, x, wr, part, T, H, E, rp.slab_rows, x16); break;
+    case 4: hipLaunchKernelGGL((router_gemv_kernel<4>), grid, dim3(RT_THREADS), lds, s, x, wr, part, T, H, E, rp.slab_rows, x16); break;
+    default: hipLaunchKernelGGL((router_gemv_kernel<8>), grid, dim3(RT_THREADS), lds, s, x, wr, part, T, H, E, rp.slab_rows, x16); break;
   }
   return hipGetLastError();
 }
@@ -778,28 +828,26 @@ bool route_fused(int T) { return T <= ROUTE_SMALL_T; }
 
 hipError_t launch_route_small(const float* part, int slabs, const float* bias, float* logits, int T, int E, int k,
                               int32_t* ids, float* w, int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_pos,
-                              int32_t* active, int32_t* n_active, const uint16_t* x, f16* x16, int H,
-                              hipStream_t s) {
+                              int32_t* active, int32_t* n_active, hipStream_t s) {
   hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(1024), 0, s, part, slabs, bias, logits, T, E, k, ids, w,
-                     offsets, sorted_pairs, pair_pos, active, n_active, x, x16, H);
+                     offsets, sorted_pairs, pair_pos, active, n_active);
   return hipGetLastError();
 }
 
 hipError_t launch_permute(const int32_t* ids, int T, int E, int k, uint64_t* masks, int32_t* counts, int32_t* base,
                           int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_pos, int32_t* active,
-                          int32_t* n_active, int32_t* mtiles, int32_t* n_mtiles, const uint16_t* x, f16* x16,
-                          int H, hipStream_t s) {
+                          int32_t* n_active, int32_t* mtiles, int32_t* n_mtiles, hipStream_t s) {
   if (T <= 64) {
     hipLaunchKernelGGL(perm_small_kernel, dim3(1), dim3(1024), 0, s, ids, T, E, k, offsets, sorted_pairs, pair_pos,
-                       active, n_active, x, x16, H);
+                       active, n_active);
     return hipGetLastError();
   }
   const int nb = perm_blocks(T);
   hipLaunchKernelGGL(perm_count_kernel, dim3(nb), dim3(WAVE), 0, s, ids, T, E, k, masks, counts);
   hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, s, counts, nb, E, T * k, base, offsets, active,
                      n_active, mtiles, n_mtiles);
-  hipLaunchKernelGGL(perm_scatter_kernel, dim3(nb), dim3(256), 0, s, ids, T, E, k, masks, base, sorted_pairs,
-                     pair_pos, x, x16, H);
+  hipLaunchKernelGGL(perm_scatter_kernel, dim3(nb), dim3(WAVE), 0, s, ids, T, E, k, masks, base, sorted_pairs,
+                     pair_pos);
   return hipGetLastError();
 }
 

@@ -195,10 +195,15 @@ def test_wide_k_scales_from_memory(H, I, fmt, T):
     assert_close(y, ref["y"], "y")
 
 
-def test_route_ties_logits_in():
+@pytest.mark.parametrize("T", [6, 40, 100])
+def test_route_ties_logits_in(T):
     """Constructed fp32 logits with exact ties (all equal, +-0, duplicated
-    values): the selection must follow (logit desc, index asc) bit-exactly."""
-    T, E, k = 6, 896, 16
+    values, more tied maxima than a wavefront has lanes): the selection must
+    follow (logit desc, index asc) bit-exactly.  T = 6, 40 and 100 run the
+    single-launch routing, the one-block-per-token and the four-tokens-per-
+    block top-k kernels."""
+    E, k = 896, 16
+    say(f"ties T={T}")
     rng = np.random.default_rng(2)
     L = rng.normal(0, 1.7, size=(T, E)).astype(np.float32)
     L[0] = 0.0
@@ -208,6 +213,7 @@ def test_route_ties_logits_in():
     L[3, 500:530] = 7.0
     L[4] = -3.0
     L[4, 895] = -2.0
+    L[5, 100:170] = 9.0
     inp = Inputs(T, 256, 256, E, k, seed=1, store=build_store(E, 256, 256, 1, experts=[]))
     r = inp.route(logits_in=L)
     np.testing.assert_array_equal(r["logits"], L)
@@ -216,6 +222,7 @@ def test_route_ties_logits_in():
     np.testing.assert_array_equal(r["ids"][1], np.arange(16))
     np.testing.assert_array_equal(r["ids"][3], np.arange(500, 516))
     assert r["ids"][4][0] == 895 and list(r["ids"][4][1:]) == list(range(15))
+    np.testing.assert_array_equal(r["ids"][5], np.arange(100, 116))
 
 
 def test_all_tokens_to_the_same_experts():
