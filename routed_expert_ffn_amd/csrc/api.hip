@@ -448,7 +448,7 @@ moe_status moe_layer(moe_dims d, const void* x, const void* w_router, const floa
   // the down GEMM writes each record's row times its routing weight in fp16
   f16* rows16 = at<f16>(ws, L.rows);
   TRY(enqueue_ffn(d, offsets, sorted, w, rows, ws, s, 0, rows16, wts));
-  LAUNCH(MOE_KERNEL_COMBINE, s, moe::launch_combine16(rows16, pos, d.T, d.H, d.k, static_cast<uint16_t*>(y), s),
+  LAUNCH(MOE_KERNEL_COMBINE, s, moe::launch_combine16(rows16, d.T, d.H, d.k, static_cast<uint16_t*>(y), s),
          "combine");
   return MOE_OK;
 }
@@ -503,7 +503,7 @@ moe_status moe_layer_shared(moe_dims d, const moe_shared* shared, const void* x,
                             moe::router_plan(T, width, H), s),
          "shared experts, down");
   LAUNCH(MOE_KERNEL_COMBINE, s,
-         moe::launch_combine16(rows16, pos, T, H, d.k, static_cast<uint16_t*>(y), s, dpart, SL.d_slabs), "combine");
+         moe::launch_combine16(rows16, T, H, d.k, static_cast<uint16_t*>(y), s, dpart, SL.d_slabs), "combine");
   return MOE_OK;
 }
 
@@ -575,7 +575,7 @@ moe_status moe_latent_layer(moe_dims d, const moe_latent* lat, const void* x, co
   float* rows = at<float>(ws, L.rows);
   f16* rows16 = at<f16>(ws, L.rows);
   TRY(enqueue_ffn(d, offsets, sorted, w, rows, ws, s, 0, rows16, wts));
-  LAUNCH(MOE_KERNEL_COMBINE, s, moe::launch_combine16(rows16, pos, T, H, k, ylat, s), "combine");
+  LAUNCH(MOE_KERNEL_COMBINE, s, moe::launch_combine16(rows16, T, H, k, ylat, s), "combine");
   // routed-up projection back to the hidden width
   LAUNCH(MOE_KERNEL_PROJECT, s,
          moe::launch_projection(ylat, static_cast<const uint16_t*>(lat->w_up), ppart, T, H, Hm,

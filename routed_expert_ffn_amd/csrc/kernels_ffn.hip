@@ -52,7 +52,7 @@ struct GroupedParams {
   const float* gs1;
   f16* h;              // gate/up output [P][I]
   float* rows;         // down output [P][H], fp32 unweighted (when rows16 is NULL)
-  f16* rows16;         // or: down output [P][H] fp16, each row times its routing weight
+  f16* rows16;         // or: down output [P][H] fp16 in record order (row t*k+j), each row times its routing weight
   const float* pair_w; //     the routing weights [T*k], indexed by record (sorted_pairs[p])
 };
 
@@ -459,10 +459,11 @@ __global__ __launch_bounds__(FFN_THREADS, WAVES_PER_EU) void expert_gemm_kernel(
                 p.h[(size_t)(mb + m) * N + tile * 32 + 16 * cp + r] = (f16)hv;
               }
             } else if (p.rows16) {
-              const float ws = p.pair_w[p.sorted_pairs[mb + m]] * gsa;
+              const int rec = p.sorted_pairs[mb + m];  // stored at its record's row
+              const float ws = p.pair_w[rec] * gsa;
 #pragma unroll
               for (int ng = 0; ng < 4; ng++)
-                p.rows16[(size_t)(mb + m) * N + tile * 64 + 16 * ng + r] = (f16)(ws * acc[f][ng][i]);
+                p.rows16[(size_t)rec * N + tile * 64 + 16 * ng + r] = (f16)(ws * acc[f][ng][i]);
             } else {
 #pragma unroll
               for (int ng = 0; ng < 4; ng++) p.rows[(size_t)(mb + m) * N + tile * 64 + 16 * ng + r] = gsa * acc[f][ng][i];
@@ -540,7 +541,8 @@ constexpr int BIG_OFF_RQ = BIG_OFF_A + 3 * BIG_TILE_BYTES;          // [2][256][
 constexpr int BIG_OFF_RS = BIG_OFF_RQ + 2 * BIG_SPANQ_BYTES;        // [2][256][16] u8
 constexpr int BIG_OFF_ROW = BIG_OFF_RS + 2 * BIG_SPANS_BYTES;       // [224] i32
 constexpr int BIG_OFF_RW = BIG_OFF_ROW + BIG_M * 4;                 // [224] f32 routing weights (down, fp16 rows)
-constexpr int BIG_LDS = BIG_OFF_RW + BIG_M * 4;
+constexpr int BIG_OFF_REC = BIG_OFF_RW + BIG_M * 4;                 // [224] i32 record ids (down, fp16 rows)
+constexpr int BIG_LDS = BIG_OFF_REC + BIG_M * 4;
 static_assert(BIG_LDS <= 160 * 1024, "LDS budget of one CU");
 
 struct BigParams {
@@ -944,8 +946,10 @@ __device__ __forceinline__ void big_tile(const GroupedParams& p, const BigTile& 
           *reinterpret_cast<f16x4*>(p.h + (size_t)(t.mb + m) * t.N + t.rtile * (BIG_N / 2) + 32 * wv + n4) = o;
         }
       } else {
-        // fp16 rows carry the routing weight of their record
+        // fp16 rows carry the routing weight of their record and are stored
+        // at the record's row
         const float ws = p.rows16 ? reinterpret_cast<const float*>(smem + BIG_OFF_RW)[min(m, BIG_M - 1)] : 1.0f;
+        const int rec = p.rows16 ? reinterpret_cast<const int*>(smem + BIG_OFF_REC)[min(m, BIG_M - 1)] : 0;
 #pragma unroll
         for (int nf = 0; nf < 2; nf++) {
           float v[4];
@@ -953,14 +957,14 @@ __device__ __forceinline__ void big_tile(const GroupedParams& p, const BigTile& 
           for (int r = 0; r < 4; r++) v[r] = gsa * acc[f][nf][4 * q4 + r];
           quad_transpose(v);
           if (m < t.nvalid) {
-            const size_t at = (size_t)(t.mb + m) * t.N + t.rtile * BIG_N + 64 * wv + 32 * nf + n4;
+            const size_t col = (size_t)t.rtile * BIG_N + 64 * wv + 32 * nf + n4;
             if (p.rows16) {
               f16x4 o;
 #pragma unroll
               for (int r = 0; r < 4; r++) o[r] = (f16)(ws * v[r]);
-              *reinterpret_cast<f16x4*>(p.rows16 + at) = o;
+              *reinterpret_cast<f16x4*>(p.rows16 + (size_t)rec * t.N + col) = o;
             } else {
-              *reinterpret_cast<float4*>(p.rows + at) = make_float4(v[0], v[1], v[2], v[3]);
+              *reinterpret_cast<float4*>(p.rows + (size_t)(t.mb + m) * t.N + col) = make_float4(v[0], v[1], v[2], v[3]);
             }
           }
         }
@@ -995,7 +999,11 @@ __global__ __launch_bounds__(BIG_THREADS, 1) void expert_gemm_big_kernel(BigPara
   for (int m = threadIdx.x; m < BIG_M; m += BIG_THREADS) {
     const int pp = t.mb + min(m, t.nvalid - 1);
     rowoff[m] = GATEUP ? p.sorted_pairs[pp] / p.k : pp;
-    if (!GATEUP && p.rows16) reinterpret_cast<float*>(big_smem + BIG_OFF_RW)[m] = p.pair_w[p.sorted_pairs[pp]];
+    if (!GATEUP && p.rows16) {
+      const int rec = p.sorted_pairs[pp];
+      reinterpret_cast<float*>(big_smem + BIG_OFF_RW)[m] = p.pair_w[rec];
+      reinterpret_cast<int*>(big_smem + BIG_OFF_REC)[m] = rec;
+    }
   }
   __syncthreads();
   switch ((t.nvalid + 31) / 32) {  // token fragments, 1 .. 7
@@ -1048,12 +1056,12 @@ hipError_t launch_big(const FfnArgs& a, const GroupedParams& p, hipStream_t s) {
 // loads, are issued together before the sums.
 constexpr int COMBINE_JB = 16;
 
-// y[t][n] = bf16( sum_j rows16[pair_pos[t*k+j]][n] (+ add) ): the rows
-// already carry their routing weights; fp32 sum over ascending j, then the
-// add_slabs partials in order.  Four columns per thread, 16 records' loads
-// issued together.
-__global__ __launch_bounds__(256) void combine16_kernel(const f16* __restrict__ rows, const int32_t* __restrict__ pair_pos,
-                                                       int H, int k, uint16_t* __restrict__ y,
+// y[t][n] = bf16( sum_j rows16[t*k+j][n] (+ add) ): the rows are in record
+// order and already carry their routing weights; fp32 sum over ascending j,
+// then the add_slabs partials in order.  Four columns per thread, 16
+// records' loads issued together.
+__global__ __launch_bounds__(256) void combine16_kernel(const f16* __restrict__ rows, int H, int k,
+                                                       uint16_t* __restrict__ y,
                                                        const float* __restrict__ add, int add_slabs,
                                                        long long add_stride) {
   typedef _Float16 h4 __attribute__((ext_vector_type(4)));
@@ -1062,13 +1070,10 @@ __global__ __launch_bounds__(256) void combine16_kernel(const f16* __restrict__ 
   if (n >= H) return;
   float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
   for (int j0 = 0; j0 < k; j0 += COMBINE_JB) {
-    int pos[COMBINE_JB];
-#pragma unroll
-    for (int u = 0; u < COMBINE_JB; u++) pos[u] = j0 + u < k ? pair_pos[(size_t)t * k + j0 + u] : 0;
     h4 v[COMBINE_JB];
 #pragma unroll
     for (int u = 0; u < COMBINE_JB; u++)
-      v[u] = j0 + u < k ? *reinterpret_cast<const h4*>(rows + (size_t)pos[u] * H + n) : h4{};
+      v[u] = j0 + u < k ? *reinterpret_cast<const h4*>(rows + ((size_t)t * k + j0 + u) * H + n) : h4{};
 #pragma unroll
     for (int u = 0; u < COMBINE_JB; u++)
       if (j0 + u < k) {
@@ -1222,11 +1227,11 @@ hipError_t launch_down(const FfnArgs& a, hipStream_t s) {
   return launch_gemm<DN_KSPLIT, false>(p, pick_mf(a.T), a.T, grid, s, a.w->format);
 }
 
-hipError_t launch_combine16(const f16* rows, const int32_t* pair_pos, int T, int H, int k, uint16_t* y, hipStream_t s,
-                            const float* add, int add_slabs) {
+hipError_t launch_combine16(const f16* rows, int T, int H, int k, uint16_t* y, hipStream_t s, const float* add,
+                            int add_slabs) {
   const int threads = T < 64 ? 64 : 256;
-  hipLaunchKernelGGL(combine16_kernel, dim3((H / 4 + threads - 1) / threads, T), dim3(threads), 0, s, rows, pair_pos, H,
-                     k, y, add, add_slabs, (long long)T * H);
+  hipLaunchKernelGGL(combine16_kernel, dim3((H / 4 + threads - 1) / threads, T), dim3(threads), 0, s, rows, H, k, y,
+                     add, add_slabs, (long long)T * H);
   return hipGetLastError();
 }
 

@@ -241,10 +241,22 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   const uint32_t lo = wave_max_u32((uint32_t)(v >> 32) == hi ? (uint32_t)v : 0u);
   return ((uint64_t)hi << 32) | lo;
 }
+// Wavefront sum in a fixed order with the same DPP moves (lanes without a
+// source add 0): quads, then rows of 16, then across rows into lane 63,
+// whose value is the result.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_float(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf,
+                                                               false));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, WAVE);
-  return v;
+  v += dpp_float<0xb1>(v);
+  v += dpp_float<0x4e>(v);
+  v += dpp_float<0x124>(v);
+  v += dpp_float<0x128>(v);
+  v += dpp_float<0x142, 0xa>(v);
+  v += dpp_float<0x143, 0xc>(v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 __device__ __forceinline__ void cas_desc(uint64_t& a, uint64_t& b) {
