@@ -776,9 +776,10 @@ constexpr int ROUTER_MFMA_MIN_T = 32;
 RouterPlan router_plan(int T, int H, int E) {
   RouterPlan p;
   if (T >= ROUTER_MFMA_MIN_T) {
-    // one wavefront per (128 experts, 64 tokens, K slab); aim for >= 512
+    // one wavefront per (128 experts, 64 tokens, K slab); aim for >= 2048
+    // (eight per CU)
     const int tiles = ((E + RM_EXPERTS - 1) / RM_EXPERTS) * ((T + RM_TOKENS - 1) / RM_TOKENS);
-    int s = (512 + tiles - 1) / tiles;
+    int s = (2048 + tiles - 1) / tiles;
     if (s > ROUTER_MAX_SLABS) s = ROUTER_MAX_SLABS;
     const int steps = H / 32;
     if (s > steps) s = steps;
@@ -830,8 +831,11 @@ hipError_t launch_topk(const float* part, int slabs, const float* bias, float* l
   if (T <= 64)
     hipLaunchKernelGGL(topk_block_kernel, dim3(T), dim3(TOPK_THREADS), 0, s, part, slabs, bias, logits, T, E, k, ids,
                        w);
-  else
+  else if (T < 2048)  // four tokens a block: at least 17 blocks
     hipLaunchKernelGGL((topk_kernel<4>), dim3((T + 3) / 4), dim3(TOPK_THREADS), 0, s, part, slabs, bias, logits, T,
+                       E, k, ids, w);
+  else  // sixteen: one per wavefront, at least 128 blocks
+    hipLaunchKernelGGL((topk_kernel<16>), dim3((T + 15) / 16), dim3(TOPK_THREADS), 0, s, part, slabs, bias, logits, T,
                        E, k, ids, w);
   return hipGetLastError();
 }
