@@ -710,7 +710,6 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* __restri
   const int slot = block_exclusive_scan(flag, lds, &nact);
   if (e < E) {
     offsets[e] = off;
-    for (int b = 0; b < nblocks; b++) base[(size_t)b * E + e] += off;
     if (flag) active[slot] = e;
   }
   if (e == 0) {
@@ -723,22 +722,28 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* __restri
 __global__ __launch_bounds__(WAVE) void perm_scatter_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
                                                           const uint64_t* __restrict__ masks,
                                                           const int32_t* __restrict__ base,
+                                                          const int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ sorted_pairs,
                                                           int32_t* __restrict__ pair_pos) {
-  const int b = blockIdx.x;
-  if (threadIdx.x < WAVE) {
-    const int lane = threadIdx.x;
-    const int t = b * WAVE + lane;
-    if (t < T) {
-      const uint64_t below = (1ull << lane) - 1ull;
-      for (int j = 0; j < k; j++) {
-        const int f = t * k + j;
-        const int e = ids[f];
-        const int pos = base[(size_t)b * E + e] + __popcll(masks[(size_t)b * E + e] & below);
-        sorted_pairs[pos] = f;
-        pair_pos[f] = pos;
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const int t = b * WAVE + lane;
+  if (t >= T) return;
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int j0 = 0; j0 < k; j0 += 16) {  // 16 records' loads in flight
+    int e[16];
+#pragma unroll
+    for (int u = 0; u < 16; u++) e[u] = j0 + u < k ? ids[(size_t)t * k + j0 + u] : 0;
+    int pos[16];
+#pragma unroll
+    for (int u = 0; u < 16; u++)
+      pos[u] = offsets[e[u]] + base[(size_t)b * E + e[u]] + __popcll(masks[(size_t)b * E + e[u]] & below);
+#pragma unroll
+    for (int u = 0; u < 16; u++)
+      if (j0 + u < k) {
+        const int f = t * k + j0 + u;
+        sorted_pairs[pos[u]] = f;
+        pair_pos[f] = pos[u];
       }
-    }
   }
 }
 
@@ -862,8 +867,8 @@ hipError_t launch_permute(const int32_t* ids, int T, int E, int k, uint64_t* mas
   hipLaunchKernelGGL(perm_count_kernel, dim3(nb), dim3(WAVE), 0, s, ids, T, E, k, masks, counts);
   hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, s, counts, nb, E, T * k, base, offsets, active,
                      n_active, mtiles, n_mtiles);
-  hipLaunchKernelGGL(perm_scatter_kernel, dim3(nb), dim3(WAVE), 0, s, ids, T, E, k, masks, base, sorted_pairs,
-                     pair_pos);
+  hipLaunchKernelGGL(perm_scatter_kernel, dim3(nb), dim3(WAVE), 0, s, ids, T, E, k, masks, base, offsets,
+                     sorted_pairs, pair_pos);
   return hipGetLastError();
 }
 
