@@ -441,29 +441,84 @@ __device__ __forceinline__ void wave_topk(const float* ls, int E, int k, int32_t
   }
 }
 
+// Logits of the consecutive tokens row0 .. row0+nrows-1 (a contiguous run of
+// [T][E]) into LDS rows of 1024 (and out to `logits`): each thread takes
+// float4 pieces u = 0..U-1 (a block-stride apart) and issues the loads of
+// ZB slabs for all of them before adding; slabs are added in ascending
+// order, as sum_slabs does.  With part == NULL the logits are an input.
+template <int U, int ZB>
+__device__ __forceinline__ void logits_rows(const float* __restrict__ part, int slabs, size_t slab_stride,
+                                            const float* __restrict__ bias, float* __restrict__ logits, float* ls,
+                                            int row0, int nrows, int E) {
+  const int n4 = nrows * E / 4;  // E % 8 == 0
+  const size_t base = (size_t)row0 * E;
+  for (int q0 = threadIdx.x; q0 < n4; q0 += U * blockDim.x) {
+    float4 acc[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) acc[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (part) {
+      for (int z0 = 0; z0 < slabs; z0 += ZB) {
+        float4 b[U][ZB];
+#pragma unroll
+        for (int u = 0; u < U; u++)
+#pragma unroll
+          for (int z = 0; z < ZB; z++) {
+            const int q = q0 + u * blockDim.x;
+            b[u][z] = (q < n4 && z0 + z < slabs)
+                          ? *reinterpret_cast<const float4*>(part + (size_t)(z0 + z) * slab_stride + base + 4 * q)
+                          : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+          }
+#pragma unroll
+        for (int u = 0; u < U; u++)
+#pragma unroll
+          for (int z = 0; z < ZB; z++)
+            if (z0 + z < slabs) {
+              acc[u].x += b[u][z].x;
+              acc[u].y += b[u][z].y;
+              acc[u].z += b[u][z].z;
+              acc[u].w += b[u][z].w;
+            }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int q = q0 + u * blockDim.x;
+      if (q >= n4) continue;
+      const int a = 4 * q / E, e = 4 * q % E;
+      float4 v = acc[u];
+      if (part) {
+        if (bias) {
+          const float4 bb = *reinterpret_cast<const float4*>(bias + e);
+          v.x += bb.x;
+          v.y += bb.y;
+          v.z += bb.z;
+          v.w += bb.w;
+        }
+        *reinterpret_cast<float4*>(logits + base + 4 * q) = v;
+      } else {
+        v = *reinterpret_cast<const float4*>(logits + base + 4 * q);  // logits given by the caller
+      }
+      *reinterpret_cast<float4*>(ls + a * 1024 + e) = v;
+    }
+  }
+}
+
 template <int TB>
 __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(const float* __restrict__ part, int slabs,
                                                            const float* __restrict__ bias,
                                                            float* __restrict__ logits, int T, int E, int k,
                                                            int32_t* __restrict__ ids, float* __restrict__ wout) {
-  __shared__ float ls[TB * 1024];
+  __shared__ __attribute__((aligned(16))) float ls[TB * 1024];
   __shared__ __attribute__((aligned(16))) WaveTopkLds tk[TB];
   const int t0 = blockIdx.x * TB;
   // Phase 1: logits of this block's tokens (slab partials added in ascending
-  // slab order, or the caller's logits).
-  for (int idx = threadIdx.x; idx < TB * E; idx += TOPK_THREADS) {
-    const int a = idx / E, e = idx % E, t = t0 + a;
-    if (t >= T) continue;
-    float v;
-    if (part) {
-      v = sum_slabs(part + (size_t)t * E + e, (size_t)T * E, slabs);
-      if (bias) v += bias[e];
-      logits[(size_t)t * E + e] = v;
-    } else {
-      v = logits[(size_t)t * E + e];  // logits given by the caller
-    }
-    ls[a * 1024 + e] = v;
-  }
+  // slab order, or the caller's logits), with many loads in flight: four
+  // pieces of four slabs when there are few slabs, else sixteen slabs.
+  const int nrows = min(TB, T - t0);
+  if (slabs <= 4)
+    logits_rows<4, 4>(part, slabs, (size_t)T * E, bias, logits, ls, t0, nrows, E);
+  else
+    logits_rows<1, 16>(part, slabs, (size_t)T * E, bias, logits, ls, t0, nrows, E);
   __syncthreads();
   // Phase 2: wavefront w selects for token t0 + w.
   const int wv = threadIdx.x / WAVE;
