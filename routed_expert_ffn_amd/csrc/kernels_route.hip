@@ -285,22 +285,6 @@ __device__ __forceinline__ void sort16_desc(uint64_t (&k)[TOPK_KEYS]) {
 
 constexpr int TOPK_THREADS = 1024;
 
-// Sum of the slab partials of one logit, in ascending slab order; the loads
-// are issued together, so a thread waits for memory once (the router plan
-// keeps the slab count at or below ROUTER_MAX_SLABS).
-__device__ __forceinline__ float sum_slabs(const float* __restrict__ p, size_t step, int slabs) {
-  float v = 0.0f;
-  for (int z0 = 0; z0 < slabs; z0 += ROUTER_MAX_SLABS) {
-    float b[ROUTER_MAX_SLABS];
-#pragma unroll
-    for (int u = 0; u < ROUTER_MAX_SLABS; u++) b[u] = z0 + u < slabs ? p[(size_t)(z0 + u) * step] : 0.0f;
-#pragma unroll
-    for (int u = 0; u < ROUTER_MAX_SLABS; u++)
-      if (z0 + u < slabs) v += b[u];
-  }
-  return v;
-}
-
 // One wavefront: the top k of E logits (LDS) and their renormalised softmax
 // weights, written to ids[0..k) / w[0..k) (and ids_copy, if given).
 __device__ __forceinline__ void select_topk(const float* ls, int E, int k, int32_t* __restrict__ ids, float* __restrict__ w,
@@ -445,7 +429,7 @@ __device__ __forceinline__ void wave_topk(const float* ls, int E, int k, int32_t
 // [T][E]) into LDS rows of 1024 (and out to `logits`): each thread takes
 // float4 pieces u = 0..U-1 (a block-stride apart) and issues the loads of
 // ZB slabs for all of them before adding; slabs are added in ascending
-// order, as sum_slabs does.  With part == NULL the logits are an input.
+// order.  With part == NULL the logits are an input.
 template <int U, int ZB>
 __device__ __forceinline__ void logits_rows(const float* __restrict__ part, int slabs, size_t slab_stride,
                                             const float* __restrict__ bias, float* __restrict__ logits, float* ls,
@@ -499,6 +483,71 @@ __device__ __forceinline__ void logits_rows(const float* __restrict__ part, int 
         v = *reinterpret_cast<const float4*>(logits + base + 4 * q);  // logits given by the caller
       }
       *reinterpret_cast<float4*>(ls + a * 1024 + e) = v;
+    }
+  }
+}
+
+// Logits of the first `nrows` rows of [T][E] (rows row0 ..) into LDS rows of
+// 1024, for a block of 1024 threads: thread (g, q) = (tid / 256, tid % 256)
+// adds slab group g (a quarter of the slabs, at most eight, their loads
+// issued together) for float4 piece q; the four group sums meet in LDS
+// (gsum, 256 float4) and are added in group order.  One round of loads for
+// up to 256 pieces (one token at E = 1024) and 32 slabs.
+__device__ __forceinline__ void logits_rows_grouped(const float* __restrict__ part, int slabs, size_t slab_stride,
+                                                    const float* __restrict__ bias, float* __restrict__ logits,
+                                                    float* ls, int row0, int nrows, int E, float4* gsum) {
+  const int n4 = nrows * E / 4;  // E % 8 == 0
+  const size_t base = (size_t)row0 * E;
+  const int g = threadIdx.x / 256, ql = threadIdx.x % 256;
+  const int zper = (slabs + 3) / 4;  // <= ROUTER_MAX_SLABS / 4
+  for (int q0 = 0; q0 < n4; q0 += 256) {
+    const int q = q0 + ql;
+    if (part) {
+      float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if (q < n4) {
+        float4 b[ROUTER_MAX_SLABS / 4];
+#pragma unroll
+        for (int z = 0; z < ROUTER_MAX_SLABS / 4; z++) {
+          const int zz = g * zper + z;
+          b[z] = (z < zper && zz < slabs) ? *reinterpret_cast<const float4*>(part + (size_t)zz * slab_stride + base + 4 * q)
+                                          : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+#pragma unroll
+        for (int z = 0; z < ROUTER_MAX_SLABS / 4; z++)
+          if (z < zper && g * zper + z < slabs) {
+            acc.x += b[z].x;
+            acc.y += b[z].y;
+            acc.z += b[z].z;
+            acc.w += b[z].w;
+          }
+      }
+      gsum[threadIdx.x] = acc;
+      __syncthreads();
+      if (g == 0 && q < n4) {
+        float4 v = gsum[ql];
+#pragma unroll
+        for (int h = 1; h < 4; h++) {
+          const float4 o = gsum[h * 256 + ql];
+          v.x += o.x;
+          v.y += o.y;
+          v.z += o.z;
+          v.w += o.w;
+        }
+        const int e = 4 * q % E;
+        if (bias) {
+          const float4 bb = *reinterpret_cast<const float4*>(bias + e);
+          v.x += bb.x;
+          v.y += bb.y;
+          v.z += bb.z;
+          v.w += bb.w;
+        }
+        *reinterpret_cast<float4*>(logits + base + 4 * q) = v;
+        *reinterpret_cast<float4*>(ls + (4 * q / E) * 1024 + e) = v;
+      }
+      __syncthreads();
+    } else if (g == 0 && q < n4) {  // logits given by the caller
+      const int e = 4 * q % E;
+      *reinterpret_cast<float4*>(ls + (4 * q / E) * 1024 + e) = *reinterpret_cast<const float4*>(logits + base + 4 * q);
     }
   }
 }
@@ -580,27 +629,18 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* lds /*[16]*/, in
   return base + incl - v;
 }
 
-// One token per block: the logits (as topk_kernel), then wave_topk by
+// One token per block: the logits (grouped slab sums), then wave_topk by
 // wavefront 0.
 __global__ __launch_bounds__(TOPK_THREADS) void topk_block_kernel(const float* __restrict__ part, int slabs,
                                                                  const float* __restrict__ bias,
                                                                  float* __restrict__ logits, int T, int E, int k,
                                                                  int32_t* __restrict__ ids,
                                                                  float* __restrict__ wout) {
-  __shared__ float ls[1024];
+  __shared__ __attribute__((aligned(16))) float ls[1024];
   __shared__ __attribute__((aligned(16))) WaveTopkLds tk;
-  const int t = blockIdx.x, e = threadIdx.x;
-  if (e < E) {
-    float v;
-    if (part) {
-      v = sum_slabs(part + (size_t)t * E + e, (size_t)T * E, slabs);
-      if (bias) v += bias[e];
-      logits[(size_t)t * E + e] = v;
-    } else {
-      v = logits[(size_t)t * E + e];
-    }
-    ls[e] = v;
-  }
+  __shared__ float4 gsum[1024];
+  const int t = blockIdx.x;
+  logits_rows_grouped(part, slabs, (size_t)T * E, bias, logits, ls, t, 1, E, gsum);
   __syncthreads();
   if (threadIdx.x < WAVE) wave_topk(ls, E, k, ids + (size_t)t * k, wout + (size_t)t * k, nullptr, tk);
 }
@@ -681,26 +721,16 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const float* __restri
                                                           int32_t* __restrict__ pair_pos,
                                                           int32_t* __restrict__ active,
                                                           int32_t* __restrict__ n_active) {
-  __shared__ float ls[ROUTE_SMALL_T * PERM_MAX_E];
+  __shared__ __attribute__((aligned(16))) float ls[ROUTE_SMALL_T * PERM_MAX_E];
   __shared__ int ids_s[ROUTE_SMALL_T * 64];
   __shared__ unsigned long long m[PERM_MAX_E];
   __shared__ int off_s[PERM_MAX_E];
   __shared__ __attribute__((aligned(16))) int lds[16];
   __shared__ __attribute__((aligned(16))) WaveTopkLds tk[ROUTE_SMALL_T];
+  __shared__ float4 gsum[1024];
   const int tid = threadIdx.x;
-  for (int idx = tid; idx < T * E; idx += 1024) {
-    const int t = idx / E, e = idx % E;
-    float v;
-    if (part) {
-      v = sum_slabs(part + (size_t)t * E + e, (size_t)T * E, slabs);
-      if (bias) v += bias[e];
-      logits[(size_t)t * E + e] = v;
-    } else {
-      v = logits[(size_t)t * E + e];
-    }
-    ls[t * PERM_MAX_E + e] = v;
-  }
   if (tid < E) m[tid] = 0ull;
+  logits_rows_grouped(part, slabs, (size_t)T * E, bias, logits, ls, 0, T, E, gsum);
   __syncthreads();
   const int wv = tid / WAVE;
   if (wv < T)
