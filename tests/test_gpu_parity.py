@@ -175,7 +175,26 @@ def test_ragged_layer(T, E, k, beta):
     assert_close(y, ref["y"], "y")
 
 
-@pytest.mark.parametrize("H,I,fmt,T", [(8448, 256, "nvfp4", 8), (512, 4352, "nvfp4", 300), (512, 8448, "mxfp4", 40)])
+@pytest.mark.parametrize("I,T", [(768, 1), (1280, 16), (2048, 7)])
+def test_small_batch_chunk_counts(I, T):
+    """Small batches (whole-line code loads, staged scales) over odd and even
+    numbers of 256-k chunks: K = I = 768, 1280 and 2048 are 3, 5 and 8
+    chunks for the down GEMM, split two ways for gate/up at H = 512."""
+    say(f"chunk counts I={I} T={T}")
+    H, E, k = 512, 16, 4
+    store = build_store(E, H, I, 13)
+    inp = Inputs(T, H, I, E, k, seed=13, store=store, router_std=0.1)
+    r = inp.route()
+    ox = OracleExperts(13, H, I)
+    ref = oracle.moe_layer(inp.host_x(), ox.get(r["ids"]), E, k, logits_in=r["logits"], want_rows=True, nthreads=16)
+    assert_close(inp.ffn(r["offsets"], r["sorted_pairs"]), ref["rows"], "rows")
+    y, ids, _ = inp.layer()
+    np.testing.assert_array_equal(ids, ref["ids"])
+    assert_close(y, ref["y"], "y")
+
+
+@pytest.mark.parametrize("H,I,fmt,T", [(8448, 256, "nvfp4", 8), (512, 4352, "nvfp4", 300), (512, 4352, "nvfp4", 12),
+                                       (512, 8448, "mxfp4", 40), (512, 8448, "mxfp4", 6)])
 def test_wide_k_scales_from_memory(H, I, fmt, T):
     """K beyond what a block can stage of its block scales in LDS (gate/up K
     over 8192, down K over 4096 for NVFP4, twice that for MXFP4): those GEMMs
