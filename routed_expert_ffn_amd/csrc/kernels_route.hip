@@ -199,14 +199,15 @@ __global__ __launch_bounds__(WAVE) void router_mfma_kernel(const uint16_t* __res
 }
 
 // ---- logits reduction + softmax + top-k ------------------------------------------
-// A block takes TB tokens.  All 1024 threads first sum the slab partials of
-// those tokens' logits (fixed ascending slab order), add the bias and store
-// the logits; then wavefront w selects the top k of token w.
+// A block takes one or more tokens.  All its threads first sum the slab
+// partials of those tokens' logits (a fixed order), add the bias and store
+// the logits; then wavefront w selects the top k of token w (wave_topk).
 // Selection key: a 64-bit integer ordered as (logit descending, expert index
 // ascending): the high word maps the fp32 logit to an order-preserving
-// unsigned integer (-0 folded onto +0), the low word is ~index.  Each lane
-// sorts its (up to) 16 keys, then k rounds each take the wavefront maximum
-// of the lanes' heads and pop it from the winning lane.
+// unsigned integer (-0 folded onto +0), the low word is ~index.  wave_topk
+// filters the keys down to a few candidates and ranks them; its fallback
+// (select_topk) sorts each lane's (up to) 16 keys and takes k rounds of the
+// wavefront maximum of the lanes' heads, popping it from the winning lane.
 constexpr int TOPK_KEYS = 16;  // E <= 1024
 
 __device__ __forceinline__ uint32_t float_order(float f) {
