@@ -478,14 +478,17 @@ __global__ __launch_bounds__(FFN_THREADS, WAVES_PER_EU) void expert_gemm_kernel(
 // ---- large batches: 224-token x 256-row tiles on 32x32x16 matrix cores ---------
 // Work items are (expert, token tile) entries of a list built with the
 // permutation (mtiles), times the row tiles of the matrix; an expert's
-// records are split evenly over ceil(n / 224) tiles.  A block of four
-// wavefronts computes a tile of up to 224 tokens (NF = ceil(n / 32) token
-// fragments, a template parameter so the inner loop is straight-line code)
-// against 256 weight rows: wavefront w takes every token fragment against
-// its own 64 weight rows (two fragments), as v_mfma_f32_32x32x16_f16 (lane l
-// holds A[l%32][8(l/32)..+7], B[8(l/32)..+7][l%32] and D[8(i/4) + 4(l/32) +
-// i%4][l%32]).  Each weight row is thus dequantised once per block and the
-// four wavefronts carry equal work.
+// records are split evenly over ceil(n / 224) tiles.  A block of eight
+// wavefronts, two per SIMD, computes a tile of up to 224 tokens (NF =
+// ceil(n / 32) token fragments, a template parameter so the inner loop is
+// straight-line code) against 256 weight rows: wavefronts w and w + 4 share
+// one SIMD and its 64 weight rows (two fragments) and take the even and the
+// odd token fragments, as v_mfma_f32_32x32x16_f16 (lane l holds
+// A[l%32][8(l/32)..+7], B[8(l/32)..+7][l%32] and D[8(i/4) + 4(l/32) +
+// i%4][l%32]).  Each SIMD thus multiplies every token fragment against its
+// rows once; the two wavefronts each dequantise the rows (at most 128
+// accumulator registers each, so two fit a SIMD), and one's LDS reads and
+// barrier waits overlap the other's matrix-core work.
 //
 // K runs in chunks of 64.  Inside a chunk the sum is taken in a permuted
 // order: lane half g = l/32 in step s covers the chunk's k = 32g + 8s .. +7,
@@ -511,11 +514,12 @@ __global__ __launch_bounds__(FFN_THREADS, WAVES_PER_EU) void expert_gemm_kernel(
 // after the one it issued in, when nothing else of its own is in flight; a
 // partial vmcnt wait that leaves newer DMA in flight was measured not to
 // guarantee that older DMA writes are visible in LDS, so only vmcnt(0) is
-// used.
+// used.  Wavefronts 4-7 copy nothing; they only meet the others at the
+// chunk barriers.
 //
-// Gate/up tiles pair 128 gate rows with the same 128 up rows (wavefront w:
-// gate rows 32w .. and up rows 128 + 32w ..), so SiLU * up happens in
-// registers.  Items are mapped to blocks so that the row tiles of one
+// Gate/up tiles pair 128 gate rows with the same 128 up rows (wavefronts w
+// and w + 4: gate rows 32w .. and up rows 128 + 32w ..), so SiLU * up
+// happens in registers.  Items are mapped to blocks so that the row tiles of one
 // (expert, token tile) run back to back on one XCD (blocks are dealt to the
 // eight XCDs round robin): its activations stay in that XCD's L2 while the
 // weights stream once.
@@ -528,9 +532,9 @@ __device__ __forceinline__ f32x16 mfma32x32x16(f16x8 a, f16x8 b, f32x16 c) {
 constexpr int BIG_M = MTILE;    // tokens per tile (7 fragments of 32)
 constexpr int BIG_MF = BIG_M / 32;
 constexpr int BIG_N = 256;      // weight rows per tile (8 fragments of 32)
-constexpr int BIG_THREADS = 256;
 constexpr int BIG_KC = 64;      // k per chunk: 8 pieces of 8 halves per token row
 constexpr int BIG_SPAN = 4;     // chunks per raw weight span
+constexpr int BIG_WAVES = 8;    // two wavefronts per SIMD
 static_assert(BIG_M % 32 == 0 && BIG_MF <= 8, "token tile of whole fragments");
 // LDS layout (bytes)
 constexpr int BIG_TILE_BYTES = BIG_M * BIG_KC * 2;                  // tokens of one chunk
@@ -633,10 +637,19 @@ __device__ __forceinline__ void dequant_step(f16x8 (&bv)[2], const u32x4 (&q)[2]
   }
 }
 
-template <int NF>
+// Token fragments a wavefront multiplies: of the tile's NF, the even ones
+// (HALF 0, wavefronts 0-3) or the odd ones (HALF 1, wavefronts 4-7).
+template <int NF, int HALF>
+struct Frags {
+  static constexpr int n = (NF + 1 - HALF) / 2;            // this wavefront's count
+  static constexpr int at(int f) { return 2 * f + HALF; }  // its f-th, in the tile
+};
+
+template <int NF, int HALF>
 __device__ __forceinline__ void read_a(f16x8 (&av)[8], const unsigned char* Ab, int aoff) {
 #pragma unroll
-  for (int f = 0; f < NF; f++) av[f] = *reinterpret_cast<const f16x8*>(Ab + aoff + 32 * f * BIG_KC * 2);
+  for (int f = 0; f < Frags<NF, HALF>::n; f++)
+    av[f] = *reinterpret_cast<const f16x8*>(Ab + aoff + 32 * Frags<NF, HALF>::at(f) * BIG_KC * 2);
 }
 
 template <int NF>
@@ -657,7 +670,8 @@ __device__ __forceinline__ void mma_step(f32x16 (&acc)[8][2], const f16x8 (&av)[
 // LDS command queue and hold up the next MFMA's issue.
 template <int NF, int LEAD = 0, int NDS = 0>
 __device__ __forceinline__ void interleave_mfma_valu() {
-  constexpr int rest = 2 * NF - LEAD;
+  if constexpr (NF == 0) return;
+  constexpr int rest = 2 * NF - LEAD > 0 ? 2 * NF - LEAD : 1;
   constexpr int per = (20 + rest - 1) / rest;
 #pragma unroll
   for (int i = 0; i < 2 * NF; i++) {
@@ -721,9 +735,12 @@ __device__ __forceinline__ void convert_scales(const BigLane& L, BigStep& st) {
 // MFMAs run, so the matrix cores do not idle at the chunk boundary.  (Every
 // read of chunk c's token buffer has completed at the barrier, which is what
 // lets the next chunk's DMA overwrite it.)
-template <int NF, int J, bool TOK, bool SPAN, bool NEXT, int FMT>
+template <int NF, int HALF, int J, bool TOK_, bool SPAN_, bool NEXT, int FMT>
 __device__ __forceinline__ void big_chunk(const BigLane& L, f32x16 (&acc)[8][2], unsigned char* smem, int c, int wv,
                                           BigStep& st) {
+  // (only the first four wavefronts, HALF 0, copy)
+  constexpr bool TOK = TOK_ && HALF == 0, SPAN = SPAN_ && HALF == 0;
+  constexpr int NW = Frags<NF, HALF>::n;
   const int pair = wv >> 1, par = wv & 1;
   const int span = c / BIG_SPAN, slot = span & 1;
   const bool tok_issuer = pair == (J & 1);
@@ -735,20 +752,20 @@ __device__ __forceinline__ void big_chunk(const BigLane& L, f32x16 (&acc)[8][2],
   const unsigned char* Ab = smem + BIG_OFF_A + (c % 3) * BIG_TILE_BYTES;
   // Steps, each fenced so that the compiler keeps the order.
   f16x8 a1[8], b1[2];
-  mma_step<NF>(acc, st.a, st.b);
-  read_a<NF>(a1, Ab, L.aoff[1]);
+  mma_step<NW>(acc, st.a, st.b);
+  read_a<NF, HALF>(a1, Ab, L.aoff[1]);
   dequant_step<FMT>(b1, st.q, st.sig, st.pw, 1);
-  interleave_mfma_valu<NF, 0, NF>();
+  interleave_mfma_valu<NW, 0, NW>();
   __builtin_amdgcn_sched_barrier(0);
-  mma_step<NF>(acc, a1, b1);
-  read_a<NF>(st.a, Ab, L.aoff[2]);
+  mma_step<NW>(acc, a1, b1);
+  read_a<NF, HALF>(st.a, Ab, L.aoff[2]);
   dequant_step<FMT>(st.b, st.q, st.sig, st.pw, 2);
-  interleave_mfma_valu<NF, 0, NF>();
+  interleave_mfma_valu<NW, 0, NW>();
   __builtin_amdgcn_sched_barrier(0);
-  mma_step<NF>(acc, st.a, st.b);
-  read_a<NF>(a1, Ab, L.aoff[3]);
+  mma_step<NW>(acc, st.a, st.b);
+  read_a<NF, HALF>(a1, Ab, L.aoff[3]);
   dequant_step<FMT>(b1, st.q, st.sig, st.pw, 3);
-  interleave_mfma_valu<NF, 0, NF>();
+  interleave_mfma_valu<NW, 0, NW>();
   __builtin_amdgcn_sched_barrier(0);
   // (step 3's weights are computed here, beside step 2's MFMAs; without this
   // the compiler sinks them past the barrier's branch)
@@ -762,25 +779,25 @@ __device__ __forceinline__ void big_chunk(const BigLane& L, f32x16 (&acc)[8][2],
     constexpr int JN = (J + 1) % BIG_SPAN;
     read_chunk_b<JN, FMT>(L, smem, JN == 0 ? slot ^ 1 : slot, st);
     __builtin_amdgcn_sched_barrier(0);
-    mma_step<NF>(acc, a1, b1);
-    read_a<NF>(st.a, smem + BIG_OFF_A + ((c + 1) % 3) * BIG_TILE_BYTES, L.aoff[0]);
+    mma_step<NW>(acc, a1, b1);
+    read_a<NF, HALF>(st.a, smem + BIG_OFF_A + ((c + 1) % 3) * BIG_TILE_BYTES, L.aoff[0]);
     convert_scales<FMT>(L, st);
     dequant_step<FMT>(st.b, st.q, st.sig, st.pw, 0);
-    interleave_mfma_valu<NF, NF, NF>();
+    interleave_mfma_valu<NW, NW, NW>();
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" : "+v"(st.b[0]), "+v"(st.b[1]));  // (kept beside step 3's MFMAs)
   } else {
-    mma_step<NF>(acc, a1, b1);
+    mma_step<NW>(acc, a1, b1);
   }
 }
 
-template <int NF, bool TOK, bool SPAN, int FMT>
+template <int NF, int HALF, bool TOK, bool SPAN, int FMT>
 __device__ __forceinline__ void big_span(const BigLane& L, f32x16 (&acc)[8][2], unsigned char* smem, int c, int wv,
                                          BigStep& st) {
-  big_chunk<NF, 0, TOK, SPAN, true, FMT>(L, acc, smem, c, wv, st);
-  big_chunk<NF, 1, TOK, SPAN, true, FMT>(L, acc, smem, c + 1, wv, st);
-  big_chunk<NF, 2, TOK, SPAN, true, FMT>(L, acc, smem, c + 2, wv, st);
-  big_chunk<NF, 3, TOK, SPAN, true, FMT>(L, acc, smem, c + 3, wv, st);
+  big_chunk<NF, HALF, 0, TOK, SPAN, true, FMT>(L, acc, smem, c, wv, st);
+  big_chunk<NF, HALF, 1, TOK, SPAN, true, FMT>(L, acc, smem, c + 1, wv, st);
+  big_chunk<NF, HALF, 2, TOK, SPAN, true, FMT>(L, acc, smem, c + 2, wv, st);
+  big_chunk<NF, HALF, 3, TOK, SPAN, true, FMT>(L, acc, smem, c + 3, wv, st);
 }
 
 // 4x4 transpose across the four lanes of a quad: lane j's v[r] becomes lane
@@ -817,10 +834,15 @@ __device__ __forceinline__ void quad_transpose(float (&v)[4]) {
   }
 }
 
-template <int NF, bool GATEUP, int FMT>
+// Wavefronts w and w + 4 (one SIMD) take the same 64 weight rows (w % 4) and
+// the even (HALF 0) and odd (HALF 1) token fragments; only the first four
+// copy.
+template <int NF, bool GATEUP, int FMT, int HALF>
 __device__ __forceinline__ void big_tile(const GroupedParams& p, const BigTile& t, unsigned char* smem) {
+  constexpr int NW = Frags<NF, HALF>::n;
   const int lane = threadIdx.x % WAVE, m32 = lane % 32, g2 = lane / 32;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE), par = wv & 1;
+  const int wr = wv & 3;  // weight rows 64 wr ..  (gate/up: 32 wr .. of each matrix)
   const int K = t.K, nch = K / BIG_KC;
   const int32_t* rowoff = reinterpret_cast<const int32_t*>(smem + BIG_OFF_ROW);
   BigLane L;
@@ -882,7 +904,7 @@ __device__ __forceinline__ void big_tile(const GroupedParams& p, const BigTile& 
     }
 #pragma unroll
     for (int nf = 0; nf < 2; nf++) {
-      const int row = (GATEUP ? 32 * wv + 128 * nf : 64 * wv + 32 * nf) + m32;
+      const int row = (GATEUP ? 32 * wr + 128 * nf : 64 * wr + 32 * nf) + m32;
       L.qrow[nf] = row * 128;
       L.srow[nf] = row * (FMT == FMT_MX ? 8 : 16);
     }
@@ -899,7 +921,9 @@ __device__ __forceinline__ void big_tile(const GroupedParams& p, const BigTile& 
   // chunk -1) and waits at the end of chunk 0.  nch % 4 == 0, nch >= 4.
   {
     const int pair = wv >> 1;
-    if (pair == 0) {
+    if (HALF > 0) {
+      lds_barrier_vm<0>();  // nothing of its own in flight
+    } else if (pair == 0) {
       dma_tokens(L, smem, 0, 0, par);
       dma_span_half<FMT>(L, smem, 0, 0, 0, par);
       dma_span_half<FMT>(L, smem, 0, 0, 1, par);
@@ -912,16 +936,16 @@ __device__ __forceinline__ void big_tile(const GroupedParams& p, const BigTile& 
   // chunk 0's codes, scales and step 0
   BigStep st;
   read_chunk_b<0, FMT>(L, smem, 0, st);
-  read_a<NF>(st.a, smem + BIG_OFF_A, L.aoff[0]);
+  read_a<NF, HALF>(st.a, smem + BIG_OFF_A, L.aoff[0]);
   convert_scales<FMT>(L, st);
   dequant_step<FMT>(st.b, st.q, st.sig, st.pw, 0);
   int c = 0;
-  for (; c + BIG_SPAN < nch; c += BIG_SPAN) big_span<NF, true, true, FMT>(L, acc, smem, c, wv, st);
+  for (; c + BIG_SPAN < nch; c += BIG_SPAN) big_span<NF, HALF, true, true, FMT>(L, acc, smem, c, wv, st);
   // the last span: tokens of chunks c+2, c+3 still to copy, no next span
-  big_chunk<NF, 0, true, false, true, FMT>(L, acc, smem, c, wv, st);
-  big_chunk<NF, 1, true, false, true, FMT>(L, acc, smem, c + 1, wv, st);
-  big_chunk<NF, 2, false, false, true, FMT>(L, acc, smem, c + 2, wv, st);
-  big_chunk<NF, 3, false, false, false, FMT>(L, acc, smem, c + 3, wv, st);
+  big_chunk<NF, HALF, 0, true, false, true, FMT>(L, acc, smem, c, wv, st);
+  big_chunk<NF, HALF, 1, true, false, true, FMT>(L, acc, smem, c + 1, wv, st);
+  big_chunk<NF, HALF, 2, false, false, true, FMT>(L, acc, smem, c + 2, wv, st);
+  big_chunk<NF, HALF, 3, false, false, false, FMT>(L, acc, smem, c + 3, wv, st);
   // Epilogue.  Accumulator registers 4q .. 4q+3 of a lane hold rows
   // 8q + 4 g2 + 0..3 of its column m32; a quad transpose turns them into
   // four consecutive columns (m32 & ~3 ..) of row 8q + 4 g2 + (lane & 3), so
@@ -930,10 +954,10 @@ __device__ __forceinline__ void big_tile(const GroupedParams& p, const BigTile& 
   const float gsa = p.gs0[t.e - p.e_base], gsb = GATEUP ? p.gs1[t.e - p.e_base] : 0.0f;
   const int n4 = m32 & ~3, j4 = lane & 3;
 #pragma unroll
-  for (int f = 0; f < NF; f++)
+  for (int f = 0; f < NW; f++)
 #pragma unroll
     for (int q4 = 0; q4 < 4; q4++) {
-      const int m = 32 * f + 8 * q4 + 4 * g2 + j4;
+      const int m = 32 * Frags<NF, HALF>::at(f) + 8 * q4 + 4 * g2 + j4;
       if (GATEUP) {
         float hv[4];
 #pragma unroll
@@ -943,7 +967,7 @@ __device__ __forceinline__ void big_tile(const GroupedParams& p, const BigTile& 
           f16x4 o;
 #pragma unroll
           for (int r = 0; r < 4; r++) o[r] = (f16)hv[r];
-          *reinterpret_cast<f16x4*>(p.h + (size_t)(t.mb + m) * t.N + t.rtile * (BIG_N / 2) + 32 * wv + n4) = o;
+          *reinterpret_cast<f16x4*>(p.h + (size_t)(t.mb + m) * t.N + t.rtile * (BIG_N / 2) + 32 * wr + n4) = o;
         }
       } else {
         // fp16 rows carry the routing weight of their record and are stored
@@ -957,7 +981,7 @@ __device__ __forceinline__ void big_tile(const GroupedParams& p, const BigTile& 
           for (int r = 0; r < 4; r++) v[r] = gsa * acc[f][nf][4 * q4 + r];
           quad_transpose(v);
           if (m < t.nvalid) {
-            const size_t col = (size_t)t.rtile * BIG_N + 64 * wv + 32 * nf + n4;
+            const size_t col = (size_t)t.rtile * BIG_N + 64 * wr + 32 * nf + n4;
             if (p.rows16) {
               f16x4 o;
 #pragma unroll
@@ -973,7 +997,7 @@ __device__ __forceinline__ void big_tile(const GroupedParams& p, const BigTile& 
 }
 
 template <bool GATEUP, int FMT>
-__global__ __launch_bounds__(BIG_THREADS, 1) void expert_gemm_big_kernel(BigParams bp) {
+__global__ __launch_bounds__(BIG_WAVES * WAVE, 1) void expert_gemm_big_kernel(BigParams bp) {
   extern __shared__ __attribute__((aligned(16))) unsigned char big_smem[];
   int32_t* rowoff = reinterpret_cast<int32_t*>(big_smem + BIG_OFF_ROW);
   const GroupedParams& p = bp.g;
@@ -996,7 +1020,7 @@ __global__ __launch_bounds__(BIG_THREADS, 1) void expert_gemm_big_kernel(BigPara
   t.N = GATEUP ? p.I : p.H;
   // source row (in units of K elements) of every token row of the tile;
   // rows past the count repeat the last row
-  for (int m = threadIdx.x; m < BIG_M; m += BIG_THREADS) {
+  for (int m = threadIdx.x; m < BIG_M; m += BIG_WAVES * WAVE) {
     const int pp = t.mb + min(m, t.nvalid - 1);
     rowoff[m] = GATEUP ? p.sorted_pairs[pp] / p.k : pp;
     if (!GATEUP && p.rows16) {
@@ -1006,14 +1030,27 @@ __global__ __launch_bounds__(BIG_THREADS, 1) void expert_gemm_big_kernel(BigPara
     }
   }
   __syncthreads();
-  switch ((t.nvalid + 31) / 32) {  // token fragments, 1 .. 7
-    case 1: big_tile<1, GATEUP, FMT>(p, t, big_smem); break;
-    case 2: big_tile<2, GATEUP, FMT>(p, t, big_smem); break;
-    case 3: big_tile<3, GATEUP, FMT>(p, t, big_smem); break;
-    case 4: big_tile<4, GATEUP, FMT>(p, t, big_smem); break;
-    case 5: big_tile<5, GATEUP, FMT>(p, t, big_smem); break;
-    case 6: big_tile<6, GATEUP, FMT>(p, t, big_smem); break;
-    default: big_tile<BIG_MF, GATEUP, FMT>(p, t, big_smem); break;
+  const int nf = (t.nvalid + 31) / 32;  // token fragments, 1 .. 7
+  if (threadIdx.x < 4 * WAVE) {
+    switch (nf) {
+      case 1: big_tile<1, GATEUP, FMT, 0>(p, t, big_smem); break;
+      case 2: big_tile<2, GATEUP, FMT, 0>(p, t, big_smem); break;
+      case 3: big_tile<3, GATEUP, FMT, 0>(p, t, big_smem); break;
+      case 4: big_tile<4, GATEUP, FMT, 0>(p, t, big_smem); break;
+      case 5: big_tile<5, GATEUP, FMT, 0>(p, t, big_smem); break;
+      case 6: big_tile<6, GATEUP, FMT, 0>(p, t, big_smem); break;
+      default: big_tile<BIG_MF, GATEUP, FMT, 0>(p, t, big_smem); break;
+    }
+  } else {
+    switch (nf) {
+      case 1: big_tile<1, GATEUP, FMT, 1>(p, t, big_smem); break;
+      case 2: big_tile<2, GATEUP, FMT, 1>(p, t, big_smem); break;
+      case 3: big_tile<3, GATEUP, FMT, 1>(p, t, big_smem); break;
+      case 4: big_tile<4, GATEUP, FMT, 1>(p, t, big_smem); break;
+      case 5: big_tile<5, GATEUP, FMT, 1>(p, t, big_smem); break;
+      case 6: big_tile<6, GATEUP, FMT, 1>(p, t, big_smem); break;
+      default: big_tile<BIG_MF, GATEUP, FMT, 1>(p, t, big_smem); break;
+    }
   }
 }
 
@@ -1043,7 +1080,7 @@ hipError_t launch_big_fmt(const FfnArgs& a, const GroupedParams& p, hipStream_t 
   if (e != hipSuccess) return e;
   const long long items = (long long)a.max_mtiles * bp.n_row_tiles;
   const unsigned grid = (unsigned)(8 * ((items + 7) / 8));
-  hipLaunchKernelGGL((expert_gemm_big_kernel<GATEUP, FMT>), dim3(grid), dim3(BIG_THREADS), lds, s, bp);
+  hipLaunchKernelGGL((expert_gemm_big_kernel<GATEUP, FMT>), dim3(grid), dim3(BIG_WAVES * WAVE), lds, s, bp);
   return hipGetLastError();
 }
 
