@@ -660,14 +660,16 @@ __device__ __forceinline__ void mma_step(f32x16 (&acc)[8][2], const f16x8 (&av)[
     for (int nf = 0; nf < 2; nf++) acc[f][nf] = mfma32x32x16(av[f], bv[nf], acc[f][nf]);
 }
 
-// One wavefront per SIMD issues in order, and an MFMA blocks issue until the
-// matrix core takes it, so vector work only overlaps the matrix core when
-// it sits between MFMAs: a step's 2 NF MFMAs are spread over the next
-// step's dequantisation (about 18 vector instructions), the first LEAD of
-// them with no vector work between them (time for LDS reads to land).
+// A wavefront issues in order, and an MFMA blocks its issue until the matrix
+// core takes it, so a wavefront's vector work only overlaps the matrix core
+// when it sits between its MFMAs: a step's 2 NF MFMAs are spread over the
+// next step's dequantisation (about 18 vector instructions), the first LEAD
+// of them with no vector work between them (time for LDS reads to land).
 // The next step's NDS token-fragment reads are spread over the first MFMAs
 // as well, one after each, rather than issued in a burst that can fill the
-// LDS command queue and hold up the next MFMA's issue.
+// LDS command queue and hold up the next MFMA's issue.  (This order was
+// tuned with one wavefront per SIMD; with two, the other wavefront fills the
+// gaps as well, and the hints neither help nor hurt measurably.)
 template <int NF, int LEAD = 0, int NDS = 0>
 __device__ __forceinline__ void interleave_mfma_valu() {
   if constexpr (NF == 0) return;
