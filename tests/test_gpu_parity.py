@@ -25,7 +25,10 @@ def check_route(inp, r, rows=None):
     ids, w = oracle.topk_softmax(r["logits"], inp.k)
     np.testing.assert_array_equal(r["ids"], ids)
     assert np.abs(r["w"] - w).max() <= WEIGHT_ABS
-    assert np.abs(r["w"].astype(np.float64).sum(axis=1) - 1).max() <= 1e-6
+    # each fp32 weight carries a rounding of about 2^-24 of itself and the
+    # shared denominator one per doubling of k: 1e-6 up to k = 16, growing
+    # in proportion beyond
+    assert np.abs(r["w"].astype(np.float64).sum(axis=1) - 1).max() <= 1e-6 * max(1.0, inp.k / 16)
     offsets, sp, pp = oracle.permute(r["ids"], inp.E)
     np.testing.assert_array_equal(r["offsets"], offsets)
     np.testing.assert_array_equal(r["sorted_pairs"][:inp.T * inp.k], sp)
@@ -173,6 +176,33 @@ def test_ragged_layer(T, E, k, beta):
     assert_close(rows, ref["rows"], "rows")
     y, ids, _ = inp.layer()
     assert_close(y, ref["y"], "y")
+
+
+@pytest.mark.parametrize("T", [3, 70, 1030])
+def test_largest_expert_count_and_k(T):
+    """The largest shapes the routing takes: E = 1024 experts and k = 64
+    (16 keys per lane in the top-k; a token's 64 records; more than 64
+    top-k candidates send some tokens through the fallback selection), in
+    the single-launch routing (T = 3), the single-block permutation
+    (T = 70) and the multi-block permutation with the large-tile GEMMs
+    (T = 1030); outputs checked on sampled tokens."""
+    E, k, H, I = 1024, 64, 512, 256
+    say(f"largest E={E} k={k} T={T}")
+    inp = Inputs(T, H, I, E, k, seed=14, store=build_store(E, H, I, 14), router_std=0.1)
+    r = inp.route()
+    sample = np.unique(np.array([0, T // 2, T - 1]))
+    check_route(inp, r, rows=sample)
+    assert np.diff(r["offsets"]).sum() == T * k
+    rows = inp.ffn(r["offsets"], r["sorted_pairs"])
+    y, ids, _ = inp.layer()
+    np.testing.assert_array_equal(ids, r["ids"])
+    ox = OracleExperts(14, H, I)
+    ref = oracle.moe_layer(inp.host_x(sample), ox.get(r["ids"][sample]), E, k, logits_in=r["logits"][sample],
+                           want_rows=True, nthreads=16)
+    got_rows = np.stack([rows[r["pair_pos"][t * k + j]] for t in sample for j in range(k)])
+    ref_rows = np.stack([ref["rows"][ref["pair_pos"][i * k + j]] for i in range(len(sample)) for j in range(k)])
+    assert_close(got_rows, ref_rows, "rows")
+    assert_close(y[sample], ref["y"], "y")
 
 
 @pytest.mark.parametrize("I,T", [(768, 1), (1280, 16), (2048, 7)])
