@@ -59,3 +59,24 @@ __device__ __forceinline__ f32x4 mfma16x16x32(f16x8 a, f16x8 b, f32x4 c) {
 }
 
 __device__ __forceinline__ f16x8 load_f16x8(const f16* p) { return *reinterpret_cast<const f16x8*>(p); }
+
+// acc += p[s * stride] for s = first .. slabs-1 in ascending order (float4
+// partial sums of K slabs), with the loads of eight slabs issued together.
+__device__ __forceinline__ void add_slab_partials4(float4& acc, const float* p, long long stride, int first,
+                                                   int slabs) {
+  for (int s0 = first; s0 < slabs; s0 += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; u++)
+      v[u] = s0 + u < slabs ? *reinterpret_cast<const float4*>(p + (size_t)(s0 + u) * stride)
+                            : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+    for (int u = 0; u < 8; u++)
+      if (s0 + u < slabs) {
+        acc.x += v[u].x;
+        acc.y += v[u].y;
+        acc.z += v[u].z;
+        acc.w += v[u].w;
+      }
+  }
+}

@@ -35,13 +35,7 @@ __global__ __launch_bounds__(PROJ_THREADS) void proj_reduce_kernel(const float* 
   const long long i = (long long)blockIdx.x * PROJ_THREADS + threadIdx.x;
   if (i >= n4) return;
   float4 acc = reinterpret_cast<const float4*>(part)[i];
-  for (int s = 1; s < slabs; s++) {
-    const float4 v = reinterpret_cast<const float4*>(part + (size_t)s * stride)[i];
-    acc.x += v.x;
-    acc.y += v.y;
-    acc.z += v.z;
-    acc.w += v.w;
-  }
+  add_slab_partials4(acc, part + 4 * i, stride, 1, slabs);
   const uint16_t b0 = f32_to_bf16(acc.x), b1 = f32_to_bf16(acc.y), b2 = f32_to_bf16(acc.z), b3 = f32_to_bf16(acc.w);
   uint2 o;
   o.x = (uint32_t)b0 | ((uint32_t)b1 << 16);
@@ -73,18 +67,8 @@ __global__ __launch_bounds__(PROJ_THREADS) void swiglu_reduce_kernel(const float
   const long long stride = (long long)T * 2 * width;
   const float* gp = part + (size_t)t * 2 * width + 2 * s * I + i;
   float4 g = *reinterpret_cast<const float4*>(gp), u = *reinterpret_cast<const float4*>(gp + I);
-  for (int sl = 1; sl < slabs; sl++) {
-    const float4 a = *reinterpret_cast<const float4*>(gp + sl * stride);
-    const float4 b = *reinterpret_cast<const float4*>(gp + sl * stride + I);
-    g.x += a.x;
-    g.y += a.y;
-    g.z += a.z;
-    g.w += a.w;
-    u.x += b.x;
-    u.y += b.y;
-    u.z += b.z;
-    u.w += b.w;
-  }
+  add_slab_partials4(g, gp, stride, 1, slabs);
+  add_slab_partials4(u, gp + I, stride, 1, slabs);
   const float v0 = g.x / (1.0f + expf(-g.x)) * u.x, v1 = g.y / (1.0f + expf(-g.y)) * u.y;
   const float v2 = g.z / (1.0f + expf(-g.z)) * u.z, v3 = g.w / (1.0f + expf(-g.w)) * u.w;
   uint2 o;

@@ -1122,14 +1122,14 @@ __global__ __launch_bounds__(256) void combine16_kernel(const f16* __restrict__ 
         a3 += (float)v[u][3];
       }
   }
-  if (add)
-    for (int s = 0; s < add_slabs; s++) {
-      const float4 v = *reinterpret_cast<const float4*>(add + (size_t)s * add_stride + (size_t)t * H + n);
-      a0 += v.x;
-      a1 += v.y;
-      a2 += v.z;
-      a3 += v.w;
-    }
+  if (add) {
+    float4 acc = make_float4(a0, a1, a2, a3);
+    add_slab_partials4(acc, add + (size_t)t * H + n, add_stride, 0, add_slabs);
+    a0 = acc.x;
+    a1 = acc.y;
+    a2 = acc.z;
+    a3 = acc.w;
+  }
   uint2 o;
   o.x = (uint32_t)f32_to_bf16(a0) | ((uint32_t)f32_to_bf16(a1) << 16);
   o.y = (uint32_t)f32_to_bf16(a2) | ((uint32_t)f32_to_bf16(a3) << 16);
