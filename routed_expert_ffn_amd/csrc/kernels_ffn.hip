@@ -1156,15 +1156,32 @@ __global__ __launch_bounds__(256) void combine_share_kernel(const float* __restr
   const int n = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (n >= H) return;
   float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  for (int j = 0; j < k; j++) {
-    const int e = ids[(size_t)t * k + j];
-    if (e < lo || e >= hi) continue;
-    const float wj = w[(size_t)t * k + j];
-    const float4 v = *reinterpret_cast<const float4*>(rows + (size_t)pair_pos[(size_t)t * k + j] * H + n);
-    a.x = fmaf(wj, v.x, a.x);
-    a.y = fmaf(wj, v.y, a.y);
-    a.z = fmaf(wj, v.z, a.z);
-    a.w = fmaf(wj, v.w, a.w);
+  // 16 records at a time: their ids, weights and positions, then their row
+  // loads, are issued together; the sum stays in ascending j
+  for (int j0 = 0; j0 < k; j0 += COMBINE_JB) {
+    bool in[COMBINE_JB];
+    float wj[COMBINE_JB];
+    int pos[COMBINE_JB];
+#pragma unroll
+    for (int u = 0; u < COMBINE_JB; u++) {
+      const int j = j0 + u;
+      const int e = j < k ? ids[(size_t)t * k + j] : -1;
+      in[u] = e >= lo && e < hi;
+      wj[u] = j < k ? w[(size_t)t * k + j] : 0.0f;
+      pos[u] = j < k ? pair_pos[(size_t)t * k + j] : 0;
+    }
+    float4 v[COMBINE_JB];
+#pragma unroll
+    for (int u = 0; u < COMBINE_JB; u++)
+      v[u] = in[u] ? *reinterpret_cast<const float4*>(rows + (size_t)pos[u] * H + n) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+    for (int u = 0; u < COMBINE_JB; u++)
+      if (in[u]) {
+        a.x = fmaf(wj[u], v[u].x, a.x);
+        a.y = fmaf(wj[u], v[u].y, a.y);
+        a.z = fmaf(wj[u], v[u].z, a.z);
+        a.w = fmaf(wj[u], v[u].w, a.w);
+      }
   }
   *reinterpret_cast<float4*>(y + (size_t)t * H + n) = a;
 }
