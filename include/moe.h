@@ -33,7 +33,14 @@
  *     has finished; the library never allocates, frees or synchronises.
  *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
  *     the null stream).  Calls are asynchronous and may be captured in a
- *     HIP graph.
+ *     HIP graph.  moe_layer_shared runs the shared experts, which do not
+ *     depend on the routing, on a second stream of the library, which waits
+ *     for what was enqueued on `stream` before the call and which `stream`
+ *     waits for before their result is read, so ordering towards the caller
+ *     is as if everything ran on `stream`.  That stream and its two events are
+ *     created once per device, with default priority, by the first such
+ *     call whose stream is not being captured, and live until the process
+ *     ends; a call before that runs everything on `stream`.
  *   - Arguments are validated on the host before anything is enqueued; on a
  *     non-OK return nothing was launched and moe_last_error() says why.  A
  *     launch failure returns MOE_ERR_HIP; outputs are then undefined.

@@ -1,15 +1,91 @@
 // C ABI of libmoe.so (declared and documented in include/moe.h): argument
 // validation, workspace carve-up and the launch sequence on the caller's
-// stream.  Nothing here allocates, frees, synchronises or reads device
+// stream (with one side stream for the shared experts).
+// Nothing here allocates device memory, frees, synchronises or reads device
 // memory, so every entry point can be captured in a HIP graph.
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <vector>
 
 #include "internal.h"
 
 namespace {
+
+// Work that does not depend on the routing (the shared experts) runs on a
+// second stream of the library, forked from the caller's stream after what
+// the caller enqueued before and joined back before its result is read.  At
+// decode sizes it is an HBM-bound GEMV and the routing is latency-bound, so
+// the two overlap; the join comes before the combine, long after the branch
+// has finished, so its latency is off the critical path.  Graph capture
+// records the fork and the join as dependencies.  The stream and its two
+// events are created, per device, by the first such call whose stream is not
+// being captured (creation is not enqueued work); until then, and if creation
+// fails, the branch runs on the caller's stream.  One lock per process is held
+// from fork to join, so calls from several host threads use the events one at
+// a time.
+constexpr int SIDE_MAX_DEVICES = 64;
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+SideStream g_side[SIDE_MAX_DEVICES];
+
+class SideBranch {
+ public:
+  explicit SideBranch(hipStream_t main) : main_(main), lk_(g_side_mu) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= SIDE_MAX_DEVICES) {
+      (void)hipGetLastError();
+      return;
+    }
+    SideStream& d = g_side[dev];
+    if (!d.s && !create(d, main)) return;
+    if (hipEventRecord(d.fork, main) != hipSuccess || hipStreamWaitEvent(d.s, d.fork, 0) != hipSuccess) {
+      (void)hipGetLastError();
+      return;
+    }
+    side_ = &d;
+  }
+  ~SideBranch() { (void)join(); }
+  hipStream_t stream() const { return side_ ? side_->s : main_; }
+  // the caller's stream waits for everything enqueued on the branch
+  hipError_t join() {
+    if (!side_) return hipSuccess;
+    SideStream* d = side_;
+    side_ = nullptr;
+    hipError_t e = hipEventRecord(d->join, d->s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(main_, d->join, 0);
+    return e;
+  }
+
+ private:
+  static bool create(SideStream& d, hipStream_t main) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(main, &st) != hipSuccess || st != hipStreamCaptureStatusNone) {
+      (void)hipGetLastError();
+      return false;
+    }
+    SideStream n;
+    const bool ok = hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking) == hipSuccess &&
+                    hipEventCreateWithFlags(&n.fork, hipEventDisableTiming) == hipSuccess &&
+                    hipEventCreateWithFlags(&n.join, hipEventDisableTiming) == hipSuccess;
+    if (!ok) {
+      (void)hipGetLastError();
+      if (n.join) (void)hipEventDestroy(n.join);
+      if (n.fork) (void)hipEventDestroy(n.fork);
+      if (n.s) (void)hipStreamDestroy(n.s);
+      return false;
+    }
+    d = n;
+    return true;
+  }
+  hipStream_t main_;
+  std::lock_guard<std::mutex> lk_;
+  SideStream* side_ = nullptr;
+};
 
 thread_local char g_err[512] = "";
 
@@ -488,20 +564,24 @@ moe_status moe_layer_shared(moe_dims d, const moe_shared* shared, const void* x,
   float* rows = at<float>(ws, L.rows);
   uint16_t* h = at<uint16_t>(ws, SL.h);
   float* dpart = at<float>(ws, SL.dpart);
+  // the shared experts on every token (hidden layer, then the down partials),
+  // on the side stream beside the routing and the routed experts
+  SideBranch branch(s);
+  const hipStream_t s2 = branch.stream();
+  LAUNCH(MOE_KERNEL_SHARED, s2,
+         moe::launch_shared_hidden(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(shared->w_gate_up),
+                                   at<float>(ws, SL.gupart), T, H, shared->count, shared->I,
+                                   moe::router_plan(T, H, 2 * width), h, s2),
+         "shared experts, gate/up");
+  LAUNCH(MOE_KERNEL_SHARED, s2,
+         moe::launch_router(h, static_cast<const uint16_t*>(shared->w_down), dpart, T, width, H,
+                            moe::router_plan(T, width, H), s2),
+         "shared experts, down");
   TRY(enqueue_route(d, x, w_router, bias, at<float>(ws, L.logits), ids, wts, offsets, sorted, pos, ws,
                     at<f16>(ws, L.x16), s));
   f16* rows16 = at<f16>(ws, L.rows);
   TRY(enqueue_ffn(d, offsets, sorted, w, rows, ws, s, 0, rows16, wts));
-  // the shared experts on every token: hidden layer, then the down partials
-  LAUNCH(MOE_KERNEL_SHARED, s,
-         moe::launch_shared_hidden(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(shared->w_gate_up),
-                                   at<float>(ws, SL.gupart), T, H, shared->count, shared->I,
-                                   moe::router_plan(T, H, 2 * width), h, s),
-         "shared experts, gate/up");
-  LAUNCH(MOE_KERNEL_SHARED, s,
-         moe::launch_router(h, static_cast<const uint16_t*>(shared->w_down), dpart, T, width, H,
-                            moe::router_plan(T, width, H), s),
-         "shared experts, down");
+  if (hipError_t e = branch.join(); e != hipSuccess) return hip_fail(e, "join of the shared experts");
   LAUNCH(MOE_KERNEL_COMBINE, s,
          moe::launch_combine16(rows16, T, H, d.k, static_cast<uint16_t*>(y), s, dpart, SL.d_slabs), "combine");
   return MOE_OK;
@@ -552,7 +632,9 @@ moe_status moe_latent_layer(moe_dims d, const moe_latent* lat, const void* x, co
          moe::launch_router(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router), rpart, T, Hm, E,
                             rp, s),
          "router");
-  // routed-down projection: the latent in bf16 and its fp16 copy for the experts
+  // routed-down projection: the latent in bf16 and its fp16 copy for the
+  // experts.  (Beside the routing on the side stream it was slower: the
+  // experts need it at once, so the join's latency is on the critical path.)
   LAUNCH(MOE_KERNEL_PROJECT, s,
          moe::launch_projection(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(lat->w_down), ppart, T,
                                 Hm, H, moe::router_plan(T, Hm, H), z, x16, s),
