@@ -30,7 +30,8 @@
  * Conventions for every entry point:
  *   - Pointers named d_* or documented as device pointers point to device
  *     memory that the caller owns and keeps alive until the enqueued work
- *     has finished; the library never allocates, frees or synchronises.
+ *     has finished; the library never allocates device memory, frees it
+ *     or synchronises.
  *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
  *     the null stream).  Calls are asynchronous and may be captured in a
  *     HIP graph.  moe_layer_shared runs the shared experts, which do not
