@@ -36,8 +36,12 @@ SideStream g_side[SIDE_MAX_DEVICES];
 class SideBranch {
  public:
   explicit SideBranch(hipStream_t main) : main_(main), lk_(g_side_mu) {
+    // the branch's kernels run on the side stream's device: use it only when
+    // the caller's stream belongs to the current device
     int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= SIDE_MAX_DEVICES) {
+    hipDevice_t sdev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || hipStreamGetDevice(main, &sdev) != hipSuccess || sdev != dev || dev < 0 ||
+        dev >= SIDE_MAX_DEVICES) {
       (void)hipGetLastError();
       return;
     }
