@@ -41,7 +41,8 @@
  *     is as if everything ran on `stream`.  That stream and its two events are
  *     created once per device, with default priority, by the first such
  *     call whose stream is not being captured, and live until the process
- *     ends; a call before that runs everything on `stream`.
+ *     ends; a call before that, or one whose `stream` belongs to another
+ *     device than the current one, runs everything on `stream`.
  *   - Arguments are validated on the host before anything is enqueued; on a
  *     non-OK return nothing was launched and moe_last_error() says why.  A
  *     launch failure returns MOE_ERR_HIP; outputs are then undefined.
