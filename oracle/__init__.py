@@ -53,6 +53,8 @@ def lib():
         L.oracle_moe_layer.restype = ctypes.c_int
         L.oracle_moe_layer.argtypes = [_p, _c_i64, _c_i64, _c_i64, _p, _p, _p, _c_i64, ctypes.c_int, _p,
                                        ctypes.c_int, _p, _p, _p, _p, _p, _p, _p, _p]
+        L.oracle_expert_ffn.restype = ctypes.c_int
+        L.oracle_expert_ffn.argtypes = [_p, _c_i64, _c_i64, _c_i64, ctypes.c_int, _p, _p, _p, ctypes.c_int, _p]
         L.oracle_e8m0_value.restype = ctypes.c_double
         L.oracle_e8m0_value.argtypes = [ctypes.c_uint8]
         L.oracle_mxfp4_quantize.restype = None
@@ -167,13 +169,9 @@ class _Expert(ctypes.Structure):
                 ("format", ctypes.c_int32)]
 
 
-def moe_layer(x_bf16, experts, E, k, wr_bf16=None, bias=None, logits_in=None, nthreads=1, want_rows=False):
-    """experts: mapping expert id -> (gate, up, down) NVFP4 triples; experts
-    that no token selects may be absent.  Returns a dict of numpy arrays."""
-    x = _c(x_bf16, np.uint16)
-    T, H = x.shape
-    any_ex = next(iter(experts.values()))
-    I = any_ex[0].shape[0]
+def _expert_structs(experts, E):
+    """ctypes array of E expert pointers (NULL where absent) and the arrays
+    it points into (kept alive by the caller)."""
     keep = []
     structs = (ctypes.POINTER(_Expert) * E)()
     for e, mats in experts.items():
@@ -188,6 +186,17 @@ def moe_layer(x_bf16, experts, E, k, wr_bf16=None, bias=None, logits_in=None, nt
         s.format = getattr(mats[0], "format", 0)
         keep.append(s)
         structs[e] = ctypes.pointer(s)
+    return structs, keep
+
+
+def moe_layer(x_bf16, experts, E, k, wr_bf16=None, bias=None, logits_in=None, nthreads=1, want_rows=False):
+    """experts: mapping expert id -> (gate, up, down) NVFP4 triples; experts
+    that no token selects may be absent.  Returns a dict of numpy arrays."""
+    x = _c(x_bf16, np.uint16)
+    T, H = x.shape
+    any_ex = next(iter(experts.values()))
+    I = any_ex[0].shape[0]
+    structs, keep = _expert_structs(experts, E)
     wr = None if wr_bf16 is None else _c(wr_bf16, np.uint16)
     b = None if bias is None else _c(bias, np.float32)
     li = None if logits_in is None else _c(logits_in, np.float32)
@@ -204,12 +213,33 @@ def moe_layer(x_bf16, experts, E, k, wr_bf16=None, bias=None, logits_in=None, nt
     rc = lib().oracle_moe_layer(_ptr(x), T, H, I, _ptr(wr), _ptr(b), _ptr(li), E, k,
                                 ctypes.cast(structs, ctypes.c_void_p), nthreads, _ptr(logits), _ptr(ids), _ptr(w),
                                 _ptr(offsets), _ptr(sp), _ptr(pp), _ptr(rows), _ptr(y))
+    del keep
     if rc != 0:
         raise RuntimeError("oracle_moe_layer: a selected expert was not provided")
     out = dict(logits=logits, ids=ids, w=w, offsets=offsets, sorted_pairs=sp, pair_pos=pp, y=y)
     if want_rows:
         out["rows"] = rows
     return out
+
+
+def expert_rows(x_bf16, experts, E, k, offsets, sorted_pairs, nthreads=1):
+    """The expert pass on a given permutation (oracle_permute's, masked
+    records included): rows[p] for p < offsets[E] (fp64, unweighted, sorted
+    order); later rows are NaN.  experts maps the ids 0..E-1 that have
+    records to their NVFP4 / MXFP4 triples."""
+    x = _c(x_bf16, np.uint16)
+    T, H = x.shape
+    offsets = _c(offsets, np.int32)
+    sp = _c(sorted_pairs, np.int32)
+    I = next(iter(experts.values()))[0].shape[0]
+    structs, keep = _expert_structs(experts, E)
+    rows = np.full((max(T * k, 1), H), np.nan, np.float64)
+    rc = lib().oracle_expert_ffn(_ptr(x), H, I, E, k, ctypes.cast(structs, ctypes.c_void_p), _ptr(offsets),
+                                 _ptr(sp), nthreads, _ptr(rows))
+    del keep
+    if rc != 0:
+        raise RuntimeError("oracle_expert_ffn: an expert with records was not provided")
+    return rows
 
 
 # ---- latent routed-expert block (oracle.h: "latent routed-expert block") --------
@@ -260,23 +290,42 @@ def latent_layer(x_bf16, experts, E, k, w_down_bf16, w_up_bf16, wr_bf16=None, bi
 
 # ---- one share of the experts (expert parallelism) ---------------------------------
 
-def layer_share(out, base, count, k):
-    """The part of the layer that the experts [base, base + count) compute,
-    from a moe_layer(..., want_rows=True) result: served[t][j] = whether
-    record (t, j) selected one of them, and y_partial[t] = sum over those j of
-    w[t][j] * rows[pos(t, j)] in fp64 over ascending j.  al-engr.com Kimi-K3
+def layer_partial(out, served):
+    """The part of the layer that one device computes, from a
+    moe_layer(..., want_rows=True) result and the mask served[t][j] of the
+    records it serves: y_partial[t] = sum over the served j of
+    w[t][j] * rows[pos(t, j)], fp64 over ascending j.  al-engr.com Kimi-K3
     plan, "What has to be built - and the discovery that changed it" (a mask
-    on the router's chosen ids, a local expert offset) and "Track A" (a
-    worker returns rows plus the ids it served)."""
-    ids, w, rows, pos = out["ids"], out["w"], out["rows"], out["pair_pos"]
-    T = ids.shape[0]
-    served = (ids >= base) & (ids < base + count)
+    on the router's chosen ids) and "Track A" (a worker returns rows plus the
+    ids it served)."""
+    w, rows, pos = out["w"], out["rows"], out["pair_pos"]
+    T, k = w.shape
     y = np.zeros((T, rows.shape[1]), np.float64)
     for t in range(T):
         for j in range(k):
             if served[t, j]:
                 y[t] += w[t, j] * rows[pos[t * k + j]]
-    return served.astype(np.uint8), y
+    return y
+
+
+def layer_share(out, base, count, k):
+    """layer_partial for the contiguous share of experts [base, base +
+    count): served[t][j] = whether record (t, j) selected one of them (a
+    local expert offset of base)."""
+    ids = out["ids"]
+    served = (ids >= base) & (ids < base + count)
+    return served.astype(np.uint8), layer_partial(out, served)
+
+
+def layer_mapped(out, expert_map):
+    """layer_partial for the experts a device holds, given as the map from
+    global expert id to its slot in the device's store (-1: served
+    elsewhere).  Returns the ids with the map applied (the router's chosen
+    ids, remote ones masked to -1), served and y_partial."""
+    expert_map = np.asarray(expert_map, np.int64)
+    local = expert_map[out["ids"]]
+    served = local >= 0
+    return np.where(served, local, -1).astype(np.int32), served.astype(np.uint8), layer_partial(out, served)
 
 
 # ---- shared experts (every token uses them) ------------------------------------------

@@ -197,14 +197,20 @@ void oracle_permute(const int32_t* ids, int64_t T, int64_t E, int k, int32_t* of
                     int32_t* pair_pos) {
   int64_t P = T * k;
   int32_t* cursor = (int32_t*)calloc((size_t)E + 1, sizeof(int32_t));
-  for (int64_t f = 0; f < P; f++) cursor[ids[f] + 1]++;
+  for (int64_t f = 0; f < P; f++)
+    if (ids[f] >= 0 && ids[f] < E) cursor[ids[f] + 1]++;
   for (int64_t e = 0; e < E; e++) cursor[e + 1] += cursor[e];
   memcpy(offsets, cursor, sizeof(int32_t) * ((size_t)E + 1));
   for (int64_t f = 0; f < P; f++) { /* ascending record = ascending token */
+    if (ids[f] < 0 || ids[f] >= E) { /* masked: served elsewhere */
+      pair_pos[f] = -1;
+      continue;
+    }
     int32_t p = cursor[ids[f]]++;
     sorted_pairs[p] = (int32_t)f;
     pair_pos[f] = p;
   }
+  for (int64_t p = offsets[E]; p < P; p++) sorted_pairs[p] = -1;
   free(cursor);
 }
 
@@ -283,6 +289,26 @@ static void* expert_bucket_worker(void* arg) {
   return NULL;
 }
 
+int oracle_expert_ffn(const uint16_t* x, int64_t H, int64_t I, int64_t E, int k,
+                      const oracle_expert_nvfp4* const* experts, const int32_t* offsets, const int32_t* sorted_pairs,
+                      int nthreads, double* rows) {
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 64) nthreads = 64;
+  pthread_t th[64];
+  layer_job jobs[64];
+  for (int i = 0; i < nthreads; i++) {
+    layer_job jb = {x, H, I, E, k, experts, offsets, sorted_pairs, rows, i, nthreads, 0};
+    jobs[i] = jb;
+  }
+  for (int i = 1; i < nthreads; i++) pthread_create(&th[i], NULL, expert_bucket_worker, &jobs[i]);
+  expert_bucket_worker(&jobs[0]);
+  for (int i = 1; i < nthreads; i++) pthread_join(th[i], NULL);
+  int status = 0;
+  for (int i = 0; i < nthreads; i++)
+    if (jobs[i].status) status = jobs[i].status;
+  return status;
+}
+
 int oracle_moe_layer(const uint16_t* x, int64_t T, int64_t H, int64_t I, const uint16_t* wr, const float* bias,
                      const float* logits_in, int64_t E, int k, const oracle_expert_nvfp4* const* experts,
                      int nthreads, float* logits_out, int32_t* ids, double* w, int32_t* offsets,
@@ -297,20 +323,7 @@ int oracle_moe_layer(const uint16_t* x, int64_t T, int64_t H, int64_t I, const u
   oracle_permute(ids, T, E, k, offsets, sorted_pairs, pair_pos);
 
   double* r = rows ? rows : (double*)malloc(sizeof(double) * (size_t)(P * H));
-  if (nthreads < 1) nthreads = 1;
-  if (nthreads > 64) nthreads = 64;
-  pthread_t th[64];
-  layer_job jobs[64];
-  for (int i = 0; i < nthreads; i++) {
-    layer_job jb = {x, H, I, E, k, experts, offsets, sorted_pairs, r, i, nthreads, 0};
-    jobs[i] = jb;
-  }
-  for (int i = 1; i < nthreads; i++) pthread_create(&th[i], NULL, expert_bucket_worker, &jobs[i]);
-  expert_bucket_worker(&jobs[0]);
-  for (int i = 1; i < nthreads; i++) pthread_join(th[i], NULL);
-  int status = 0;
-  for (int i = 0; i < nthreads; i++)
-    if (jobs[i].status) status = jobs[i].status;
+  int status = oracle_expert_ffn(x, H, I, E, k, experts, offsets, sorted_pairs, nthreads, r);
 
   for (int64_t t = 0; t < T; t++)
     for (int64_t n = 0; n < H; n++) {

@@ -96,13 +96,20 @@ void oracle_router_logits(const uint16_t* x, int64_t T, int64_t H, const uint16_
  * assigns several experts to every token. */
 void oracle_topk_softmax(const float* logits, int64_t T, int64_t E, int k, int32_t* ids, double* w);
 /* Expert-order permutation of the T*k route records f = t*k + j:
- *   offsets[e] = number of records with expert < e (offsets[E] = T*k),
- *   sorted_pairs[p] = the records in (expert, token) order,
- *   pair_pos[f] = position of record f in sorted_pairs.
+ *   offsets[e] = number of served records with expert < e (offsets[E] = the
+ *   served records, T*k when none is masked),
+ *   sorted_pairs[p] = the served records in (expert, token) order, p <
+ *   offsets[E]; the entries from offsets[E] on are -1,
+ *   pair_pos[f] = position of record f in sorted_pairs, -1 if masked.
+ * A record whose id lies outside [0, E) (by convention -1) is masked: it is
+ * served elsewhere and takes no position.
  * [p5] section 4: records are sorted by expert id so one load of an expert's
  * weights serves its whole bucket; section 15: expert e000 processes all of
  * its tokens, then e001, and so on; building counts and the permutation, and
- * restoring token order, are part of the cost. */
+ * restoring token order, are part of the cost.  [p3] "What has to be built -
+ * and the discovery that changed it": splitting the experts across devices
+ * takes a mask on the router's chosen ids, a masked id (-1) being one that
+ * another device serves. */
 void oracle_permute(const int32_t* ids, int64_t T, int64_t E, int k, int32_t* offsets, int32_t* sorted_pairs,
                     int32_t* pair_pos);
 
@@ -124,6 +131,19 @@ typedef struct {
  * the activation the workload configurations name; the pages do not. */
 void oracle_swiglu_token(const double* gate, const double* up, const double* down, const uint16_t* x, int64_t H,
                          int64_t I, double* out);
+
+/* The expert pass of the layer: for each expert e with a non-empty bucket
+ * [offsets[e], offsets[e+1]) (as oracle_permute builds it), dequantise its
+ * three matrices once and run every record of the bucket through them in
+ * sorted order ([p5] sections 4 and 15):
+ *   rows[p] = SwiGLU FFN of expert e on token sorted_pairs[p] / k,
+ * unweighted, fp64, for p < offsets[E]; rows of other positions are not
+ * written.  x [T][H] bf16 bits, rows [*][H].  nthreads > 1 spreads experts
+ * over threads; results are bit-identical for any thread count.  Returns 0,
+ * or -1 if an expert with records is NULL. */
+int oracle_expert_ffn(const uint16_t* x, int64_t H, int64_t I, int64_t E, int k,
+                      const oracle_expert_nvfp4* const* experts, const int32_t* offsets, const int32_t* sorted_pairs,
+                      int nthreads, double* rows);
 
 /* The whole layer.  If logits_in is non-NULL it is used in place of the
  * router (so the selection can be evaluated on another implementation's fp32

@@ -444,6 +444,103 @@ def test_layer_shares_partition_the_layer():
     assert whole[0].all() and np.array_equal(whole[1], out["y"])
 
 
+# ---- masked ids (one device's experts, the rest served elsewhere) -------------------
+
+def test_masked_permutation_matches_stable_argsort():
+    """Records whose id is -1 (or any id outside [0, E)) are masked: they are
+    not counted, take no position (pair_pos -1), and the served records keep
+    the (expert, token) order among themselves."""
+    rng = np.random.default_rng(21)
+    T, E, k = 200, 64, 8
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    masked = rng.random((T, k)) < 0.4
+    ids[masked] = -1
+    ids[3, 2], ids[7, 0] = E, -9  # also outside [0, E)
+    flat = ids.ravel()
+    keep = (flat >= 0) & (flat < E)
+    offsets, sp, pp = oracle.permute(ids, E)
+    n = int(keep.sum())
+    np.testing.assert_array_equal(offsets, np.concatenate([[0], np.cumsum(np.bincount(flat[keep], minlength=E))]))
+    served_records = np.flatnonzero(keep)
+    np.testing.assert_array_equal(sp[:n], served_records[np.argsort(flat[keep], kind="stable")])
+    assert np.all(sp[n:] == -1)
+    assert np.all(pp[~keep] == -1)
+    np.testing.assert_array_equal(pp[sp[:n]], np.arange(n))
+    # nothing masked: the unmasked permutation
+    full = np.where(keep, flat, 0).reshape(T, k)
+    o2, s2, p2 = oracle.permute(full, E)
+    np.testing.assert_array_equal(s2, np.argsort(full.ravel(), kind="stable"))
+    # everything masked: no records
+    o3, s3, p3 = oracle.permute(np.full((T, k), -1, np.int32), E)
+    assert not o3.any() and np.all(s3 == -1) and np.all(p3 == -1)
+
+
+def _random_partition(rng, E, parts):
+    """A random assignment of the E experts to `parts` devices, each device's
+    experts in a random slot order: one global -> local map per device."""
+    owner = rng.integers(0, parts, size=E)
+    maps = []
+    for d in range(parts):
+        mine = np.flatnonzero(owner == d)
+        m = np.full(E, -1, np.int64)
+        m[mine] = rng.permutation(len(mine))
+        maps.append(m)
+    return maps
+
+
+def test_masked_expert_pass_gives_the_layer_rows():
+    """A device's store holds its experts in its own slot order; the router's
+    ids mapped to those slots (-1 for experts held elsewhere) run through the
+    expert pass, and every served record's row equals the whole layer's row
+    for that record, bit for bit."""
+    T, H, I, E, k = 7, 64, 32, 24, 4
+    x = synth.x_bf16(31, T, H)
+    wr = synth.router_bf16(31, H, E, std=0.3)
+    ex = _tiny_experts(31, E, H, I)
+    out = oracle.moe_layer(x, ex, E, k, wr_bf16=wr, want_rows=True)
+    for m in _random_partition(np.random.default_rng(3), E, 3):
+        n_local = int((m >= 0).sum())
+        local_ids, served, _ = oracle.layer_mapped(out, m)
+        store = {int(m[e]): ex[e] for e in range(E) if m[e] >= 0}
+        offsets, sp, pp = oracle.permute(local_ids, n_local)
+        rows = oracle.expert_rows(x, store, n_local, k, offsets, sp)
+        for f in range(T * k):
+            if served.ravel()[f]:
+                np.testing.assert_array_equal(rows[pp[f]], out["rows"][out["pair_pos"][f]])
+            else:
+                assert pp[f] == -1
+        assert np.all(np.isnan(rows[offsets[-1]:]))
+
+
+def test_mapped_partials_partition_the_layer():
+    """Devices whose experts partition the E experts: served masks are
+    disjoint and cover every record, and the partial outputs add up to the
+    layer's output.  Each partial is also checked against a numpy brute
+    force over the served records (independent dequantiser)."""
+    T, H, I, E, k = 6, 64, 32, 20, 5
+    x = synth.x_bf16(33, T, H)
+    wr = synth.router_bf16(33, H, E, std=0.3)
+    ex = _tiny_experts(33, E, H, I)
+    out = oracle.moe_layer(x, ex, E, k, wr_bf16=wr, want_rows=True)
+    xd = synth.bf16_to_f32(x).astype(np.float64)
+    deq = {e: [_dequant_independent(mm)[0] for mm in mats] for e, mats in ex.items()}
+    maps = _random_partition(np.random.default_rng(8), E, 4)
+    parts = [oracle.layer_mapped(out, m) for m in maps]
+    np.testing.assert_array_equal(sum(p[1].astype(int) for p in parts), np.ones((T, k), int))
+    np.testing.assert_allclose(sum(p[2] for p in parts), out["y"], rtol=1e-13, atol=1e-15)
+    for m, (local_ids, served, yp) in zip(maps, parts):
+        np.testing.assert_array_equal(local_ids, np.where(m[out["ids"]] >= 0, m[out["ids"]], -1))
+        ref = np.zeros_like(yp)
+        for t in range(T):
+            for j in range(k):
+                e = out["ids"][t, j]
+                if m[e] >= 0:
+                    g, u, d = deq[e]
+                    a, b = xd[t] @ g.T, xd[t] @ u.T
+                    ref[t] += out["w"][t, j] * ((a / (1 + np.exp(-a)) * b) @ d.T)
+        np.testing.assert_allclose(yp, ref, rtol=1e-11, atol=1e-13)
+
+
 # ---- shared experts -------------------------------------------------------------------
 
 def _shared_weights(seed, H, I, count):
