@@ -50,7 +50,9 @@
  *   - Same inputs on the same GPU give bit-identical outputs: there are no
  *     floating-point atomics.
  *   - Shape limits: 1 <= k <= 64, k <= E <= 1024 with E a multiple of 8,
- *     H and I multiples of 256, 0 <= T and T*k < 2^31.  T = 0 is a no-op
+ *     H and I multiples of 256, 0 <= T and T*k < 2^31.  moe_permute,
+ *     moe_expert_ffn and moe_workspace_bytes, which take expert ids rather
+ *     than route, accept any 1 <= E <= 1024 (e.g. one device's experts).  T = 0 is a no-op
  *     returning MOE_OK once the dimensions are valid (pointers are then not
  *     examined).
  *   - Pointers must be 16-byte aligned, except the per-tensor scales gs
@@ -171,9 +173,34 @@ moe_status moe_route(moe_dims d, const void* x, const void* w_router, const floa
                      int32_t* topk_ids, float* topk_w, int32_t* expert_offsets, int32_t* sorted_pairs,
                      int32_t* pair_pos, void* ws, size_t ws_bytes, void* stream);
 
+/* Build the expert-order permutation from ids the caller holds (device
+ * pointers): topk_ids [T][k] int32, each an expert id in [0, E) or masked.
+ * al-engr.com Kimi-K3 plan, section "What has to be built - and the
+ * discovery that changed it": splitting one model's experts across devices
+ * takes a mask on the router's chosen ids, an id of -1 standing for an
+ * expert that another device serves.  A record whose id lies outside
+ * [0, E) (by convention -1) is masked: it is not counted and takes no
+ * position.  Outputs:
+ *   expert_offsets [E+1]: exclusive prefix sum of the per-expert counts of
+ *                  the served records (expert_offsets[E] = the number of
+ *                  served records, T*k when none is masked);
+ *   sorted_pairs   [T*k]: the served records f = t*k + j in (expert, token)
+ *                  order, positions 0 .. expert_offsets[E]-1; the entries
+ *                  from expert_offsets[E] on are left as they were;
+ *   pair_pos       [T*k]: position of record f in sorted_pairs, -1 if masked.
+ * The result is an exact function of the ids (moe_route builds the same
+ * permutation from its own ids, none masked).  moe_expert_ffn takes it as it
+ * is and computes only the served records.  Workspace as moe_route (dims d,
+ * E being the size of the id space, e.g. a device's own experts). */
+moe_status moe_permute(moe_dims d, const int32_t* topk_ids, int32_t* expert_offsets, int32_t* sorted_pairs,
+                       int32_t* pair_pos, void* ws, size_t ws_bytes, void* stream);
+
 /* Run every selected expert on its bucket (device pointers):
  *   x              [T][H] bf16 activations;
- *   expert_offsets [E+1], sorted_pairs [T*k]: as produced by moe_route;
+ *   expert_offsets [E+1], sorted_pairs [T*k]: as produced by moe_route or
+ *                  moe_permute; only the records at positions
+ *                  0 .. expert_offsets[E]-1 are computed (masked records
+ *                  have none);
  *   w              NVFP4 experts (the struct itself is host memory, read
  *                  during the call only);
  *   rows           [T*k][H] fp32 output: rows[p] = SwiGLU FFN of expert e
@@ -258,6 +285,34 @@ moe_status moe_expert_ffn_share(moe_dims d, moe_expert_share share, const void* 
 moe_status moe_layer_share(moe_dims d, moe_expert_share share, const void* x, const void* w_router, const float* bias,
                            const moe_experts* w, float* y_partial, uint8_t* served, int32_t* topk_ids_out,
                            float* topk_w_out, void* ws, size_t ws_bytes, void* stream);
+
+/* moe_layer for the experts one device holds, in any placement: routing
+ * over all E experts, then the mask on the chosen ids (al-engr.com plan,
+ * section "What has to be built - and the discovery that changed it": the
+ * split hook maps the router's global ids to this device's rows and masks
+ * the rest to -1), the device's experts on their records, and its partial
+ * output (device pointers):
+ *   expert_map    [E] int32: slot in w of global expert e (0 .. n_local-1),
+ *                 or -1 when another device serves e (an entry outside
+ *                 [0, n_local) counts as -1); distinct experts should have
+ *                 distinct slots;
+ *   w             the n_local experts of this device, in slot order;
+ *   y_partial     [T][H] fp32: sum, over ascending j with expert_map of
+ *                 topk_ids[t][j] a slot, of topk_w[t][j] *
+ *                 FFN_{topk_ids[t][j]}(x[t]), in fp32;
+ *   served        [T][k] uint8 or NULL: 1 where this device computed record
+ *                 (t, j), else 0;
+ *   local_ids_out [T][k] int32 or NULL: the chosen ids as slots, -1 masked
+ *                 ("Track A": a worker returns rows plus the ids it served).
+ * Devices whose maps partition the experts produce partials that add up to
+ * moe_layer's sum; rounding the total to bf16 is left to the caller.
+ * moe_layer_share is the special case of a contiguous range.  Workspace as
+ * moe_layer (dims d with the global E).  Errors as moe_layer, plus
+ * MOE_ERR_SHAPE for n_local outside [1, E] and MOE_ERR_ARG for a NULL map. */
+moe_status moe_layer_mapped(moe_dims d, const int32_t* expert_map, int32_t n_local, const void* x,
+                            const void* w_router, const float* bias, const moe_experts* w, float* y_partial,
+                            uint8_t* served, int32_t* topk_ids_out, float* topk_w_out, int32_t* local_ids_out,
+                            void* ws, size_t ws_bytes, void* stream);
 
 /* ---- the latent routed-expert block (K3's LatentMoE) -------------------------
  * lightseek.org, "Kimi K3 optimization on GB300" (part I), sections

@@ -22,7 +22,7 @@ EXPORTS = ("moe_workspace_bytes", "moe_quantize_workspace_bytes", "moe_quantize_
            "moe_expert_ffn", "moe_layer", "moe_status_string", "moe_last_error", "moe_profile_arm",
            "moe_profile_read", "moe_stream_read", "moe_latent_workspace_bytes", "moe_latent_layer",
            "moe_expert_ffn_share", "moe_layer_share", "moe_layer_shared_workspace_bytes", "moe_layer_shared",
-           "moe_quantize_mxfp4")
+           "moe_quantize_mxfp4", "moe_permute", "moe_layer_mapped")
 FORMATS = {"nvfp4": 0, "mxfp4": 1}  # moe_weight_format
 # MOE_STREAM_SINK_WORDS of moe.h
 STREAM_SINK_WORDS = 4096
@@ -91,6 +91,11 @@ def lib():
         L.moe_layer_share.restype = ctypes.c_int
         L.moe_layer_share.argtypes = [Dims, Share, _p, _p, _p, ctypes.POINTER(Experts), _p, _p, _p, _p, _p,
                                       ctypes.c_size_t, _p]
+        L.moe_permute.restype = ctypes.c_int
+        L.moe_permute.argtypes = [Dims, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]
+        L.moe_layer_mapped.restype = ctypes.c_int
+        L.moe_layer_mapped.argtypes = [Dims, _p, ctypes.c_int32, _p, _p, _p, ctypes.POINTER(Experts), _p, _p, _p, _p,
+                                       _p, _p, ctypes.c_size_t, _p]
         L.moe_layer_shared_workspace_bytes.restype = ctypes.c_size_t
         L.moe_layer_shared_workspace_bytes.argtypes = [Dims, ctypes.POINTER(Shared)]
         L.moe_layer_shared.restype = ctypes.c_int
@@ -199,6 +204,23 @@ def moe_layer_share(d, base, count, x, w_router, bias, experts, y_partial, serve
     _check(lib().moe_layer_share(d, Share(int(base), int(count)), _ptr(x), _ptr(w_router), _ptr(bias),
                                  ctypes.byref(experts.c()), _ptr(y_partial), _ptr(served), _ptr(topk_ids_out),
                                  _ptr(topk_w_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_permute(d, topk_ids, expert_offsets, sorted_pairs, pair_pos, ws, stream=None):
+    """Expert-order permutation of caller ids, -1 (any id outside [0, E))
+    masked (moe.h: moe_permute)."""
+    _check(lib().moe_permute(d, _ptr(topk_ids), _ptr(expert_offsets), _ptr(sorted_pairs), _ptr(pair_pos), _ptr(ws),
+                             ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_layer_mapped(d, expert_map, n_local, x, w_router, bias, experts, y_partial, served, topk_ids_out, topk_w_out,
+                     local_ids_out, ws, stream=None):
+    """The layer's part for the experts one device holds, placed by a global
+    -> local map (-1: served elsewhere) (moe.h: moe_layer_mapped)."""
+    _check(lib().moe_layer_mapped(d, _ptr(expert_map), int(n_local), _ptr(x), _ptr(w_router), _ptr(bias),
+                                  ctypes.byref(experts.c()), _ptr(y_partial), _ptr(served), _ptr(topk_ids_out),
+                                  _ptr(topk_w_out), _ptr(local_ids_out), _ptr(ws), ws.numel() * ws.element_size(),
+                                  _stream(stream)))
 
 
 def moe_layer_shared_workspace_bytes(d, count, I):

@@ -120,13 +120,17 @@ struct Prof {
 };
 thread_local Prof g_prof;
 
-moe_status check_dims(const moe_dims& d) {
+// Routing (the router, top-k) needs E a multiple of 8 with at least k
+// experts; the permutation of given ids and the expert pass take any id
+// space of 1 .. 1024 experts (router = false), e.g. one device's experts.
+moe_status check_dims(const moe_dims& d, bool router = true) {
   if (d.T < 0) return fail(MOE_ERR_SHAPE, "T = %d is negative", d.T);
   if (d.H <= 0 || d.H % 256) return fail(MOE_ERR_SHAPE, "H = %d must be a positive multiple of 256", d.H);
   if (d.I <= 0 || d.I % 256) return fail(MOE_ERR_SHAPE, "I = %d must be a positive multiple of 256", d.I);
   if (d.k < 1 || d.k > 64) return fail(MOE_ERR_SHAPE, "k = %d must be in [1, 64]", d.k);
-  if (d.E < d.k || d.E > 1024 || d.E % 8)
+  if (router && (d.E < d.k || d.E > 1024 || d.E % 8))
     return fail(MOE_ERR_SHAPE, "E = %d must be a multiple of 8 in [k, 1024]", d.E);
+  if (!router && (d.E < 1 || d.E > 1024)) return fail(MOE_ERR_SHAPE, "E = %d must be in [1, 1024]", d.E);
   if ((long long)d.T * d.k >= (1LL << 31)) return fail(MOE_ERR_SHAPE, "T*k = %lld is too large", (long long)d.T * d.k);
   return MOE_OK;
 }
@@ -136,8 +140,8 @@ size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 // Workspace regions (byte offsets, 256-byte aligned).  moe_layer uses all of
 // them; moe_route and moe_expert_ffn use subsets of the same layout.
 struct Layout {
-  size_t part, logits, ids, w, masks, counts, base, offsets, sorted, pos, active, nact, mtiles, nmt, x16, h, rows,
-      total;
+  size_t part, logits, ids, w, lids, masks, counts, base, offsets, sorted, pos, active, nact, mtiles, nmt, x16, h,
+      rows, total;
 };
 
 Layout layout(const moe_dims& d) {
@@ -154,6 +158,7 @@ Layout layout(const moe_dims& d) {
   L.logits = take(T * E * 4);
   L.ids = take(P * 4);
   L.w = take(P * 4);
+  L.lids = take(P * 4);
   L.masks = take(nb * E * 8);
   L.counts = take(nb * E * 4);
   L.base = take(nb * E * 4);
@@ -354,7 +359,7 @@ moe_status enqueue_ffn(const moe_dims& d, const int32_t* offsets, const int32_t*
 moe_status expert_ffn_range(moe_dims d, int lo, int hi, const void* x, const int32_t* expert_offsets,
                             const int32_t* sorted_pairs, const moe_experts* w, float* rows, void* ws, size_t ws_bytes,
                             void* stream) {
-  TRY(check_dims(d));
+  TRY(check_dims(d, false));
   if (d.T == 0) return MOE_OK;
   TRY(check_ptr(x, "x"));
   TRY(check_ptr(expert_offsets, "expert_offsets"));
@@ -398,7 +403,7 @@ void moe::prof_after(moe_kernel k, hipStream_t s) {
 extern "C" {
 
 size_t moe_workspace_bytes(moe_dims d) {
-  if (check_dims(d) != MOE_OK) return 0;
+  if (check_dims(d, false) != MOE_OK) return 0;
   return layout(d).total;
 }
 
@@ -500,6 +505,83 @@ moe_status moe_layer_share(moe_dims d, moe_expert_share share, const void* x, co
   TRY(enqueue_ffn(d, offsets, sorted, w, rows, ws, s, lo));
   LAUNCH(MOE_KERNEL_COMBINE, s,
          moe::launch_combine_share(rows, pos, wts, ids, lo, hi, d.T, d.H, d.k, y_partial, served, s), "combine");
+  return MOE_OK;
+}
+
+moe_status moe_permute(moe_dims d, const int32_t* topk_ids, int32_t* expert_offsets, int32_t* sorted_pairs,
+                       int32_t* pair_pos, void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_dims(d, false));
+  if (d.T == 0) return MOE_OK;
+  TRY(check_ptr(topk_ids, "topk_ids"));
+  TRY(check_ptr(expert_offsets, "expert_offsets"));
+  TRY(check_ptr(sorted_pairs, "sorted_pairs"));
+  TRY(check_ptr(pair_pos, "pair_pos"));
+  TRY(check_ws(d, ws, ws_bytes));
+  const Layout L = layout(d);
+  hipStream_t s = (hipStream_t)stream;
+  LAUNCH(MOE_KERNEL_PERMUTE, s,
+         moe::launch_permute(topk_ids, d.T, d.E, d.k, at<uint64_t>(ws, L.masks), at<int32_t>(ws, L.counts),
+                             at<int32_t>(ws, L.base), expert_offsets, sorted_pairs, pair_pos, at<int32_t>(ws, L.active),
+                             at<int32_t>(ws, L.nact), at<int32_t>(ws, L.mtiles), at<int32_t>(ws, L.nmt), s),
+         "permute");
+  return MOE_OK;
+}
+
+moe_status moe_layer_mapped(moe_dims d, const int32_t* expert_map, int32_t n_local, const void* x,
+                            const void* w_router, const float* bias, const moe_experts* w, float* y_partial,
+                            uint8_t* served, int32_t* topk_ids_out, float* topk_w_out, int32_t* local_ids_out,
+                            void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_dims(d));
+  if (n_local < 1 || n_local > d.E) return fail(MOE_ERR_SHAPE, "n_local = %d must be in [1, E = %d]", n_local, d.E);
+  if (d.T == 0) return MOE_OK;
+  TRY(check_ptr(expert_map, "expert_map"));
+  TRY(check_ptr(x, "x"));
+  TRY(check_ptr(w_router, "w_router"));
+  TRY(check_ptr(bias, "bias", false));
+  TRY(check_experts(w));
+  TRY(check_ptr(y_partial, "y_partial"));
+  TRY(check_ptr(topk_ids_out, "topk_ids_out", false));
+  TRY(check_ptr(topk_w_out, "topk_w_out", false));
+  TRY(check_ptr(local_ids_out, "local_ids_out", false));
+  TRY(check_ws(d, ws, ws_bytes));
+  const Layout L = layout(d);
+  hipStream_t s = (hipStream_t)stream;
+  const int T = d.T, E = d.E, k = d.k;
+  int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, L.ids);
+  float* wts = topk_w_out ? topk_w_out : at<float>(ws, L.w);
+  int32_t* lids = local_ids_out ? local_ids_out : at<int32_t>(ws, L.lids);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* sorted = at<int32_t>(ws, L.sorted);
+  int32_t* pos = at<int32_t>(ws, L.pos);
+  float* rows = at<float>(ws, L.rows);
+  // routing over all E experts (the router also writes the fp16 copy of x);
+  // the single-launch routing of small batches also permutes over all E,
+  // which the local permutation below replaces
+  const moe::RouterPlan rp = moe::router_plan(T, d.H, E);
+  LAUNCH(MOE_KERNEL_ROUTER, s,
+         moe::launch_router(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router),
+                            at<float>(ws, L.part), T, d.H, E, rp, s, at<f16>(ws, L.x16)),
+         "router");
+  if (moe::route_fused(T))
+    LAUNCH(MOE_KERNEL_TOPK, s,
+           moe::launch_route_small(at<float>(ws, L.part), rp.slabs, bias, at<float>(ws, L.logits), T, E, k, ids, wts,
+                                   offsets, sorted, pos, at<int32_t>(ws, L.active), at<int32_t>(ws, L.nact), s),
+           "route");
+  else
+    LAUNCH(MOE_KERNEL_TOPK, s,
+           moe::launch_topk(at<float>(ws, L.part), rp.slabs, bias, at<float>(ws, L.logits), T, E, k, ids, wts, s),
+           "top-k");
+  // the mask on the chosen ids: global ids to slots of this store, -1 elsewhere
+  LAUNCH(MOE_KERNEL_PERMUTE, s, moe::launch_remap_ids(ids, expert_map, E, n_local, (long long)T * k, lids, s),
+         "remap");
+  LAUNCH(MOE_KERNEL_PERMUTE, s,
+         moe::launch_permute(lids, T, n_local, k, at<uint64_t>(ws, L.masks), at<int32_t>(ws, L.counts),
+                             at<int32_t>(ws, L.base), offsets, sorted, pos, at<int32_t>(ws, L.active),
+                             at<int32_t>(ws, L.nact), at<int32_t>(ws, L.mtiles), at<int32_t>(ws, L.nmt), s),
+         "permute");
+  TRY(enqueue_ffn(d, offsets, sorted, w, rows, ws, s, 0));
+  LAUNCH(MOE_KERNEL_COMBINE, s,
+         moe::launch_combine_share(rows, pos, wts, lids, 0, n_local, T, d.H, k, y_partial, served, s), "combine");
   return MOE_OK;
 }
 

@@ -44,6 +44,8 @@ bool route_fused(int T);
 hipError_t launch_route_small(const float* part, int slabs, const float* bias, float* logits, int T, int E, int k,
                               int32_t* ids, float* w, int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_pos,
                               int32_t* active, int32_t* n_active, hipStream_t s);
+// Ids outside [0, E) (by convention -1) are masked: not counted, no
+// position (pair_pos -1), offsets[E] = the served records.
 hipError_t launch_permute(const int32_t* ids, int T, int E, int k, uint64_t* masks, int32_t* counts, int32_t* base,
                           int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_pos, int32_t* active,
                           int32_t* n_active, int32_t* mtiles, int32_t* n_mtiles, hipStream_t s);
@@ -57,6 +59,10 @@ constexpr int MTILE = 224;
 // Upper bound on the (expert, token tile) entries of T tokens.
 inline int max_mtiles(const moe_dims& d) { return max_active(d) + (int)(((long long)d.T * d.k) / MTILE) + 1; }
 hipError_t launch_cast(const uint16_t* x, f16* x16, long long n, hipStream_t s);
+// local[f] = map[ids[f]] for the n records (-1 where the expert is served
+// elsewhere, or the map entry is outside [0, n_local)).
+hipError_t launch_remap_ids(const int32_t* ids, const int32_t* map, int E, int n_local, long long n, int32_t* local,
+                            hipStream_t s);
 
 struct FfnArgs {
   int T, H, I, E, k;

@@ -659,6 +659,11 @@ __device__ __forceinline__ void cast_rows(const uint16_t* __restrict__ x, f16* _
   }
 }
 
+// A record is served here when its expert id lies in [0, E); any other id
+// (by convention -1: an expert another device serves) is masked, takes no
+// position and is not counted.
+__device__ __forceinline__ bool served_id(int e, int E) { return (unsigned)e < (unsigned)E; }
+
 // The permutation of up to 64 tokens in one block of 1024 threads (thread e
 // = expert e for the counts): m and off_s are LDS arrays of E entries, m
 // zeroed by the caller before a barrier.  Also writes the active-expert list.
@@ -667,7 +672,10 @@ __device__ __forceinline__ void permute_block(const int32_t* ids, int T, int E, 
                               int32_t* __restrict__ active, int32_t* __restrict__ n_active, unsigned long long* m,
                               int* off_s, int* lds) {
   const int tid = threadIdx.x;
-  for (int f = tid; f < T * k; f += 1024) atomicOr(&m[ids[f]], 1ull << (f / k));
+  for (int f = tid; f < T * k; f += 1024) {
+    const int e = ids[f];
+    if (served_id(e, E)) atomicOr(&m[e], 1ull << (f / k));
+  }
   __syncthreads();
   const int cnt = tid < E ? __popcll(m[tid]) : 0;
   // offsets (< T k <= 4096) and active slots (< E <= 1024) in one scan
@@ -680,12 +688,16 @@ __device__ __forceinline__ void permute_block(const int32_t* ids, int T, int E, 
     if (cnt > 0) active[slot] = tid;
   }
   if (tid == 0) {
-    offsets[E] = T * k;
+    offsets[E] = packed_total & 0xFFFF;  // the served records (T k when none is masked)
     *n_active = nact;
   }
   __syncthreads();
   for (int f = tid; f < T * k; f += 1024) {
     const int t = f / k, e = ids[f];
+    if (!served_id(e, E)) {
+      pair_pos[f] = -1;
+      continue;
+    }
     const int pos = off_s[e] + __popcll(m[e] & ((1ull << t) - 1ull));
     sorted_pairs[pos] = f;
     pair_pos[f] = pos;
@@ -748,7 +760,10 @@ __global__ __launch_bounds__(WAVE) void perm_count_kernel(const int32_t* __restr
   __syncthreads();
   const int t = b * WAVE + lane;
   if (t < T)
-    for (int j = 0; j < k; j++) atomicOr(&m[ids[(size_t)t * k + j]], 1ull << lane);
+    for (int j = 0; j < k; j++) {
+      const int e = ids[(size_t)t * k + j];
+      if (served_id(e, E)) atomicOr(&m[e], 1ull << lane);
+    }
   __syncthreads();
   for (int e = lane; e < E; e += WAVE) {
     masks[(size_t)b * E + e] = m[e];
@@ -799,7 +814,7 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* __restri
     if (flag) active[slot] = e;
   }
   if (e == 0) {
-    offsets[E] = P;
+    offsets[E] = total;  // the served records (P when none is masked)
     *n_active = nact;
   }
   write_mtiles(e, e < E ? running : 0, lds, mtiles, n_mtiles);
@@ -817,8 +832,13 @@ __global__ __launch_bounds__(WAVE) void perm_scatter_kernel(const int32_t* __res
   const uint64_t below = (1ull << lane) - 1ull;
   for (int j0 = 0; j0 < k; j0 += 16) {  // 16 records' loads in flight
     int e[16];
+    bool in[16];
 #pragma unroll
-    for (int u = 0; u < 16; u++) e[u] = j0 + u < k ? ids[(size_t)t * k + j0 + u] : 0;
+    for (int u = 0; u < 16; u++) {
+      e[u] = j0 + u < k ? ids[(size_t)t * k + j0 + u] : 0;
+      in[u] = served_id(e[u], E);
+      if (!in[u]) e[u] = 0;  // (masked: no lookups of its own)
+    }
     int pos[16];
 #pragma unroll
     for (int u = 0; u < 16; u++)
@@ -827,8 +847,8 @@ __global__ __launch_bounds__(WAVE) void perm_scatter_kernel(const int32_t* __res
     for (int u = 0; u < 16; u++)
       if (j0 + u < k) {
         const int f = t * k + j0 + u;
-        sorted_pairs[pos[u]] = f;
-        pair_pos[f] = pos[u];
+        if (in[u]) sorted_pairs[pos[u]] = f;
+        pair_pos[f] = in[u] ? pos[u] : -1;
       }
   }
 }
@@ -857,6 +877,19 @@ __global__ __launch_bounds__(256) void cast_kernel(const uint16_t* __restrict__ 
   const size_t per = 256 * 8;
   const size_t first = (size_t)blockIdx.x * per;
   if (first < (size_t)n8) cast_rows(x, x16, first, min((size_t)n8 - first, per), threadIdx.x, 256);
+}
+
+// local[f] = map[ids[f]]: the router's global expert ids as slots of this
+// device's store, -1 where the map says the expert is served elsewhere (a
+// map entry outside [0, n_local) counts as -1).
+__global__ __launch_bounds__(256) void remap_ids_kernel(const int32_t* __restrict__ ids,
+                                                       const int32_t* __restrict__ map, int E, int n_local,
+                                                       long long n, int32_t* __restrict__ local) {
+  const long long f = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (f >= n) return;
+  const int e = ids[f];
+  const int l = served_id(e, E) ? map[e] : -1;
+  local[f] = served_id(l, n_local) ? l : -1;
 }
 
 int router_tt(int T) { return T <= 1 ? 1 : (T <= 2 ? 2 : (T <= 4 ? 4 : 8)); }
@@ -962,6 +995,14 @@ hipError_t launch_active_list(const int32_t* offsets, int E, int lo, int hi, int
                               int32_t* mtiles, int32_t* n_mtiles, hipStream_t s) {
   hipLaunchKernelGGL(active_list_kernel, dim3(1), dim3(1024), 0, s, offsets, E, lo, hi, active, n_active, mtiles,
                      n_mtiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_remap_ids(const int32_t* ids, const int32_t* map, int E, int n_local, long long n, int32_t* local,
+                            hipStream_t s) {
+  const long long g = (n + 255) / 256;
+  hipLaunchKernelGGL(remap_ids_kernel, dim3((unsigned)(g > 0 ? g : 1)), dim3(256), 0, s, ids, map, E, n_local, n,
+                     local);
   return hipGetLastError();
 }
 

@@ -183,3 +183,22 @@ def test_mxfp4_quantize_and_format_validation_without_hip():
     ex = moe.Experts(nv, nv, nv, 5)
     rows_ws = moe.moe_workspace_bytes(d)
     assert L.moe_expert_ffn(d, FAKE, FAKE, FAKE, ctypes.byref(ex), FAKE, FAKE, rows_ws, None) == 1
+
+
+def test_permute_and_mapped_validation_without_hip():
+    """moe_permute and moe_layer_mapped refuse bad arguments before any
+    launch; T = 0 is a no-op."""
+    L = moe.lib()
+    d = moe.dims(8, 512, 256, 64, 8)
+    ws_bytes = moe.moe_workspace_bytes(d)
+    assert L.moe_permute(d, None, FAKE, FAKE, FAKE, FAKE, ws_bytes, None) == 1
+    assert L.moe_permute(d, FAKE + 4, FAKE, FAKE, FAKE, FAKE, ws_bytes, None) == 3
+    assert L.moe_permute(d, FAKE, FAKE, FAKE, FAKE, FAKE, ws_bytes - 256, None) == 4
+    assert L.moe_permute(moe.dims(8, 512, 256, 64, 0), FAKE, FAKE, FAKE, FAKE, FAKE, ws_bytes, None) == 2
+    assert L.moe_permute(moe.dims(0, 512, 256, 64, 8), None, None, None, None, None, 0, None) == 0
+    ex = moe.Experts()
+    for n_local in (0, -1, 65):
+        assert L.moe_layer_mapped(d, FAKE, n_local, FAKE, FAKE, None, ctypes.byref(ex), FAKE, None, None, None, None,
+                                  FAKE, ws_bytes, None) == 2
+    assert L.moe_layer_mapped(d, None, 4, FAKE, FAKE, None, ctypes.byref(ex), FAKE, None, None, None, None, FAKE,
+                              ws_bytes, None) == 1
