@@ -220,6 +220,30 @@ moe_status moe_expert_ffn(moe_dims d, const void* x, const int32_t* expert_offse
 moe_status moe_layer(moe_dims d, const void* x, const void* w_router, const float* bias, const moe_experts* w,
                      void* y, int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes, void* stream);
 
+/* ---- the layer without a caller workspace -----------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): moe_layer
+ * with its workspace taken from a scratch array of MOE_NOALLOC_SCRATCH_BYTES
+ * that the library holds in device memory, one per device, until the process
+ * ends.  The call allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine); the caller still passes the inputs and outputs, as for
+ * moe_layer, and gets the same results.
+ *   - Limit: the layer's workspace without the fp32 rows of moe_expert_ffn
+ *     (about half of moe_workspace_bytes) must fit the scratch; at H = 7168,
+ *     I = 2048, E = 896, k = 16 that holds up to T = 156 tokens.  Larger
+ *     calls return MOE_ERR_WORKSPACE before anything is enqueued.
+ *   - The first call on a device looks up that device's scratch address
+ *     (with the device current; `stream` must belong to the current device,
+ *     else MOE_ERR_ARG); make that first call outside graph capture.
+ *   - Every call on one GPU shares that GPU's scratch, which keeps the last
+ *     call's contents (nothing in it needs to start at zero): calls that
+ *     overlap on one GPU (on different streams, or from several host threads
+ *     without ordering) race and give undefined results.
+ * Errors as moe_layer. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_layer_noalloc(moe_dims d, const void* x, const void* w_router, const float* bias, const moe_experts* w,
+                             void* y, int32_t* topk_ids_out, float* topk_w_out, void* stream);
+
 /* ---- shared experts ------------------------------------------------------------
  * wpnews.pro, "Serving Kimi K3 End to End", section 3.3: every token also
  * uses the model's 2 shared experts, whose output joins the MoE layer's sum;

@@ -22,10 +22,13 @@ EXPORTS = ("moe_workspace_bytes", "moe_quantize_workspace_bytes", "moe_quantize_
            "moe_expert_ffn", "moe_layer", "moe_status_string", "moe_last_error", "moe_profile_arm",
            "moe_profile_read", "moe_stream_read", "moe_latent_workspace_bytes", "moe_latent_layer",
            "moe_expert_ffn_share", "moe_layer_share", "moe_layer_shared_workspace_bytes", "moe_layer_shared",
-           "moe_quantize_mxfp4", "moe_permute", "moe_layer_mapped")
+           "moe_quantize_mxfp4", "moe_permute", "moe_layer_mapped",
+           "moe_layer_noalloc")
 FORMATS = {"nvfp4": 0, "mxfp4": 1}  # moe_weight_format
 # MOE_STREAM_SINK_WORDS of moe.h
 STREAM_SINK_WORDS = 4096
+# MOE_NOALLOC_SCRATCH_BYTES of moe.h
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class MoeError(RuntimeError):
@@ -91,6 +94,8 @@ def lib():
         L.moe_layer_share.restype = ctypes.c_int
         L.moe_layer_share.argtypes = [Dims, Share, _p, _p, _p, ctypes.POINTER(Experts), _p, _p, _p, _p, _p,
                                       ctypes.c_size_t, _p]
+        L.moe_layer_noalloc.restype = ctypes.c_int
+        L.moe_layer_noalloc.argtypes = [Dims, _p, _p, _p, ctypes.POINTER(Experts), _p, _p, _p, _p]
         L.moe_permute.restype = ctypes.c_int
         L.moe_permute.argtypes = [Dims, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]
         L.moe_layer_mapped.restype = ctypes.c_int
@@ -187,6 +192,13 @@ def moe_layer(d, x, w_router, bias, experts, y, topk_ids_out, topk_w_out, ws, st
     _check(lib().moe_layer(d, _ptr(x), _ptr(w_router), _ptr(bias), ctypes.byref(experts.c()), _ptr(y),
                            _ptr(topk_ids_out), _ptr(topk_w_out), _ptr(ws), ws.numel() * ws.element_size(),
                            _stream(stream)))
+
+
+def moe_layer_noalloc(d, x, w_router, bias, experts, y, topk_ids_out, topk_w_out, stream=None):
+    """moe_layer with the library's own scratch as workspace; allocates
+    nothing (moe.h: moe_layer_noalloc)."""
+    _check(lib().moe_layer_noalloc(d, _ptr(x), _ptr(w_router), _ptr(bias), ctypes.byref(experts.c()), _ptr(y),
+                                   _ptr(topk_ids_out), _ptr(topk_w_out), _stream(stream)))
 
 
 def moe_expert_ffn_share(d, base, count, x, expert_offsets, sorted_pairs, experts, rows, ws, stream=None):

@@ -585,10 +585,12 @@ moe_status moe_layer_mapped(moe_dims d, const int32_t* expert_map, int32_t n_loc
   return MOE_OK;
 }
 
-moe_status moe_layer(moe_dims d, const void* x, const void* w_router, const float* bias, const moe_experts* w,
-                     void* y, int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes, void* stream) {
-  TRY(check_dims(d));
-  if (d.T == 0) return MOE_OK;
+}  // extern "C"
+
+namespace {
+
+moe_status check_layer_args(const moe_dims& d, const void* x, const void* w_router, const float* bias,
+                            const moe_experts* w, void* y, int32_t* topk_ids_out, float* topk_w_out) {
   TRY(check_ptr(x, "x"));
   TRY(check_ptr(w_router, "w_router"));
   TRY(check_ptr(bias, "bias", false));
@@ -596,9 +598,15 @@ moe_status moe_layer(moe_dims d, const void* x, const void* w_router, const floa
   TRY(check_ptr(y, "y"));
   TRY(check_ptr(topk_ids_out, "topk_ids_out", false));
   TRY(check_ptr(topk_w_out, "topk_w_out", false));
-  TRY(check_ws(d, ws, ws_bytes));
+  return MOE_OK;
+}
+
+// moe_layer's launches on a validated call; ws holds at least the regions
+// up to and including the fp16 rows (layout_rows16_bytes).
+moe_status enqueue_layer(const moe_dims& d, const void* x, const void* w_router, const float* bias,
+                         const moe_experts* w, void* y, int32_t* topk_ids_out, float* topk_w_out, void* ws,
+                         hipStream_t s) {
   const Layout L = layout(d);
-  hipStream_t s = (hipStream_t)stream;
   int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, L.ids);
   float* wts = topk_w_out ? topk_w_out : at<float>(ws, L.w);
   int32_t* offsets = at<int32_t>(ws, L.offsets);
@@ -613,6 +621,73 @@ moe_status moe_layer(moe_dims d, const void* x, const void* w_router, const floa
   LAUNCH(MOE_KERNEL_COMBINE, s, moe::launch_combine16(rows16, d.T, d.H, d.k, static_cast<uint16_t*>(y), s),
          "combine");
   return MOE_OK;
+}
+
+// Bytes of workspace moe_layer itself touches: every region up to the rows,
+// whose fp16 half (the weighted rows in record order) is all it uses.
+size_t layout_rows16_bytes(const moe_dims& d) {
+  return layout(d).rows + align256((size_t)d.T * d.k * d.H * 2);
+}
+
+// ---- moe_layer_noalloc: the workspace in a file-scope device array ------------
+// For callers that cannot allocate device memory.  Every device that the
+// library runs on holds its own copy of `scratch` until the process ends;
+// its device address is looked up once per device (with that device
+// current) and kept.  Host code uses only that address: the array's name in
+// host code is a host-side stand-in, not a device address.
+constexpr size_t NOALLOC_BYTES = MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_BYTES];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[SIDE_MAX_DEVICES] = {};
+
+moe_status scratch_of_current_device(hipStream_t s, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= SIDE_MAX_DEVICES) return fail(MOE_ERR_ARG, "device %d is beyond the library's table", dev);
+  if (s) {  // the kernels run on the stream's device: it must be the current one
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(s, &sdev);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+    if ((int)sdev != dev) return fail(MOE_ERR_ARG, "stream is on device %d, the current device is %d", (int)sdev, dev);
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "scratch address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_layer(moe_dims d, const void* x, const void* w_router, const float* bias, const moe_experts* w,
+                     void* y, int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_dims(d));
+  if (d.T == 0) return MOE_OK;
+  TRY(check_layer_args(d, x, w_router, bias, w, y, topk_ids_out, topk_w_out));
+  TRY(check_ws(d, ws, ws_bytes));
+  return enqueue_layer(d, x, w_router, bias, w, y, topk_ids_out, topk_w_out, ws, (hipStream_t)stream);
+}
+
+moe_status moe_layer_noalloc(moe_dims d, const void* x, const void* w_router, const float* bias, const moe_experts* w,
+                             void* y, int32_t* topk_ids_out, float* topk_w_out, void* stream) {
+  TRY(check_dims(d));
+  if (d.T == 0) return MOE_OK;
+  TRY(check_layer_args(d, x, w_router, bias, w, y, topk_ids_out, topk_w_out));
+  const size_t need = layout_rows16_bytes(d);
+  if (need > NOALLOC_BYTES)
+    return fail(MOE_ERR_WORKSPACE, "T = %d needs %zu bytes of scratch; the library's scratch holds %zu", d.T, need,
+                NOALLOC_BYTES);
+  hipStream_t s = (hipStream_t)stream;
+  void* ws = nullptr;
+  TRY(scratch_of_current_device(s, &ws));
+  return enqueue_layer(d, x, w_router, bias, w, y, topk_ids_out, topk_w_out, ws, s);
 }
 
 size_t moe_layer_shared_workspace_bytes(moe_dims d, const moe_shared* shared) {

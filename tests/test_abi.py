@@ -202,3 +202,18 @@ def test_permute_and_mapped_validation_without_hip():
                                   FAKE, ws_bytes, None) == 2
     assert L.moe_layer_mapped(d, None, 4, FAKE, FAKE, None, ctypes.byref(ex), FAKE, None, None, None, None, FAKE,
                               ws_bytes, None) == 1
+
+
+def test_noalloc_limit_without_hip():
+    """moe_layer_noalloc refuses, before any HIP call, a batch whose
+    workspace exceeds the library's scratch (T = 157 at the full shape)."""
+    L = moe.lib()
+    nv = moe.NVFP4(FAKE, FAKE, FAKE)
+    ex = moe.Experts(nv, nv, nv, 0)
+    assert L.moe_layer_noalloc(moe.dims(157, 7168, 2048, 896, 16), FAKE, FAKE, None, ctypes.byref(ex), FAKE, None,
+                               None, None) == 4
+    assert L.moe_layer_noalloc(moe.dims(8, 500, 256, 896, 16), FAKE, FAKE, None, ctypes.byref(ex), FAKE, None,
+                               None, None) == 2
+    assert L.moe_layer_noalloc(moe.dims(8, 512, 256, 896, 16), None, FAKE, None, ctypes.byref(ex), FAKE, None,
+                               None, None) == 1
+    assert moe.NOALLOC_SCRATCH_BYTES == 64 << 20
