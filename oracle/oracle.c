@@ -22,13 +22,23 @@ double oracle_e4m3_value(uint8_t code) {
   return sign ? -mag : mag;
 }
 
+/* The value of every code, from the decoders above, tabulated once so the
+ * searches below do not re-decode each candidate. */
+static double g_e2m1_table[16], g_e4m3_table[256];
+static pthread_once_t g_tables_once = PTHREAD_ONCE_INIT;
+static void fill_tables(void) {
+  for (int c = 0; c < 16; c++) g_e2m1_table[c] = oracle_e2m1_value((uint8_t)c);
+  for (int c = 0; c < 256; c++) g_e4m3_table[c] = oracle_e4m3_value((uint8_t)c);
+}
+
 /* Nearest representable value by exhaustive search over the candidate
  * codes, ties to the even code.  Distances are exact in fp64 here. */
 uint8_t oracle_e2m1_round(double r) {
+  pthread_once(&g_tables_once, fill_tables);
   uint8_t best = 0;
-  double bestd = fabs(r - oracle_e2m1_value(0));
+  double bestd = fabs(r - g_e2m1_table[0]);
   for (uint8_t c = 1; c < 8; c++) {
-    double d = fabs(r - oracle_e2m1_value(c));
+    double d = fabs(r - g_e2m1_table[c]);
     if (d < bestd || (d == bestd && (c & 1) == 0 && (best & 1) == 1)) {
       best = c;
       bestd = d;
@@ -38,10 +48,11 @@ uint8_t oracle_e2m1_round(double r) {
 }
 
 uint8_t oracle_e4m3_round(double t) {
+  pthread_once(&g_tables_once, fill_tables);
   uint8_t best = 0;
-  double bestd = fabs(t - oracle_e4m3_value(0));
+  double bestd = fabs(t - g_e4m3_table[0]);
   for (uint8_t c = 1; c < 127; c++) { /* 0x7F is NaN */
-    double d = fabs(t - oracle_e4m3_value(c));
+    double d = fabs(t - g_e4m3_table[c]);
     if (d < bestd || (d == bestd && (c & 1) == 0 && (best & 1) == 1)) {
       best = c;
       bestd = d;
