@@ -11,7 +11,7 @@ import os
 
 import numpy as np
 
-from .build import LIB, build
+from .build import LIB, LIB_SAN, build, sanitize_requested
 
 _lib = None
 _c_i64 = ctypes.c_int64
@@ -24,9 +24,9 @@ def lib():
         path = os.environ.get("ORACLE_LIB")  # a mutated build, for checking the pins
         if not path:
             src = os.path.join(os.path.dirname(LIB), "oracle.c")
-            if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(src):
+            path = LIB_SAN if sanitize_requested() else LIB
+            if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(src):
                 build()
-            path = LIB
         L = ctypes.CDLL(path)
         L.oracle_e2m1_value.restype = ctypes.c_double
         L.oracle_e2m1_value.argtypes = [ctypes.c_uint8]

@@ -7,7 +7,7 @@ import os
 
 import numpy as np
 
-from .build import LIB_CPU, LIB_GPU, build_cpu
+from .build import LIB_CPU, LIB_CPU_SAN, LIB_GPU, build_cpu, sanitize_requested
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 _cpu = None
@@ -26,9 +26,10 @@ def cpu():
     if _cpu is None:
         src = os.path.join(HERE, "synth.c")
         hdr = os.path.join(HERE, "synth_def.h")
-        if not os.path.exists(LIB_CPU) or os.path.getmtime(LIB_CPU) < max(os.path.getmtime(src), os.path.getmtime(hdr)):
+        path = LIB_CPU_SAN if sanitize_requested() else LIB_CPU
+        if not os.path.exists(path) or os.path.getmtime(path) < max(os.path.getmtime(src), os.path.getmtime(hdr)):
             build_cpu()
-        L = ctypes.CDLL(LIB_CPU)
+        L = ctypes.CDLL(path)
         L.synth_x_bf16.argtypes = [_u64, _i64, _i, _i, _p]
         L.synth_router_bf16.argtypes = [_u64, _i, _i, _f, _p]
         L.synth_expert_f32.argtypes = [_u64, _i, _i, _i, _i, _f, _p, _i]

@@ -6,17 +6,27 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_CPU = os.path.join(HERE, "libsynth.so")
 LIB_GPU = os.path.join(HERE, "libsynth_gpu.so")
+LIB_CPU_SAN = os.path.join(HERE, "libsynth_san.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+# host-only instrumentation of the gcc build (ORACLE_SANITIZE=1): the CPU
+# generator next to the sanitized oracle; the GPU generator is never built so
+SANITIZE_FLAGS = ["-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined", "-fno-sanitize-recover=all"]
 
 
-def build_cpu(verbose=False):
-    cmd = ["gcc", "-O2", "-std=c99", "-Wall", "-Wextra", "-fPIC", "-shared", os.path.join(HERE, "synth.c"),
-           "-o", LIB_CPU + ".tmp", "-lm", "-lpthread"]
+def sanitize_requested():
+    return os.environ.get("ORACLE_SANITIZE") == "1"
+
+
+def build_cpu(verbose=False, sanitize=None):
+    san = sanitize_requested() if sanitize is None else sanitize
+    out = LIB_CPU_SAN if san else LIB_CPU
+    cmd = ["gcc", "-O1" if san else "-O2", "-std=c99", "-Wall", "-Wextra", "-fPIC", "-shared",
+           *(SANITIZE_FLAGS if san else []), os.path.join(HERE, "synth.c"), "-o", out + ".tmp", "-lm", "-lpthread"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
-    os.replace(LIB_CPU + ".tmp", LIB_CPU)
-    return LIB_CPU
+    os.replace(out + ".tmp", out)
+    return out
 
 
 def build_gpu(verbose=False):

@@ -273,7 +273,7 @@ def _numpy_layer(x_bf16, wr_bf16, bias, experts, k):
             g, u, d = deq[e]
             a = x[t] @ g.T
             b = x[t] @ u.T
-            h = a / (1 + np.exp(-a)) * b
+            h = torch.nn.functional.silu(torch.from_numpy(a)).numpy() * b  # SiLU from torch, in fp64
             y[t] += w[j] * (h @ d.T)
     return logits, ids, y
 
