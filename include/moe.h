@@ -50,7 +50,8 @@
  *   - Same inputs on the same GPU give bit-identical outputs: there are no
  *     floating-point atomics.
  *   - Shape limits: 1 <= k <= 64, k <= E <= 1024 with E a multiple of 8,
- *     H and I multiples of 256, 0 <= T and T*k < 2^31.  moe_permute,
+ *     H and I multiples of 256, 0 <= T <= 65535 and T * max(H, k*I) < 2^31
+ *     (at H = 7168, I = 2048, k = 16: T <= 65535).  moe_permute,
  *     moe_expert_ffn and moe_workspace_bytes, which take expert ids rather
  *     than route, accept any 1 <= E <= 1024 (e.g. one device's experts).  T = 0 is a no-op
  *     returning MOE_OK once the dimensions are valid (pointers are then not
@@ -62,7 +63,9 @@
  *     intermediate h = SiLU(x.W_gate)*(x.W_up): the expert GEMMs run on
  *     fp16 matrix cores (the NVFP4 products are exact in fp16; see the
  *     design notes).  Outside that range results are inf/NaN, not silently
- *     wrong. */
+ *     wrong.  x's bf16 values are exact in fp16 from 2^-17 up; smaller
+ *     magnitudes fall in fp16's subnormal range and are rounded to a
+ *     multiple of 2^-24 (an error of at most 2^-25 each). */
 #ifndef MOE_H
 #define MOE_H
 #include <stddef.h>

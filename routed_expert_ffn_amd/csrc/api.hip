@@ -132,6 +132,12 @@ moe_status check_dims(const moe_dims& d, bool router = true) {
     return fail(MOE_ERR_SHAPE, "E = %d must be a multiple of 8 in [k, 1024]", d.E);
   if (!router && (d.E < 1 || d.E > 1024)) return fail(MOE_ERR_SHAPE, "E = %d must be in [1, 1024]", d.E);
   if ((long long)d.T * d.k >= (1LL << 31)) return fail(MOE_ERR_SHAPE, "T*k = %lld is too large", (long long)d.T * d.k);
+  // grids take one row per token (at most 65535), and the large-batch GEMMs
+  // address token rows (2 T H bytes of x, 2 T k I of h) with 32-bit offsets
+  if (d.T > 65535) return fail(MOE_ERR_SHAPE, "T = %d exceeds 65535 tokens per call", d.T);
+  const long long ki = (long long)d.k * d.I, wide = d.H > ki ? d.H : ki;
+  if ((long long)d.T * wide >= (1LL << 31))
+    return fail(MOE_ERR_SHAPE, "T * max(H, k*I) = %lld must be below 2^31", (long long)d.T * wide);
   return MOE_OK;
 }
 

@@ -42,7 +42,9 @@ __global__ __launch_bounds__(PROJ_THREADS) void proj_reduce_kernel(const float* 
   o.y = (uint32_t)b2 | ((uint32_t)b3 << 16);
   reinterpret_cast<uint2*>(out)[i] = o;
   if (out16) {
-    // the bf16 values are exact in fp16 within its range (|v| < 65504)
+    // bf16 values of 2^-17 <= |v| < 65504 (and zero) are exact in fp16;
+    // smaller ones fall in fp16's subnormal range and round to a multiple
+    // of 2^-24 (an error of at most 2^-25)
     typedef _Float16 h4 __attribute__((ext_vector_type(4)));
     h4 h;
     h[0] = (f16)bf16_to_f32(b0);

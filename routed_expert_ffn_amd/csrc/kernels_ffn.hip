@@ -1056,18 +1056,13 @@ __global__ __launch_bounds__(BIG_WAVES * WAVE, 1) void expert_gemm_big_kernel(Bi
   }
 }
 
-// Token batches from this size use the large-tile kernels when the tiles
-// divide the matrices: H and I both in row tiles (256 and 128 rows) and in
-// multiples of four chunks of 64 (the DMA rotation), i.e. H % 256 == 0 and
-// I % 256 == 0.  Otherwise the small-batch kernels run with four fragments
-// per pass.
+// Token batches from this size use the large-tile kernels.  Their tiles
+// divide the matrices because the C ABI takes H and I in multiples of 256
+// (row tiles of 256 and 128 rows, multiples of four chunks of 64 for the DMA
+// rotation), and it bounds T max(H, k I) below 2^31, so that token rows
+// (2 T H bytes of x, 2 T k I of h) have 32-bit byte offsets.
 constexpr int BIG_MIN_T = 1024;
-// Token rows are addressed with 32-bit byte offsets: 2 T H and 2 T k I must
-// stay below 2^32.
-bool use_big(const FfnArgs& a) {
-  const long long ki = (long long)a.k * a.I, span = (long long)a.T * (a.H > ki ? a.H : ki);
-  return a.T >= BIG_MIN_T && a.I % 256 == 0 && a.H % 256 == 0 && span < (1LL << 31);
-}
+bool use_big(const FfnArgs& a) { return a.T >= BIG_MIN_T; }
 
 template <bool GATEUP, int FMT>
 hipError_t launch_big_fmt(const FfnArgs& a, const GroupedParams& p, hipStream_t s) {
@@ -1186,12 +1181,6 @@ __global__ __launch_bounds__(256) void combine_share_kernel(const float* __restr
   *reinterpret_cast<float4*>(y + (size_t)t * H + n) = a;
 }
 
-// Fragments per pass: an expert never has more pairs than there are tokens.
-// At decode sizes one 16-token fragment per pass keeps two wavefronts per
-// SIMD resident; an expert with more tokens takes several passes, the later
-// ones re-reading its weights from the caches.  Large batches use four.
-int pick_mf(int T) { return T <= 1024 ? 1 : 4; }
-
 GroupedParams base_params(const FfnArgs& a) {
   GroupedParams p{};
   p.H = a.H;
@@ -1241,19 +1230,22 @@ hipError_t launch_gemm_stage(const GroupedParams& p, dim3 grid, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Code loads in whole lines (R8) for gate/up at every small batch, and for
-// down while every expert has at most 16 records (one token pass): T <= 16.
+// Small batches (below BIG_MIN_T tokens) take tokens in passes of one
+// 16-token fragment, which keeps two wavefronts per SIMD resident; an expert
+// with more tokens takes several passes, the later ones re-reading its
+// weights from the caches.  Code loads in whole lines (R8) for gate/up at
+// every small batch, and for down while every expert has at most 16 records
+// (one token pass): T <= 16.
 template <int KSPLIT, bool GATEUP, int FMT>
-hipError_t launch_gemm_fmt(const GroupedParams& p, int mf, int T, dim3 grid, hipStream_t s) {
-  if (mf != 1) return launch_gemm_stage<4, KSPLIT, GATEUP, 1, FMT, false>(p, grid, s);
+hipError_t launch_gemm_fmt(const GroupedParams& p, int T, dim3 grid, hipStream_t s) {
   return GATEUP || T <= 16 ? launch_gemm_stage<1, KSPLIT, GATEUP, GEMM_WAVES, FMT, true>(p, grid, s)
                            : launch_gemm_stage<1, KSPLIT, GATEUP, GEMM_WAVES, FMT, false>(p, grid, s);
 }
 
 template <int KSPLIT, bool GATEUP>
-hipError_t launch_gemm(const GroupedParams& p, int mf, int T, dim3 grid, hipStream_t s, int fmt) {
-  return fmt == MOE_FMT_MXFP4 ? launch_gemm_fmt<KSPLIT, GATEUP, FMT_MX>(p, mf, T, grid, s)
-                              : launch_gemm_fmt<KSPLIT, GATEUP, FMT_NV>(p, mf, T, grid, s);
+hipError_t launch_gemm(const GroupedParams& p, int T, dim3 grid, hipStream_t s, int fmt) {
+  return fmt == MOE_FMT_MXFP4 ? launch_gemm_fmt<KSPLIT, GATEUP, FMT_MX>(p, T, grid, s)
+                              : launch_gemm_fmt<KSPLIT, GATEUP, FMT_NV>(p, T, grid, s);
 }
 
 }  // namespace
@@ -1269,7 +1261,7 @@ hipError_t launch_gateup(const FfnArgs& a, hipStream_t s) {
   p.gs1 = a.w->up.gs;
   if (use_big(a)) return launch_big<true>(a, p, s);
   const dim3 grid(a.I / (32 * (4 / GU_KSPLIT)), a.max_active);
-  return launch_gemm<GU_KSPLIT, true>(p, pick_mf(a.T), a.T, grid, s, a.w->format);
+  return launch_gemm<GU_KSPLIT, true>(p, a.T, grid, s, a.w->format);
 }
 
 hipError_t launch_down(const FfnArgs& a, hipStream_t s) {
@@ -1280,7 +1272,7 @@ hipError_t launch_down(const FfnArgs& a, hipStream_t s) {
   p.gs0 = a.w->down.gs;
   if (use_big(a)) return launch_big<false>(a, p, s);
   const dim3 grid(a.H / (64 * (4 / DN_KSPLIT)), a.max_active);
-  return launch_gemm<DN_KSPLIT, false>(p, pick_mf(a.T), a.T, grid, s, a.w->format);
+  return launch_gemm<DN_KSPLIT, false>(p, a.T, grid, s, a.w->format);
 }
 
 hipError_t launch_combine16(const f16* rows, int T, int H, int k, uint16_t* y, hipStream_t s, const float* add,

@@ -41,18 +41,22 @@ def assert_close(got, ref, what, max_abs=MAX_ABS, rel=REL_L2):
     assert a <= max_abs and r <= rel, f"{what}: max_abs={a:.3e} rel_l2={r:.3e}"
 
 
-def assert_close_bf16_out(got, ref, what):
+def assert_close_bf16_out(got, ref, what, extra=None):
     """A bf16 output against the oracle's fp64 value: relative L2 within
-    REL_L2, and each element within MAX_ABS or one bf16 unit of its
-    magnitude, whichever is larger (at |y| >= 4 the output's own rounding to
-    bf16 alone reaches half a unit, 1.6e-2, and one unit past 8 exceeds
-    MAX_ABS)."""
+    REL_L2, and each element within MAX_ABS or, where that is larger, half a
+    bf16 unit of its magnitude (the output's own rounding) plus 4e-3 (the
+    computation's error).  Half a unit exceeds MAX_ABS only from |y| = 8
+    (0.031 there), which the shared experts and the latent block reach.
+    extra (per element, optional) widens the allowance by a stated bound on
+    an error source upstream of this output."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     unit = np.ldexp(1.0, np.frexp(np.abs(ref))[1] - 8)
-    worst = float(np.max(np.abs(got - ref) / np.maximum(MAX_ABS, unit)))
+    allow = np.maximum(MAX_ABS, 0.5 * unit + 4e-3) + (0.0 if extra is None else extra)
+    worst = float(np.max(np.abs(got - ref) / allow))
     a, r = errors(got, ref)
-    say(f"  {what}: max_abs={a:.3e} (worst {worst:.2f} of its allowance) rel_l2={r:.3e}")
+    say(f"  {what}: max_abs={a:.3e} (worst {worst:.2f} of its allowance, |y| up to {np.abs(ref).max():.2f}) "
+        f"rel_l2={r:.3e}")
     assert worst <= 1.0 and r <= REL_L2, f"{what}: worst {worst:.2f}, rel_l2={r:.3e}"
 
 
@@ -73,13 +77,18 @@ def build_store(E, H, I, seed, experts=None, fmt="nvfp4"):
     return store
 
 
+_ORACLE_EXPERTS = {}  # (seed, H, I, fmt) -> {expert: quantised triple}, shared by the test modules
+
+
 class OracleExperts:
-    """Experts generated and quantised on the CPU by the oracle, on demand."""
+    """Experts generated and quantised on the CPU by the oracle, on demand,
+    kept for the rest of the test session (the same experts serve several
+    full-size tests)."""
 
     def __init__(self, seed, H, I, fmt="nvfp4"):
         self.seed, self.H, self.I = seed, H, I
         self.quant = oracle.mxfp4_quantize if fmt == "mxfp4" else oracle.nvfp4_quantize
-        self.cache = {}
+        self.cache = _ORACLE_EXPERTS.setdefault((seed, H, I, fmt), {})
 
     def _make(self, e):
         return tuple(self.quant(synth.expert_f32(self.seed, e, m, *synth.expert_shape(m, self.H, self.I), nthreads=1))

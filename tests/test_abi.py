@@ -217,3 +217,15 @@ def test_noalloc_limit_without_hip():
     assert L.moe_layer_noalloc(moe.dims(8, 512, 256, 896, 16), None, FAKE, None, ctypes.byref(ex), FAKE, None,
                                None, None) == 1
     assert moe.NOALLOC_SCRATCH_BYTES == 64 << 20
+
+
+def test_token_bounds_without_hip():
+    """T above 65535, or T * max(H, k*I) at 2^31 or more, is refused (the
+    grids and the large-tile GEMMs' 32-bit row offsets); just below is
+    accepted."""
+    assert moe.moe_workspace_bytes(moe.dims(65536, 512, 256, 896, 16)) == 0
+    assert moe.moe_workspace_bytes(moe.dims(65535, 512, 256, 896, 16)) > 0
+    assert moe.moe_workspace_bytes(moe.dims(16384, 512, 2048, 1024, 64)) == 0  # 16384 * 131072 = 2^31
+    assert moe.moe_workspace_bytes(moe.dims(16383, 512, 2048, 1024, 64)) > 0
+    d = moe.dims(16384, 512, 2048, 1024, 64)
+    assert _route(d, ws_bytes=1 << 40) == 2

@@ -10,9 +10,15 @@ The latent z is the bf16 rounding of an fp32 (GPU) or fp64 (oracle) sum, so
 an element may differ by one bf16 unit in the last place where the sum sits
 near a rounding boundary.  y is held to the layer's tolerances (max-abs
 2e-2, relative L2 5e-3 against the oracle's fp64 value), except that an
-element may also differ by one bf16 unit of its magnitude: y has the hidden
-width's scale, where its own rounding to bf16 alone reaches half a unit
-(1.6e-2 at |y| in [4, 8))."""
+element of |y| >= 8 may differ by half a bf16 unit of its magnitude plus
+4e-3: y has the hidden width's scale, where its own rounding to bf16 alone
+reaches half a unit (3.1e-2 at |y| in [8, 16)).  The block also rounds the
+combined latent y_lat to bf16 before the up projection, the GPU from its fp32
+sum and the oracle from its fp64 one; where the two sit on either side of a
+rounding boundary they differ by one bf16 unit, which the up projection
+carries into y.  Each element of y is allowed 3 times the root-sum-square of
+those units weighted by its column of P_up, the spread of that carried
+difference when any element of y_lat may differ."""
 import numpy as np
 import pytest
 import torch
@@ -101,7 +107,12 @@ def compare(case, rows, y, z, ids, logits, ex):
                               logits_in=logits[rows], nthreads=16)
     np.testing.assert_array_equal(ids[rows], ref["ids"])
     check_z(z[rows], ref["z"], x, pd)
-    assert_close_bf16_out(y[rows], ref["y"], "y")
+    # the bf16 seam at y_lat: one unit per element, carried through P_up
+    y_lat = synth.bf16_to_f32(ref["y_lat"]).astype(np.float64)
+    ulp = np.ldexp(1.0, np.frexp(np.abs(y_lat))[1] - 8)
+    pu = synth.bf16_to_f32(synth.proj_bf16(case.seed, 1, case.H, case.Hm)).astype(np.float64)
+    seam = 3.0 * np.sqrt((ulp ** 2) @ (pu ** 2))
+    assert_close_bf16_out(y[rows], ref["y"], "y", extra=seam)
     return ref
 
 
@@ -141,6 +152,8 @@ def test_latent_block_k3_shape(name, k3_store):
     y, z, ids, w = case.run()
     assert np.all(np.isfinite(y))
     logits = case.logits()
-    rows = np.array(sorted(set([0, wl.T // 2, wl.T - 1])))
+    rng = np.random.default_rng(3)
+    rows = np.array(sorted(set([0, wl.T // 2, wl.T - 1]) | set(rng.choice(wl.T, size=min(wl.T, 29), replace=False))))
+    say(f"  {len(rows)} sampled tokens")
     ox = OracleExperts(wl.seed, wl.H, wl.I)
     compare(case, rows, y, z, ids, logits, ox.get(ids[rows]))

@@ -3,8 +3,9 @@ the oracle's bit for bit (codes and e8m0 scales; gs the stated power of
 two), and the layer on an MXFP4 store against the oracle's layer on the
 oracle's MXFP4 experts, through moe_expert_ffn (rows) and moe_layer (y), at
 small shapes (small-batch GEMMs below 1024 tokens, the large-tile GEMMs from
-there) and at the full single-user decode and 8192-token prefill shapes (the
-prefill on sampled tokens the oracle computes one by one)."""
+there) and at every full-size workload (single-user and 64-session decode,
+speculative verify, the 8192-token prefill chunk), on sampled tokens that the
+oracle computes."""
 import numpy as np
 import pytest
 import torch
@@ -17,7 +18,7 @@ if torch.cuda.is_available():
     import synth
     from synth.workloads import WORKLOADS
     from tests.gpu_helpers import DEV, WEIGHT_ABS, Inputs, OracleExperts, assert_close, build_store, say, to_np
-    from tests.test_gpu_full import _sample_tokens
+    from tests.test_gpu_full import check_sampled, sample_tokens
 
 
 def mx_cases():
@@ -76,35 +77,18 @@ def full_store():
     return build_store(wl.E, wl.H, wl.I, wl.seed, fmt="mxfp4")
 
 
-def test_mxfp4_layer_decode_full_size(full_store):
-    wl = WORKLOADS["decode_1"]
+@pytest.mark.parametrize("name", ["decode_1", "decode_64", "verify_256", "prefill_8192"])
+def test_mxfp4_layer_full_size(name, full_store):
+    """Every full-size workload on the MXFP4 store: routing bit-exact (the
+    plain layer's), rows and y of at least 32 sampled tokens (tile and pass
+    edges of the most loaded expert) against the oracle's MXFP4 layer."""
+    wl = WORKLOADS[name]
+    say(f"mxfp4 full-size {name}: T={wl.T}")
     inp = Inputs.for_workload(wl, store=full_store)
     r = inp.route()
-    ox = OracleExperts(wl.seed, wl.H, wl.I, fmt="mxfp4")
-    ref = oracle.moe_layer(inp.host_x(), ox.get(r["ids"]), wl.E, wl.k, logits_in=r["logits"], want_rows=True,
-                           nthreads=16)
-    rows = inp.ffn(r["offsets"], r["sorted_pairs"])
-    assert_close(rows, ref["rows"], "decode_1 mxfp4 rows")
-    y, _, _ = inp.layer()
-    assert_close(y, ref["y"], "decode_1 mxfp4 y")
-
-
-def test_mxfp4_layer_prefill_full_size(full_store):
-    wl = WORKLOADS["prefill_8192"]
-    say(f"mxfp4 full-size prefill: T={wl.T}")
-    inp = Inputs.for_workload(wl, store=full_store)
-    r = inp.route()
-    sample = _sample_tokens(wl.T, r, wl.k)
+    sample = sample_tokens(wl.T, r, wl.k)
     rows = inp.ffn(r["offsets"], r["sorted_pairs"])
     y, ids, w = inp.layer()
     np.testing.assert_array_equal(ids, r["ids"])
     assert np.all(np.isfinite(y))
-    ox = OracleExperts(wl.seed, wl.H, wl.I, fmt="mxfp4")
-    ref = oracle.moe_layer(inp.host_x(sample), ox.get(r["ids"][sample]), wl.E, wl.k, logits_in=r["logits"][sample],
-                           nthreads=16, want_rows=True)
-    np.testing.assert_array_equal(ref["ids"], r["ids"][sample])
-    assert np.abs(ref["w"] - r["w"][sample]).max() <= WEIGHT_ABS
-    got_rows = np.stack([rows[r["pair_pos"][t * wl.k + j]] for t in sample for j in range(wl.k)])
-    ref_rows = np.stack([ref["rows"][ref["pair_pos"][s * wl.k + j]] for s in range(len(sample)) for j in range(wl.k)])
-    assert_close(got_rows, ref_rows, f"prefill mxfp4 rows of tokens {sample}")
-    assert_close(y[sample], ref["y"], f"prefill mxfp4 y of tokens {sample}")
+    check_sampled(name, wl, inp, r, rows, y, sample, OracleExperts(wl.seed, wl.H, wl.I, fmt="mxfp4"), " mxfp4")

@@ -244,6 +244,27 @@ def test_wide_k_scales_from_memory(H, I, fmt, T):
     assert_close(y, ref["y"], "y")
 
 
+@pytest.mark.parametrize("T,H,I,E,k", [(1100, 2048, 2048, 16, 2), (1030, 3072, 1280, 8, 2)])
+def test_large_tiles_many_spans(T, H, I, E, k):
+    """The large-tile GEMMs at a K of many four-chunk spans (2048: eight
+    spans for gate/up and for down; 3072 and 1280: twelve and five), so the
+    steady-state loop of the LDS DMA pipeline runs many times in both GEMMs:
+    every token's rows and output against the oracle."""
+    say(f"many spans T={T} H={H} I={I} E={E} k={k}")
+    store = build_store(E, H, I, 15)
+    inp = Inputs(T, H, I, E, k, seed=15, store=store, router_std=0.1, bias=synth.zipf_bias(15, E, 0.6))
+    r = inp.route()
+    check_route(inp, r, rows=np.arange(8))
+    counts = np.diff(r["offsets"])
+    say(f"  counts: max={counts.max()} min={counts.min()}")
+    ox = OracleExperts(15, H, I)
+    ref = oracle.moe_layer(inp.host_x(), ox.get(r["ids"]), E, k, logits_in=r["logits"], want_rows=True, nthreads=16)
+    assert_close(inp.ffn(r["offsets"], r["sorted_pairs"]), ref["rows"], "rows")
+    y, ids, _ = inp.layer()
+    np.testing.assert_array_equal(ids, ref["ids"])
+    assert_close(y, ref["y"], "y")
+
+
 @pytest.mark.parametrize("T", [6, 40, 100])
 def test_route_ties_logits_in(T):
     """Constructed fp32 logits with exact ties (all equal, +-0, duplicated
