@@ -624,13 +624,13 @@ moe_status enqueue_layer(const moe_dims& d, const void* x, const void* w_router,
   // the down GEMM writes each record's row times its routing weight in fp16
   f16* rows16 = at<f16>(ws, L.rows);
   TRY(enqueue_ffn(d, offsets, sorted, w, rows, ws, s, 0, rows16, wts));
-  LAUNCH(MOE_KERNEL_COMBINE, s, moe::launch_combine16(rows16, d.T, d.H, d.k, static_cast<uint16_t*>(y), s),
+  LAUNCH(MOE_KERNEL_COMBINE, s, moe::launch_combine16(rows16, pos, d.T, d.H, d.k, static_cast<uint16_t*>(y), s),
          "combine");
   return MOE_OK;
 }
 
 // Bytes of workspace moe_layer itself touches: every region up to the rows,
-// whose fp16 half (the weighted rows in record order) is all it uses.
+// whose fp16 half (the weighted fp16 rows) is all it uses.
 size_t layout_rows16_bytes(const moe_dims& d) {
   return layout(d).rows + align256((size_t)d.T * d.k * d.H * 2);
 }
@@ -750,7 +750,7 @@ moe_status moe_layer_shared(moe_dims d, const moe_shared* shared, const void* x,
   TRY(enqueue_ffn(d, offsets, sorted, w, rows, ws, s, 0, rows16, wts));
   if (hipError_t e = branch.join(); e != hipSuccess) return hip_fail(e, "join of the shared experts");
   LAUNCH(MOE_KERNEL_COMBINE, s,
-         moe::launch_combine16(rows16, T, H, d.k, static_cast<uint16_t*>(y), s, dpart, SL.d_slabs), "combine");
+         moe::launch_combine16(rows16, pos, T, H, d.k, static_cast<uint16_t*>(y), s, dpart, SL.d_slabs), "combine");
   return MOE_OK;
 }
 
@@ -824,7 +824,7 @@ moe_status moe_latent_layer(moe_dims d, const moe_latent* lat, const void* x, co
   float* rows = at<float>(ws, L.rows);
   f16* rows16 = at<f16>(ws, L.rows);
   TRY(enqueue_ffn(d, offsets, sorted, w, rows, ws, s, 0, rows16, wts));
-  LAUNCH(MOE_KERNEL_COMBINE, s, moe::launch_combine16(rows16, T, H, k, ylat, s), "combine");
+  LAUNCH(MOE_KERNEL_COMBINE, s, moe::launch_combine16(rows16, pos, T, H, k, ylat, s), "combine");
   // routed-up projection back to the hidden width
   LAUNCH(MOE_KERNEL_PROJECT, s,
          moe::launch_projection(ylat, static_cast<const uint16_t*>(lat->w_up), ppart, T, H, Hm,

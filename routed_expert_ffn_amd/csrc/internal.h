@@ -79,16 +79,21 @@ struct FfnArgs {
   const moe_experts* w;
   f16* h;                         // [P][I]
   float* rows;                    // [P][H] fp32, unweighted (when rows16 is NULL)
-  f16* rows16;                    // or [P][H] fp16 in record order (row t*k+j), times its routing weight
+  f16* rows16;                    // or [P][H] fp16 times its routing weight, at rows16_sorted(T) ? sorted position
+                                  // : record (t*k+j)
   const float* pair_w;            // routing weights [T*k] for rows16
 };
 hipError_t launch_gateup(const FfnArgs& a, hipStream_t s);
 hipError_t launch_down(const FfnArgs& a, hipStream_t s);
-// Combine of weighted fp16 rows in record order: y = bf16(sum_j
-// rows16[t*k+j] (+ add)), add (may be NULL) being add_slabs fp32 partials
-// [T][H] summed after the records (the shared experts' output).
-hipError_t launch_combine16(const f16* rows, int T, int H, int k, uint16_t* y, hipStream_t s,
-                            const float* add = nullptr, int add_slabs = 0);
+// The down GEMM's weighted fp16 rows of T tokens are in sorted order (row p)
+// when this holds (the large-tile kernel), else in record order (row t*k+j).
+bool rows16_sorted(int T);
+// Combine of the weighted fp16 rows: y = bf16(sum_j rows16[row(t, j)] (+
+// add)), row(t, j) = pair_pos[t*k+j] or t*k+j as rows16_sorted(T) says, add
+// (may be NULL) being add_slabs fp32 partials [T][H] summed after the records
+// (the shared experts' output).
+hipError_t launch_combine16(const f16* rows, const int32_t* pair_pos, int T, int H, int k, uint16_t* y,
+                            hipStream_t s, const float* add = nullptr, int add_slabs = 0);
 // One share of the experts: only records whose expert is in [lo, hi) are
 // summed, into fp32 partial outputs; served[t*k+j] (may be NULL) = 1 for
 // those records, 0 for the others.

@@ -52,7 +52,8 @@ struct GroupedParams {
   const float* gs1;
   f16* h;              // gate/up output [P][I]
   float* rows;         // down output [P][H], fp32 unweighted (when rows16 is NULL)
-  f16* rows16;         // or: down output [P][H] fp16 in record order (row t*k+j), each row times its routing weight
+  f16* rows16;         // or: down output [P][H] fp16, each row times its routing weight, in record order (row
+                       //     t*k+j; small-batch kernel) or in sorted order (row p; large-tile kernel)
   const float* pair_w; //     the routing weights [T*k], indexed by record (sorted_pairs[p])
 };
 
@@ -297,7 +298,15 @@ __device__ __forceinline__ void mma_chunk(f32x4 (&acc)[MF][4], Chunk<MF>& ch, co
   }
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+// SiLU(z) = z / (1 + e^-z) with the hardware base-2 exponential and
+// reciprocal (each within about one fp32 ulp); h is rounded to fp16 (2^-11)
+// right after, so their error does not show.  e^-z overflows to infinity
+// for z below about -88, giving z * 0 = -0, within fp16 rounding of the
+// true value there.
+__device__ __forceinline__ float silu(float z) {
+  const float e = __builtin_amdgcn_exp2f(-z * 1.4426950408889634f);
+  return z * __builtin_amdgcn_rcpf(1.0f + e);
+}
 
 // One grouped NVFP4 GEMM over the active experts (blockIdx.y indexes the
 // active list).  A block is four wavefronts; KSPLIT consecutive wavefronts
@@ -545,8 +554,7 @@ constexpr int BIG_OFF_RQ = BIG_OFF_A + 3 * BIG_TILE_BYTES;          // [2][256][
 constexpr int BIG_OFF_RS = BIG_OFF_RQ + 2 * BIG_SPANQ_BYTES;        // [2][256][16] u8
 constexpr int BIG_OFF_ROW = BIG_OFF_RS + 2 * BIG_SPANS_BYTES;       // [224] i32
 constexpr int BIG_OFF_RW = BIG_OFF_ROW + BIG_M * 4;                 // [224] f32 routing weights (down, fp16 rows)
-constexpr int BIG_OFF_REC = BIG_OFF_RW + BIG_M * 4;                 // [224] i32 record ids (down, fp16 rows)
-constexpr int BIG_LDS = BIG_OFF_REC + BIG_M * 4;
+constexpr int BIG_LDS = BIG_OFF_RW + BIG_M * 4;
 static_assert(BIG_LDS <= 160 * 1024, "LDS budget of one CU");
 
 struct BigParams {
@@ -973,9 +981,11 @@ __device__ __forceinline__ void big_tile(const GroupedParams& p, const BigTile& 
         }
       } else {
         // fp16 rows carry the routing weight of their record and are stored
-        // at the record's row
+        // in sorted order: a tile's rows are then one contiguous region.
+        // (Stored at their records' rows, t*k+j, the 224 rows of a tile are
+        // spread over the whole buffer, which made this kernel 20% slower at
+        // 8192 tokens, in the K loop as well as in the stores.)
         const float ws = p.rows16 ? reinterpret_cast<const float*>(smem + BIG_OFF_RW)[min(m, BIG_M - 1)] : 1.0f;
-        const int rec = p.rows16 ? reinterpret_cast<const int*>(smem + BIG_OFF_REC)[min(m, BIG_M - 1)] : 0;
 #pragma unroll
         for (int nf = 0; nf < 2; nf++) {
           float v[4];
@@ -988,7 +998,7 @@ __device__ __forceinline__ void big_tile(const GroupedParams& p, const BigTile& 
               f16x4 o;
 #pragma unroll
               for (int r = 0; r < 4; r++) o[r] = (f16)(ws * v[r]);
-              *reinterpret_cast<f16x4*>(p.rows16 + (size_t)rec * t.N + col) = o;
+              *reinterpret_cast<f16x4*>(p.rows16 + (size_t)(t.mb + m) * t.N + col) = o;
             } else {
               *reinterpret_cast<float4*>(p.rows + (size_t)(t.mb + m) * t.N + col) = make_float4(v[0], v[1], v[2], v[3]);
             }
@@ -1025,11 +1035,7 @@ __global__ __launch_bounds__(BIG_WAVES * WAVE, 1) void expert_gemm_big_kernel(Bi
   for (int m = threadIdx.x; m < BIG_M; m += BIG_WAVES * WAVE) {
     const int pp = t.mb + min(m, t.nvalid - 1);
     rowoff[m] = GATEUP ? p.sorted_pairs[pp] / p.k : pp;
-    if (!GATEUP && p.rows16) {
-      const int rec = p.sorted_pairs[pp];
-      reinterpret_cast<float*>(big_smem + BIG_OFF_RW)[m] = p.pair_w[rec];
-      reinterpret_cast<int*>(big_smem + BIG_OFF_REC)[m] = rec;
-    }
+    if (!GATEUP && p.rows16) reinterpret_cast<float*>(big_smem + BIG_OFF_RW)[m] = p.pair_w[p.sorted_pairs[pp]];
   }
   __syncthreads();
   const int nf = (t.nvalid + 31) / 32;  // token fragments, 1 .. 7
@@ -1090,11 +1096,14 @@ hipError_t launch_big(const FfnArgs& a, const GroupedParams& p, hipStream_t s) {
 // loads, are issued together before the sums.
 constexpr int COMBINE_JB = 16;
 
-// y[t][n] = bf16( sum_j rows16[t*k+j][n] (+ add) ): the rows are in record
-// order and already carry their routing weights; fp32 sum over ascending j,
-// then the add_slabs partials in order.  Four columns per thread, 16
-// records' loads issued together.
-__global__ __launch_bounds__(256) void combine16_kernel(const f16* __restrict__ rows, int H, int k,
+// y[t][n] = bf16( sum_j rows16[row(t, j)][n] (+ add) ): the rows already
+// carry their routing weights and sit at their records' rows (row(t, j) =
+// t*k+j, pos NULL) or at their sorted positions (row(t, j) = pos[t*k+j]);
+// fp32 sum over ascending j, then the add_slabs partials in order.  Four
+// columns per thread; 16 records' positions, then their 16 row loads, are
+// issued together.
+__global__ __launch_bounds__(256) void combine16_kernel(const f16* __restrict__ rows,
+                                                       const int32_t* __restrict__ pos, int H, int k,
                                                        uint16_t* __restrict__ y,
                                                        const float* __restrict__ add, int add_slabs,
                                                        long long add_stride) {
@@ -1104,10 +1113,16 @@ __global__ __launch_bounds__(256) void combine16_kernel(const f16* __restrict__ 
   if (n >= H) return;
   float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
   for (int j0 = 0; j0 < k; j0 += COMBINE_JB) {
+    size_t row[COMBINE_JB];
+#pragma unroll
+    for (int u = 0; u < COMBINE_JB; u++) {
+      const size_t f = (size_t)t * k + j0 + u;
+      row[u] = j0 + u < k ? (pos ? (size_t)pos[f] : f) : 0;
+    }
     h4 v[COMBINE_JB];
 #pragma unroll
     for (int u = 0; u < COMBINE_JB; u++)
-      v[u] = j0 + u < k ? *reinterpret_cast<const h4*>(rows + ((size_t)t * k + j0 + u) * H + n) : h4{};
+      v[u] = j0 + u < k ? *reinterpret_cast<const h4*>(rows + row[u] * H + n) : h4{};
 #pragma unroll
     for (int u = 0; u < COMBINE_JB; u++)
       if (j0 + u < k) {
@@ -1275,11 +1290,14 @@ hipError_t launch_down(const FfnArgs& a, hipStream_t s) {
   return launch_gemm<DN_KSPLIT, false>(p, a.T, grid, s, a.w->format);
 }
 
-hipError_t launch_combine16(const f16* rows, int T, int H, int k, uint16_t* y, hipStream_t s, const float* add,
-                            int add_slabs) {
+bool rows16_sorted(int T) { return T >= BIG_MIN_T; }
+
+hipError_t launch_combine16(const f16* rows, const int32_t* pair_pos, int T, int H, int k, uint16_t* y,
+                            hipStream_t s, const float* add, int add_slabs) {
   const int threads = T < 64 ? 64 : 256;
-  hipLaunchKernelGGL(combine16_kernel, dim3((H / 4 + threads - 1) / threads, T), dim3(threads), 0, s, rows, H, k, y,
-                     add, add_slabs, (long long)T * H);
+  const int32_t* pos = rows16_sorted(T) ? pair_pos : nullptr;
+  hipLaunchKernelGGL(combine16_kernel, dim3((H / 4 + threads - 1) / threads, T), dim3(threads), 0, s, rows, pos, H,
+                     k, y, add, add_slabs, (long long)T * H);
   return hipGetLastError();
 }
 
