@@ -175,8 +175,8 @@ Layout layout(const moe_dims& d) {
   L.nact = take(4);
   L.mtiles = take((size_t)moe::max_mtiles(d) * 4);
   L.nmt = take(4);
-  L.x16 = take(T * H * 2);
-  L.h = take(P * I * 2);
+  L.x16 = take((T + 1) * H * 2);  // row T: zeros (the large-tile GEMMs' padding rows)
+  L.h = take((P + 1) * I * 2);    // row P: zeros
   L.rows = take(P * H * 4);
   L.total = o;
   return L;
@@ -357,6 +357,8 @@ moe_status enqueue_ffn(const moe_dims& d, const int32_t* offsets, const int32_t*
   a.rows = rows;
   a.rows16 = rows16;
   a.pair_w = pair_w;
+  if (moe::pads_with_zero_rows(a))  // (a one-block kernel, outside the timing hooks)
+    if (hipError_t e = moe::launch_zero_pad_rows(a, s); e != hipSuccess) return hip_fail(e, "zero rows");
   LAUNCH(MOE_KERNEL_GATEUP, s, moe::launch_gateup(a, s), "gate/up");
   LAUNCH(MOE_KERNEL_DOWN, s, moe::launch_down(a, s), "down");
   return MOE_OK;

@@ -67,6 +67,9 @@ hipError_t launch_remap_ids(const int32_t* ids, const int32_t* map, int E, int n
 struct FfnArgs {
   int T, H, I, E, k;
   int e_base;                     // first expert of the store (weights of e at e - e_base)
+  // x16 holds T + 1 rows and h P + 1: the last row of each is zeroed before
+  // the large-tile GEMMs (pads_with_zero_rows), whose token tiles fill their
+  // padding rows from it
   int max_active;                 // grid bound on the number of active experts
   const f16* x16;                 // [T][H]
   const int32_t* offsets;         // [E+1]
@@ -83,6 +86,8 @@ struct FfnArgs {
                                   // : record (t*k+j)
   const float* pair_w;            // routing weights [T*k] for rows16
 };
+bool pads_with_zero_rows(const FfnArgs& a);
+hipError_t launch_zero_pad_rows(const FfnArgs& a, hipStream_t s);
 hipError_t launch_gateup(const FfnArgs& a, hipStream_t s);
 hipError_t launch_down(const FfnArgs& a, hipStream_t s);
 // The down GEMM's weighted fp16 rows of T tokens are in sorted order (row p)

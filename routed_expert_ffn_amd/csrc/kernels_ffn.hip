@@ -33,11 +33,10 @@
 namespace moe {
 namespace {
 
-constexpr int FFN_THREADS = 256;
 constexpr int KCHUNK = 256;
 
 struct GroupedParams {
-  int H, I, k;
+  int T, H, I, k;
   int e_base;          // expert e's weights are entry e - e_base of the store
   const int32_t* offsets;
   const int32_t* sorted_pairs;
@@ -235,13 +234,14 @@ __device__ __forceinline__ void sq_pick(uint32_t (&w)[4], const uint32_t (&sq)[4
 // from memory in 64-byte pieces per row and group of four chunks instead,
 // every 128-byte line was fetched twice: its two halves are read some
 // microseconds apart, and by then the L2 no longer holds it.
+template <int NW>
 __device__ __forceinline__ void stage_scales(unsigned char* lds, const uint8_t* src, int bytes, int wv, int lane) {
   // src is the same in every lane (one block's piece); the DMA takes it in scalar registers
   const uint64_t sa = (uint64_t)(size_t)src;
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)sa), hi = __builtin_amdgcn_readfirstlane((uint32_t)(sa >> 32));
   src = reinterpret_cast<const uint8_t*>((size_t)(((uint64_t)hi << 32) | lo));
   const uint32_t dst = lds_addr(lds);
-  for (int i = __builtin_amdgcn_readfirstlane(wv); i * 1024 < bytes; i += FFN_THREADS / WAVE)
+  for (int i = __builtin_amdgcn_readfirstlane(wv); i * 1024 < bytes; i += NW)
     if (i * 1024 + 16 * lane < bytes) dma16(src, (uint32_t)(i * 1024 + 16 * lane), dst + (uint32_t)(i * 1024));
 }
 
@@ -323,10 +323,11 @@ __device__ __forceinline__ float silu(float z) {
 // looked up; each later chunk's loads are issued once the previous chunk has
 // been multiplied.  Partial sums of the KSPLIT wavefronts meet in LDS and
 // are added in a fixed order.
-template <int MF, int KSPLIT, bool GATEUP, int WAVES_PER_EU, int FMT, bool SLDS, bool R8>
-__global__ __launch_bounds__(FFN_THREADS, WAVES_PER_EU) void expert_gemm_kernel(GroupedParams p) {
-  constexpr int RT = 4 / KSPLIT;
-  __shared__ float red[KSPLIT > 1 ? 4 : 1][WAVE][MF * 16];
+template <int MF, int KSPLIT, bool GATEUP, int WAVES_PER_EU, int FMT, bool SLDS, bool R8, int NW = 4>
+__global__ __launch_bounds__(NW * WAVE, WAVES_PER_EU) void expert_gemm_kernel(GroupedParams p) {
+  constexpr int RT = NW / KSPLIT;
+  static_assert(NW % KSPLIT == 0, "whole row tiles per block");
+  __shared__ float red[KSPLIT > 1 ? NW : 1][WAVE][MF * 16];
   extern __shared__ __align__(16) unsigned char staged[];
   if ((int)blockIdx.y >= *p.n_active) return;
   const int e = p.active[blockIdx.y], el = e - p.e_base;
@@ -364,10 +365,10 @@ __global__ __launch_bounds__(FFN_THREADS, WAVES_PER_EU) void expert_gemm_kernel(
   if (SLDS) {
     const size_t r0 = (size_t)el * N + (size_t)blockIdx.x * RT * (GATEUP ? 32 : 64);
     if (GATEUP) {
-      stage_scales(staged, p.sf0 + r0 * SB, RT * 32 * SB, wv, lane);
-      stage_scales(staged + RT * 32 * SB, p.sf1 + r0 * SB, RT * 32 * SB, wv, lane);
+      stage_scales<NW>(staged, p.sf0 + r0 * SB, RT * 32 * SB, wv, lane);
+      stage_scales<NW>(staged + RT * 32 * SB, p.sf1 + r0 * SB, RT * 32 * SB, wv, lane);
     } else {
-      stage_scales(staged, p.sf0 + r0 * SB, RT * 64 * SB, wv, lane);
+      stage_scales<NW>(staged, p.sf0 + r0 * SB, RT * 64 * SB, wv, lane);
     }
 #pragma unroll
     for (int ng = 0; ng < 4; ng++)
@@ -1031,10 +1032,12 @@ __global__ __launch_bounds__(BIG_WAVES * WAVE, 1) void expert_gemm_big_kernel(Bi
   t.K = GATEUP ? p.H : p.I;
   t.N = GATEUP ? p.I : p.H;
   // source row (in units of K elements) of every token row of the tile;
-  // rows past the count repeat the last row
+  // rows past the count take the zero row after the last token row (x16 row
+  // T, h row T k): the padding MFMAs then multiply zeros, which costs the
+  // power-limited chip far less energy than real values
   for (int m = threadIdx.x; m < BIG_M; m += BIG_WAVES * WAVE) {
     const int pp = t.mb + min(m, t.nvalid - 1);
-    rowoff[m] = GATEUP ? p.sorted_pairs[pp] / p.k : pp;
+    rowoff[m] = m < t.nvalid ? (GATEUP ? p.sorted_pairs[pp] / p.k : pp) : (GATEUP ? p.T : p.T * p.k);
     if (!GATEUP && p.rows16) reinterpret_cast<float*>(big_smem + BIG_OFF_RW)[m] = p.pair_w[p.sorted_pairs[pp]];
   }
   __syncthreads();
@@ -1198,6 +1201,7 @@ __global__ __launch_bounds__(256) void combine_share_kernel(const float* __restr
 
 GroupedParams base_params(const FfnArgs& a) {
   GroupedParams p{};
+  p.T = a.T;
   p.H = a.H;
   p.I = a.I;
   p.k = a.k;
@@ -1228,19 +1232,19 @@ constexpr int GEMM_WAVES = 2;
 // down with NVFP4.  Larger K reads them from memory in groups of four chunks.
 constexpr int STAGE_MAX = 64 * 1024;
 
-template <int MF, int KSPLIT, bool GATEUP, int WAVES, int FMT, bool R8>
+template <int MF, int KSPLIT, bool GATEUP, int WAVES, int FMT, bool R8, int NW = 4>
 hipError_t launch_gemm_stage(const GroupedParams& p, dim3 grid, hipStream_t s) {
   const int K = GATEUP ? p.H : p.I;
-  const int bytes = (4 / KSPLIT) * 64 * (K / (FMT == FMT_MX ? 32 : 16));
+  const int bytes = (NW / KSPLIT) * 64 * (K / (FMT == FMT_MX ? 32 : 16));
   if (bytes <= STAGE_MAX) {
-    const void* f = reinterpret_cast<const void*>(&expert_gemm_kernel<MF, KSPLIT, GATEUP, WAVES, FMT, true, R8>);
+    const void* f = reinterpret_cast<const void*>(&expert_gemm_kernel<MF, KSPLIT, GATEUP, WAVES, FMT, true, R8, NW>);
     const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, STAGE_MAX);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((expert_gemm_kernel<MF, KSPLIT, GATEUP, WAVES, FMT, true, R8>), grid, dim3(FFN_THREADS), bytes,
-                       s, p);
+    hipLaunchKernelGGL((expert_gemm_kernel<MF, KSPLIT, GATEUP, WAVES, FMT, true, R8, NW>), grid, dim3(NW * WAVE),
+                       bytes, s, p);
   } else {
-    hipLaunchKernelGGL((expert_gemm_kernel<MF, KSPLIT, GATEUP, WAVES, FMT, false, R8>), grid, dim3(FFN_THREADS), 0, s,
-                       p);
+    hipLaunchKernelGGL((expert_gemm_kernel<MF, KSPLIT, GATEUP, WAVES, FMT, false, R8, NW>), grid, dim3(NW * WAVE), 0,
+                       s, p);
   }
   return hipGetLastError();
 }
@@ -1263,7 +1267,33 @@ hipError_t launch_gemm(const GroupedParams& p, int T, dim3 grid, hipStream_t s, 
                               : launch_gemm_fmt<KSPLIT, GATEUP, FMT_NV>(p, T, grid, s);
 }
 
+// Down GEMM of a single-pass batch (T <= 16) whose k <= 16 experts' H rows
+// split into 7 row tiles of 64 per block: blocks of seven wavefronts, H / 448
+// blocks per expert.  At 16 active experts and H = 7168 that is 256 blocks,
+// one per CU, each streaming the same bytes; blocks of four wavefronts (448
+// of them) leave 64 CUs with half the work of the others.
+constexpr int DN_WIDE_NW = 7;
+bool down_wide(const FfnArgs& a) {
+  return a.T <= 16 && a.H % (64 * DN_WIDE_NW) == 0 && (long long)a.max_active * (a.H / (64 * DN_WIDE_NW)) <= 256;
+}
+
+// The zero rows that the large-tile GEMMs' padding rows read: x16 row T
+// (H halves) and h row T k (I halves).
+__global__ __launch_bounds__(256) void zero_rows_kernel(f16* __restrict__ x_row, int H, f16* __restrict__ h_row,
+                                                       int I) {
+  for (int i = threadIdx.x; i < H / 8; i += 256) reinterpret_cast<uint4*>(x_row)[i] = make_uint4(0, 0, 0, 0);
+  for (int i = threadIdx.x; i < I / 8; i += 256) reinterpret_cast<uint4*>(h_row)[i] = make_uint4(0, 0, 0, 0);
+}
+
 }  // namespace
+
+bool pads_with_zero_rows(const FfnArgs& a) { return use_big(a); }
+
+hipError_t launch_zero_pad_rows(const FfnArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(zero_rows_kernel, dim3(1), dim3(256), 0, s, const_cast<f16*>(a.x16) + (size_t)a.T * a.H, a.H,
+                     a.h + (size_t)a.T * a.k * a.I, a.I);
+  return hipGetLastError();
+}
 
 hipError_t launch_gateup(const FfnArgs& a, hipStream_t s) {
   GroupedParams p = base_params(a);
@@ -1286,6 +1316,12 @@ hipError_t launch_down(const FfnArgs& a, hipStream_t s) {
   p.sf0 = a.w->down.sf;
   p.gs0 = a.w->down.gs;
   if (use_big(a)) return launch_big<false>(a, p, s);
+  if (down_wide(a)) {
+    const dim3 grid(a.H / (64 * DN_WIDE_NW), a.max_active);
+    return a.w->format == MOE_FMT_MXFP4
+               ? launch_gemm_stage<1, 1, false, GEMM_WAVES, FMT_MX, true, DN_WIDE_NW>(p, grid, s)
+               : launch_gemm_stage<1, 1, false, GEMM_WAVES, FMT_NV, true, DN_WIDE_NW>(p, grid, s);
+  }
   const dim3 grid(a.H / (64 * (4 / DN_KSPLIT)), a.max_active);
   return launch_gemm<DN_KSPLIT, false>(p, a.T, grid, s, a.w->format);
 }
