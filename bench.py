@@ -12,7 +12,9 @@ experts and reads their weights cold, as a decode step of a real model does.
 The headline (`value`) is the prefill chunk, T = 8192: the largest workload,
 bound by the matrix cores; its roofline is the grouped gate/up GEMM's MFMA
 rate against the dense fp16 peak (and, as `frac_fp8`, against the dense FP8
-peak).  In the same process and on the same resident store, `configs` times
+peak, and, as `frac_of_sustained`, against what the library's calibration
+kernel measures the fp16 matrix cores to sustain on this GPU under its power
+limit, on operands with the GEMMs' value patterns).  In the same process and on the same resident store, `configs` times
 the decode-sized workloads (single-user decode, 64-session decode,
 speculative verify), which are bound by HBM: layer tokens/s, the gate/up
 kernel's achieved bandwidth and the layer's algorithmic bytes per second,
@@ -122,6 +124,24 @@ def stream_read_GBps(moe, torch, region_bytes=256 << 20, regions=16):
     return float(sorted(rates)[len(rates) // 2])
 
 
+def mfma_sustained_TFLOPs(moe, torch, iters=16000, runs=5):
+    """What the fp16 matrix cores sustain on this GPU under its power limit,
+    on operands with the expert GEMMs' value patterns: the library's
+    calibration kernel (iters * MFMA_RATE_FLOPS_PER_ITER flops a call, about
+    12 ms), median over the runs after one untimed call."""
+    sink = torch.zeros(moe.MFMA_RATE_BLOCKS, dtype=torch.float32, device="cuda")
+    moe.moe_mfma_rate(iters // 8, sink)
+    rates = []
+    for _ in range(runs):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        moe.moe_mfma_rate(iters, sink)
+        b.record()
+        b.synchronize()
+        rates.append(iters * moe.MFMA_RATE_FLOPS_PER_ITER / (a.elapsed_time(b) * 1e-3) / 1e12)
+    return float(sorted(rates)[len(rates) // 2])
+
+
 def load_traffic(workload, sha):
     """HBM traffic of the gate/up kernel per launch, from the committed
     rocprofv3 counter summary, if it was taken on this kernel source."""
@@ -199,6 +219,7 @@ class Bench:
         torch.cuda.synchronize()
         self.setup_s = time.perf_counter() - t0
         self.stream_peak = stream_read_GBps(moe, torch)
+        self.mfma_sustained = mfma_sustained_TFLOPs(moe, torch)
         self.sha = kernel_source_sha()
 
     def run(self, wl, steps, warmup, headline):
@@ -388,6 +409,8 @@ def main():
         roofline = {"bound": "mfma", "achieved": tf, "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(tf / FP16_MFMA_PEAK_TFLOPS, 4), "traffic": gu["traffic"],
                     "peak_fp8": FP8_MFMA_PEAK_TFLOPS, "frac_fp8": round(tf / FP8_MFMA_PEAK_TFLOPS, 4),
+                    "sustained_TFLOPs": round(B.mfma_sustained, 1),
+                    "frac_of_sustained": round(tf / B.mfma_sustained, 4),
                     "kernel": "gateup_kernel (grouped gate/up + SiLU*mul, fp16 MFMA on exactly dequantised NVFP4)",
                     "algorithmic_flops_per_launch": gu["algorithmic_flops_per_launch"],
                     "avg_launch_ms": gu["avg_launch_ms"], "timed_launches": gu["timed_launches"],
@@ -398,7 +421,8 @@ def main():
                     "kernel": "gateup_kernel (grouped gate/up + SiLU*mul)",
                     "algorithmic_bytes_per_launch": gu["algorithmic_bytes_per_launch"],
                     "avg_launch_ms": gu["avg_launch_ms"], "timed_launches": gu["timed_launches"],
-                    "stream_read_GBps": round(B.stream_peak, 1), "frac_of_stream_read": gu["frac_of_stream_read"]}
+                    "stream_read_GBps": round(B.stream_peak, 1),
+        "mfma_sustained_TFLOPs": round(B.mfma_sustained, 1), "frac_of_stream_read": gu["frac_of_stream_read"]}
     out = {
         "metric": METRIC,
         "value": head["tokens_per_s"],
@@ -420,6 +444,7 @@ def main():
         "roofline": roofline,
         "layer": head["layer"],
         "stream_read_GBps": round(B.stream_peak, 1),
+        "mfma_sustained_TFLOPs": round(B.mfma_sustained, 1),
         "setup_s": round(B.setup_s, 2),
         "kernel_source_sha": B.sha,
     }

@@ -424,6 +424,25 @@ int moe_profile_read(float* ms, int max);
 #define MOE_STREAM_SINK_WORDS 4096
 moe_status moe_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
+/* ---- matrix-core calibration --------------------------------------------------
+ * The prefill chunk is bound by the chip's power limit: at it the fp16
+ * matrix cores run far below the datasheet peak, at a rate that depends on
+ * how much the operand bits toggle.  This call measures what they sustain
+ * on operands with the expert GEMMs' value patterns (bf16-valued
+ * activations, e2m1 x e4m3 weights, generated in the kernel), so that
+ * bench.py can set the prefill GEMMs' rate against it as well as against
+ * the datasheet.  It enqueues on `stream` one kernel of MOE_MFMA_RATE_BLOCKS
+ * blocks of eight wavefronts; each wavefront runs `iters` rounds of four
+ * v_mfma_f32_32x32x16_f16 (32768 flops each) on operands held in registers,
+ * so one call performs iters * MOE_MFMA_RATE_FLOPS_PER_ITER floating-point
+ * operations, and writes one checksum per block to sink[0 ..
+ * MOE_MFMA_RATE_BLOCKS-1] (fp32, device memory).  Returns MOE_OK,
+ * MOE_ERR_ARG (NULL sink, iters outside [1, 10^7]), MOE_ERR_ALIGN or
+ * MOE_ERR_HIP. */
+#define MOE_MFMA_RATE_BLOCKS 1024
+#define MOE_MFMA_RATE_FLOPS_PER_ITER (1024.0 * 8.0 * 4.0 * 32768.0)
+moe_status moe_mfma_rate(int iters, float* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

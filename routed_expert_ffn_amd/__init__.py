@@ -23,12 +23,15 @@ EXPORTS = ("moe_workspace_bytes", "moe_quantize_workspace_bytes", "moe_quantize_
            "moe_profile_read", "moe_stream_read", "moe_latent_workspace_bytes", "moe_latent_layer",
            "moe_expert_ffn_share", "moe_layer_share", "moe_layer_shared_workspace_bytes", "moe_layer_shared",
            "moe_quantize_mxfp4", "moe_permute", "moe_layer_mapped",
-           "moe_layer_noalloc")
+           "moe_layer_noalloc", "moe_mfma_rate")
 FORMATS = {"nvfp4": 0, "mxfp4": 1}  # moe_weight_format
 # MOE_STREAM_SINK_WORDS of moe.h
 STREAM_SINK_WORDS = 4096
 # MOE_NOALLOC_SCRATCH_BYTES of moe.h
 NOALLOC_SCRATCH_BYTES = 64 << 20
+# MOE_MFMA_RATE_BLOCKS and MOE_MFMA_RATE_FLOPS_PER_ITER of moe.h
+MFMA_RATE_BLOCKS = 1024
+MFMA_RATE_FLOPS_PER_ITER = 1024 * 8 * 4 * 32768
 
 
 class MoeError(RuntimeError):
@@ -119,6 +122,8 @@ def lib():
         L.moe_profile_arm.argtypes = [ctypes.c_int, ctypes.c_int]
         L.moe_profile_read.restype = ctypes.c_int
         L.moe_profile_read.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_int]
+        L.moe_mfma_rate.restype = ctypes.c_int
+        L.moe_mfma_rate.argtypes = [ctypes.c_int, _p, _p]
         L.moe_stream_read.restype = ctypes.c_int
         L.moe_stream_read.argtypes = [_p, ctypes.c_size_t, _p, _p]
         _lib = L
@@ -277,6 +282,15 @@ def moe_stream_read(buf, sink, stream=None):
     if sink.numel() * sink.element_size() < STREAM_SINK_WORDS * 4:
         raise ValueError("sink holds fewer than STREAM_SINK_WORDS words")
     _check(lib().moe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)))
+
+
+def moe_mfma_rate(iters, sink, stream=None):
+    """Enqueue the matrix-core calibration kernel: iters * MFMA_RATE_FLOPS_PER_ITER
+    flops; per-block checksums to sink (a device tensor of at least
+    MFMA_RATE_BLOCKS fp32 values)."""
+    if sink.numel() * sink.element_size() < MFMA_RATE_BLOCKS * 4:
+        raise ValueError("sink holds fewer than MFMA_RATE_BLOCKS words")
+    _check(lib().moe_mfma_rate(int(iters), _ptr(sink), _stream(stream)))
 
 
 def moe_profile_read(max_launches):

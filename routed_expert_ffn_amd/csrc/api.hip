@@ -845,6 +845,15 @@ moe_status moe_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* 
   return MOE_OK;
 }
 
+moe_status moe_mfma_rate(int iters, float* sink, void* stream) {
+  if (!sink) return fail(MOE_ERR_ARG, "sink must not be NULL");
+  if (iters < 1 || iters > 10000000) return fail(MOE_ERR_ARG, "iters = %d must be in [1, 10^7]", iters);
+  if ((uintptr_t)sink & 3u) return fail(MOE_ERR_ALIGN, "sink is not 4-byte aligned");
+  hipError_t e = moe::launch_mfma_rate(iters, sink, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "mfma rate");
+  return MOE_OK;
+}
+
 const char* moe_status_string(moe_status s) {
   switch (s) {
     case MOE_OK: return "ok";

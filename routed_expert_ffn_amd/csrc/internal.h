@@ -109,6 +109,9 @@ hipError_t launch_combine_share(const float* rows, const int32_t* pair_pos, cons
 // STREAM_SINK_WORDS per-block XOR words.
 constexpr int STREAM_SINK_WORDS = MOE_STREAM_SINK_WORDS;
 hipError_t launch_stream_read(const void* buf, long long bytes, uint32_t* sink, hipStream_t s);
+// Sustained fp16 MFMA on the expert GEMMs' value patterns: MOE_MFMA_RATE_BLOCKS
+// blocks of eight wavefronts, `iters` rounds of four MFMAs each.
+hipError_t launch_mfma_rate(int iters, float* sink, hipStream_t s);
 
 // x [T][K] . w [K][N] (bf16, input-major) into out [T][N] bf16 and, if
 // out16 is non-NULL, its fp16 copy; part holds rp.slabs * T * N fp32.

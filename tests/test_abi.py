@@ -229,3 +229,11 @@ def test_token_bounds_without_hip():
     assert moe.moe_workspace_bytes(moe.dims(16383, 512, 2048, 1024, 64)) > 0
     d = moe.dims(16384, 512, 2048, 1024, 64)
     assert _route(d, ws_bytes=1 << 40) == 2
+
+
+def test_mfma_rate_validation_without_hip():
+    L = moe.lib()
+    assert L.moe_mfma_rate(100, None, None) == 1
+    assert L.moe_mfma_rate(0, FAKE, None) == 1
+    assert L.moe_mfma_rate(10 ** 7 + 1, FAKE, None) == 1
+    assert L.moe_mfma_rate(100, FAKE + 2, None) == 3

@@ -154,3 +154,24 @@ def test_latent_layer_graph_replays_match_eager(T, E, k):
         for got, want in zip(o, ref):
             assert torch.equal(got.cpu(), want), f"replay {replay}"
         assert not torch.equal(oo[0].cpu(), ref[0])
+
+
+def test_mfma_rate_calibration():
+    """moe_mfma_rate runs its MFMA rounds and leaves finite, non-zero
+    per-block checksums; its rate is plausible for the chip (between a tenth
+    of the datasheet peak and the peak)."""
+    sink = torch.full((moe.MFMA_RATE_BLOCKS,), float("nan"), dtype=torch.float32, device=DEV)
+    moe.moe_mfma_rate(200, sink)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    moe.moe_mfma_rate(4000, sink)
+    b.record()
+    b.synchronize()
+    tf = 4000 * moe.MFMA_RATE_FLOPS_PER_ITER / (a.elapsed_time(b) * 1e-3) / 1e12
+    say(f"  sustained fp16 MFMA: {tf:.0f} TFLOP/s")
+    v = sink.cpu()
+    assert torch.isfinite(v).all() and (v != 0).all()
+    assert 250 < tf <= 2500
+    with pytest.raises(moe.MoeError):
+        moe.moe_mfma_rate(0, sink)
