@@ -1272,9 +1272,13 @@ hipError_t launch_gemm(const GroupedParams& p, int T, dim3 grid, hipStream_t s, 
 // blocks per expert.  At 16 active experts and H = 7168 that is 256 blocks,
 // one per CU, each streaming the same bytes; blocks of four wavefronts (448
 // of them) leave 64 CUs with half the work of the others.
+// Only where the block's scales fit the LDS staging (I up to 2304 for NVFP4):
+// reading them from memory instead costs more than the balance gains.
 constexpr int DN_WIDE_NW = 7;
 bool down_wide(const FfnArgs& a) {
-  return a.T <= 16 && a.H % (64 * DN_WIDE_NW) == 0 && (long long)a.max_active * (a.H / (64 * DN_WIDE_NW)) <= 256;
+  const int scale_bytes = DN_WIDE_NW * 64 * (a.I / (a.w->format == MOE_FMT_MXFP4 ? 32 : 16));
+  return a.T <= 16 && a.H % (64 * DN_WIDE_NW) == 0 && (long long)a.max_active * (a.H / (64 * DN_WIDE_NW)) <= 256 &&
+         scale_bytes <= STAGE_MAX;
 }
 
 // The zero rows that the large-tile GEMMs' padding rows read: x16 row T
