@@ -260,6 +260,26 @@ __device__ __forceinline__ float wave_sum(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+// Inclusive scan over the 64 lanes with DPP lane moves: three row shifts
+// (1, 2, 3) of the input give each lane the sum of its quad-aligned run of
+// four; shifts by 4 and 8 (upper banks only) complete each row of 16; row
+// broadcasts 15 and 31 carry the row totals into the rows above.  Lanes
+// without a source add 0.
+template <int CTRL, int ROW_MASK = 0xf, int BANK_MASK = 0xf>
+__device__ __forceinline__ int dpp_int(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, BANK_MASK, false);
+}
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  int v = x + dpp_int<0x111>(x);
+  v += dpp_int<0x112>(x);
+  v += dpp_int<0x113>(x);
+  v += dpp_int<0x114, 0xf, 0xe>(v);
+  v += dpp_int<0x118, 0xf, 0xc>(v);
+  v += dpp_int<0x142, 0xa, 0xf>(v);
+  v += dpp_int<0x143, 0xc, 0xf>(v);
+  return v;
+}
+
 __device__ __forceinline__ void cas_desc(uint64_t& a, uint64_t& b) {
   const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
   a = hi;
@@ -288,8 +308,9 @@ constexpr int TOPK_THREADS = 1024;
 
 // One wavefront: the top k of E logits (LDS) and their renormalised softmax
 // weights, written to ids[0..k) / w[0..k) (and ids_copy, if given).
-__device__ __forceinline__ void select_topk(const float* ls, int E, int k, int32_t* __restrict__ ids, float* __restrict__ w,
-                            int32_t* ids_copy) {
+// Returns lane j's id (j < k), -1 in the other lanes.
+__device__ __forceinline__ int select_topk(const float* ls, int E, int k, int32_t* __restrict__ ids, float* __restrict__ w,
+                                           int32_t* ids_copy) {
   const int lane = threadIdx.x % WAVE;
   uint64_t key[TOPK_KEYS];
 #pragma unroll
@@ -323,6 +344,7 @@ __device__ __forceinline__ void select_topk(const float* ls, int E, int k, int32
     w[lane] = ex / sum;
     if (ids_copy) ids_copy[lane] = my_id;
   }
+  return lane < k ? my_id : -1;
 }
 
 // ---- top-k of one token by one wavefront, by filtering ---------------------------
@@ -335,17 +357,20 @@ __device__ __forceinline__ void select_topk(const float* ls, int E, int k, int32
 //      with hi >= tau, so at least k keys have hi >= tau, and since a larger
 //      hi means a larger key, every key of the top k has hi >= tau;
 //   3. the keys with hi >= tau (the candidates, a few more than k for
-//      ordinary logits) are gathered in LDS in ascending expert order, one
-//      ballot per i;
+//      ordinary logits) are gathered in LDS: each lane counts its own, a
+//      wavefront prefix sum of the counts gives each lane its first slot,
+//      and every key is written, a non-candidate to a spare slot of its lane
+//      (no branch);
 //   4. a candidate's rank is the number of larger candidates (keys are
 //      unique: the index is part of the key).
 // Winners are placed at lane = rank and weighted as in select_topk, so the
 // results are the same bit for bit.  More than 64 candidates (heavy ties)
 // fall back to select_topk.  No block barrier is involved: the lanes of a
 // wavefront exchange values through LDS, whose operations complete in issue
-// order for one wavefront.
+// order for one wavefront.  The reads of the 64 maxima and of the
+// candidates go eight at a time, with one wait.
 struct WaveTopkLds {
-  uint64_t cand[WAVE];
+  uint64_t cand[2 * WAVE];  // slots 0..63 candidates, 64 + l lane l's spare
   uint32_t m[WAVE];
   float out_l[WAVE];
   int out_e[WAVE];
@@ -353,9 +378,30 @@ struct WaveTopkLds {
 
 // Keeps the compiler from moving this wavefront's LDS accesses across.
 __device__ __forceinline__ void wave_lds_order() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
+// Eight 16-byte LDS reads of p[0..128) issued back to back, and one wait
+// for all of them in the same block (the compiler would otherwise issue two
+// at a time, waiting between).
+typedef unsigned int u32x4n __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void lds_read8(const void* p, u32x4n (&q)[8]) {
+  const uint32_t a = (uint32_t)(size_t)(const __attribute__((address_space(3))) unsigned char*)p;
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %8 offset:16\n\t"
+      "ds_read_b128 %2, %8 offset:32\n\t"
+      "ds_read_b128 %3, %8 offset:48\n\t"
+      "ds_read_b128 %4, %8 offset:64\n\t"
+      "ds_read_b128 %5, %8 offset:80\n\t"
+      "ds_read_b128 %6, %8 offset:96\n\t"
+      "ds_read_b128 %7, %8 offset:112\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(q[0]), "=&v"(q[1]), "=&v"(q[2]), "=&v"(q[3]), "=&v"(q[4]), "=&v"(q[5]), "=&v"(q[6]), "=&v"(q[7])
+      : "v"(a)
+      : "memory");
+}
 
-__device__ __forceinline__ void wave_topk(const float* ls, int E, int k, int32_t* __restrict__ ids,
-                                          float* __restrict__ w, int32_t* ids_copy, WaveTopkLds& S) {
+// Returns lane j's id (j < k), -1 in the other lanes.
+__device__ __forceinline__ int wave_topk(const float* ls, int E, int k, int32_t* __restrict__ ids,
+                                         float* __restrict__ w, int32_t* ids_copy, WaveTopkLds& S) {
   const int lane = threadIdx.x % WAVE;
   const int n = (E + WAVE - 1) / WAVE;
   // ls holds 1024 entries: all reads are issued together, the ones past E
@@ -374,38 +420,37 @@ __device__ __forceinline__ void wave_topk(const float* ls, int E, int k, int32_t
   wave_lds_order();
   int above = 0;
 #pragma unroll
-  for (int j = 0; j < WAVE; j += 4) {
-    const uint4 q = *reinterpret_cast<const uint4*>(&S.m[j]);
-    above += (q.x > m ? 1 : 0) + (q.y > m ? 1 : 0) + (q.z > m ? 1 : 0) + (q.w > m ? 1 : 0);
+  for (int h = 0; h < 2; h++) {
+    u32x4n q[8];
+    lds_read8(&S.m[32 * h], q);
+#pragma unroll
+    for (int u = 0; u < 8; u++)
+      above += (q[u][0] > m ? 1 : 0) + (q[u][1] > m ? 1 : 0) + (q[u][2] > m ? 1 : 0) + (q[u][3] > m ? 1 : 0);
   }
   // smallest maximum with fewer than k maxima above it (a max of inverted values)
   const uint32_t tau = ~wave_max_u32(above < k ? ~m : 0u);
-  int total = 0;
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < TOPK_KEYS; i++) cnt += (i < n && hi[i] >= tau) ? 1 : 0;
+  const int incl = wave_inclusive_scan(cnt);
+  const int total = __builtin_amdgcn_readlane(incl, WAVE - 1);
+  if (total > WAVE) return select_topk(ls, E, k, ids, w, ids_copy);
+  int slot = incl - cnt;
 #pragma unroll
   for (int i = 0; i < TOPK_KEYS; i++) {
-    if (i < n) {
-      const bool c = hi[i] >= tau;
-      const uint64_t b = __ballot(c);
-      const int below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
-      const int pos = total + below;
-      if (c && pos < WAVE) S.cand[pos] = ((uint64_t)hi[i] << 32) | (uint32_t)~(uint32_t)(lane + WAVE * i);
-      total += __popcll(b);
-    }
-  }
-  if (total > WAVE) {
-    select_topk(ls, E, k, ids, w, ids_copy);
-    return;
+    const bool c = i < n && hi[i] >= tau;
+    S.cand[c ? slot : WAVE + lane] = ((uint64_t)hi[i] << 32) | (uint32_t)~(uint32_t)(lane + WAVE * i);
+    slot += c ? 1 : 0;
   }
   wave_lds_order();
   const uint64_t mine = lane < total ? S.cand[lane] : 0ull;
   int rank = 0;
   for (int j0 = 0; j0 < total; j0 += 16) {  // 16 keys (8 reads) at a time, all 64 slots in bounds
-    uint4 q[8];
-#pragma unroll
-    for (int u = 0; u < 8; u++) q[u] = *reinterpret_cast<const uint4*>(&S.cand[j0 + 2 * u]);
+    u32x4n q[8];
+    lds_read8(&S.cand[j0], q);
 #pragma unroll
     for (int u = 0; u < 8; u++) {
-      const uint64_t a = ((uint64_t)q[u].y << 32) | q[u].x, b = ((uint64_t)q[u].w << 32) | q[u].z;
+      const uint64_t a = ((uint64_t)q[u][1] << 32) | q[u][0], b = ((uint64_t)q[u][3] << 32) | q[u][2];
       rank += (j0 + 2 * u < total && a > mine ? 1 : 0) + (j0 + 2 * u + 1 < total && b > mine ? 1 : 0);
     }
   }
@@ -416,14 +461,15 @@ __device__ __forceinline__ void wave_topk(const float* ls, int E, int k, int32_t
   wave_lds_order();
   const float l = lane < k ? S.out_l[lane] : 0.0f;
   const float top = S.out_l[0];
+  const int e = lane < k ? S.out_e[lane] : -1;
   const float ex = lane < k ? expf(l - top) : 0.0f;
   const float sum = wave_sum(ex);
   if (lane < k) {
-    const int e = S.out_e[lane];
     ids[lane] = e;
     w[lane] = ex / sum;
     if (ids_copy) ids_copy[lane] = e;
   }
+  return e;
 }
 
 // Logits of the consecutive tokens row0 .. row0+nrows-1 (a contiguous run of
@@ -496,7 +542,8 @@ __device__ __forceinline__ void logits_rows(const float* __restrict__ part, int 
 // up to 256 pieces (one token at E = 1024) and 32 slabs.
 __device__ __forceinline__ void logits_rows_grouped(const float* __restrict__ part, int slabs, size_t slab_stride,
                                                     const float* __restrict__ bias, float* __restrict__ logits,
-                                                    float* ls, int row0, int nrows, int E, float4* gsum) {
+                                                    float* ls, int row0, int nrows, int E, float4* gsum,
+                                                    bool store_logits = true) {
   const int n4 = nrows * E / 4;  // E % 8 == 0
   const size_t base = (size_t)row0 * E;
   const int g = threadIdx.x / 256, ql = threadIdx.x % 256;
@@ -542,7 +589,7 @@ __device__ __forceinline__ void logits_rows_grouped(const float* __restrict__ pa
           v.z += bb.z;
           v.w += bb.w;
         }
-        *reinterpret_cast<float4*>(logits + base + 4 * q) = v;
+        if (store_logits) *reinterpret_cast<float4*>(logits + base + 4 * q) = v;
         *reinterpret_cast<float4*>(ls + (4 * q / E) * 1024 + e) = v;
       }
       __syncthreads();
@@ -584,26 +631,6 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(const float* __restr
 // popcount of the mask bits below l.  Integer work only: exact and
 // deterministic.
 constexpr int PERM_MAX_E = 1024;
-
-// Inclusive scan over the 64 lanes with DPP lane moves: three row shifts
-// (1, 2, 3) of the input give each lane the sum of its quad-aligned run of
-// four; shifts by 4 and 8 (upper banks only) complete each row of 16; row
-// broadcasts 15 and 31 carry the row totals into the rows above.  Lanes
-// without a source add 0.
-template <int CTRL, int ROW_MASK = 0xf, int BANK_MASK = 0xf>
-__device__ __forceinline__ int dpp_int(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, BANK_MASK, false);
-}
-__device__ __forceinline__ int wave_inclusive_scan(int x) {
-  int v = x + dpp_int<0x111>(x);
-  v += dpp_int<0x112>(x);
-  v += dpp_int<0x113>(x);
-  v += dpp_int<0x114, 0xf, 0xe>(v);
-  v += dpp_int<0x118, 0xf, 0xc>(v);
-  v += dpp_int<0x142, 0xa, 0xf>(v);
-  v += dpp_int<0x143, 0xc, 0xf>(v);
-  return v;
-}
 
 // Block-wide exclusive scan of one int per thread (blockDim.x = 1024, lds
 // 16-byte aligned).
@@ -723,7 +750,12 @@ __global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t* __restr
 // T <= ROUTE_SMALL_T: the whole routing in one block of 1024 threads (one
 // launch instead of three): logits from the slab partials (or the caller's
 // logits), top-k and weights (wave_topk, wavefront t for token t), then the
-// permutation and the active-expert list.
+// permutation and the active-expert list.  The logits reach memory from
+// wavefronts that select nothing (wavefront 0 never waits on those stores).
+// One token: its k experts are distinct, so a record's sorted position is
+// the number of selected ids below its own, and offsets[e] the number below
+// e; wavefront 0 places the records right after selecting them, and a
+// single barrier later every thread writes its experts' offsets.
 constexpr int ROUTE_SMALL_T = 8;
 
 __global__ __launch_bounds__(1024) void route_small_kernel(const float* __restrict__ part, int slabs,
@@ -735,17 +767,52 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const float* __restri
                                                           int32_t* __restrict__ active,
                                                           int32_t* __restrict__ n_active) {
   __shared__ __attribute__((aligned(16))) float ls[ROUTE_SMALL_T * PERM_MAX_E];
-  __shared__ int ids_s[ROUTE_SMALL_T * 64];
+  __shared__ __attribute__((aligned(16))) int ids_s[ROUTE_SMALL_T * 64];
   __shared__ unsigned long long m[PERM_MAX_E];
   __shared__ int off_s[PERM_MAX_E];
   __shared__ __attribute__((aligned(16))) int lds[16];
   __shared__ __attribute__((aligned(16))) WaveTopkLds tk[ROUTE_SMALL_T];
   __shared__ float4 gsum[1024];
   const int tid = threadIdx.x;
-  if (tid < E) m[tid] = 0ull;
-  logits_rows_grouped(part, slabs, (size_t)T * E, bias, logits, ls, 0, T, E, gsum);
+  if (T > 1 && tid < E) m[tid] = 0ull;
+  logits_rows_grouped(part, slabs, (size_t)T * E, bias, logits, ls, 0, T, E, gsum, false);
   __syncthreads();
-  const int wv = tid / WAVE;
+  const int wv = tid / WAVE, lane = tid % WAVE;
+  if (part && wv >= ROUTE_SMALL_T)  // the logits out to memory (E % 8 == 0)
+    for (int q = tid - ROUTE_SMALL_T * WAVE; q < T * E / 4; q += 1024 - ROUTE_SMALL_T * WAVE)
+      reinterpret_cast<float4*>(logits)[q] = *reinterpret_cast<const float4*>(ls + (4 * q / E) * PERM_MAX_E + 4 * q % E);
+  if (T == 1) {
+    if (wv == 0) {
+      const int e = wave_topk(ls, E, k, ids, wout, ids_s, tk[0]);
+      wave_lds_order();
+      int pos = 0;
+      for (int j0 = 0; j0 < k; j0 += 4) {  // ids_s holds 64 entries: reads past k are discarded
+        const int4 v = *reinterpret_cast<const int4*>(ids_s + j0);
+        pos += (v.x < e ? 1 : 0) + (j0 + 1 < k && v.y < e ? 1 : 0) + (j0 + 2 < k && v.z < e ? 1 : 0) +
+               (j0 + 3 < k && v.w < e ? 1 : 0);
+      }
+      if (lane < k) {
+        sorted_pairs[pos] = lane;
+        pair_pos[lane] = pos;
+        active[pos] = e;
+      }
+      if (lane == 0) {
+        *n_active = k;
+        offsets[E] = k;
+      }
+    }
+    __syncthreads();
+    if (tid < E) {
+      int below = 0;
+      for (int j0 = 0; j0 < k; j0 += 4) {
+        const int4 v = *reinterpret_cast<const int4*>(ids_s + j0);
+        below += (v.x < tid ? 1 : 0) + (j0 + 1 < k && v.y < tid ? 1 : 0) + (j0 + 2 < k && v.z < tid ? 1 : 0) +
+                 (j0 + 3 < k && v.w < tid ? 1 : 0);
+      }
+      offsets[tid] = below;
+    }
+    return;
+  }
   if (wv < T)
     wave_topk(ls + wv * PERM_MAX_E, E, k, ids + (size_t)wv * k, wout + (size_t)wv * k, ids_s + wv * k, tk[wv]);
   __syncthreads();

@@ -178,12 +178,13 @@ def test_ragged_layer(T, E, k, beta):
     assert_close(y, ref["y"], "y")
 
 
-@pytest.mark.parametrize("T", [3, 70, 1030])
+@pytest.mark.parametrize("T", [1, 3, 70, 1030])
 def test_largest_expert_count_and_k(T):
     """The largest shapes the routing takes: E = 1024 experts and k = 64
     (16 keys per lane in the top-k; a token's 64 records; more than 64
     top-k candidates send some tokens through the fallback selection), in
-    the single-launch routing (T = 3), the single-block permutation
+    the single-launch routing (T = 1, whose permutation ranks the selected
+    ids directly, and T = 3), the single-block permutation
     (T = 70) and the multi-block permutation with the large-tile GEMMs
     (T = 1030); outputs checked on sampled tokens."""
     E, k, H, I = 1024, 64, 512, 256
@@ -265,34 +266,37 @@ def test_large_tiles_many_spans(T, H, I, E, k):
     assert_close(y, ref["y"], "y")
 
 
-@pytest.mark.parametrize("T", [6, 40, 100])
+@pytest.mark.parametrize("T", [1, 6, 40, 100])
 def test_route_ties_logits_in(T):
     """Constructed fp32 logits with exact ties (all equal, +-0, duplicated
     values, more tied maxima than a wavefront has lanes): the selection must
-    follow (logit desc, index asc) bit-exactly.  T = 6, 40 and 100 run the
-    single-launch routing, the one-block-per-token and the four-tokens-per-
-    block top-k kernels."""
+    follow (logit desc, index asc) bit-exactly.  T = 1 and 6 run the
+    single-launch routing (T = 1: all 896 logits equal, the fallback
+    selection and the single-token permutation), T = 40 and 100 the
+    one-block-per-token and the four-tokens-per-block top-k kernels."""
     E, k = 896, 16
     say(f"ties T={T}")
     rng = np.random.default_rng(2)
     L = rng.normal(0, 1.7, size=(T, E)).astype(np.float32)
     L[0] = 0.0
-    L[1, ::2] = -0.0
-    L[1, 1::2] = 0.0
-    L[2] = np.round(L[2])
-    L[3, 500:530] = 7.0
-    L[4] = -3.0
-    L[4, 895] = -2.0
-    L[5, 100:170] = 9.0
+    if T > 1:
+        L[1, ::2] = -0.0
+        L[1, 1::2] = 0.0
+        L[2] = np.round(L[2])
+        L[3, 500:530] = 7.0
+        L[4] = -3.0
+        L[4, 895] = -2.0
+        L[5, 100:170] = 9.0
     inp = Inputs(T, 256, 256, E, k, seed=1, store=build_store(E, 256, 256, 1, experts=[]))
     r = inp.route(logits_in=L)
     np.testing.assert_array_equal(r["logits"], L)
     check_route(inp, r)
     np.testing.assert_array_equal(r["ids"][0], np.arange(16))
-    np.testing.assert_array_equal(r["ids"][1], np.arange(16))
-    np.testing.assert_array_equal(r["ids"][3], np.arange(500, 516))
-    assert r["ids"][4][0] == 895 and list(r["ids"][4][1:]) == list(range(15))
-    np.testing.assert_array_equal(r["ids"][5], np.arange(100, 116))
+    if T > 1:
+        np.testing.assert_array_equal(r["ids"][1], np.arange(16))
+        np.testing.assert_array_equal(r["ids"][3], np.arange(500, 516))
+        assert r["ids"][4][0] == 895 and list(r["ids"][4][1:]) == list(range(15))
+        np.testing.assert_array_equal(r["ids"][5], np.arange(100, 116))
 
 
 def test_all_tokens_to_the_same_experts():
