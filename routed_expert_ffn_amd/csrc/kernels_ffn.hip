@@ -329,8 +329,14 @@ __global__ __launch_bounds__(NW * WAVE, WAVES_PER_EU) void expert_gemm_kernel(Gr
   static_assert(NW % KSPLIT == 0, "whole row tiles per block");
   __shared__ float red[KSPLIT > 1 ? NW : 1][WAVE][MF * 16];
   extern __shared__ __align__(16) unsigned char staged[];
-  if ((int)blockIdx.y >= *p.n_active) return;
-  const int e = p.active[blockIdx.y], el = e - p.e_base;
+  // both loads issued before either is waited for (the empty asm takes the
+  // id before the test; the compiler would otherwise load it only after);
+  // active has gridDim.y entries, and an id past n_active is never used
+  const int n_act = *p.n_active;
+  const int e = p.active[blockIdx.y];
+  asm volatile("" ::"s"(e));
+  if ((int)blockIdx.y >= n_act) return;
+  const int el = e - p.e_base;
   const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE, r = lane % 16, g = lane / 16;
   const int rt = wv / KSPLIT, ks = wv % KSPLIT;
   const int K = GATEUP ? p.H : p.I;
@@ -411,12 +417,27 @@ __global__ __launch_bounds__(NW * WAVE, WAVES_PER_EU) void expert_gemm_kernel(Gr
       }
       load_a(cur, arow, c_lo * KCHUNK + 64 * g, nvalid);
     }
+    // weighted fp16 rows: each output row's record and its routing weight,
+    // loaded here so that their two dependent round trips overlap the K loop
+    // (in the epilogue they stalled every block for both)
+    int rec_pf[MF][4];
+    float w_pf[MF][4];
+    if (!GATEUP && p.rows16)
+#pragma unroll
+      for (int f = 0; f < MF; f++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) rec_pf[f][i] = p.sorted_pairs[mb + min(f * 16 + 4 * g + i, nvalid - 1)];
     uint32_t sw[4];
     if (SLDS) {
       if (first_pass) lds_barrier_vm<0>();  // the staged scales (and chunk c_lo) have landed
       if (c_lo < c_hi) staged_words<FMT>(sw, staged, lsrow, c_lo, g);
     }
     first_pass = false;
+    if (!GATEUP && p.rows16)
+#pragma unroll
+      for (int f = 0; f < MF; f++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) w_pf[f][i] = p.pair_w[rec_pf[f][i]];
     for (int c = c_lo; c < c_hi; c++) {
       if (!SLDS) {
         if (c == c_lo || (c & 3) == 0) sq_transpose<FMT>(sq);
@@ -469,8 +490,8 @@ __global__ __launch_bounds__(NW * WAVE, WAVES_PER_EU) void expert_gemm_kernel(Gr
                 p.h[(size_t)(mb + m) * N + tile * 32 + 16 * cp + r] = (f16)hv;
               }
             } else if (p.rows16) {
-              const int rec = p.sorted_pairs[mb + m];  // stored at its record's row
-              const float ws = p.pair_w[rec] * gsa;
+              const int rec = rec_pf[f][i];  // stored at its record's row
+              const float ws = w_pf[f][i] * gsa;
 #pragma unroll
               for (int ng = 0; ng < 4; ng++)
                 p.rows16[(size_t)rec * N + tile * 64 + 16 * ng + r] = (f16)(ws * acc[f][ng][i]);
