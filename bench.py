@@ -16,7 +16,8 @@ peak, and, as `frac_of_sustained`, against what the library's calibration
 kernel measures the fp16 matrix cores to sustain on this GPU under its power
 limit, on operands with the GEMMs' value patterns).  In the same process and on the same resident store, `configs` times
 the decode-sized workloads (single-user decode, 64-session decode,
-speculative verify), which are bound by HBM: layer tokens/s, the gate/up
+speculative verify), which are bound by HBM, each over at least 50 ms of
+back-to-back steps (`timed_steps`): layer tokens/s, the gate/up
 kernel's achieved bandwidth and the layer's algorithmic bytes per second,
 against 8 TB/s and against the streaming-read rate the library's calibration
 kernel measures on this GPU.  `parity` checks sampled tokens of the timed
@@ -38,6 +39,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/s + achieved HBM TB/s (decode) / MFMA TFLOPS (prefill), 1 GPU"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+CONFIG_MIN_MS = 50.0            # shortest timed loop of a config (more steps for short ones)
 FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix, published
 FP8_MFMA_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 matrix, published
 PROFILES = os.path.join(ROOT, "profiles")
@@ -235,14 +237,23 @@ class Bench:
         T, H, I, E, k, Hm = wl.T, wl.H, wl.I, wl.E, wl.k, self.Hm
         assert (H, I, E, k) == (self.H, self.I, self.E, self.k) and (wl.H_model or H) == Hm
         dev = self.dev
-        n_batches = steps + warmup
-        n_graph = 0 if args.no_graph else steps  # fresh batches for the graph replay
         n_kern = 0 if args.no_breakdown and headline else KERNEL_REPS
         b = bias_for(wl)
         bias = None if b is None else torch.tensor(b, device=dev)
-        total = n_batches + n_graph + n_kern
-        xs = torch.empty((total * T, Hm), dtype=torch.bfloat16, device=dev)
-        synth.gpu_x_bf16(wl.seed, xs)
+
+        def batches(n_steps):
+            # fresh token batches for warmup, the timed steps, the graph replay
+            # and the kernel loop (the generator is deterministic: the first
+            # batches are the same whatever the count)
+            nb = n_steps + warmup
+            n_gr = 0 if args.no_graph else n_steps
+            tot = nb + n_gr + n_kern
+            x_all = torch.empty((tot * T, Hm), dtype=torch.bfloat16, device=dev)
+            synth.gpu_x_bf16(wl.seed, x_all)
+            return nb, n_gr, tot, x_all, torch.empty((tot, T, k), dtype=torch.int32, device=dev), \
+                torch.empty((tot, T, k), dtype=torch.float32, device=dev)
+
+        n_batches, n_graph, total, xs, ids, wts = batches(steps)
         d = moe.dims(T, H, I, E, k)
         if wl.H_model:
             ws = torch.empty(moe.moe_latent_workspace_bytes(d, Hm), dtype=torch.uint8, device=dev)
@@ -251,8 +262,6 @@ class Bench:
         else:
             ws = torch.empty(moe.moe_workspace_bytes(d), dtype=torch.uint8, device=dev)
         y = torch.empty((T, Hm), dtype=torch.float32 if args.ep > 1 else torch.bfloat16, device=dev)
-        ids = torch.empty((total, T, k), dtype=torch.int32, device=dev)
-        wts = torch.empty((total, T, k), dtype=torch.float32, device=dev)
         share = self.share
 
         def step(i):
@@ -268,9 +277,21 @@ class Bench:
             else:
                 moe.moe_layer(d, x, self.wr, bias, self.store, y, ids[i], wts[i], ws)
 
+        w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0.record()
         for i in range(warmup):
             step(i)
+        w1.record()
         torch.cuda.synchronize()
+        if not headline and warmup > 0:
+            # a config's timed loop spans at least CONFIG_MIN_MS of back-to-back
+            # steps, so that the launch ramp after the synchronisation before
+            # it (about 0.1 ms) is not charged to a handful of 0.1 ms steps
+            need = int(np.ceil(CONFIG_MIN_MS / max(w0.elapsed_time(w1) / warmup, 1e-3)))
+            if need > steps:
+                steps = need
+                del xs, ids, wts
+                n_batches, n_graph, total, xs, ids, wts = batches(steps)
 
         # ---- timed region ----------------------------------------------------
         if headline:
@@ -325,7 +346,7 @@ class Bench:
         gu_TF = gu_flops / (gu_ms * 1e-3) / 1e12
         layer_GBps = layer_bytes / (ms_per_step * 1e-3) / 1e9
         res = {
-            "T": T, "ms_per_step": round(ms_per_step, 5),
+            "T": T, "ms_per_step": round(ms_per_step, 5), "timed_steps": steps,
             "tokens_per_s": round(T * steps / (elapsed_ms * 1e-3), 2),
             "distinct_experts_mean": float(distinct.mean()),
             "layer": {"algorithmic_bytes": int(layer_bytes), "hbm_GBps": round(layer_GBps, 1),
