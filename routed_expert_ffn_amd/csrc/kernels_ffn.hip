@@ -1170,6 +1170,51 @@ __global__ __launch_bounds__(256) void combine16_kernel(const f16* __restrict__ 
   *reinterpret_cast<uint2*>(y + (size_t)t * H + n) = o;
 }
 
+// The same combine for large batches (rows in sorted order, gathered through
+// pos): eight columns per thread, each row's 16-byte piece loaded
+// non-temporally (the rows are read once, and one wavefront load covers
+// eight whole lines), the same fp32 sums in the same order.
+__global__ __launch_bounds__(128) void combine16_wide_kernel(const f16* __restrict__ rows,
+                                                            const int32_t* __restrict__ pos, int H, int k,
+                                                            uint16_t* __restrict__ y, const float* __restrict__ add,
+                                                            int add_slabs, long long add_stride) {
+  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+  const int t = blockIdx.y;
+  const int n = (blockIdx.x * blockDim.x + threadIdx.x) * 8;
+  if (n >= H) return;
+  float a[8];
+#pragma unroll
+  for (int c = 0; c < 8; c++) a[c] = 0.0f;
+  for (int j0 = 0; j0 < k; j0 += COMBINE_JB) {
+    size_t row[COMBINE_JB];
+#pragma unroll
+    for (int u = 0; u < COMBINE_JB; u++) row[u] = j0 + u < k ? (size_t)pos[(size_t)t * k + j0 + u] : 0;
+    h8 v[COMBINE_JB];
+#pragma unroll
+    for (int u = 0; u < COMBINE_JB; u++)
+      v[u] = j0 + u < k ? __builtin_bit_cast(h8, load_nt16(reinterpret_cast<const uint8_t*>(rows + row[u] * H + n)))
+                        : h8{};
+#pragma unroll
+    for (int u = 0; u < COMBINE_JB; u++)
+      if (j0 + u < k)
+#pragma unroll
+        for (int c = 0; c < 8; c++) a[c] += (float)v[u][c];
+  }
+  if (add) {
+    float4 lo = make_float4(a[0], a[1], a[2], a[3]), hi = make_float4(a[4], a[5], a[6], a[7]);
+    add_slab_partials4(lo, add + (size_t)t * H + n, add_stride, 0, add_slabs);
+    add_slab_partials4(hi, add + (size_t)t * H + n + 4, add_stride, 0, add_slabs);
+    a[0] = lo.x; a[1] = lo.y; a[2] = lo.z; a[3] = lo.w;
+    a[4] = hi.x; a[5] = hi.y; a[6] = hi.z; a[7] = hi.w;
+  }
+  uint4 o;
+  o.x = (uint32_t)f32_to_bf16(a[0]) | ((uint32_t)f32_to_bf16(a[1]) << 16);
+  o.y = (uint32_t)f32_to_bf16(a[2]) | ((uint32_t)f32_to_bf16(a[3]) << 16);
+  o.z = (uint32_t)f32_to_bf16(a[4]) | ((uint32_t)f32_to_bf16(a[5]) << 16);
+  o.w = (uint32_t)f32_to_bf16(a[6]) | ((uint32_t)f32_to_bf16(a[7]) << 16);
+  *reinterpret_cast<uint4*>(y + (size_t)t * H + n) = o;
+}
+
 // One share of the experts ([lo, hi)): fp32 unweighted rows; only records
 // whose expert lies in the share are summed, in ascending j, into fp32
 // partial outputs, and block 0 of each token writes which records it
@@ -1355,8 +1400,13 @@ bool rows16_sorted(int T) { return T >= BIG_MIN_T; }
 
 hipError_t launch_combine16(const f16* rows, const int32_t* pair_pos, int T, int H, int k, uint16_t* y,
                             hipStream_t s, const float* add, int add_slabs) {
-  const int threads = T < 64 ? 64 : 256;
   const int32_t* pos = rows16_sorted(T) ? pair_pos : nullptr;
+  if (pos && H % 8 == 0) {
+    hipLaunchKernelGGL(combine16_wide_kernel, dim3((H / 8 + 127) / 128, T), dim3(128), 0, s, rows, pos, H, k, y, add,
+                       add_slabs, (long long)T * H);
+    return hipGetLastError();
+  }
+  const int threads = T < 64 ? 64 : 256;
   hipLaunchKernelGGL(combine16_kernel, dim3((H / 4 + threads - 1) / threads, T), dim3(threads), 0, s, rows, pos, H,
                      k, y, add, add_slabs, (long long)T * H);
   return hipGetLastError();
