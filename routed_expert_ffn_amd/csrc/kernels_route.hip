@@ -691,21 +691,29 @@ __device__ __forceinline__ void cast_rows(const uint16_t* __restrict__ x, f16* _
 // position and is not counted.
 __device__ __forceinline__ bool served_id(int e, int E) { return (unsigned)e < (unsigned)E; }
 
-// The permutation of up to 64 tokens in one block of 1024 threads (thread e
-// = expert e for the counts): m and off_s are LDS arrays of E entries, m
-// zeroed by the caller before a barrier.  Also writes the active-expert list.
+// The permutation of up to 64 * NWD tokens in one block of 1024 threads
+// (thread e = expert e for the counts): m holds NWD 64-bit token masks per
+// expert ([E][NWD], word w bit l = token 64w + l selected e) and off_s E
+// ints, LDS arrays with m zeroed by the caller before a barrier.  A
+// record's position is its expert's offset plus the bits set in the words
+// before its own and below it in its own.  Also writes the active-expert
+// list.
+template <int NWD>
 __device__ __forceinline__ void permute_block(const int32_t* ids, int T, int E, int k, int32_t* __restrict__ offsets,
                               int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_pos,
                               int32_t* __restrict__ active, int32_t* __restrict__ n_active, unsigned long long* m,
                               int* off_s, int* lds) {
   const int tid = threadIdx.x;
   for (int f = tid; f < T * k; f += 1024) {
-    const int e = ids[f];
-    if (served_id(e, E)) atomicOr(&m[e], 1ull << (f / k));
+    const int e = ids[f], t = f / k;
+    if (served_id(e, E)) atomicOr(&m[e * NWD + t / 64], 1ull << (t % 64));
   }
   __syncthreads();
-  const int cnt = tid < E ? __popcll(m[tid]) : 0;
-  // offsets (< T k <= 4096) and active slots (< E <= 1024) in one scan
+  int cnt = 0;
+  if (tid < E)
+#pragma unroll
+    for (int w = 0; w < NWD; w++) cnt += __popcll(m[tid * NWD + w]);
+  // offsets (< T k <= 64 NWD * 64 <= 2^16) and active slots (< E <= 1024) in one scan
   int packed_total;
   const int packed = block_exclusive_scan(cnt + (cnt > 0 ? 1 << 16 : 0), lds, &packed_total);
   const int off = packed & 0xFFFF, slot = packed >> 16, nact = packed_total >> 16;
@@ -725,27 +733,34 @@ __device__ __forceinline__ void permute_block(const int32_t* ids, int T, int E, 
       pair_pos[f] = -1;
       continue;
     }
-    const int pos = off_s[e] + __popcll(m[e] & ((1ull << t) - 1ull));
+    const int w = t / 64;
+    int pos = off_s[e] + __popcll(m[e * NWD + w] & ((1ull << (t % 64)) - 1ull));
+#pragma unroll
+    for (int w2 = 0; w2 < NWD - 1; w2++)
+      if (w2 < w) pos += __popcll(m[e * NWD + w2]);
     sorted_pairs[pos] = f;
     pair_pos[f] = pos;
   }
 }
 
-// T <= 64: the whole permutation and the active-expert list, in one block of
-// 1024 threads.
+// T <= 64 * NWD: the whole permutation and the active-expert list, in one
+// block of 1024 threads.
+template <int NWD>
 __global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
                                                          int32_t* __restrict__ offsets,
                                                          int32_t* __restrict__ sorted_pairs,
                                                          int32_t* __restrict__ pair_pos,
                                                          int32_t* __restrict__ active,
                                                          int32_t* __restrict__ n_active) {
-  __shared__ unsigned long long m[PERM_MAX_E];
+  __shared__ unsigned long long m[PERM_MAX_E * NWD];
   __shared__ int off_s[PERM_MAX_E];
   __shared__ __attribute__((aligned(16))) int lds[16];
-  if (threadIdx.x < E) m[threadIdx.x] = 0ull;
+  for (int i = threadIdx.x; i < E * NWD; i += 1024) m[i] = 0ull;
   __syncthreads();
-  permute_block(ids, T, E, k, offsets, sorted_pairs, pair_pos, active, n_active, m, off_s, lds);
+  permute_block<NWD>(ids, T, E, k, offsets, sorted_pairs, pair_pos, active, n_active, m, off_s, lds);
 }
+// Largest batch of the single-block permutation (four mask words per expert).
+constexpr int PERM_ONE_BLOCK_T = 256;
 
 // T <= ROUTE_SMALL_T: the whole routing in one block of 1024 threads (one
 // launch instead of three): logits from the slab partials (or the caller's
@@ -816,7 +831,7 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const float* __restri
   if (wv < T)
     wave_topk(ls + wv * PERM_MAX_E, E, k, ids + (size_t)wv * k, wout + (size_t)wv * k, ids_s + wv * k, tk[wv]);
   __syncthreads();
-  permute_block(ids_s, T, E, k, offsets, sorted_pairs, pair_pos, active, n_active, m, off_s, lds);
+  permute_block<1>(ids_s, T, E, k, offsets, sorted_pairs, pair_pos, active, n_active, m, off_s, lds);
 }
 
 __global__ __launch_bounds__(WAVE) void perm_count_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
@@ -1045,8 +1060,13 @@ hipError_t launch_permute(const int32_t* ids, int T, int E, int k, uint64_t* mas
                           int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_pos, int32_t* active,
                           int32_t* n_active, int32_t* mtiles, int32_t* n_mtiles, hipStream_t s) {
   if (T <= 64) {
-    hipLaunchKernelGGL(perm_small_kernel, dim3(1), dim3(1024), 0, s, ids, T, E, k, offsets, sorted_pairs, pair_pos,
+    hipLaunchKernelGGL(perm_small_kernel<1>, dim3(1), dim3(1024), 0, s, ids, T, E, k, offsets, sorted_pairs, pair_pos,
                        active, n_active);
+    return hipGetLastError();
+  }
+  if (T <= PERM_ONE_BLOCK_T) {  // (no token-tile list: it serves only the large-tile GEMMs, T >= 1024)
+    hipLaunchKernelGGL(perm_small_kernel<PERM_ONE_BLOCK_T / 64>, dim3(1), dim3(1024), 0, s, ids, T, E, k, offsets,
+                       sorted_pairs, pair_pos, active, n_active);
     return hipGetLastError();
   }
   const int nb = perm_blocks(T);

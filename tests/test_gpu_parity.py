@@ -151,7 +151,8 @@ def test_determinism(tiny):
 SMALL = dict(H=512, I=256)
 
 
-@pytest.mark.parametrize("T,E,k,beta", [(1, 64, 8, None), (3, 32, 16, None), (2, 8, 8, None), (8, 8, 8, 1.0),
+@pytest.mark.parametrize("T,E,k,beta", [(1, 64, 8, None), (1, 40, 6, 0.5), (1, 8, 8, None), (1, 896, 1, None),
+                                        (3, 32, 16, None), (2, 8, 8, None), (8, 8, 8, 1.0),
                                         (17, 64, 8, 0.5), (65, 32, 16, 0.8),
                                         (130, 16, 16, None), (200, 40, 4, 1.0), (33, 8, 8, None), (70, 48, 1, 0.3),
                                         (1100, 32, 8, 0.5), (2048, 16, 4, None), (1500, 64, 16, 1.0),
@@ -159,6 +160,8 @@ SMALL = dict(H=512, I=256)
 def test_ragged_layer(T, E, k, beta):
     """Token counts that are not multiples of 16 or 64, experts with more
     than 64 tokens (several passes), every expert selected (k = E), k = 1,
+    single tokens (whose permutation ranks the selected ids directly) with E
+    not a multiple of 64, k = E and k = 1,
     up to 8 tokens with every token on every expert,
     and batches of 1024+ tokens (the 224-token tile kernels) with experts
     holding several ragged 224-token tiles, or only a handful of tokens
