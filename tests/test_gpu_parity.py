@@ -269,6 +269,35 @@ def test_large_tiles_many_spans(T, H, I, E, k):
     assert_close(y, ref["y"], "y")
 
 
+def test_maximum_token_count():
+    """The largest batch the boundary accepts, T = 65535 (the combines launch
+    one row of blocks per token), at a small H and I with Zipf-skewed routing
+    (the hottest expert takes several hundred 224-token tiles' worth of
+    records): routing and the permutation checked for every token, the rows
+    and y of sampled tokens against the oracle, among them the first and
+    last records of the hottest expert."""
+    from tests.test_gpu_full import sample_tokens
+    T, H, I, E, k = 65535, 512, 256, 896, 16
+    say(f"maximum T={T} H={H} I={I} E={E} k={k}")
+    inp = Inputs(T, H, I, E, k, seed=23, bias=synth.zipf_bias(23, E, 1.0), router_std=0.1)
+    r = inp.route()
+    sample = sample_tokens(T, r, k, n=24, seed=23)
+    check_route(inp, r, rows=np.array(sample))
+    counts = np.diff(r["offsets"])
+    say(f"  max count {counts.max()}, active {np.count_nonzero(counts)}; {len(sample)} sampled tokens")
+    assert counts.sum() == T * k
+    rows = inp.ffn(r["offsets"], r["sorted_pairs"])
+    y, ids, _ = inp.layer()
+    np.testing.assert_array_equal(ids, r["ids"])
+    assert np.all(np.isfinite(y))
+    ref = oracle.moe_layer(inp.host_x(sample), OracleExperts(23, H, I).get(r["ids"][sample]), E, k,
+                           logits_in=r["logits"][sample], want_rows=True, nthreads=16)
+    got_rows = np.stack([rows[r["pair_pos"][t * k + j]] for t in sample for j in range(k)])
+    ref_rows = np.stack([ref["rows"][ref["pair_pos"][i * k + j]] for i in range(len(sample)) for j in range(k)])
+    assert_close(got_rows, ref_rows, f"rows of {len(sample)} tokens")
+    assert_close(y[sample], ref["y"], f"y of {len(sample)} tokens")
+
+
 @pytest.mark.parametrize("T", [1, 6, 40, 100])
 def test_route_ties_logits_in(T):
     """Constructed fp32 logits with exact ties (all equal, +-0, duplicated
