@@ -146,8 +146,8 @@ size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 // Workspace regions (byte offsets, 256-byte aligned).  moe_layer uses all of
 // them; moe_route and moe_expert_ffn use subsets of the same layout.
 struct Layout {
-  size_t part, logits, ids, w, lids, masks, counts, base, offsets, sorted, pos, active, nact, mtiles, nmt, x16, h,
-      rows, total;
+  size_t part, wt, logits, ids, w, lids, masks, counts, base, offsets, sorted, pos, active, nact, mtiles, nmt, x16,
+      h, rows, total;
 };
 
 Layout layout(const moe_dims& d) {
@@ -159,8 +159,10 @@ Layout layout(const moe_dims& d) {
     return r;
   };
   const size_t T = (size_t)d.T, H = (size_t)d.H, I = (size_t)d.I, E = (size_t)d.E, P = T * (size_t)d.k;
-  const size_t S = (size_t)moe::router_plan(d.T, d.H, d.E).slabs, nb = (size_t)moe::perm_blocks(d.T);
+  const moe::RouterPlan rp = moe::router_plan(d.T, d.H, d.E, true);
+  const size_t S = (size_t)rp.slabs, nb = (size_t)moe::perm_blocks(d.T);
   L.part = take(S * T * E * 4);
+  L.wt = take(rp.tiled ? H * E * 2 : 0);  // the tiled router's transposed weight
   L.logits = take(T * E * 4);
   L.ids = take(P * 4);
   L.w = take(P * 4);
@@ -187,7 +189,7 @@ Layout layout(const moe_dims& d) {
 // latent z and the combined latent output.
 struct LatentLayout {
   Layout base;
-  size_t rpart, ppart, z, ylat, total;
+  size_t rpart, ppart, wt, z, ylat, total;
 };
 
 LatentLayout latent_layout(const moe_dims& d, int Hm) {
@@ -200,10 +202,18 @@ LatentLayout latent_layout(const moe_dims& d, int Hm) {
     return r;
   };
   const size_t T = (size_t)d.T, H = (size_t)d.H, E = (size_t)d.E, M = (size_t)Hm;
-  LL.rpart = take((size_t)moe::router_plan(d.T, Hm, d.E).slabs * T * E * 4);
-  const size_t down = (size_t)moe::router_plan(d.T, Hm, d.H).slabs * T * H * 4;
-  const size_t up = (size_t)moe::router_plan(d.T, d.H, Hm).slabs * T * M * 4;
+  const moe::RouterPlan rr = moe::router_plan(d.T, Hm, d.E, true), rd = moe::router_plan(d.T, Hm, d.H, true),
+                        ru = moe::router_plan(d.T, d.H, Hm, true);
+  LL.rpart = take((size_t)rr.slabs * T * E * 4);
+  // a tiled projection of one slab writes its output directly
+  const size_t down = rd.tiled && rd.slabs == 1 ? 0 : (size_t)rd.slabs * T * H * 4;
+  const size_t up = ru.tiled && ru.slabs == 1 ? 0 : (size_t)ru.slabs * T * M * 4;
   LL.ppart = take(down > up ? down : up);
+  // the transposed weight of whichever of the three runs (one at a time, in order)
+  size_t wt = 0;
+  if (rr.tiled) wt = M * E * 2;
+  if (rd.tiled || ru.tiled) wt = wt > M * H * 2 ? wt : M * H * 2;
+  LL.wt = take(wt);
   LL.z = take(T * H * 2);
   LL.ylat = take(T * H * 2);
   LL.total = o;
@@ -304,11 +314,11 @@ moe_status enqueue_route(const moe_dims& d, const void* x, const void* wr, const
                          int32_t* ids, float* w, int32_t* offsets, int32_t* sorted, int32_t* pos, void* ws,
                          f16* x16, hipStream_t s) {
   const Layout L = layout(d);
-  const moe::RouterPlan rp = moe::router_plan(d.T, d.H, d.E);
+  const moe::RouterPlan rp = moe::router_plan(d.T, d.H, d.E, true);
   if (x)
     LAUNCH(MOE_KERNEL_ROUTER, s,
            moe::launch_router(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wr),
-                              at<float>(ws, L.part), d.T, d.H, d.E, rp, s, x16),
+                              at<float>(ws, L.part), d.T, d.H, d.E, rp, s, x16, at<uint16_t>(ws, L.wt)),
            "router");
   if (moe::route_fused(d.T)) {  // top-k and permutation in one launch, timed as top-k
     LAUNCH(MOE_KERNEL_TOPK, s,
@@ -565,10 +575,10 @@ moe_status moe_layer_mapped(moe_dims d, const int32_t* expert_map, int32_t n_loc
   // routing over all E experts (the router also writes the fp16 copy of x);
   // the single-launch routing of small batches also permutes over all E,
   // which the local permutation below replaces
-  const moe::RouterPlan rp = moe::router_plan(T, d.H, E);
+  const moe::RouterPlan rp = moe::router_plan(T, d.H, E, true);
   LAUNCH(MOE_KERNEL_ROUTER, s,
          moe::launch_router(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router),
-                            at<float>(ws, L.part), T, d.H, E, rp, s, at<f16>(ws, L.x16)),
+                            at<float>(ws, L.part), T, d.H, E, rp, s, at<f16>(ws, L.x16), at<uint16_t>(ws, L.wt)),
          "router");
   if (moe::route_fused(T))
     LAUNCH(MOE_KERNEL_TOPK, s,
@@ -796,17 +806,18 @@ moe_status moe_latent_layer(moe_dims d, const moe_latent* lat, const void* x, co
   float* rpart = at<float>(ws, LL.rpart);
   float* ppart = at<float>(ws, LL.ppart);
   // router on the hidden state
-  const moe::RouterPlan rp = moe::router_plan(T, Hm, E);
+  uint16_t* wt = at<uint16_t>(ws, LL.wt);
+  const moe::RouterPlan rp = moe::router_plan(T, Hm, E, true);
   LAUNCH(MOE_KERNEL_ROUTER, s,
          moe::launch_router(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router), rpart, T, Hm, E,
-                            rp, s),
+                            rp, s, nullptr, wt),
          "router");
   // routed-down projection: the latent in bf16 and its fp16 copy for the
   // experts.  (Beside the routing on the side stream it was slower: the
   // experts need it at once, so the join's latency is on the critical path.)
   LAUNCH(MOE_KERNEL_PROJECT, s,
          moe::launch_projection(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(lat->w_down), ppart, T,
-                                Hm, H, moe::router_plan(T, Hm, H), z, x16, s),
+                                Hm, H, moe::router_plan(T, Hm, H, true), z, x16, s, wt),
          "routed-down projection");
   // top-k and permutation on the router's partials (x16 is already in place)
   if (moe::route_fused(T)) {
@@ -830,7 +841,7 @@ moe_status moe_latent_layer(moe_dims d, const moe_latent* lat, const void* x, co
   // routed-up projection back to the hidden width
   LAUNCH(MOE_KERNEL_PROJECT, s,
          moe::launch_projection(ylat, static_cast<const uint16_t*>(lat->w_up), ppart, T, H, Hm,
-                                moe::router_plan(T, H, Hm), static_cast<uint16_t*>(y), nullptr, s),
+                                moe::router_plan(T, H, Hm, true), static_cast<uint16_t*>(y), nullptr, s, wt),
          "routed-up projection");
   return MOE_OK;
 }

@@ -16,10 +16,11 @@
 // assembly" and "Routed-up projection: sharding the post-expert tail").
 //
 // out[T][N] = bf16(x[T][K] . W[K][N]) with W stored input-major, the layout
-// of the router weight: the router's GEMV (small T) and bf16 matrix-core GEMM
-// (large T) compute the K-slab partial sums in fp32, and one more kernel adds
-// the slabs in a fixed order and rounds to bf16 (and, for the latent that
-// feeds the experts, also writes its exact fp16 copy).
+// of the router weight.  Small batches: the router's GEMV or its one-wave
+// bf16 matrix-core GEMM compute K-slab partial sums in fp32, and one more
+// kernel adds the slabs in a fixed order and rounds to bf16 (and, for the
+// latent that feeds the experts, also writes its exact fp16 copy).  Large
+// batches (and the router itself there): the LDS-tiled GEMM below.
 #include "internal.h"
 
 namespace moe {
@@ -79,7 +80,287 @@ __global__ __launch_bounds__(PROJ_THREADS) void swiglu_reduce_kernel(const float
   *reinterpret_cast<uint2*>(h + (size_t)t * width + c) = o;
 }
 
+
+// ---- LDS-tiled bf16 GEMM of large batches ----------------------------------------
+// A block computes a tile of DT_M tokens x DT_N output columns over one K
+// slab.  The weight is first transposed to wt [N][K] so both operands are
+// k-contiguous rows; each 64-k chunk of the tile's rows (128 bytes a row)
+// reaches LDS by LDS DMA, two stages: the copies of chunk c+1 are issued as
+// chunk c's multiply starts, into the stage that chunk c-1 held.  A 128-byte
+// row is 8 pieces of 16 bytes, piece q of row r stored in slot
+// q ^ ((r/2) % 8), so that the 16 rows one fragment read touches cover all
+// of LDS's banks.
+//
+// Eight wavefronts, 4 (tokens, 64 each) x 2 (columns, 112 each); wavefront
+// products are v_mfma_f32_16x16x32_bf16 with the weight rows as the A operand
+// and the tokens as B, so a lane's four accumulators are four consecutive
+// output columns of one token.  Inside a chunk, step s (32 k) of lane group
+// g = lane/16 covers piece 4s + g of both operands.
+//
+// Tiles: DT_N = 224 divides the widths of a K3-shaped layer (896 router
+// columns, 3584 latent, 7168 hidden), and a prefill chunk of 8192 tokens
+// fills whole waves of 256 blocks.  Items are laid out (slab, column group,
+// token tile, column tile in group) and dealt to the eight XCDs in
+// contiguous runs, so the 32 blocks an XCD runs at once share a few token
+// tiles and a group of column tiles in its L2.
+constexpr int DT_M = 256;
+constexpr int DT_N = 224;
+constexpr int DT_KC = 64;
+constexpr int DT_WAVES = 8;
+constexpr int DT_ROWB = DT_KC * 2;                 // bytes of a row's chunk
+constexpr int DT_X_BYTES = DT_M * DT_ROWB;         // token rows of one chunk
+constexpr int DT_W_BYTES = DT_N * DT_ROWB;         // weight rows of one chunk
+constexpr int DT_STAGE = DT_X_BYTES + DT_W_BYTES;
+constexpr int DT_LDS = 2 * DT_STAGE;
+constexpr int DT_X_INSTR = DT_M / 8;  // DMA instructions (8 rows each) per chunk
+constexpr int DT_W_INSTR = DT_N / 8;
+constexpr int DT_MIN_T = 1024;
+constexpr int DT_MAX_SLABS = 16;
+static_assert(DT_LDS <= 160 * 1024, "LDS budget of one CU");
+static_assert(DT_X_INSTR == 4 * DT_WAVES && DT_W_INSTR <= 4 * DT_WAVES, "DMA instructions per wavefront");
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+struct DenseParams {
+  const unsigned char* x;   // [T][K] bf16
+  const unsigned char* wt;  // [N][K] bf16
+  float* part;              // [slabs][T][N] fp32, or NULL
+  uint16_t* out;            // [T][N] bf16 (one slab, part NULL)
+  f16* out16;               // fp16 copy of out, or NULL
+  f16* x16;                 // fp16 copy of x, or NULL
+  int T, K, N, kslab;
+  int n_tt, n_ct, cg, n_items;
+};
+
+__device__ __forceinline__ uint32_t dt_lds_addr(const unsigned char* p) {
+  return (uint32_t)(size_t)(const __attribute__((address_space(3))) unsigned char*)p;
+}
+
+// LDS DMA of 16 bytes per lane from gbase + voff to LDS address lds + 16 *
+// lane.  Written as an instruction of our own, so the compiler does not count
+// it as outstanding LDS work (it would wait for it before every fragment
+// read); the only wait for it is the vmcnt(0) of dt_barrier.
+__device__ __forceinline__ void dt_dma16(const unsigned char* gbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "s"(lds)
+               : "memory", "m0");
+}
+
+// All of this wavefront's vector-memory work (its DMA copies included) and
+// LDS reads are complete, then the block meets.
+__device__ __forceinline__ void dt_barrier() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__global__ __launch_bounds__(DT_WAVES * WAVE, 1) void dense_tile_kernel(DenseParams p) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char dt_smem[];
+  const int per_xcd = (p.n_items + 7) / 8;
+  const int slot = blockIdx.x / 8, item = (blockIdx.x % 8) * per_xcd + slot;
+  if (slot >= per_xcd || item >= p.n_items) return;
+  int r = item / p.cg;
+  const int ci = item % p.cg;
+  const int tt = r % p.n_tt;
+  r /= p.n_tt;
+  const int n_grp = p.n_ct / p.cg;
+  const int ct = (r % n_grp) * p.cg + ci, slab = r / n_grp;
+  const int t0 = tt * DT_M, n0 = ct * DT_N;
+  const int k_begin = slab * p.kslab;
+  const int nchunks = (min(p.K, k_begin + p.kslab) - k_begin) / DT_KC;
+
+  const int lane = threadIdx.x % WAVE, w = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
+  const size_t row_bytes = (size_t)p.K * 2;
+  // DMA: instruction i (rows 8i .. 8i+7 of the token or weight rows) of
+  // wavefront w is i = w + 8m; lane l copies row 8i + l/8, piece
+  // (l%8) ^ ((row/2)%8) into slot l%8.  Rows past T (N) repeat the last one.
+  const unsigned char* xb = p.x + (size_t)t0 * row_bytes + 2 * (size_t)k_begin;
+  const unsigned char* wb = p.wt + (size_t)n0 * row_bytes + 2 * (size_t)k_begin;
+  uint32_t xoff[4], woff[4];
+#pragma unroll
+  for (int m = 0; m < 4; m++) {
+    const int row = 8 * (w + 8 * m) + lane / 8;
+    const uint32_t piece = (uint32_t)((lane % 8) ^ ((row / 2) % 8));
+    xoff[m] = (uint32_t)(min(t0 + row, p.T - 1) - t0) * (uint32_t)row_bytes + 16 * piece;
+    woff[m] = (uint32_t)(min(n0 + row, p.N - 1) - n0) * (uint32_t)row_bytes + 16 * piece;
+  }
+  const uint32_t lds0 = dt_lds_addr(dt_smem);
+  auto issue = [&](int c) {
+    const uint32_t st = lds0 + (uint32_t)((c % 2) * DT_STAGE);
+    const unsigned char* xc = xb + (size_t)c * DT_ROWB;
+    const unsigned char* wc = wb + (size_t)c * DT_ROWB;
+#pragma unroll
+    for (int m = 0; m < 4; m++) dt_dma16(xc, xoff[m], st + 1024 * (w + 8 * m));
+#pragma unroll
+    for (int m = 0; m < 4; m++)
+      if (w + 8 * m < DT_W_INSTR) dt_dma16(wc, woff[m], st + DT_X_BYTES + 1024 * (w + 8 * m));
+  };
+
+  // fragment reads: row 16 f + l%16 of a 16-row group, piece 4s + l/16
+  const int rl = lane % 16, g = lane / 16;
+  int roff[2];
+#pragma unroll
+  for (int s = 0; s < 2; s++) roff[s] = rl * DT_ROWB + 16 * ((4 * s + g) ^ (rl / 2));
+  const int wr = w % 4, wc = w / 4;
+  const int xrow0 = 64 * wr, wrow0 = 112 * wc;
+
+  f32x4 acc[7][4];
+#pragma unroll
+  for (int j = 0; j < 7; j++)
+#pragma unroll
+    for (int f = 0; f < 4; f++) acc[j][f] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  issue(0);
+  for (int c = 0; c < nchunks; c++) {
+    dt_barrier();  // chunk c is in its stage; everyone is done with chunk c-1
+    if (c + 1 < nchunks) issue(c + 1);
+    const unsigned char* S = dt_smem + (c % 2) * DT_STAGE;
+    // the fp16 copy of x: chunk c of a (token tile, slab) by column tile c % n_ct
+    if (p.x16 != nullptr && c % p.n_ct == ct) {
+#pragma unroll
+      for (int h = 0; h < 4; h++) {
+        const int row = threadIdx.x / 2, q = 4 * (threadIdx.x % 2) + h;
+        const uint4 v = *reinterpret_cast<const uint4*>(S + row * DT_ROWB + 16 * (q ^ ((row / 2) % 8)));
+        if (t0 + row < p.T) {
+          f16x8 o;
+          o[0] = (f16)__uint_as_float(v.x << 16); o[1] = (f16)__uint_as_float(v.x & 0xFFFF0000u);
+          o[2] = (f16)__uint_as_float(v.y << 16); o[3] = (f16)__uint_as_float(v.y & 0xFFFF0000u);
+          o[4] = (f16)__uint_as_float(v.z << 16); o[5] = (f16)__uint_as_float(v.z & 0xFFFF0000u);
+          o[6] = (f16)__uint_as_float(v.w << 16); o[7] = (f16)__uint_as_float(v.w & 0xFFFF0000u);
+          *reinterpret_cast<f16x8*>(p.x16 + (size_t)(t0 + row) * p.K + k_begin + c * DT_KC + 8 * q) = o;
+        }
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 2; s++) {
+      bf16x8 xa[4], wa[7];
+#pragma unroll
+      for (int f = 0; f < 4; f++)
+        xa[f] = *reinterpret_cast<const bf16x8*>(S + (xrow0 + 16 * f) * DT_ROWB + roff[s]);
+#pragma unroll
+      for (int j = 0; j < 7; j++)
+        wa[j] = *reinterpret_cast<const bf16x8*>(S + DT_X_BYTES + (wrow0 + 16 * j) * DT_ROWB + roff[s]);
+#pragma unroll
+      for (int j = 0; j < 7; j++)
+#pragma unroll
+        for (int f = 0; f < 4; f++) acc[j][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[j], xa[f], acc[j][f], 0, 0, 0);
+    }
+  }
+
+  // D[4g+i][l%16] of product (j, f): column n0 + 112 wc + 16 j + 4 g + i of
+  // token t0 + 64 wr + 16 f + l%16
+#pragma unroll
+  for (int f = 0; f < 4; f++) {
+    const int t = t0 + xrow0 + 16 * f + rl;
+    if (t >= p.T) continue;
+#pragma unroll
+    for (int j = 0; j < 7; j++) {
+      const int n = n0 + wrow0 + 16 * j + 4 * g;
+      if (n >= p.N) continue;
+      const f32x4 v = acc[j][f];
+      if (p.part != nullptr) {
+        *reinterpret_cast<float4*>(p.part + ((size_t)slab * p.T + t) * p.N + n) = make_float4(v[0], v[1], v[2], v[3]);
+      } else {
+        const uint16_t b0 = f32_to_bf16(v[0]), b1 = f32_to_bf16(v[1]), b2 = f32_to_bf16(v[2]), b3 = f32_to_bf16(v[3]);
+        uint2 o;
+        o.x = (uint32_t)b0 | ((uint32_t)b1 << 16);
+        o.y = (uint32_t)b2 | ((uint32_t)b3 << 16);
+        *reinterpret_cast<uint2*>(p.out + (size_t)t * p.N + n) = o;
+        if (p.out16 != nullptr) {
+          typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+          h4 h;
+          h[0] = (f16)bf16_to_f32(b0);
+          h[1] = (f16)bf16_to_f32(b1);
+          h[2] = (f16)bf16_to_f32(b2);
+          h[3] = (f16)bf16_to_f32(b3);
+          *reinterpret_cast<h4*>(p.out16 + (size_t)t * p.N + n) = h;
+        }
+      }
+    }
+  }
+}
+
+// wt[n][k] = w[k][n] (bf16).  A wavefront moves one 64 x 64 block: lane
+// 8a + b the 8 x 8 sub-block at k = 8a, n = 8b, transposed in registers, so
+// that eight lanes read one 128-byte piece of a row of w and eight lanes
+// write one of wt.  (K % 64 == 0, N % 8 == 0.)
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ w, uint16_t* __restrict__ wt,
+                                                             int K, int N, int nbn, long long nblk) {
+  const long long blk = (long long)blockIdx.x * 4 + threadIdx.x / WAVE;
+  if (blk >= nblk) return;
+  const int lane = threadIdx.x % WAVE;
+  const int k = 64 * (int)(blk / nbn) + 8 * (lane / 8), n = 64 * (int)(blk % nbn) + 8 * (lane % 8);
+  if (n >= N) return;
+  uint4 rw[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) rw[i] = *reinterpret_cast<const uint4*>(w + (size_t)(k + i) * N + n);
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    // column j: (w[k][n+j], ..., w[k+7][n+j]); element j of a row is half j%2 of dword j/2
+    uint32_t col[4];
+#pragma unroll
+    for (int p2 = 0; p2 < 4; p2++) {
+      const uint32_t lo = (&rw[2 * p2].x)[j / 2], hi = (&rw[2 * p2 + 1].x)[j / 2];
+      col[p2] = (j & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+    }
+    *reinterpret_cast<uint4*>(wt + (size_t)(n + j) * K + k) = make_uint4(col[0], col[1], col[2], col[3]);
+  }
+}
+
 }  // namespace
+
+DensePlan dense_plan(int T, int K, int N) {
+  DensePlan d;
+  d.tiled = T >= DT_MIN_T && K >= DT_KC && K % DT_KC == 0 && N >= 8 && N % 8 == 0;
+  d.slabs = 1;
+  d.kslab = K;
+  if (!d.tiled) return d;
+  const long long tiles = (long long)((T + DT_M - 1) / DT_M) * ((N + DT_N - 1) / DT_N);
+  const int chunks = K / DT_KC;
+  int s = (int)((256 + tiles - 1) / tiles);  // at least one wave of 256 blocks
+  if (s > DT_MAX_SLABS) s = DT_MAX_SLABS;
+  if (s > chunks) s = chunks;
+  if (s < 1) s = 1;
+  const int per = (chunks + s - 1) / s;
+  d.kslab = per * DT_KC;
+  d.slabs = (chunks + per - 1) / per;
+  return d;
+}
+
+size_t dense_wt_bytes(const DensePlan& dp, int K, int N) { return dp.tiled ? (size_t)K * N * 2 : 0; }
+
+hipError_t launch_dense_tiled(const uint16_t* x, const uint16_t* w, uint16_t* wt, int T, int K, int N,
+                              const DensePlan& dp, float* part, uint16_t* out, f16* out16, f16* x16, hipStream_t s) {
+  if (!dp.tiled || wt == nullptr || (part == nullptr && (dp.slabs != 1 || out == nullptr))) return hipErrorInvalidValue;
+  const int nbn = (N + 63) / 64;
+  const long long nblk = (long long)(K / 64) * nbn;
+  hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)((nblk + 3) / 4)), dim3(256), 0, s, w, wt, K, N, nbn, nblk);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  DenseParams p;
+  p.x = reinterpret_cast<const unsigned char*>(x);
+  p.wt = reinterpret_cast<const unsigned char*>(wt);
+  p.part = part;
+  p.out = out;
+  p.out16 = out16;
+  p.x16 = x16;
+  p.T = T;
+  p.K = K;
+  p.N = N;
+  p.kslab = dp.kslab;
+  p.n_tt = (T + DT_M - 1) / DT_M;
+  p.n_ct = (N + DT_N - 1) / DT_N;
+  p.cg = 1;
+  for (int c = 8; c >= 1; c--)
+    if (p.n_ct % c == 0) {
+      p.cg = c;
+      break;
+    }
+  const long long items = (long long)dp.slabs * p.n_ct * p.n_tt;
+  if (items > (1LL << 30)) return hipErrorInvalidValue;
+  p.n_items = (int)items;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dense_tile_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          DT_LDS);
+  if (e != hipSuccess) return e;
+  const long long per_xcd = (items + 7) / 8;
+  hipLaunchKernelGGL(dense_tile_kernel, dim3((unsigned)(8 * per_xcd)), dim3(DT_WAVES * WAVE), DT_LDS, s, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_shared_hidden(const uint16_t* x, const uint16_t* w_gate_up, float* part, int T, int H, int count,
                                 int I, const RouterPlan& rp, uint16_t* h, hipStream_t s) {
@@ -93,8 +374,15 @@ hipError_t launch_shared_hidden(const uint16_t* x, const uint16_t* w_gate_up, fl
 }
 
 hipError_t launch_projection(const uint16_t* x, const uint16_t* w, float* part, int T, int K, int N,
-                             const RouterPlan& rp, uint16_t* out, f16* out16, hipStream_t s) {
-  hipError_t e = launch_router(x, w, part, T, K, N, rp, s);
+                             const RouterPlan& rp, uint16_t* out, f16* out16, hipStream_t s, uint16_t* wt) {
+  if (rp.tiled && rp.slabs == 1) {  // the tile writes the rounded output itself
+    DensePlan dp;
+    dp.tiled = true;
+    dp.slabs = 1;
+    dp.kslab = rp.slab_rows;
+    return launch_dense_tiled(x, w, wt, T, K, N, dp, nullptr, out, out16, nullptr, s);
+  }
+  hipError_t e = launch_router(x, w, part, T, K, N, rp, s, nullptr, wt);
   if (e != hipSuccess) return e;
   const long long n4 = (long long)T * N / 4;
   const long long blocks = (n4 + PROJ_THREADS - 1) / PROJ_THREADS;

@@ -979,8 +979,19 @@ constexpr int ROUTER_MFMA_MIN_T = 32;
 
 }  // namespace
 
-RouterPlan router_plan(int T, int H, int E) {
+RouterPlan router_plan(int T, int H, int E, bool tiled_ok) {
   RouterPlan p;
+  p.tiled = false;
+  if (tiled_ok) {
+    const DensePlan d = dense_plan(T, H, E);
+    if (d.tiled) {
+      p.mfma = true;
+      p.tiled = true;
+      p.slabs = d.slabs;
+      p.slab_rows = d.kslab;
+      return p;
+    }
+  }
   if (T >= ROUTER_MFMA_MIN_T) {
     // one wavefront per (128 experts, 64 tokens, K slab); aim for >= 2048
     // (eight per CU)
@@ -1014,7 +1025,14 @@ RouterPlan router_plan(int T, int H, int E) {
 }
 
 hipError_t launch_router(const uint16_t* x, const uint16_t* wr, float* part, int T, int H, int E,
-                         const RouterPlan& rp, hipStream_t s, f16* x16) {
+                         const RouterPlan& rp, hipStream_t s, f16* x16, uint16_t* wt) {
+  if (rp.tiled) {
+    DensePlan dp;
+    dp.tiled = true;
+    dp.slabs = rp.slabs;
+    dp.kslab = rp.slab_rows;
+    return launch_dense_tiled(x, wr, wt, T, H, E, dp, part, nullptr, nullptr, x16, s);
+  }
   if (rp.mfma) {
     const dim3 grid((E + RM_EXPERTS - 1) / RM_EXPERTS, (T + RM_TOKENS - 1) / RM_TOKENS, rp.slabs);
     hipLaunchKernelGGL(router_mfma_kernel, grid, dim3(WAVE), 0, s, x, wr, part, T, H, E, rp.slab_rows, x16);
