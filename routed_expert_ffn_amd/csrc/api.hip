@@ -224,7 +224,7 @@ LatentLayout latent_layout(const moe_dims& d, int Hm) {
 // partials, their hidden layer and their down partials.
 struct SharedLayout {
   Layout base;
-  size_t gupart, h, dpart, total;
+  size_t gupart, h, dpart, wt, total;
   int gu_slabs, d_slabs;
 };
 
@@ -239,11 +239,17 @@ SharedLayout shared_layout(const moe_dims& d, const moe_shared& sh) {
   };
   const int width = sh.count * sh.I;
   const size_t T = (size_t)d.T;
-  SL.gu_slabs = moe::router_plan(d.T, d.H, 2 * width).slabs;
-  SL.d_slabs = moe::router_plan(d.T, width, d.H).slabs;
+  const moe::RouterPlan gu = moe::router_plan(d.T, d.H, 2 * width, true), dn = moe::router_plan(d.T, width, d.H, true);
+  SL.gu_slabs = gu.slabs;
+  SL.d_slabs = dn.slabs;
   SL.gupart = take((size_t)SL.gu_slabs * T * 2 * width * 4);
   SL.h = take(T * width * 2);
   SL.dpart = take((size_t)SL.d_slabs * T * d.H * 4);
+  // the transposed weight of the tiled GEMMs (gate/up, then down, on the
+  // side stream; the router's own region is the base layout's)
+  size_t wt = gu.tiled ? (size_t)d.H * 2 * width * 2 : 0;
+  if (dn.tiled && (size_t)width * d.H * 2 > wt) wt = (size_t)width * d.H * 2;
+  SL.wt = take(wt);
   SL.total = o;
   return SL;
 }
@@ -750,11 +756,11 @@ moe_status moe_layer_shared(moe_dims d, const moe_shared* shared, const void* x,
   LAUNCH(MOE_KERNEL_SHARED, s2,
          moe::launch_shared_hidden(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(shared->w_gate_up),
                                    at<float>(ws, SL.gupart), T, H, shared->count, shared->I,
-                                   moe::router_plan(T, H, 2 * width), h, s2),
+                                   moe::router_plan(T, H, 2 * width, true), h, s2, at<uint16_t>(ws, SL.wt)),
          "shared experts, gate/up");
   LAUNCH(MOE_KERNEL_SHARED, s2,
          moe::launch_router(h, static_cast<const uint16_t*>(shared->w_down), dpart, T, width, H,
-                            moe::router_plan(T, width, H), s2),
+                            moe::router_plan(T, width, H, true), s2, nullptr, at<uint16_t>(ws, SL.wt)),
          "shared experts, down");
   TRY(enqueue_route(d, x, w_router, bias, at<float>(ws, L.logits), ids, wts, offsets, sorted, pos, ws,
                     at<f16>(ws, L.x16), s));

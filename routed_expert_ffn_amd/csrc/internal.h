@@ -140,9 +140,10 @@ hipError_t launch_projection(const uint16_t* x, const uint16_t* w, float* part, 
                              uint16_t* wt = nullptr);
 
 // Shared experts' hidden layer: h [T][count*I] bf16 from x [T][H] and the
-// gate/up weights [H][count*2I]; part holds rp.slabs * T * 2*count*I fp32.
+// gate/up weights [H][count*2I]; part holds rp.slabs * T * 2*count*I fp32,
+// wt the transposed weight of a tiled plan.
 hipError_t launch_shared_hidden(const uint16_t* x, const uint16_t* w_gate_up, float* part, int T, int H, int count,
-                                int I, const RouterPlan& rp, uint16_t* h, hipStream_t s);
+                                int I, const RouterPlan& rp, uint16_t* h, hipStream_t s, uint16_t* wt = nullptr);
 
 hipError_t launch_quantize(const float* w, int64_t N, int64_t K, uint8_t* q, uint8_t* sf, float* gs, uint32_t* ws,
                            hipStream_t s);

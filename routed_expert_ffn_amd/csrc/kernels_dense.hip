@@ -363,9 +363,9 @@ hipError_t launch_dense_tiled(const uint16_t* x, const uint16_t* w, uint16_t* wt
 }
 
 hipError_t launch_shared_hidden(const uint16_t* x, const uint16_t* w_gate_up, float* part, int T, int H, int count,
-                                int I, const RouterPlan& rp, uint16_t* h, hipStream_t s) {
+                                int I, const RouterPlan& rp, uint16_t* h, hipStream_t s, uint16_t* wt) {
   const int width = count * I;
-  hipError_t e = launch_router(x, w_gate_up, part, T, H, 2 * width, rp, s);
+  hipError_t e = launch_router(x, w_gate_up, part, T, H, 2 * width, rp, s, nullptr, wt);
   if (e != hipSuccess) return e;
   const long long n4 = (long long)T * width / 4;
   hipLaunchKernelGGL(swiglu_reduce_kernel, dim3((unsigned)((n4 + PROJ_THREADS - 1) / PROJ_THREADS)),
