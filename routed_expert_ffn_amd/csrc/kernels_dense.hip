@@ -120,6 +120,7 @@ static_assert(DT_LDS <= 160 * 1024, "LDS budget of one CU");
 static_assert(DT_X_INSTR == 4 * DT_WAVES && DT_W_INSTR <= 4 * DT_WAVES, "DMA instructions per wavefront");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 
 struct DenseParams {
   const unsigned char* x;   // [T][K] bf16
@@ -146,8 +147,14 @@ __device__ __forceinline__ void dt_dma16(const unsigned char* gbase, uint32_t vo
 }
 
 // All of this wavefront's vector-memory work (its DMA copies included) and
-// LDS reads are complete, then the block meets.
-__device__ __forceinline__ void dt_barrier() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// LDS reads are complete, then the block meets.  Builtins rather than inline
+// asm, so the compiler's own wait counting knows that every earlier LDS read
+// has landed (after an opaque asm wait it re-waits for them later, behind
+// newer reads).  The callers fence it with scheduling barriers.
+__device__ __forceinline__ void dt_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) expcnt(7) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
 
 __global__ __launch_bounds__(DT_WAVES * WAVE, 1) void dense_tile_kernel(DenseParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char dt_smem[];
@@ -205,41 +212,70 @@ __global__ __launch_bounds__(DT_WAVES * WAVE, 1) void dense_tile_kernel(DensePar
 #pragma unroll
     for (int f = 0; f < 4; f++) acc[j][f] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  issue(0);
-  for (int c = 0; c < nchunks; c++) {
-    dt_barrier();  // chunk c is in its stage; everyone is done with chunk c-1
-    if (c + 1 < nchunks) issue(c + 1);
+  // the fp16 copy of x: chunk c of a (token tile, slab) by column tile c % n_ct
+  auto copy_x16 = [&](int c) {
     const unsigned char* S = dt_smem + (c % 2) * DT_STAGE;
-    // the fp16 copy of x: chunk c of a (token tile, slab) by column tile c % n_ct
-    if (p.x16 != nullptr && c % p.n_ct == ct) {
 #pragma unroll
-      for (int h = 0; h < 4; h++) {
-        const int row = threadIdx.x / 2, q = 4 * (threadIdx.x % 2) + h;
-        const uint4 v = *reinterpret_cast<const uint4*>(S + row * DT_ROWB + 16 * (q ^ ((row / 2) % 8)));
-        if (t0 + row < p.T) {
-          f16x8 o;
-          o[0] = (f16)__uint_as_float(v.x << 16); o[1] = (f16)__uint_as_float(v.x & 0xFFFF0000u);
-          o[2] = (f16)__uint_as_float(v.y << 16); o[3] = (f16)__uint_as_float(v.y & 0xFFFF0000u);
-          o[4] = (f16)__uint_as_float(v.z << 16); o[5] = (f16)__uint_as_float(v.z & 0xFFFF0000u);
-          o[6] = (f16)__uint_as_float(v.w << 16); o[7] = (f16)__uint_as_float(v.w & 0xFFFF0000u);
-          *reinterpret_cast<f16x8*>(p.x16 + (size_t)(t0 + row) * p.K + k_begin + c * DT_KC + 8 * q) = o;
-        }
+    for (int h = 0; h < 4; h++) {
+      const int row = threadIdx.x / 2, q = 4 * (threadIdx.x % 2) + h;
+      const uint4 v = *reinterpret_cast<const uint4*>(S + row * DT_ROWB + 16 * (q ^ ((row / 2) % 8)));
+      if (t0 + row < p.T) {
+        f16x8 o;
+        o[0] = (f16)__uint_as_float(v.x << 16); o[1] = (f16)__uint_as_float(v.x & 0xFFFF0000u);
+        o[2] = (f16)__uint_as_float(v.y << 16); o[3] = (f16)__uint_as_float(v.y & 0xFFFF0000u);
+        o[4] = (f16)__uint_as_float(v.z << 16); o[5] = (f16)__uint_as_float(v.z & 0xFFFF0000u);
+        o[6] = (f16)__uint_as_float(v.w << 16); o[7] = (f16)__uint_as_float(v.w & 0xFFFF0000u);
+        *reinterpret_cast<f16x8*>(p.x16 + (size_t)(t0 + row) * p.K + k_begin + c * DT_KC + 8 * q) = o;
       }
     }
+  };
+  // (fragments are held as integer vectors: as __bf16 vectors the compiler
+  // repacks their halves when they cross the loop's back edge)
+  auto read_step = [&](int c, int s, u32x4v (&xa)[4], u32x4v (&wa)[7]) {
+    const unsigned char* S = dt_smem + (c % 2) * DT_STAGE;
 #pragma unroll
-    for (int s = 0; s < 2; s++) {
-      bf16x8 xa[4], wa[7];
+    for (int f = 0; f < 4; f++) xa[f] = *reinterpret_cast<const u32x4v*>(S + (xrow0 + 16 * f) * DT_ROWB + roff[s]);
+#pragma unroll
+    for (int j = 0; j < 7; j++)
+      wa[j] = *reinterpret_cast<const u32x4v*>(S + DT_X_BYTES + (wrow0 + 16 * j) * DT_ROWB + roff[s]);
+  };
+  auto mma_step = [&](const u32x4v (&xa)[4], const u32x4v (&wa)[7]) {
+#pragma unroll
+    for (int j = 0; j < 7; j++)
 #pragma unroll
       for (int f = 0; f < 4; f++)
-        xa[f] = *reinterpret_cast<const bf16x8*>(S + (xrow0 + 16 * f) * DT_ROWB + roff[s]);
-#pragma unroll
-      for (int j = 0; j < 7; j++)
-        wa[j] = *reinterpret_cast<const bf16x8*>(S + DT_X_BYTES + (wrow0 + 16 * j) * DT_ROWB + roff[s]);
-#pragma unroll
-      for (int j = 0; j < 7; j++)
-#pragma unroll
-        for (int f = 0; f < 4; f++) acc[j][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[j], xa[f], acc[j][f], 0, 0, 0);
+        acc[j][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wa[j]),
+                                                            __builtin_bit_cast(bf16x8, xa[f]), acc[j][f], 0, 0, 0);
+  };
+
+  // Software pipeline over chunks: the barrier of chunk c sits between its
+  // two steps.  Before it the wavefront has read all of chunk c (step 1's
+  // fragments are in registers), so after it chunk c's stage takes the
+  // copies of chunk c+2, and the wavefront reads chunk c+1's first
+  // fragments while step 1's MFMAs run; the copies of a chunk have one
+  // chunk's time to land.
+  issue(0);
+  if (nchunks > 1) issue(1);
+  __builtin_amdgcn_sched_barrier(0);
+  dt_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  if (p.x16 != nullptr && ct == 0) copy_x16(0);
+  u32x4v xa0[4], wa0[7], xa1[4], wa1[7];
+  read_step(0, 0, xa0, wa0);
+  for (int c = 0; c < nchunks; c++) {
+    read_step(c, 1, xa1, wa1);
+    mma_step(xa0, wa0);
+    // (the compiler would otherwise move the MFMAs, which touch no memory,
+    // past the barrier)
+    __builtin_amdgcn_sched_barrier(0);
+    dt_barrier();  // all reads of chunk c are done; chunk c+1 is in its stage
+    __builtin_amdgcn_sched_barrier(0);
+    if (c + 2 < nchunks) issue(c + 2);
+    if (c + 1 < nchunks) {
+      if (p.x16 != nullptr && (c + 1) % p.n_ct == ct) copy_x16(c + 1);
+      read_step(c + 1, 0, xa0, wa0);
     }
+    mma_step(xa1, wa1);
   }
 
   // D[4g+i][l%16] of product (j, f): column n0 + 112 wc + 16 j + 4 g + i of
