@@ -33,6 +33,8 @@ struct SideStream {
 std::mutex g_side_mu;
 SideStream g_side[SIDE_MAX_DEVICES];
 
+constexpr int SHARED_AFTER_ROUTE_T = 1024;
+
 class SideBranch {
  public:
   explicit SideBranch(hipStream_t main) : main_(main), lk_(g_side_mu) {
@@ -750,7 +752,14 @@ moe_status moe_layer_shared(moe_dims d, const moe_shared* shared, const void* x,
   uint16_t* h = at<uint16_t>(ws, SL.h);
   float* dpart = at<float>(ws, SL.dpart);
   // the shared experts on every token (hidden layer, then the down partials),
-  // on the side stream beside the routing and the routed experts
+  // on the side stream beside the routing and the routed experts.  From
+  // SHARED_AFTER_ROUTE_T tokens the branch forks after the routing: both
+  // branches are then compute-bound, and the shared GEMMs, started first,
+  // held every CU while the latency-bound routing kernels waited for one.
+  const bool route_first = T >= SHARED_AFTER_ROUTE_T;
+  if (route_first)
+    TRY(enqueue_route(d, x, w_router, bias, at<float>(ws, L.logits), ids, wts, offsets, sorted, pos, ws,
+                      at<f16>(ws, L.x16), s));
   SideBranch branch(s);
   const hipStream_t s2 = branch.stream();
   LAUNCH(MOE_KERNEL_SHARED, s2,
@@ -762,8 +771,9 @@ moe_status moe_layer_shared(moe_dims d, const moe_shared* shared, const void* x,
          moe::launch_router(h, static_cast<const uint16_t*>(shared->w_down), dpart, T, width, H,
                             moe::router_plan(T, width, H, true), s2, nullptr, at<uint16_t>(ws, SL.wt)),
          "shared experts, down");
-  TRY(enqueue_route(d, x, w_router, bias, at<float>(ws, L.logits), ids, wts, offsets, sorted, pos, ws,
-                    at<f16>(ws, L.x16), s));
+  if (!route_first)
+    TRY(enqueue_route(d, x, w_router, bias, at<float>(ws, L.logits), ids, wts, offsets, sorted, pos, ws,
+                      at<f16>(ws, L.x16), s));
   f16* rows16 = at<f16>(ws, L.rows);
   TRY(enqueue_ffn(d, offsets, sorted, w, rows, ws, s, 0, rows16, wts));
   if (hipError_t e = branch.join(); e != hipSuccess) return hip_fail(e, "join of the shared experts");
