@@ -181,6 +181,24 @@ def test_ragged_layer(T, E, k, beta):
     assert_close(y, ref["y"], "y")
 
 
+@pytest.mark.parametrize("T,H,E", [(1100, 512, 200), (2300, 1024, 456), (1030, 7168, 896)])
+def test_tiled_router_every_token(T, H, E):
+    """From 1024 tokens the router is the LDS-tiled GEMM (256-token x
+    224-column tiles over K slabs): every token's logits against the
+    oracle's, with a ragged last token tile (1100 = 4 x 256 + 76), column
+    tiles that are ragged or nearly empty (200 < 224; 456 = 2 x 224 + 8),
+    and K3's width with K slabs of unequal length (1030 tokens: twelve slabs
+    of nine 64-k chunks and one of four)."""
+    say(f"tiled router T={T} H={H} E={E}")
+    inp = Inputs(T, H, 256, E, 8, seed=21, store="unused")
+    r = inp.route()
+    ref = oracle.router_logits(inp.host_x(), inp.host_wr(), None)
+    err = np.abs(r["logits"] - ref)
+    say(f"  max |logit - oracle| = {err.max():.3e}")
+    assert err.max() <= LOGIT_ABS
+    check_route(inp, r)
+
+
 @pytest.mark.parametrize("T", [1, 3, 70, 1030])
 def test_largest_expert_count_and_k(T):
     """The largest shapes the routing takes: E = 1024 experts and k = 64
