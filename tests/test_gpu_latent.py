@@ -129,6 +129,24 @@ def test_latent_block_small(T, E, k):
     assert np.abs(w - ref["w"]).max() <= 1e-6
 
 
+def test_latent_block_one_slab_projections():
+    """8192 tokens at hidden 2048 -> latent 2048: both projections fill a
+    wave of 256 tiles (32 token tiles x 10 column tiles of 224), so each
+    takes one K slab and the tile writes the rounded bf16 output (and the
+    latent's fp16 copy for the experts) itself; every token of the first, a
+    middle and the last token tile, and 64 more, checked."""
+    T, Hm, H, I, E, k = 8192, 2048, 2048, 256, 32, 4
+    say(f"latent one-slab projections T={T} Hm={Hm} H={H}")
+    case = LatentCase(T, Hm, H, I, E, k, seed=23, router_std=0.1)
+    y, z, ids, w = case.run()
+    logits = case.logits()
+    rng = np.random.default_rng(5)
+    rows = np.array(sorted(set(range(256)) | set(range(3840, 4096)) | set(range(T - 256, T)) |
+                           set(rng.choice(T, size=64, replace=False))))
+    ox = OracleExperts(23, H, I)
+    compare(case, rows, y, z, ids, logits, ox.get(ids[rows]))
+
+
 def test_latent_block_deterministic():
     case = LatentCase(8, 1024, 512, 256, 64, 8, seed=22)
     a = case.run()
