@@ -85,11 +85,10 @@ __global__ __launch_bounds__(PROJ_THREADS) void swiglu_reduce_kernel(const float
 // A block computes a tile of DT_M tokens x DT_N output columns over one K
 // slab.  The weight is first transposed to wt [N][K] so both operands are
 // k-contiguous rows; each 64-k chunk of the tile's rows (128 bytes a row)
-// reaches LDS by LDS DMA, two stages: the copies of chunk c+1 are issued as
-// chunk c's multiply starts, into the stage that chunk c-1 held.  A 128-byte
-// row is 8 pieces of 16 bytes, piece q of row r stored in slot
-// q ^ ((r/2) % 8), so that the 16 rows one fragment read touches cover all
-// of LDS's banks.
+// reaches LDS by LDS DMA into one of two stages, two chunks ahead (the
+// software pipeline is described at the K loop).  A 128-byte row is 8 pieces
+// of 16 bytes, piece q of row r stored in slot q ^ ((r/2) % 8), so that the
+// 16 rows one fragment read touches cover all of LDS's banks.
 //
 // Eight wavefronts, 4 (tokens, 64 each) x 2 (columns, 112 each); wavefront
 // products are v_mfma_f32_16x16x32_bf16 with the weight rows as the A operand
