@@ -181,14 +181,17 @@ def test_ragged_layer(T, E, k, beta):
     assert_close(y, ref["y"], "y")
 
 
-@pytest.mark.parametrize("T,H,E", [(1100, 512, 200), (2300, 1024, 456), (1030, 7168, 896)])
+@pytest.mark.parametrize("T,H,E", [(1100, 512, 200), (2300, 1024, 456), (1030, 7168, 896), (1024, 256, 8),
+                                   (1279, 8448, 1024), (4096, 512, 224)])
 def test_tiled_router_every_token(T, H, E):
     """From 1024 tokens the router is the LDS-tiled GEMM (256-token x
     224-column tiles over K slabs): every token's logits against the
-    oracle's, with a ragged last token tile (1100 = 4 x 256 + 76), column
-    tiles that are ragged or nearly empty (200 < 224; 456 = 2 x 224 + 8),
-    and K3's width with K slabs of unequal length (1030 tokens: twelve slabs
-    of nine 64-k chunks and one of four)."""
+    oracle's, with a ragged last token tile (1100 = 4 x 256 + 76; 1279),
+    column tiles that are ragged or nearly empty (200 < 224; 456 = 2 x 224 +
+    8; 8 experts; 1024 = 4 x 224 + 128), exactly one column tile (224), K3's
+    width with K slabs of unequal length (1030 tokens: twelve slabs of nine
+    64-k chunks and one of four), the smallest K of four chunks (256) and
+    the largest hidden width the boundary tests (8448)."""
     say(f"tiled router T={T} H={H} E={E}")
     inp = Inputs(T, H, 256, E, 8, seed=21, store="unused")
     r = inp.route()
