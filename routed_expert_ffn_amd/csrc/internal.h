@@ -14,6 +14,7 @@ struct RouterPlan {
   bool mfma;   // bf16 matrix-core GEMM (larger T) or the VALU GEMV
   bool tiled;  // the LDS-tiled GEMM of large batches (needs a transposed-weight workspace)
   int slabs, slab_rows;
+  int e_tile;  // the GEMV's outputs per block
 };
 // tiled_ok: the caller provides the workspace for the tiled GEMM's
 // transposed weight (dense_wt_bytes), so large batches may take it.

@@ -14,29 +14,38 @@ namespace {
 
 // ---- router logits: 2-D tiled GEMV with slab partial sums ---------------------
 // logits[t][e] = sum_h x[t][h] * W_r[h][e], W_r stored [H][E] (E contiguous).
-// A block owns 128 experts (16 lanes x 8 experts, one 16-byte load per row)
-// and a slab of rows; lane l reads row 4*wave + l/16 of each 16-row step, so
-// one wavefront load covers four 256-byte row segments.  The 16 lanes that
-// share a column group are summed with two butterfly steps and then across
-// the four waves through LDS, in a fixed order, and the block writes one
-// partial per (slab, token, expert).  bf16 x bf16 products are exact in fp32.
+// A block owns ET experts (ET/8 lanes x 8 experts, one 16-byte load per row)
+// and a slab of rows; lane l reads row (64/(ET/8)) * wave + l/(ET/8) of each
+// step, so one wavefront load covers whole 2*ET-byte row segments.  The
+// lanes that share a column group are summed with butterfly steps and then
+// across the four waves through LDS, in a fixed order, and the block writes
+// one partial per (slab, token, expert).  bf16 x bf16 products are exact in
+// fp32.  ET = 128 for wide outputs; ET = 64 for a router's few hundred
+// experts, where twice the column tiles let half the K slabs fill the chip
+// (fewer partials for the single-block routing to add).
 constexpr int RT_THREADS = 256;
 constexpr int ROUTER_MAX_SLABS = 32;  // K slabs of the router, at most
 constexpr int RT_E_TILE = 128;
-constexpr int RT_ROWS_PER_STEP = 16;
+constexpr int RT_E_TILE_NARROW = 64;
+constexpr int RT_NARROW_MAX_E = 1024;  // outputs up to this width take the narrow tile
 constexpr int RT_BATCH = 16;  // weight rows per thread in flight
+// rows of W_r one step of a block covers (four wavefronts)
+constexpr int rt_rows_per_step(int et) { return 4 * (WAVE / (et / 8)); }
 
-template <int TT>
+template <int TT, int ET>
 __global__ __launch_bounds__(RT_THREADS) void router_gemv_kernel(const uint16_t* __restrict__ x,
                                                                 const uint16_t* __restrict__ wr,
                                                                 float* __restrict__ part, int T, int H, int E,
                                                                 int slab_rows, f16* __restrict__ x16) {
+  constexpr int CG = ET / 8;                   // column groups: lanes per row
+  constexpr int RPW = WAVE / CG;               // rows of a wavefront per step
+  constexpr int RPS = rt_rows_per_step(ET);    // rows of the block per step
   extern __shared__ float smem[];
   float* xs = smem;                               // [TT][slab_rows]
-  float* red = smem + TT * slab_rows;             // [4 waves][16 groups][TT * 8]
+  float* red = smem + TT * slab_rows;             // [4 waves][CG groups][TT * 8]
   const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE;
-  const int cg = lane % 16, rr = lane / 16;
-  const int e0 = blockIdx.x * RT_E_TILE + cg * 8;
+  const int cg = lane % CG, rr = lane / CG;
+  const int e0 = blockIdx.x * ET + cg * 8;
   const int h0 = blockIdx.y * slab_rows;
   const int t0 = blockIdx.z * TT;
   const int rows = min(slab_rows, H - h0);
@@ -49,11 +58,11 @@ __global__ __launch_bounds__(RT_THREADS) void router_gemv_kernel(const uint16_t*
   auto load_batch = [&](int r0) {
 #pragma unroll
     for (int b = 0; b < RT_BATCH; b++) {
-      const int r = r0 + b * RT_ROWS_PER_STEP;
+      const int r = r0 + b * RPS;
       w8[b] = r < rows ? *reinterpret_cast<const uint4*>(wr + (size_t)(h0 + r) * E + e0) : make_uint4(0, 0, 0, 0);
     }
   };
-  if (active) load_batch(4 * wv + rr);
+  if (active) load_batch(RPW * wv + rr);
   // the blocks of the first expert tile also write the fp16 copy of their
   // slab of x (bf16 -> fp32 exact, then the fp16 rounding)
   const bool cast = x16 != nullptr && blockIdx.x == 0;
@@ -70,11 +79,11 @@ __global__ __launch_bounds__(RT_THREADS) void router_gemv_kernel(const uint16_t*
 #pragma unroll
     for (int i = 0; i < 8; i++) acc[a][i] = 0.0f;
   if (active) {
-    for (int r0 = 4 * wv + rr; r0 < rows; r0 += RT_BATCH * RT_ROWS_PER_STEP) {
-      if (r0 != 4 * wv + rr) load_batch(r0);
+    for (int r0 = RPW * wv + rr; r0 < rows; r0 += RT_BATCH * RPS) {
+      if (r0 != RPW * wv + rr) load_batch(r0);
 #pragma unroll
       for (int b = 0; b < RT_BATCH; b++) {
-        const int r = r0 + b * RT_ROWS_PER_STEP;
+        const int r = r0 + b * RPS;
         if (r < rows) {
           float wf[8];
           wf[0] = __uint_as_float(w8[b].x << 16); wf[1] = __uint_as_float(w8[b].x & 0xFFFF0000u);
@@ -96,18 +105,18 @@ __global__ __launch_bounds__(RT_THREADS) void router_gemv_kernel(const uint16_t*
 #pragma unroll
     for (int i = 0; i < 8; i++) {
       float v = acc[a][i];
-      v += __shfl_xor(v, 16, WAVE);
-      v += __shfl_xor(v, 32, WAVE);
-      if (rr == 0) red[(wv * 16 + cg) * (TT * 8) + a * 8 + i] = v;
+#pragma unroll
+      for (int o = CG; o < WAVE; o *= 2) v += __shfl_xor(v, o, WAVE);
+      if (rr == 0) red[(wv * CG + cg) * (TT * 8) + a * 8 + i] = v;
     }
   __syncthreads();
-  for (int q = threadIdx.x; q < 16 * TT * 8; q += RT_THREADS) {
+  for (int q = threadIdx.x; q < CG * TT * 8; q += RT_THREADS) {
     const int g = q / (TT * 8), ai = q % (TT * 8), a = ai / 8, i = ai % 8;
-    const int e = blockIdx.x * RT_E_TILE + g * 8 + i;
+    const int e = blockIdx.x * ET + g * 8 + i;
     if (e < E && t0 + a < T) {
-      const float s = ((red[(0 * 16 + g) * (TT * 8) + ai] + red[(1 * 16 + g) * (TT * 8) + ai]) +
-                       red[(2 * 16 + g) * (TT * 8) + ai]) +
-                      red[(3 * 16 + g) * (TT * 8) + ai];
+      const float s = ((red[(0 * CG + g) * (TT * 8) + ai] + red[(1 * CG + g) * (TT * 8) + ai]) +
+                       red[(2 * CG + g) * (TT * 8) + ai]) +
+                      red[(3 * CG + g) * (TT * 8) + ai];
       part[((size_t)blockIdx.y * T + (t0 + a)) * E + e] = s;
     }
   }
@@ -982,6 +991,7 @@ constexpr int ROUTER_MFMA_MIN_T = 32;
 RouterPlan router_plan(int T, int H, int E, bool tiled_ok) {
   RouterPlan p;
   p.tiled = false;
+  p.e_tile = RT_E_TILE;
   if (tiled_ok) {
     const DensePlan d = dense_plan(T, H, E);
     if (d.tiled) {
@@ -1008,20 +1018,39 @@ RouterPlan router_plan(int T, int H, int E, bool tiled_ok) {
     return p;
   }
   const int tt = router_tt(T);
-  const int tiles = ((E + RT_E_TILE - 1) / RT_E_TILE) * ((T + tt - 1) / tt);
-  int s = 512 / (tiles > 0 ? tiles : 1);
+  // wide tiles: blocks for up to 512 (in practice the 32-slab cap); narrow
+  // tiles: about 256 blocks, one round of loads each, about half the slabs
+  const int et = E <= RT_NARROW_MAX_E ? RT_E_TILE_NARROW : RT_E_TILE, rps = rt_rows_per_step(et);
+  const int tiles = ((E + et - 1) / et) * ((T + tt - 1) / tt);
+  int s = et == RT_E_TILE ? 512 / (tiles > 0 ? tiles : 1) : (256 + tiles - 1) / (tiles > 0 ? tiles : 1);
   if (s > ROUTER_MAX_SLABS) s = ROUTER_MAX_SLABS;
-  const int steps = H / RT_ROWS_PER_STEP;
+  const int steps = H / rps;
   if (s > steps) s = steps;
   if (s < 1) s = 1;
   int steps_per_slab = (steps + s - 1) / s;
   // the block's activations slab lives in LDS: at most 64 KB
-  const int max_steps = 16384 / (tt * RT_ROWS_PER_STEP);
+  const int max_steps = 16384 / (tt * rps);
   if (steps_per_slab > max_steps) steps_per_slab = max_steps;
   p.mfma = false;
-  p.slab_rows = steps_per_slab * RT_ROWS_PER_STEP;
+  p.e_tile = et;
+  p.slab_rows = steps_per_slab * rps;
   p.slabs = (H + p.slab_rows - 1) / p.slab_rows;
   return p;
+}
+
+template <int ET>
+hipError_t launch_gemv(const uint16_t* x, const uint16_t* wr, float* part, int T, int H, int E, const RouterPlan& rp,
+                       hipStream_t s, f16* x16) {
+  const int tt = router_tt(T);
+  const dim3 grid((E + ET - 1) / ET, rp.slabs, (T + tt - 1) / tt);
+  const size_t lds = sizeof(float) * ((size_t)tt * rp.slab_rows + 4 * (ET / 8) * tt * 8);
+  switch (tt) {
+    case 1: hipLaunchKernelGGL((router_gemv_kernel<1, ET>), grid, dim3(RT_THREADS), lds, s, x, wr, part, T, H, E, rp.slab_rows, x16); break;
+    case 2: hipLaunchKernelGGL((router_gemv_kernel<2, ET>), grid, dim3(RT_THREADS), lds, s, x, wr, part, T, H, E, rp.slab_rows, x16); break;
+    case 4: hipLaunchKernelGGL((router_gemv_kernel<4, ET>), grid, dim3(RT_THREADS), lds, s, x, wr, part, T, H, E, rp.slab_rows, x16); break;
+    default: hipLaunchKernelGGL((router_gemv_kernel<8, ET>), grid, dim3(RT_THREADS), lds, s, x, wr, part, T, H, E, rp.slab_rows, x16); break;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_router(const uint16_t* x, const uint16_t* wr, float* part, int T, int H, int E,
@@ -1038,16 +1067,8 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* wr, float* part, int
     hipLaunchKernelGGL(router_mfma_kernel, grid, dim3(WAVE), 0, s, x, wr, part, T, H, E, rp.slab_rows, x16);
     return hipGetLastError();
   }
-  const int tt = router_tt(T);
-  const dim3 grid((E + RT_E_TILE - 1) / RT_E_TILE, rp.slabs, (T + tt - 1) / tt);
-  const size_t lds = sizeof(float) * ((size_t)tt * rp.slab_rows + 4 * 16 * tt * 8);
-  switch (tt) {
-    case 1: hipLaunchKernelGGL((router_gemv_kernel<1>), grid, dim3(RT_THREADS), lds, s, x, wr, part, T, H, E, rp.slab_rows, x16); break;
-    case 2: hipLaunchKernelGGL((router_gemv_kernel<2>), grid, dim3(RT_THREADS), lds, s, x, wr, part, T, H, E, rp.slab_rows, x16); break;
-    case 4: hipLaunchKernelGGL((router_gemv_kernel<4>), grid, dim3(RT_THREADS), lds, s, x, wr, part, T, H, E, rp.slab_rows, x16); break;
-    default: hipLaunchKernelGGL((router_gemv_kernel<8>), grid, dim3(RT_THREADS), lds, s, x, wr, part, T, H, E, rp.slab_rows, x16); break;
-  }
-  return hipGetLastError();
+  return rp.e_tile == RT_E_TILE_NARROW ? launch_gemv<RT_E_TILE_NARROW>(x, wr, part, T, H, E, rp, s, x16)
+                                        : launch_gemv<RT_E_TILE>(x, wr, part, T, H, E, rp, s, x16);
 }
 
 hipError_t launch_topk(const float* part, int slabs, const float* bias, float* logits, int T, int E, int k,
