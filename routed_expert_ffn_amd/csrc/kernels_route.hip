@@ -1019,10 +1019,10 @@ RouterPlan router_plan(int T, int H, int E, bool tiled_ok) {
   }
   const int tt = router_tt(T);
   // wide tiles: blocks for up to 512 (in practice the 32-slab cap); narrow
-  // tiles: about 256 blocks, one round of loads each, about half the slabs
+  // tiles: up to 256 blocks, one round of loads each, about half the slabs
   const int et = E <= RT_NARROW_MAX_E ? RT_E_TILE_NARROW : RT_E_TILE, rps = rt_rows_per_step(et);
   const int tiles = ((E + et - 1) / et) * ((T + tt - 1) / tt);
-  int s = et == RT_E_TILE ? 512 / (tiles > 0 ? tiles : 1) : (256 + tiles - 1) / (tiles > 0 ? tiles : 1);
+  int s = (et == RT_E_TILE ? 512 : 256) / (tiles > 0 ? tiles : 1);  // (narrow: at most one block per CU)
   if (s > ROUTER_MAX_SLABS) s = ROUTER_MAX_SLABS;
   const int steps = H / rps;
   if (s > steps) s = steps;
