@@ -380,8 +380,7 @@ const char* moe_last_error(void);
 /* ---- kernel timing for measurement ----------------------------------------
  * Kernels of the path, in launch order within moe_layer. */
 typedef enum {
-  MOE_KERNEL_ROUTER = 0,  /* router logits (K-slab partials; from T =    */
-                          /* 1024 also the transpose of w_router)      */
+  MOE_KERNEL_ROUTER = 0,  /* router logits (slab partials + reduction)   */
   MOE_KERNEL_TOPK = 1,    /* softmax + top-k; for T <= 8 one launch that  */
                           /* also permutes (nothing is then PERMUTE)     */
   MOE_KERNEL_PERMUTE = 2, /* histogram, scan and scatter (three kernels) */

@@ -148,8 +148,8 @@ size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 // Workspace regions (byte offsets, 256-byte aligned).  moe_layer uses all of
 // them; moe_route and moe_expert_ffn use subsets of the same layout.
 struct Layout {
-  size_t part, wt, logits, ids, w, lids, masks, counts, base, offsets, sorted, pos, active, nact, mtiles, nmt, x16,
-      h, rows, total;
+  size_t part, logits, ids, w, lids, masks, counts, base, offsets, sorted, pos, active, nact, mtiles, nmt, x16, h,
+      rows, total;
 };
 
 Layout layout(const moe_dims& d) {
@@ -161,10 +161,8 @@ Layout layout(const moe_dims& d) {
     return r;
   };
   const size_t T = (size_t)d.T, H = (size_t)d.H, I = (size_t)d.I, E = (size_t)d.E, P = T * (size_t)d.k;
-  const moe::RouterPlan rp = moe::router_plan(d.T, d.H, d.E, true);
-  const size_t S = (size_t)rp.slabs, nb = (size_t)moe::perm_blocks(d.T);
+  const size_t S = (size_t)moe::router_plan(d.T, d.H, d.E).slabs, nb = (size_t)moe::perm_blocks(d.T);
   L.part = take(S * T * E * 4);
-  L.wt = take(rp.tiled ? H * E * 2 : 0);  // the tiled router's transposed weight
   L.logits = take(T * E * 4);
   L.ids = take(P * 4);
   L.w = take(P * 4);
@@ -191,7 +189,7 @@ Layout layout(const moe_dims& d) {
 // latent z and the combined latent output.
 struct LatentLayout {
   Layout base;
-  size_t rpart, ppart, wt, z, ylat, total;
+  size_t rpart, ppart, z, ylat, total;
 };
 
 LatentLayout latent_layout(const moe_dims& d, int Hm) {
@@ -204,18 +202,13 @@ LatentLayout latent_layout(const moe_dims& d, int Hm) {
     return r;
   };
   const size_t T = (size_t)d.T, H = (size_t)d.H, E = (size_t)d.E, M = (size_t)Hm;
-  const moe::RouterPlan rr = moe::router_plan(d.T, Hm, d.E, true), rd = moe::router_plan(d.T, Hm, d.H, true),
-                        ru = moe::router_plan(d.T, d.H, Hm, true);
+  const moe::RouterPlan rr = moe::router_plan(d.T, Hm, d.E), rd = moe::router_plan(d.T, Hm, d.H),
+                        ru = moe::router_plan(d.T, d.H, Hm);
   LL.rpart = take((size_t)rr.slabs * T * E * 4);
   // a tiled projection of one slab writes its output directly
   const size_t down = rd.tiled && rd.slabs == 1 ? 0 : (size_t)rd.slabs * T * H * 4;
   const size_t up = ru.tiled && ru.slabs == 1 ? 0 : (size_t)ru.slabs * T * M * 4;
   LL.ppart = take(down > up ? down : up);
-  // the transposed weight of whichever of the three runs (one at a time, in order)
-  size_t wt = 0;
-  if (rr.tiled) wt = M * E * 2;
-  if (rd.tiled || ru.tiled) wt = wt > M * H * 2 ? wt : M * H * 2;
-  LL.wt = take(wt);
   LL.z = take(T * H * 2);
   LL.ylat = take(T * H * 2);
   LL.total = o;
@@ -226,7 +219,7 @@ LatentLayout latent_layout(const moe_dims& d, int Hm) {
 // partials, their hidden layer and their down partials.
 struct SharedLayout {
   Layout base;
-  size_t gupart, h, dpart, wt, total;
+  size_t gupart, h, dpart, total;
   int gu_slabs, d_slabs;
 };
 
@@ -241,17 +234,12 @@ SharedLayout shared_layout(const moe_dims& d, const moe_shared& sh) {
   };
   const int width = sh.count * sh.I;
   const size_t T = (size_t)d.T;
-  const moe::RouterPlan gu = moe::router_plan(d.T, d.H, 2 * width, true), dn = moe::router_plan(d.T, width, d.H, true);
+  const moe::RouterPlan gu = moe::router_plan(d.T, d.H, 2 * width), dn = moe::router_plan(d.T, width, d.H);
   SL.gu_slabs = gu.slabs;
   SL.d_slabs = dn.slabs;
   SL.gupart = take((size_t)SL.gu_slabs * T * 2 * width * 4);
   SL.h = take(T * width * 2);
   SL.dpart = take((size_t)SL.d_slabs * T * d.H * 4);
-  // the transposed weight of the tiled GEMMs (gate/up, then down, on the
-  // side stream; the router's own region is the base layout's)
-  size_t wt = gu.tiled ? (size_t)d.H * 2 * width * 2 : 0;
-  if (dn.tiled && (size_t)width * d.H * 2 > wt) wt = (size_t)width * d.H * 2;
-  SL.wt = take(wt);
   SL.total = o;
   return SL;
 }
@@ -322,11 +310,11 @@ moe_status enqueue_route(const moe_dims& d, const void* x, const void* wr, const
                          int32_t* ids, float* w, int32_t* offsets, int32_t* sorted, int32_t* pos, void* ws,
                          f16* x16, hipStream_t s) {
   const Layout L = layout(d);
-  const moe::RouterPlan rp = moe::router_plan(d.T, d.H, d.E, true);
+  const moe::RouterPlan rp = moe::router_plan(d.T, d.H, d.E);
   if (x)
     LAUNCH(MOE_KERNEL_ROUTER, s,
            moe::launch_router(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wr),
-                              at<float>(ws, L.part), d.T, d.H, d.E, rp, s, x16, at<uint16_t>(ws, L.wt)),
+                              at<float>(ws, L.part), d.T, d.H, d.E, rp, s, x16),
            "router");
   if (moe::route_fused(d.T)) {  // top-k and permutation in one launch, timed as top-k
     LAUNCH(MOE_KERNEL_TOPK, s,
@@ -583,10 +571,10 @@ moe_status moe_layer_mapped(moe_dims d, const int32_t* expert_map, int32_t n_loc
   // routing over all E experts (the router also writes the fp16 copy of x);
   // the single-launch routing of small batches also permutes over all E,
   // which the local permutation below replaces
-  const moe::RouterPlan rp = moe::router_plan(T, d.H, E, true);
+  const moe::RouterPlan rp = moe::router_plan(T, d.H, E);
   LAUNCH(MOE_KERNEL_ROUTER, s,
          moe::launch_router(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router),
-                            at<float>(ws, L.part), T, d.H, E, rp, s, at<f16>(ws, L.x16), at<uint16_t>(ws, L.wt)),
+                            at<float>(ws, L.part), T, d.H, E, rp, s, at<f16>(ws, L.x16)),
          "router");
   if (moe::route_fused(T))
     LAUNCH(MOE_KERNEL_TOPK, s,
@@ -765,11 +753,11 @@ moe_status moe_layer_shared(moe_dims d, const moe_shared* shared, const void* x,
   LAUNCH(MOE_KERNEL_SHARED, s2,
          moe::launch_shared_hidden(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(shared->w_gate_up),
                                    at<float>(ws, SL.gupart), T, H, shared->count, shared->I,
-                                   moe::router_plan(T, H, 2 * width, true), h, s2, at<uint16_t>(ws, SL.wt)),
+                                   moe::router_plan(T, H, 2 * width), h, s2),
          "shared experts, gate/up");
   LAUNCH(MOE_KERNEL_SHARED, s2,
          moe::launch_router(h, static_cast<const uint16_t*>(shared->w_down), dpart, T, width, H,
-                            moe::router_plan(T, width, H, true), s2, nullptr, at<uint16_t>(ws, SL.wt)),
+                            moe::router_plan(T, width, H), s2),
          "shared experts, down");
   if (!route_first)
     TRY(enqueue_route(d, x, w_router, bias, at<float>(ws, L.logits), ids, wts, offsets, sorted, pos, ws,
@@ -822,18 +810,17 @@ moe_status moe_latent_layer(moe_dims d, const moe_latent* lat, const void* x, co
   float* rpart = at<float>(ws, LL.rpart);
   float* ppart = at<float>(ws, LL.ppart);
   // router on the hidden state
-  uint16_t* wt = at<uint16_t>(ws, LL.wt);
-  const moe::RouterPlan rp = moe::router_plan(T, Hm, E, true);
+  const moe::RouterPlan rp = moe::router_plan(T, Hm, E);
   LAUNCH(MOE_KERNEL_ROUTER, s,
          moe::launch_router(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router), rpart, T, Hm, E,
-                            rp, s, nullptr, wt),
+                            rp, s),
          "router");
   // routed-down projection: the latent in bf16 and its fp16 copy for the
   // experts.  (Beside the routing on the side stream it was slower: the
   // experts need it at once, so the join's latency is on the critical path.)
   LAUNCH(MOE_KERNEL_PROJECT, s,
          moe::launch_projection(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(lat->w_down), ppart, T,
-                                Hm, H, moe::router_plan(T, Hm, H, true), z, x16, s, wt),
+                                Hm, H, moe::router_plan(T, Hm, H), z, x16, s),
          "routed-down projection");
   // top-k and permutation on the router's partials (x16 is already in place)
   if (moe::route_fused(T)) {
@@ -857,7 +844,7 @@ moe_status moe_latent_layer(moe_dims d, const moe_latent* lat, const void* x, co
   // routed-up projection back to the hidden width
   LAUNCH(MOE_KERNEL_PROJECT, s,
          moe::launch_projection(ylat, static_cast<const uint16_t*>(lat->w_up), ppart, T, H, Hm,
-                                moe::router_plan(T, H, Hm, true), static_cast<uint16_t*>(y), nullptr, s, wt),
+                                moe::router_plan(T, H, Hm), static_cast<uint16_t*>(y), nullptr, s),
          "routed-up projection");
   return MOE_OK;
 }

@@ -12,28 +12,24 @@ namespace moe {
 // The router's partial sums over H: slabs of slab_rows rows each.
 struct RouterPlan {
   bool mfma;   // bf16 matrix-core GEMM (larger T) or the VALU GEMV
-  bool tiled;  // the LDS-tiled GEMM of large batches (needs a transposed-weight workspace)
+  bool tiled;  // the LDS-tiled GEMM of large batches
   int slabs, slab_rows;
   int e_tile;  // the GEMV's outputs per block
 };
-// tiled_ok: the caller provides the workspace for the tiled GEMM's
-// transposed weight (dense_wt_bytes), so large batches may take it.
-RouterPlan router_plan(int T, int H, int E, bool tiled_ok = false);
+RouterPlan router_plan(int T, int H, int E);
 
 // The LDS-tiled bf16 GEMM of large batches: x [T][K] . w [K][N] (w
-// input-major) over `slabs` K slabs of kslab rows, after w is transposed into
-// wt [N][K] (dense_wt_bytes of workspace).  Writes the fp32 slab partials
-// part [slab][T][N]; or, with part NULL and one slab, out [T][N] bf16 and,
-// when non-NULL, its fp16 copy out16.  x16, when non-NULL, receives the fp16
-// copy of x.
+// input-major, read as stored) over `slabs` K slabs of kslab rows.  Writes
+// the fp32 slab partials part [slab][T][N]; or, with part NULL and one slab,
+// out [T][N] bf16 and, when non-NULL, its fp16 copy out16.  x16, when
+// non-NULL, receives the fp16 copy of x.
 struct DensePlan {
   bool tiled;
   int slabs, kslab;
 };
 DensePlan dense_plan(int T, int K, int N);
-size_t dense_wt_bytes(const DensePlan& dp, int K, int N);
-hipError_t launch_dense_tiled(const uint16_t* x, const uint16_t* w, uint16_t* wt, int T, int K, int N,
-                              const DensePlan& dp, float* part, uint16_t* out, f16* out16, f16* x16, hipStream_t s);
+hipError_t launch_dense_tiled(const uint16_t* x, const uint16_t* w, int T, int K, int N, const DensePlan& dp,
+                              float* part, uint16_t* out, f16* out16, f16* x16, hipStream_t s);
 // The permutation works on blocks of 64 tokens (one wavefront each).
 inline int perm_blocks(int T) { return (T + 63) / 64; }
 // Largest number of distinct experts that T tokens can select.
@@ -47,10 +43,9 @@ void prof_before(moe_kernel k, hipStream_t s);
 void prof_after(moe_kernel k, hipStream_t s);
 
 // Launchers.  Each enqueues on `s` and returns hipGetLastError().
-// With x16 non-NULL the router also writes the fp16 copy of x [T][H]; wt
-// is the transposed-weight workspace of a tiled plan.
+// With x16 non-NULL the router also writes the fp16 copy of x [T][H].
 hipError_t launch_router(const uint16_t* x, const uint16_t* wr, float* part, int T, int H, int E,
-                         const RouterPlan& rp, hipStream_t s, f16* x16 = nullptr, uint16_t* wt = nullptr);
+                         const RouterPlan& rp, hipStream_t s, f16* x16 = nullptr);
 // Sums the slab partials (part may be NULL: logits are then an input), adds
 // the bias, and selects the top k with their softmax weights.
 hipError_t launch_topk(const float* part, int slabs, const float* bias, float* logits, int T, int E, int k,
@@ -135,16 +130,14 @@ hipError_t launch_mfma_rate(int iters, float* sink, hipStream_t s);
 
 // x [T][K] . w [K][N] (bf16, input-major) into out [T][N] bf16 and, if
 // out16 is non-NULL, its fp16 copy; part holds rp.slabs * T * N fp32 (unused
-// by a tiled plan of one slab), wt the transposed weight of a tiled plan.
+// by a tiled plan of one slab).
 hipError_t launch_projection(const uint16_t* x, const uint16_t* w, float* part, int T, int K, int N,
-                             const RouterPlan& rp, uint16_t* out, f16* out16, hipStream_t s,
-                             uint16_t* wt = nullptr);
+                             const RouterPlan& rp, uint16_t* out, f16* out16, hipStream_t s);
 
 // Shared experts' hidden layer: h [T][count*I] bf16 from x [T][H] and the
-// gate/up weights [H][count*2I]; part holds rp.slabs * T * 2*count*I fp32,
-// wt the transposed weight of a tiled plan.
+// gate/up weights [H][count*2I]; part holds rp.slabs * T * 2*count*I fp32.
 hipError_t launch_shared_hidden(const uint16_t* x, const uint16_t* w_gate_up, float* part, int T, int H, int count,
-                                int I, const RouterPlan& rp, uint16_t* h, hipStream_t s, uint16_t* wt = nullptr);
+                                int I, const RouterPlan& rp, uint16_t* h, hipStream_t s);
 
 hipError_t launch_quantize(const float* w, int64_t N, int64_t K, uint8_t* q, uint8_t* sf, float* gs, uint32_t* ws,
                            hipStream_t s);

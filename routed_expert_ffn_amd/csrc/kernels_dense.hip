@@ -83,12 +83,23 @@ __global__ __launch_bounds__(PROJ_THREADS) void swiglu_reduce_kernel(const float
 
 // ---- LDS-tiled bf16 GEMM of large batches ----------------------------------------
 // A block computes a tile of DT_M tokens x DT_N output columns over one K
-// slab.  The weight is first transposed to wt [N][K] so both operands are
-// k-contiguous rows; each 64-k chunk of the tile's rows (128 bytes a row)
-// reaches LDS by LDS DMA into one of two stages, two chunks ahead (the
-// software pipeline is described at the K loop).  A 128-byte row is 8 pieces
-// of 16 bytes, piece q of row r stored in slot q ^ ((r/2) % 8), so that the
-// 16 rows one fragment read touches cover all of LDS's banks.
+// slab.  Each 64-k chunk of both operands reaches LDS by LDS DMA into one of
+// two stages, two chunks ahead (the software pipeline is described at the K
+// loop):
+//   tokens: 128 bytes (64 k) of each of the tile's rows of x, a row being 8
+//           pieces of 16 bytes, piece q of row r in slot q ^ ((r/2) % 8), so
+//           that the 16 rows one fragment read touches cover all banks;
+//   weights: the chunk's 64 rows of W [K][N] as stored, DT_N columns each
+//           (448 bytes a row).  The matrix cores want 8 consecutive k of one
+//           column per lane: ds_read_b64_tr_b16 gives them, since among 16
+//           lanes, lane 4r + c passing the address of row k0 + r, columns
+//           n0 + 4c .. n0 + 4c + 3 hands lane i the values of rows
+//           k0 .. k0 + 3 in column n0 + i; two such reads make a fragment.
+//           So W is never transposed in memory.  LDS serves such reads 32
+//           lanes at a time, and lanes 16 apart read rows 8 apart, which
+//           fall on the same banks (a row is 112 dwords): rows r with
+//           (r/8) odd hold their two 112-column halves swapped, which puts
+//           those rows' reads on the other half of the banks.
 //
 // Eight wavefronts, 4 (tokens, 64 each) x 2 (columns, 112 each); wavefront
 // products are v_mfma_f32_16x16x32_bf16 with the weight rows as the A operand
@@ -108,22 +119,25 @@ constexpr int DT_KC = 64;
 constexpr int DT_WAVES = 8;
 constexpr int DT_ROWB = DT_KC * 2;                 // bytes of a row's chunk
 constexpr int DT_X_BYTES = DT_M * DT_ROWB;         // token rows of one chunk
-constexpr int DT_W_BYTES = DT_N * DT_ROWB;         // weight rows of one chunk
+constexpr int DT_W_ROWB = DT_N * 2;                // bytes of a weight row (k) of one chunk
+constexpr int DT_W_BYTES = DT_KC * DT_W_ROWB;      // weight rows of one chunk
 constexpr int DT_STAGE = DT_X_BYTES + DT_W_BYTES;
 constexpr int DT_LDS = 2 * DT_STAGE;
 constexpr int DT_X_INSTR = DT_M / 8;  // DMA instructions (8 rows each) per chunk
-constexpr int DT_W_INSTR = DT_N / 8;
+constexpr int DT_W_INSTR = DT_W_BYTES / 1024;
 constexpr int DT_MIN_T = 1024;
 constexpr int DT_MAX_SLABS = 16;
 static_assert(DT_LDS <= 160 * 1024, "LDS budget of one CU");
+static_assert(DT_W_BYTES % 1024 == 0 && DT_W_ROWB % 16 == 0, "weight chunk of whole DMA instructions and pieces");
 static_assert(DT_X_INSTR == 4 * DT_WAVES && DT_W_INSTR <= 4 * DT_WAVES, "DMA instructions per wavefront");
+static_assert(DT_N == 2 * 112 && DT_W_ROWB % 32 == 0, "two column halves of 112, swapped as whole 16-byte pieces");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 
 struct DenseParams {
   const unsigned char* x;   // [T][K] bf16
-  const unsigned char* wt;  // [N][K] bf16
+  const unsigned char* w;   // [K][N] bf16
   float* part;              // [slabs][T][N] fp32, or NULL
   uint16_t* out;            // [T][N] bf16 (one slab, part NULL)
   f16* out16;               // fp16 copy of out, or NULL
@@ -172,24 +186,30 @@ __global__ __launch_bounds__(DT_WAVES * WAVE, 1) void dense_tile_kernel(DensePar
 
   const int lane = threadIdx.x % WAVE, w = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
   const size_t row_bytes = (size_t)p.K * 2;
-  // DMA: instruction i (rows 8i .. 8i+7 of the token or weight rows) of
-  // wavefront w is i = w + 8m; lane l copies row 8i + l/8, piece
-  // (l%8) ^ ((row/2)%8) into slot l%8.  Rows past T (N) repeat the last one.
+  // DMA: instruction i of wavefront w is i = w + 8m.  Tokens: rows 8i ..
+  // 8i+7, lane l copying row 8i + l/8, piece (l%8) ^ ((row/2)%8) into slot
+  // l%8 (rows past T repeat the last one).  Weights: bytes 1024i .. of the
+  // [64][DT_N] chunk, lane l the 16 bytes at 1024i + 16l (columns past N
+  // repeat the last eight).
   const unsigned char* xb = p.x + (size_t)t0 * row_bytes + 2 * (size_t)k_begin;
-  const unsigned char* wb = p.wt + (size_t)n0 * row_bytes + 2 * (size_t)k_begin;
+  const size_t wrow_bytes = (size_t)p.N * 2;
+  const unsigned char* wb = p.w + (size_t)k_begin * wrow_bytes + 2 * (size_t)n0;
   uint32_t xoff[4], woff[4];
 #pragma unroll
   for (int m = 0; m < 4; m++) {
     const int row = 8 * (w + 8 * m) + lane / 8;
     const uint32_t piece = (uint32_t)((lane % 8) ^ ((row / 2) % 8));
     xoff[m] = (uint32_t)(min(t0 + row, p.T - 1) - t0) * (uint32_t)row_bytes + 16 * piece;
-    woff[m] = (uint32_t)(min(n0 + row, p.N - 1) - n0) * (uint32_t)row_bytes + 16 * piece;
+    const int off = 1024 * (w + 8 * m) + 16 * lane, krow = off / DT_W_ROWB;
+    const int slot = (off % DT_W_ROWB) / 16;                                       // 16-byte slot in the row
+    const int wpiece = (krow / 8) % 2 ? (slot + DT_W_ROWB / 32) % (DT_W_ROWB / 16) : slot;  // the halves swapped
+    woff[m] = (uint32_t)krow * (uint32_t)wrow_bytes + 2u * (uint32_t)(min(n0 + 8 * wpiece, p.N - 8) - n0);
   }
   const uint32_t lds0 = dt_lds_addr(dt_smem);
   auto issue = [&](int c) {
     const uint32_t st = lds0 + (uint32_t)((c % 2) * DT_STAGE);
     const unsigned char* xc = xb + (size_t)c * DT_ROWB;
-    const unsigned char* wc = wb + (size_t)c * DT_ROWB;
+    const unsigned char* wc = wb + (size_t)c * DT_KC * wrow_bytes;
 #pragma unroll
     for (int m = 0; m < 4; m++) dt_dma16(xc, xoff[m], st + 1024 * (w + 8 * m));
 #pragma unroll
@@ -197,13 +217,22 @@ __global__ __launch_bounds__(DT_WAVES * WAVE, 1) void dense_tile_kernel(DensePar
       if (w + 8 * m < DT_W_INSTR) dt_dma16(wc, woff[m], st + DT_X_BYTES + 1024 * (w + 8 * m));
   };
 
-  // fragment reads: row 16 f + l%16 of a 16-row group, piece 4s + l/16
+  // fragment reads: tokens, row 16 f + l%16 of a 16-row group, piece
+  // 4s + l/16; weights, two transposing reads of rows 32s + 8g + 4h + r
+  // (h = 0, 1), columns 16 j + 4c .. of this wavefront's (r = (l%16)/4,
+  // c = l%4), whose half is swapped where (row/8) = g is odd
   const int rl = lane % 16, g = lane / 16;
-  int roff[2];
-#pragma unroll
-  for (int s = 0; s < 2; s++) roff[s] = rl * DT_ROWB + 16 * ((4 * s + g) ^ (rl / 2));
   const int wr = w % 4, wc = w / 4;
   const int xrow0 = 64 * wr, wrow0 = 112 * wc;
+  const int half_swap = (g % 2) ? (wc ? -DT_W_ROWB / 2 : DT_W_ROWB / 2) : 0;
+  int roff[2], wtro[2][2];
+#pragma unroll
+  for (int s = 0; s < 2; s++) {
+    roff[s] = rl * DT_ROWB + 16 * ((4 * s + g) ^ (rl / 2));
+#pragma unroll
+    for (int h = 0; h < 2; h++)
+      wtro[s][h] = (32 * s + 8 * g + 4 * h + rl / 4) * DT_W_ROWB + 2 * 4 * (rl % 4) + half_swap;
+  }
 
   f32x4 acc[7][4];
 #pragma unroll
@@ -235,8 +264,15 @@ __global__ __launch_bounds__(DT_WAVES * WAVE, 1) void dense_tile_kernel(DensePar
 #pragma unroll
     for (int f = 0; f < 4; f++) xa[f] = *reinterpret_cast<const u32x4v*>(S + (xrow0 + 16 * f) * DT_ROWB + roff[s]);
 #pragma unroll
-    for (int j = 0; j < 7; j++)
-      wa[j] = *reinterpret_cast<const u32x4v*>(S + DT_X_BYTES + (wrow0 + 16 * j) * DT_ROWB + roff[s]);
+    for (int j = 0; j < 7; j++) {
+      typedef short s16x4 __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+      const unsigned char* base = S + DT_X_BYTES + 2 * (wrow0 + 16 * j);
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + wtro[s][0]));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + wtro[s][1]));
+      const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+      wa[j] = u32x4v{l2.x, l2.y, h2.x, h2.y};
+    }
   };
   auto mma_step = [&](const u32x4v (&xa)[4], const u32x4v (&wa)[7]) {
 #pragma unroll
@@ -310,33 +346,6 @@ __global__ __launch_bounds__(DT_WAVES * WAVE, 1) void dense_tile_kernel(DensePar
   }
 }
 
-// wt[n][k] = w[k][n] (bf16).  A wavefront moves one 64 x 64 block: lane
-// 8a + b the 8 x 8 sub-block at k = 8a, n = 8b, transposed in registers, so
-// that eight lanes read one 128-byte piece of a row of w and eight lanes
-// write one of wt.  (K % 64 == 0, N % 8 == 0.)
-__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ w, uint16_t* __restrict__ wt,
-                                                             int K, int N, int nbn, long long nblk) {
-  const long long blk = (long long)blockIdx.x * 4 + threadIdx.x / WAVE;
-  if (blk >= nblk) return;
-  const int lane = threadIdx.x % WAVE;
-  const int k = 64 * (int)(blk / nbn) + 8 * (lane / 8), n = 64 * (int)(blk % nbn) + 8 * (lane % 8);
-  if (n >= N) return;
-  uint4 rw[8];
-#pragma unroll
-  for (int i = 0; i < 8; i++) rw[i] = *reinterpret_cast<const uint4*>(w + (size_t)(k + i) * N + n);
-#pragma unroll
-  for (int j = 0; j < 8; j++) {
-    // column j: (w[k][n+j], ..., w[k+7][n+j]); element j of a row is half j%2 of dword j/2
-    uint32_t col[4];
-#pragma unroll
-    for (int p2 = 0; p2 < 4; p2++) {
-      const uint32_t lo = (&rw[2 * p2].x)[j / 2], hi = (&rw[2 * p2 + 1].x)[j / 2];
-      col[p2] = (j & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
-    }
-    *reinterpret_cast<uint4*>(wt + (size_t)(n + j) * K + k) = make_uint4(col[0], col[1], col[2], col[3]);
-  }
-}
-
 }  // namespace
 
 DensePlan dense_plan(int T, int K, int N) {
@@ -357,19 +366,12 @@ DensePlan dense_plan(int T, int K, int N) {
   return d;
 }
 
-size_t dense_wt_bytes(const DensePlan& dp, int K, int N) { return dp.tiled ? (size_t)K * N * 2 : 0; }
-
-hipError_t launch_dense_tiled(const uint16_t* x, const uint16_t* w, uint16_t* wt, int T, int K, int N,
-                              const DensePlan& dp, float* part, uint16_t* out, f16* out16, f16* x16, hipStream_t s) {
-  if (!dp.tiled || wt == nullptr || (part == nullptr && (dp.slabs != 1 || out == nullptr))) return hipErrorInvalidValue;
-  const int nbn = (N + 63) / 64;
-  const long long nblk = (long long)(K / 64) * nbn;
-  hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)((nblk + 3) / 4)), dim3(256), 0, s, w, wt, K, N, nbn, nblk);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+hipError_t launch_dense_tiled(const uint16_t* x, const uint16_t* w, int T, int K, int N, const DensePlan& dp,
+                              float* part, uint16_t* out, f16* out16, f16* x16, hipStream_t s) {
+  if (!dp.tiled || (part == nullptr && (dp.slabs != 1 || out == nullptr))) return hipErrorInvalidValue;
   DenseParams p;
   p.x = reinterpret_cast<const unsigned char*>(x);
-  p.wt = reinterpret_cast<const unsigned char*>(wt);
+  p.w = reinterpret_cast<const unsigned char*>(w);
   p.part = part;
   p.out = out;
   p.out16 = out16;
@@ -389,8 +391,8 @@ hipError_t launch_dense_tiled(const uint16_t* x, const uint16_t* w, uint16_t* wt
   const long long items = (long long)dp.slabs * p.n_ct * p.n_tt;
   if (items > (1LL << 30)) return hipErrorInvalidValue;
   p.n_items = (int)items;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dense_tile_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                          DT_LDS);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dense_tile_kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, DT_LDS);
   if (e != hipSuccess) return e;
   const long long per_xcd = (items + 7) / 8;
   hipLaunchKernelGGL(dense_tile_kernel, dim3((unsigned)(8 * per_xcd)), dim3(DT_WAVES * WAVE), DT_LDS, s, p);
@@ -398,9 +400,9 @@ hipError_t launch_dense_tiled(const uint16_t* x, const uint16_t* w, uint16_t* wt
 }
 
 hipError_t launch_shared_hidden(const uint16_t* x, const uint16_t* w_gate_up, float* part, int T, int H, int count,
-                                int I, const RouterPlan& rp, uint16_t* h, hipStream_t s, uint16_t* wt) {
+                                int I, const RouterPlan& rp, uint16_t* h, hipStream_t s) {
   const int width = count * I;
-  hipError_t e = launch_router(x, w_gate_up, part, T, H, 2 * width, rp, s, nullptr, wt);
+  hipError_t e = launch_router(x, w_gate_up, part, T, H, 2 * width, rp, s);
   if (e != hipSuccess) return e;
   const long long n4 = (long long)T * width / 4;
   hipLaunchKernelGGL(swiglu_reduce_kernel, dim3((unsigned)((n4 + PROJ_THREADS - 1) / PROJ_THREADS)),
@@ -409,15 +411,15 @@ hipError_t launch_shared_hidden(const uint16_t* x, const uint16_t* w_gate_up, fl
 }
 
 hipError_t launch_projection(const uint16_t* x, const uint16_t* w, float* part, int T, int K, int N,
-                             const RouterPlan& rp, uint16_t* out, f16* out16, hipStream_t s, uint16_t* wt) {
+                             const RouterPlan& rp, uint16_t* out, f16* out16, hipStream_t s) {
   if (rp.tiled && rp.slabs == 1) {  // the tile writes the rounded output itself
     DensePlan dp;
     dp.tiled = true;
     dp.slabs = 1;
     dp.kslab = rp.slab_rows;
-    return launch_dense_tiled(x, w, wt, T, K, N, dp, nullptr, out, out16, nullptr, s);
+    return launch_dense_tiled(x, w, T, K, N, dp, nullptr, out, out16, nullptr, s);
   }
-  hipError_t e = launch_router(x, w, part, T, K, N, rp, s, nullptr, wt);
+  hipError_t e = launch_router(x, w, part, T, K, N, rp, s);
   if (e != hipSuccess) return e;
   const long long n4 = (long long)T * N / 4;
   const long long blocks = (n4 + PROJ_THREADS - 1) / PROJ_THREADS;

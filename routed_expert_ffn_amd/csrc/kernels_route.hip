@@ -988,11 +988,11 @@ constexpr int ROUTER_MFMA_MIN_T = 32;
 
 }  // namespace
 
-RouterPlan router_plan(int T, int H, int E, bool tiled_ok) {
+RouterPlan router_plan(int T, int H, int E) {
   RouterPlan p;
   p.tiled = false;
   p.e_tile = RT_E_TILE;
-  if (tiled_ok) {
+  {
     const DensePlan d = dense_plan(T, H, E);
     if (d.tiled) {
       p.mfma = true;
@@ -1054,13 +1054,13 @@ hipError_t launch_gemv(const uint16_t* x, const uint16_t* wr, float* part, int T
 }
 
 hipError_t launch_router(const uint16_t* x, const uint16_t* wr, float* part, int T, int H, int E,
-                         const RouterPlan& rp, hipStream_t s, f16* x16, uint16_t* wt) {
+                         const RouterPlan& rp, hipStream_t s, f16* x16) {
   if (rp.tiled) {
     DensePlan dp;
     dp.tiled = true;
     dp.slabs = rp.slabs;
     dp.kslab = rp.slab_rows;
-    return launch_dense_tiled(x, wr, wt, T, H, E, dp, part, nullptr, nullptr, x16, s);
+    return launch_dense_tiled(x, wr, T, H, E, dp, part, nullptr, nullptr, x16, s);
   }
   if (rp.mfma) {
     const dim3 grid((E + RM_EXPERTS - 1) / RM_EXPERTS, (T + RM_TOKENS - 1) / RM_TOKENS, rp.slabs);
