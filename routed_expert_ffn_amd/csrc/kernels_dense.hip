@@ -20,7 +20,8 @@
 // bf16 matrix-core GEMM compute K-slab partial sums in fp32, and one more
 // kernel adds the slabs in a fixed order and rounds to bf16 (and, for the
 // latent that feeds the experts, also writes its exact fp16 copy).  Large
-// batches (and the router itself there): the LDS-tiled GEMM below.
+// batches (and the router itself there): the LDS-tiled GEMM below, which
+// writes the rounded output directly when one K slab fills the chip.
 #include "internal.h"
 
 namespace moe {
@@ -102,10 +103,10 @@ __global__ __launch_bounds__(PROJ_THREADS) void swiglu_reduce_kernel(const float
 //           those rows' reads on the other half of the banks.
 //
 // Eight wavefronts, 4 (tokens, 64 each) x 2 (columns, 112 each); wavefront
-// products are v_mfma_f32_16x16x32_bf16 with the weight rows as the A operand
-// and the tokens as B, so a lane's four accumulators are four consecutive
-// output columns of one token.  Inside a chunk, step s (32 k) of lane group
-// g = lane/16 covers piece 4s + g of both operands.
+// products are v_mfma_f32_16x16x32_bf16 with the weight columns as the A
+// operand and the tokens as B, so a lane's four accumulators are four
+// consecutive output columns of one token.  Inside a chunk, step s (32 k) of
+// lane group g = lane/16 covers k = 32s + 8g .. + 7 of both operands.
 //
 // Tiles: DT_N = 224 divides the widths of a K3-shaped layer (896 router
 // columns, 3584 latent, 7168 hidden), and a prefill chunk of 8192 tokens
